@@ -1,0 +1,225 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle for the INT4 group-quantized
+ * weight-only linear layer (W4A16) and its greedy-verify epilogue.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or helper with the HIP library: every decode below is written
+ * out here from the IEEE-754 and packing definitions.
+ *
+ * What is computed (sources, all about arXiv 2607.04244 "Quantize the Target,
+ * Quantize the Drafter: Efficient Inference with Qwen3.5-4B"):
+ *   - the target is served on an AWQ INT4 grid whose per-group scales are
+ *     frozen, and weights are re-packed onto that same grid, so packing and
+ *     serving stay as they were (Pith review, Referee Report: Summary and
+ *     Significance; Assumptions: "Freezing the original AWQ per-group scales");
+ *   - the drafter is group-wise INT4 with group size 128 (Pith review,
+ *     Assumptions & free parameters: "GPTQ group size for drafter = 128");
+ *   - speculative decoding with a correct verifier is lossless: draft tokens
+ *     are kept while they equal the target's greedy choice (Pith review,
+ *     Assumptions: "Speculative decoding with a correct verifier is
+ *     lossless"; mlsanity index page, Abstract).
+ * The pages print no formula, layout or worked example.  The readings used
+ * (all stated again at each function):
+ *   W[n,k] = (q[n,k] - z[n,g]) * s[n,g],  g = floor(k / group)
+ *   Y[m,n] = sum_k X[m,k] * W[n,k]
+ *   q packed 8 per uint32 along K, nibble j of word w holds k = 8w + j
+ *   (low nibble first); z packed 8 per uint32 along N the same way;
+ *   s is IEEE binary16, X is bfloat16 (upper half of an IEEE binary32).
+ *
+ * Everything here is fp64 with naive loops in index order: no blocking, no
+ * reordering, no fusion.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- exact decoders ---------------------------------------------------- */
+
+/* bfloat16 is the upper 16 bits of an IEEE-754 binary32: widen and convert. */
+double oracle_bf16_to_f64(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* IEEE-754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * Normal: (-1)^s * 2^(e-15) * (1 + f/1024); subnormal: (-1)^s * 2^-14 * f/1024. */
+double oracle_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int f = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
+
+/* ---- packing (the grid in memory) -------------------------------------- */
+
+/* Pack codes u8[N][K] (values 0..15; higher bits ignored) into
+ * qweight u32[N][K/8]: nibble j (bits 4j..4j+3) of word w of row n holds
+ * code (n, 8w + j).  Pack zeros u8[N][G] into qzeros u32[N/8][G]: nibble j of
+ * word (r, g) holds the zero of row 8r + j, group g.
+ * Reading: "packed 8 per uint32 along K" in the plainest order. */
+void oracle_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K, int group,
+                 uint32_t *qweight, uint32_t *qzeros)
+{
+    int G = K / group;
+    int KW = K / 8;
+    for (int n = 0; n < N; ++n)
+        for (int w = 0; w < KW; ++w) {
+            uint32_t word = 0;
+            for (int j = 0; j < 8; ++j)
+                word |= (uint32_t)(codes[(size_t)n * K + 8 * w + j] & 15u) << (4 * j);
+            qweight[(size_t)n * KW + w] = word;
+        }
+    for (int r = 0; r < N / 8; ++r)
+        for (int g = 0; g < G; ++g) {
+            uint32_t word = 0;
+            for (int j = 0; j < 8; ++j)
+                word |= (uint32_t)(zeros[(size_t)(8 * r + j) * G + g] & 15u) << (4 * j);
+            qzeros[(size_t)r * G + g] = word;
+        }
+}
+
+/* Inverse of oracle_pack. */
+void oracle_unpack(const uint32_t *qweight, const uint32_t *qzeros, int N, int K, int group,
+                   uint8_t *codes, uint8_t *zeros)
+{
+    int G = K / group;
+    int KW = K / 8;
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k)
+            codes[(size_t)n * K + k] =
+                (uint8_t)((qweight[(size_t)n * KW + k / 8] >> (4 * (k % 8))) & 15u);
+    for (int n = 0; n < N; ++n)
+        for (int g = 0; g < G; ++g)
+            zeros[(size_t)n * G + g] =
+                (uint8_t)((qzeros[(size_t)(n / 8) * G + g] >> (4 * (n % 8))) & 15u);
+}
+
+/* ---- the linear layer --------------------------------------------------- */
+
+/* code q[n,k], read straight from the packed word */
+static inline int q_at(const uint32_t *qweight, int K, int n, int k)
+{
+    return (int)((qweight[(size_t)n * (K / 8) + k / 8] >> (4 * (k % 8))) & 15u);
+}
+
+/* zero z[n,g], read straight from the packed word */
+static inline int z_at(const uint32_t *qzeros, int G, int n, int g)
+{
+    return (int)((qzeros[(size_t)(n / 8) * G + g] >> (4 * (n % 8))) & 15u);
+}
+
+/* Dequantize row n of the weight: W[n,k] = (q - z) * s for the group of k.
+ * Exact in fp64: a small integer times an 11-bit significand. */
+static void dequant_row(const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+                        int n, int K, int group, double *w)
+{
+    int G = K / group;
+    for (int k = 0; k < K; ++k) {
+        int g = k / group;
+        int q = q_at(qweight, K, n, k);
+        int z = z_at(qzeros, G, n, g);
+        double s = oracle_f16_to_f64(scales[(size_t)n * G + g]);
+        w[k] = (double)(q - z) * s;
+    }
+}
+
+/* Y[m,n] = sum_{k ascending} X[m,k] * W[n,k], fp64, full output Y f64[M][N].
+ * X is bf16 bits [M][K] row-major, scales fp16 bits [N][K/group]. */
+void oracle_linear_f64(const uint16_t *X, const uint32_t *qweight, const uint16_t *scales,
+                       const uint32_t *qzeros, int M, int N, int K, int group, double *Y)
+{
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(static)
+        for (int n = 0; n < N; ++n) {
+            dequant_row(qweight, scales, qzeros, n, K, group, w);
+            for (int m = 0; m < M; ++m) {
+                double acc = 0.0;
+                for (int k = 0; k < K; ++k)
+                    acc += oracle_bf16_to_f64(X[(size_t)m * K + k]) * w[k];
+                Y[(size_t)m * N + n] = acc;
+            }
+        }
+        free(w);
+    }
+}
+
+/* The same definition evaluated only at the listed (row, col) pairs:
+ * out[i] = Y[rows[i], cols[i]].  Used where the full product is too large. */
+void oracle_linear_at(const uint16_t *X, const uint32_t *qweight, const uint16_t *scales,
+                      const uint32_t *qzeros, int M, int N, int K, int group,
+                      const int32_t *rows, const int32_t *cols, int count, double *out)
+{
+    (void)M;
+    (void)N;
+    int G = K / group;
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < count; ++i) {
+        int m = rows[i], n = cols[i];
+        double acc = 0.0;
+        for (int k = 0; k < K; ++k) {
+            int g = k / group;
+            double w = (double)(q_at(qweight, K, n, k) - z_at(qzeros, G, n, g)) *
+                       oracle_f16_to_f64(scales[(size_t)n * G + g]);
+            acc += oracle_bf16_to_f64(X[(size_t)m * K + k]) * w;
+        }
+        out[i] = acc;
+    }
+}
+
+/* ---- greedy verification ------------------------------------------------ */
+
+/* For each row m of logits Y f64[M][N]:
+ *   argmax[m] = the smallest n attaining max_n Y[m,n];
+ *   gap[m]    = that maximum minus the largest logit at any other column
+ *               (+inf when N == 1).
+ * accept_len = the number of leading rows i with argmax[i] == draft[i]
+ * (the lossless greedy verifier keeps draft tokens until the first one the
+ * target would not have chosen). */
+void oracle_argmax_accept(const double *Y, int M, int N, const int32_t *draft,
+                          int32_t *argmax, double *gap, int32_t *accept_len)
+{
+    for (int m = 0; m < M; ++m) {
+        const double *row = Y + (size_t)m * N;
+        int best = 0;
+        for (int n = 1; n < N; ++n)
+            if (row[n] > row[best])
+                best = n;
+        double second = -INFINITY;
+        for (int n = 0; n < N; ++n)
+            if (n != best && row[n] > second)
+                second = row[n];
+        argmax[m] = best;
+        gap[m] = row[best] - second;
+    }
+    int L = 0;
+    while (L < M && argmax[L] == draft[L])
+        ++L;
+    *accept_len = L;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

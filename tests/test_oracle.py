@@ -1,0 +1,326 @@
+"""Pins for the fp64 CPU oracle, against facts that do not come from the oracle.
+
+Each pin is chosen so that a plausible mistake in the oracle fails it:
+  decode pins      bf16/fp16 bit patterns with textbook values and the library casts
+  layout goldens   hand-worked packed words (nibble order along K, zeros along N)
+  one-hot X        Y picks one weight: catches a transposed operand, a wrong group
+                   index, a wrong zero/scale lookup, a sign error
+  equal codes      closed form s*(c - z)*rowsum(X) per group: catches a dropped zero
+                   term or scale
+  dyadic exact     integer X and power-of-two scales: Y is exact, checked with
+                   Python integers
+  plain matmul     z = 0, s = 1 reduces to X @ codes^T (numpy)
+  brute force      exact rationals on tiny shapes
+  by hand          a one-group example worked out on paper
+  permutation      permuting weight rows permutes Y columns bit-exactly
+  verify goldens   hand-worked argmax / accepted-prefix cases, ties to the lowest id
+  statistics       rms(Y) of the synthetic workloads against its closed form
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _f16(bits):
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def _bf16(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_bf16_decode_textbook_values():
+    cases = {0x3F80: 1.0, 0xC000: -2.0, 0x4049: 3.140625, 0x0000: 0.0, 0x8000: -0.0,
+             0x0001: 2.0 ** -133, 0x0080: 2.0 ** -126, 0x7F7F: (2 - 2 ** -7) * 2.0 ** 127,
+             0x4300: 128.0, 0x430F: 143.0}
+    for bits, v in cases.items():
+        assert oracle.bf16_to_f64(bits) == v, hex(bits)
+
+
+def test_f16_decode_textbook_values():
+    cases = {0x3C00: 1.0, 0xC000: -2.0, 0x0001: 2.0 ** -24, 0x03FF: 1023 * 2.0 ** -24,
+             0x0400: 2.0 ** -14, 0x7BFF: 65504.0, 0x3555: 0.333251953125, 0x1C00: 2.0 ** -8}
+    for bits, v in cases.items():
+        assert oracle.f16_to_f64(bits) == v, hex(bits)
+    assert math.isinf(oracle.f16_to_f64(0x7C00)) and math.isnan(oracle.f16_to_f64(0x7E00))
+
+
+def test_decoders_match_library_casts_on_all_patterns():
+    # fp16 through numpy's binary16, bf16 through numpy's binary32 view
+    rng = np.random.default_rng(5)
+    for bits in list(rng.integers(0, 65536, 3000)) + [0, 1, 0x3FF, 0x400, 0x7BFF, 0x8001]:
+        f = _f16(bits)
+        if not np.isnan(f):
+            assert oracle.f16_to_f64(bits) == f
+        b = _bf16(bits)
+        if not np.isnan(b):
+            assert oracle.bf16_to_f64(bits) == b
+
+
+# ---------------------------------------------------------------- packing
+
+def _read_pack_golden():
+    qw, qz = {}, {}
+    with open(os.path.join(GOLDEN, "pack_layout.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].split()
+            if not line:
+                continue
+            kind, a, b, v = line[0], int(line[1]), int(line[2]), int(line[3], 16)
+            (qw if kind == "qweight" else qz)[(a, b)] = v
+    return qw, qz
+
+
+def test_pack_layout_golden():
+    N, K = 8, 128
+    n = np.arange(N)[:, None]
+    k = np.arange(K)[None, :]
+    codes = ((n + k) % 16).astype(np.uint8)
+    zeros = ((np.arange(N) + 1) % 16).astype(np.uint8)[:, None]
+    qweight, qzeros = oracle.pack(codes, zeros)
+    gw, gz = _read_pack_golden()
+    assert gw and gz
+    for (r, w), v in gw.items():
+        assert int(qweight[r, w]) == v, (r, w, hex(int(qweight[r, w])), hex(v))
+    for (r, g), v in gz.items():
+        assert int(qzeros[r, g]) == v
+
+
+@pytest.mark.parametrize("N,K", [(8, 128), (24, 384), (64, 1024)])
+def test_pack_roundtrip_and_masking(N, K):
+    rng = np.random.default_rng(N + K)
+    codes = rng.integers(0, 256, size=(N, K), dtype=np.uint8)  # high bits must be ignored
+    zeros = rng.integers(0, 256, size=(N, K // 128), dtype=np.uint8)
+    qw, qz = oracle.pack(codes, zeros)
+    c2, z2 = oracle.unpack(qw, qz, N, K)
+    assert (c2 == (codes & 15)).all() and (z2 == (zeros & 15)).all()
+    qw2, qz2 = oracle.pack(codes & 15, zeros & 15)
+    assert (qw2 == qw).all() and (qz2 == qz).all()
+
+
+# ---------------------------------------------------------------- the linear
+
+def _rand_grid(rng, N, K):
+    G = K // 128
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    zeros = rng.integers(0, 16, size=(N, G), dtype=np.uint8)
+    scales = synth.f32_to_f16_bits(rng.uniform(0.002, 0.02, size=(N, G)).astype(np.float32))
+    return codes, zeros, scales
+
+
+def test_linear_worked_by_hand():
+    N, K = 8, 128
+    n = np.arange(N)[:, None]
+    k = np.arange(K)[None, :]
+    codes = ((n + k) % 16).astype(np.uint8)
+    zeros = np.arange(N, dtype=np.uint8)[:, None]
+    scales = synth.f32_to_f16_bits((2.0 ** -np.arange(N, dtype=np.float32))[:, None])
+    X = np.zeros((1, K), np.float32)
+    X[0, 0], X[0, 1], X[0, 127] = 1.0, 2.0, -1.0
+    qw, qz = oracle.pack(codes, zeros)
+    Y = oracle.linear(synth.f32_to_bf16_bits(X), qw, scales, qz)
+    expect = {}
+    with open(os.path.join(GOLDEN, "linear_by_hand.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].split()
+            if line:
+                expect[int(line[0])] = float(line[1])
+    assert len(expect) == N
+    for col, v in expect.items():
+        assert Y[0, col] == v
+
+
+def test_onehot_picks_one_weight():
+    rng = np.random.default_rng(11)
+    N, K = 40, 512
+    codes, zeros, scales = _rand_grid(rng, N, K)
+    ks = np.array([0, 1, 7, 8, 127, 128, 200, 255, 256, 383, 384, 511])
+    X = np.zeros((len(ks), K), np.float32)
+    X[np.arange(len(ks)), ks] = 1.0
+    qw, qz = oracle.pack(codes, zeros)
+    Y = oracle.linear(synth.f32_to_bf16_bits(X), qw, scales, qz)
+    s = _f16(scales)
+    for m, kk in enumerate(ks):
+        g = kk // 128
+        expect = (codes[:, kk].astype(np.float64) - zeros[:, g]) * s[:, g]
+        assert (Y[m] == expect).all(), (m, kk)
+
+
+def test_equal_codes_closed_form():
+    # codes all equal c: Y[m,n] = sum_g s[n,g] * (c - z[n,g]) * sum_{k in g} X[m,k]
+    rng = np.random.default_rng(12)
+    N, K, M = 16, 640, 3
+    G = K // 128
+    for c in (0, 9, 15):
+        codes = np.full((N, K), c, np.uint8)
+        zeros = rng.integers(0, 16, size=(N, G), dtype=np.uint8)
+        scales = synth.f32_to_f16_bits(rng.uniform(0.002, 0.02, size=(N, G)).astype(np.float32))
+        Xb = synth.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+        qw, qz = oracle.pack(codes, zeros)
+        Y = oracle.linear(Xb, qw, scales, qz)
+        x = _bf16(Xb)
+        s = _f16(scales)
+        for m in range(M):
+            S = [math.fsum(x[m, 128 * g:128 * (g + 1)]) for g in range(G)]
+            for n in range(N):
+                ex = math.fsum(s[n, g] * (c - int(zeros[n, g])) * S[g] for g in range(G))
+                assert abs(Y[m, n] - ex) <= 1e-12 * (1 + abs(ex))
+        # c == z everywhere: exactly zero
+        qw, qz = oracle.pack(codes, np.full((N, G), c, np.uint8))
+        assert (oracle.linear(Xb, qw, scales, qz) == 0).all()
+
+
+def test_dyadic_inputs_exact():
+    # X integers in [-8, 8], s = 2^-e: every product is a multiple of 2^-9 and fp64 is exact.
+    rng = np.random.default_rng(13)
+    M, N, K = 3, 24, 384
+    G = K // 128
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    zeros = rng.integers(0, 16, size=(N, G), dtype=np.uint8)
+    e = rng.integers(6, 10, size=(N, G))
+    scales = synth.f32_to_f16_bits((2.0 ** -e).astype(np.float32))
+    Xi = rng.integers(-8, 9, size=(M, K))
+    qw, qz = oracle.pack(codes, zeros)
+    Y = oracle.linear(synth.f32_to_bf16_bits(Xi.astype(np.float32)), qw, scales, qz)
+    for m in range(M):
+        for n in range(N):
+            tot = 0  # in units of 2^-9
+            for kk in range(K):
+                g = kk // 128
+                tot += int(Xi[m, kk]) * (int(codes[n, kk]) - int(zeros[n, g])) * (1 << (9 - int(e[n, g])))
+            assert Y[m, n] == tot / 512.0
+
+
+def test_reduces_to_plain_matmul():
+    # zero-points 0 and scales 1.0: Y = X @ codes^T
+    rng = np.random.default_rng(14)
+    M, N, K = 4, 32, 768
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    zeros = np.zeros((N, K // 128), np.uint8)
+    scales = np.full((N, K // 128), 0x3C00, np.uint16)
+    Xb = synth.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    qw, qz = oracle.pack(codes, zeros)
+    Y = oracle.linear(Xb, qw, scales, qz)
+    ref = _bf16(Xb) @ codes.T.astype(np.float64)
+    assert np.allclose(Y, ref, rtol=1e-13, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_brute_force_exact_rationals(seed):
+    rng = np.random.default_rng(100 + seed)
+    M, N, K = 2, 16, 256
+    G = K // 128
+    codes, zeros, scales = _rand_grid(rng, N, K)
+    Xb = synth.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    qw, qz = oracle.pack(codes, zeros)
+    Y = oracle.linear(Xb, qw, scales, qz)
+    x = _bf16(Xb)
+    s = _f16(scales)
+    for m in range(M):
+        for n in range(N):
+            exact = Fraction(0)
+            mag = 0.0
+            for kk in range(K):
+                g = kk // 128
+                t = Fraction(float(x[m, kk])) * (int(codes[n, kk]) - int(zeros[n, g])) * Fraction(float(s[n, g]))
+                exact += t
+                mag += abs(float(t))
+            assert abs(Fraction(float(Y[m, n])) - exact) <= Fraction(1e-12) * Fraction(mag)
+
+
+def test_weight_row_permutation_permutes_columns():
+    rng = np.random.default_rng(15)
+    M, N, K = 5, 48, 384
+    codes, zeros, scales = _rand_grid(rng, N, K)
+    Xb = synth.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    perm = rng.permutation(N)
+    qw, qz = oracle.pack(codes, zeros)
+    qwp, qzp = oracle.pack(codes[perm], zeros[perm])
+    Y = oracle.linear(Xb, qw, scales, qz)
+    Yp = oracle.linear(Xb, qwp, scales[perm], qzp)
+    assert (Yp == Y[:, perm]).all()
+    rp = rng.permutation(M)
+    assert (oracle.linear(Xb[rp], qw, scales, qz) == Y[rp]).all()
+
+
+def test_linear_at_is_the_same_definition():
+    d = synth.linear_inputs(21, 3, 64, 512)
+    qw, qz = oracle.pack(d["codes"], d["zeros"])
+    Y = oracle.linear(d["X"], qw, d["scales"], qz)
+    rng = np.random.default_rng(0)
+    rows = rng.integers(0, 3, 50)
+    cols = rng.integers(0, 64, 50)
+    assert (oracle.linear_at(d["X"], qw, d["scales"], qz, rows, cols) == Y[rows, cols]).all()
+
+
+# ---------------------------------------------------------------- verification
+
+def _read_verify_cases():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "verify_cases.txt")) as f:
+        for line in f:
+            t = line.split("#")[0].split()
+            if not t:
+                continue
+            if t[0] == "case":
+                cur = {"name": t[1], "rows": []}
+                cases.append(cur)
+            elif t[0] == "row":
+                cur["rows"].append([float(v) for v in t[1:]])
+            elif t[0] == "draft":
+                cur["draft"] = [int(v) for v in t[1:]]
+            elif t[0] == "expect_argmax":
+                cur["argmax"] = [int(v) for v in t[1:]]
+            elif t[0] == "expect_accept":
+                cur["accept"] = int(t[1])
+    return cases
+
+
+def test_verify_golden_cases():
+    cases = _read_verify_cases()
+    assert len(cases) == 4
+    for c in cases:
+        am, gap, L = oracle.argmax_accept(np.array(c["rows"]), np.array(c["draft"]))
+        assert list(am) == c["argmax"], c["name"]
+        assert L == c["accept"], c["name"]
+        for r, row in enumerate(c["rows"]):
+            srt = sorted(row, reverse=True)
+            assert gap[r] == srt[0] - srt[1]
+
+
+def test_forced_prefix_gives_exact_accept_length():
+    rng = np.random.default_rng(3)
+    M, N = 16, 1000
+    Y = rng.standard_normal((M, N))
+    am, _, _ = oracle.argmax_accept(Y, np.zeros(M, np.int32))
+    for L0 in (0, 1, 7, 15, 16):
+        draft, _, r2 = synth.draft_block(L0, M, N)
+        d = synth.force_prefix(draft, L0, am, r2, N)
+        assert oracle.argmax_accept(Y, d)[2] == L0
+
+
+# ---------------------------------------------------------------- generator
+
+@pytest.mark.parametrize("K", [512, 2560])
+def test_generator_rms_matches_closed_form(K):
+    # E[s^2] for s ~ U[0.002, 0.02) and E[(q-z)^2] = 2 * Var(U{0..15}) = 42.5
+    es2 = (0.02 ** 3 - 0.002 ** 3) / (3 * 0.018)
+    expect = math.sqrt(K * es2 * 42.5)
+    d = synth.linear_inputs(31, 8, 512, K)
+    qw, qz = oracle.pack(d["codes"], d["zeros"])
+    Y = oracle.linear(d["X"], qw, d["scales"], qz)
+    rms = float(np.sqrt((Y ** 2).mean()))
+    assert abs(rms / expect - 1) < 0.06, (rms, expect)
+    assert (d["codes"] < 16).all() and (d["zeros"] < 16).all()
+    s = _f16(d["scales"])
+    assert s.min() >= 0.002 - 1e-6 and s.max() <= 0.02 + 1e-5
