@@ -1,0 +1,148 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) INT4 group-quantized weight-only
+ * linear layer: 4-bit weights on a per-group scale/zero-point grid, bf16
+ * activations, fp32 accumulation.
+ *
+ * The method (arXiv 2607.04244, "Quantize the Target, Quantize the Drafter:
+ * Efficient Inference with Qwen3.5-4B"): the target model is served from an
+ * AWQ INT4 checkpoint whose per-group scales stay frozen, so its weights are
+ * re-packed onto the same grid and packing and serving are unchanged (Pith
+ * review, Referee Report: Summary and Significance; Assumptions & free
+ * parameters: frozen AWQ per-group scales).  The drafter is group-wise INT4
+ * with group size 128 (Pith review, free parameters: GPTQ group size 128).
+ * Each speculative step verifies a block of 16 draft tokens with a greedy,
+ * lossless verifier (Pith review, free parameters: block size 16;
+ * Assumptions: a correct verifier is lossless; mlsanity index page, Abstract).
+ *
+ * Definitions (the pages print no formula; these are the plainest readings):
+ *   G = K / group                        (group must be 128)
+ *   q[n,k] = (qweight[n*(K/8) + k/8] >> (4*(k%8))) & 15
+ *   z[n,g] = (qzeros[(n/8)*G + g]   >> (4*(n%8))) & 15
+ *   s[n,g] = scales[n*G + g]                         (IEEE binary16)
+ *   W[n,k] = (q[n,k] - z[n, k/group]) * s[n, k/group]
+ *   Y[m,n] = sum_k X[m,k] * W[n,k]                   (X bfloat16, fp32 accumulation)
+ *
+ * Conventions shared by every call:
+ *   - Every pointer is device memory owned by the caller (HIP device
+ *     allocations, e.g. torch tensors).  The library never allocates, frees or
+ *     synchronizes; it only enqueues kernels on `stream` (a hipStream_t; NULL
+ *     means the default stream).  Inputs are read-only; outputs must not
+ *     alias inputs or each other.
+ *   - bf16 and fp16 values cross the ABI as raw 16-bit patterns.
+ *   - All arguments are checked on the host before anything is enqueued; on
+ *     an error nothing is enqueued, nothing is printed, and the status code is
+ *     returned.  A failed kernel launch returns W4A16_ERR_HIP.
+ *   - Pointers must be 16-byte aligned (they are read with 128-bit loads).
+ *   - Empty problems (M == 0 or N == 0) return W4A16_OK and enqueue nothing.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ *   - Workspace: the first 8 KiB hold arrival counters and argmax keys that
+ *     must be zero when a call starts.  Zero-fill a workspace once when it is
+ *     allocated; every call returns that region to zero before it completes,
+ *     so one workspace serves calls of any shape in sequence.  Calls that
+ *     share a workspace must be ordered (same stream, or synchronized).
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum w4a16_status {
+    W4A16_OK = 0,
+    W4A16_ERR_NULL = 1,        /* a required pointer is NULL */
+    W4A16_ERR_SHAPE = 2,       /* M, N or K out of the supported range */
+    W4A16_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+    W4A16_ERR_UNSUPPORTED = 4, /* group != 128, or an unknown output dtype */
+    W4A16_ERR_WORKSPACE = 5,   /* workspace smaller than w4a16_workspace_bytes() */
+    W4A16_ERR_HIP = 6          /* a kernel launch failed */
+};
+
+enum w4a16_out_dtype {
+    W4A16_OUT_BF16 = 0, /* Y stored as bfloat16, rounded to nearest even */
+    W4A16_OUT_F32 = 1   /* Y stored as the fp32 accumulator (exactness / debug mode) */
+};
+
+enum w4a16_op {
+    W4A16_OP_LINEAR = 0, /* w4a16_linear */
+    W4A16_OP_LMHEAD = 1  /* w4a16_lmhead_verify */
+};
+
+/*
+ * w4a16_pack -- put 4-bit codes and zero-points onto the packed grid.
+ * The pages: weights are re-packed onto the frozen AWQ grid, and packing stays
+ * as it was (Pith review, Referee Report: Summary, Significance).
+ *   codes  [N][K]   uint8, one code per byte; only the low 4 bits are used
+ *   zeros  [N][G]   uint8, one zero-point per byte; only the low 4 bits are used
+ *   qweight[N][K/8] uint32 out: nibble j (bits 4j..4j+3) of word w of row n = code (n, 8w+j)
+ *   qzeros [N/8][G] uint32 out: nibble j of word (r, g) = zero of row 8r+j, group g
+ * Shapes: N % 8 == 0, K % group == 0, K >= group, group == 128.
+ */
+int w4a16_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K, int group,
+               uint32_t *qweight, uint32_t *qzeros, void *stream);
+
+/*
+ * w4a16_linear -- Y[M][N] = X[M][K] * W^T on the grid defined above.
+ * The layer the pages' INT4 target and GPTQ-INT4 drafter spend their forward
+ * passes in (Pith review, Referee Report: Summary; free parameters: group 128).
+ *   X        [M][K]    bf16, row-major
+ *   qweight  [N][K/8]  uint32 (layout of w4a16_pack)
+ *   scales   [N][G]    fp16
+ *   qzeros   [N/8][G]  uint32
+ *   Y        [M][N]    row-major, bf16 (W4A16_OUT_BF16) or fp32 (W4A16_OUT_F32)
+ *   workspace          device scratch of at least
+ *                      w4a16_workspace_bytes(W4A16_OP_LINEAR, M, N, K, group) bytes;
+ *                      it must hold zeros before its first use (allocate it
+ *                      zero-filled), and every call leaves it that way.
+ *                      May be NULL when that size is 0.
+ * Shapes: M >= 0, N >= 0, N % 8 == 0, K >= group, K % group == 0, group == 128,
+ *         M * N and N * K below 2^31.
+ */
+int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, const uint32_t *qzeros,
+                 int M, int N, int K, int group, void *Y, int y_dtype,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * w4a16_lmhead_verify -- the lm_head projection fused with greedy verification
+ * of a draft block (Pith review, Assumptions: speculative decoding with a
+ * correct verifier is lossless; free parameters: block size 16).
+ * Computes the logits Y = X * W^T as w4a16_linear does (kept in fp32), then
+ *   argmax[m]   = the smallest n attaining max_n Y[m,n]   (over the fp32 logits)
+ *   accept_len  = the number of leading rows i with argmax[i] == draft_ids[i]
+ * Row i of X is the hidden state whose next token is compared with draft_ids[i]
+ * (the caller aligns the positions).  When accept_len < M, argmax[accept_len]
+ * is the target's correction token.
+ *   draft_ids  [M] int32 device; values are only compared, never used as indices
+ *   Y_or_null  [M][N] optional logits out (bf16 or fp32 per y_dtype), or NULL
+ *   argmax     [M] int32 out;  accept_len [1] int32 out
+ *   workspace  at least w4a16_workspace_bytes(W4A16_OP_LMHEAD, M, N, K, group)
+ *              bytes, zero-filled before first use; every call leaves it zeroed.
+ * Shapes: as w4a16_linear, plus 1 <= M <= 64 and N >= 1.
+ */
+int w4a16_lmhead_verify(const void *X, const uint32_t *qweight, const void *scales,
+                        const uint32_t *qzeros, int M, int N, int K, int group,
+                        const int32_t *draft_ids, void *Y_or_null, int y_dtype,
+                        int32_t *argmax, int32_t *accept_len,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * w4a16_workspace_bytes -- scratch size a call of `op` needs for this shape
+ * (split-K partial sums, arrival counters, per-row argmax keys).  Returns 0 for
+ * shapes the call would reject or that need no scratch.
+ */
+size_t w4a16_workspace_bytes(int op, int M, int N, int K, int group);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *w4a16_status_string(int status);
+
+/* ABI version: major * 100 + minor. */
+int w4a16_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

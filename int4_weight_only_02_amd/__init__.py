@@ -1,0 +1,171 @@
+"""MI355X (gfx950) INT4 group-quantized weight-only linear (W4A16) -- Python binding.
+
+A thin ctypes layer over ``libw4a16.so`` (the C ABI in ``include/w4a16.h``).  It
+only marshals torch tensors into pointers, sizes and the current HIP stream:
+every step of the computation runs in the library's HIP kernels.  PyTorch
+supplies device memory and streams.  There is no CPU fallback: if the library is
+not built, every call raises.
+
+Calls (same names as the C ABI):
+  w4a16_pack(codes u8[N,K], zeros u8[N,G])          -> (qweight i32[N,K/8], qzeros i32[N/8,G])
+  w4a16_linear(X bf16[M,K], qweight, scales f16[N,G], qzeros, out_dtype) -> Y[M,N]
+  w4a16_lmhead_verify(X, qweight, scales, qzeros, draft i32[M], return_logits) ->
+        (argmax i32[M], accept_len i32[1], logits or None)
+  w4a16_workspace_bytes(op, M, N, K)
+Packed words travel as int32 tensors (same bits as uint32).
+"""
+import ctypes
+import os
+
+GROUP = 128
+OUT_BF16, OUT_F32 = 0, 1
+OP_LINEAR, OP_LMHEAD = 0, 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libw4a16.so")
+_lib = None
+
+EXPORTED = ("w4a16_pack", "w4a16_linear", "w4a16_lmhead_verify", "w4a16_workspace_bytes",
+            "w4a16_status_string", "w4a16_abi_version")
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+def lib():
+    """Load libw4a16.so (built in-tree by __graft_entry__.build()); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libw4a16.so is not built (run __graft_entry__.build()); "
+                           "there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.w4a16_pack.argtypes = [P, P, I, I, I, P, P, P]
+    L.w4a16_pack.restype = I
+    L.w4a16_linear.argtypes = [P, P, P, P, I, I, I, I, P, I, P, S, P]
+    L.w4a16_linear.restype = I
+    L.w4a16_lmhead_verify.argtypes = [P, P, P, P, I, I, I, I, P, P, I, P, P, P, S, P]
+    L.w4a16_lmhead_verify.restype = I
+    L.w4a16_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.w4a16_workspace_bytes.restype = S
+    L.w4a16_status_string.argtypes = [I]
+    L.w4a16_status_string.restype = ctypes.c_char_p
+    L.w4a16_abi_version.restype = I
+    _lib = L
+    return L
+
+
+def status_string(status):
+    return lib().w4a16_status_string(int(status)).decode()
+
+
+def w4a16_workspace_bytes(op, M, N, K, group=GROUP):
+    return int(lib().w4a16_workspace_bytes(int(op), int(M), int(N), int(K), int(group)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status, where):
+    if status != 0:
+        raise W4A16Error(status, where)
+
+
+class Workspace:
+    """A zero-filled device scratch buffer reused across calls (grown on demand).
+
+    The library leaves the counters it uses at zero after every call, so the
+    buffer only has to be zero when first allocated."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes):
+        import torch
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _workspace(ws, device):
+    if ws is not None:
+        return ws
+    key = str(device)
+    if key not in _default_ws:
+        _default_ws[key] = Workspace(device)
+    return _default_ws[key]
+
+
+def w4a16_pack(codes, zeros, group=GROUP, stream=None):
+    import torch
+    N, K = codes.shape
+    G = K // group
+    qweight = torch.empty((N, K // 8), dtype=torch.int32, device=codes.device)
+    qzeros = torch.empty((N // 8, G), dtype=torch.int32, device=codes.device)
+    assert codes.dtype == torch.uint8 and zeros.dtype == torch.uint8 and zeros.shape == (N, G)
+    st = lib().w4a16_pack(_ptr(codes.contiguous()), _ptr(zeros.contiguous()), N, K, group,
+                          _ptr(qweight), _ptr(qzeros), _stream(stream))
+    _check(st, "w4a16_pack")
+    return qweight, qzeros
+
+
+def w4a16_linear(X, qweight, scales, qzeros, out_dtype=None, group=GROUP, out=None,
+                 workspace=None, stream=None):
+    import torch
+    M, K = X.shape
+    N = qweight.shape[0]
+    assert X.dtype == torch.bfloat16 and scales.dtype == torch.float16
+    assert X.is_contiguous() and qweight.is_contiguous() and scales.is_contiguous() and qzeros.is_contiguous()
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    ydt = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    Y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=X.device)
+    assert Y.shape == (M, N) and Y.dtype == out_dtype and Y.is_contiguous()
+    nbytes = w4a16_workspace_bytes(OP_LINEAR, M, N, K, group)
+    ws = _workspace(workspace, X.device).get(nbytes)
+    st = lib().w4a16_linear(_ptr(X), _ptr(qweight), _ptr(scales), _ptr(qzeros), M, N, K, group,
+                            _ptr(Y), ydt, _ptr(ws), nbytes, _stream(stream))
+    _check(st, "w4a16_linear")
+    return Y
+
+
+def w4a16_lmhead_verify(X, qweight, scales, qzeros, draft_ids, return_logits=False,
+                        logits_dtype=None, group=GROUP, workspace=None, stream=None):
+    import torch
+    M, K = X.shape
+    N = qweight.shape[0]
+    assert X.dtype == torch.bfloat16 and scales.dtype == torch.float16 and draft_ids.dtype == torch.int32
+    assert X.is_contiguous() and draft_ids.is_contiguous()
+    argmax = torch.empty((M,), dtype=torch.int32, device=X.device)
+    accept = torch.empty((1,), dtype=torch.int32, device=X.device)
+    Y = None
+    ydt = OUT_BF16
+    if return_logits:
+        ldt = torch.float32 if logits_dtype is None else logits_dtype
+        ydt = OUT_F32 if ldt == torch.float32 else OUT_BF16
+        Y = torch.empty((M, N), dtype=ldt, device=X.device)
+    nbytes = w4a16_workspace_bytes(OP_LMHEAD, M, N, K, group)
+    ws = _workspace(workspace, X.device).get(nbytes)
+    st = lib().w4a16_lmhead_verify(_ptr(X), _ptr(qweight), _ptr(scales), _ptr(qzeros), M, N, K, group,
+                                   _ptr(draft_ids), _ptr(Y), ydt, _ptr(argmax), _ptr(accept),
+                                   _ptr(ws), nbytes, _stream(stream))
+    _check(st, "w4a16_lmhead_verify")
+    return argmax, accept, Y

@@ -1,0 +1,180 @@
+// api.hip -- the C ABI (include/w4a16.h): host-side validation, path choice and
+// launches.  Nothing here allocates, frees, synchronizes or prints; every check
+// runs before the first launch, so a rejected call leaves the stream untouched.
+#include "w4a16.h"
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace w4a16;
+
+namespace {
+
+constexpr long long kLimit = 0x7FFFFFFFll; // M*N and N*K stay below 2^31
+
+bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+
+// checks shared by the linear and lm_head calls (after the group check)
+int check_dims(int M, int N, int K)
+{
+    if (M < 0 || N < 0 || K < kGroup || K % kGroup != 0 || N % 8 != 0)
+        return W4A16_ERR_SHAPE;
+    if ((long long)M * N > kLimit || (long long)N * K > kLimit || (long long)M * K > kLimit)
+        return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+
+size_t linear_ws(int M, int N, int K)
+{
+    if (M <= kSkinnyMaxM)
+        return plan_skinny(M, N, K, 0).ws_bytes;
+    return plan_tiled(M, N, K).ws_bytes;
+}
+
+} // namespace
+
+extern "C" {
+
+int w4a16_abi_version(void) { return 100; }
+
+const char *w4a16_status_string(int status)
+{
+    switch (status) {
+    case W4A16_OK: return "ok";
+    case W4A16_ERR_NULL: return "null pointer";
+    case W4A16_ERR_SHAPE: return "unsupported shape";
+    case W4A16_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case W4A16_ERR_UNSUPPORTED: return "unsupported group size or output dtype";
+    case W4A16_ERR_WORKSPACE: return "workspace too small";
+    case W4A16_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+size_t w4a16_workspace_bytes(int op, int M, int N, int K, int group)
+{
+    if (group != kGroup || check_dims(M, N, K) != W4A16_OK)
+        return 0;
+    if (op == W4A16_OP_LINEAR)
+        return (M == 0 || N == 0) ? 0 : linear_ws(M, N, K);
+    if (op == W4A16_OP_LMHEAD)
+        return (M < 1 || M > 64 || N < 1) ? 0 : plan_skinny(M, N, K, 1).ws_bytes;
+    return 0;
+}
+
+int w4a16_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K, int group,
+               uint32_t *qweight, uint32_t *qzeros, void *stream)
+{
+    if (group != kGroup)
+        return W4A16_ERR_UNSUPPORTED;
+    if (check_dims(0, N, K) != W4A16_OK)
+        return W4A16_ERR_SHAPE;
+    if (N == 0)
+        return W4A16_OK;
+    if (!codes || !zeros || !qweight || !qzeros)
+        return W4A16_ERR_NULL;
+    if (misaligned(codes) || misaligned(qweight))
+        return W4A16_ERR_ALIGN;
+    if (launch_pack(codes, zeros, N, K, K / kGroup, qweight, qzeros, (hipStream_t)stream) != hipSuccess)
+        return W4A16_ERR_HIP;
+    return W4A16_OK;
+}
+
+int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, const uint32_t *qzeros,
+                 int M, int N, int K, int group, void *Y, int y_dtype,
+                 void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (group != kGroup || (y_dtype != W4A16_OUT_BF16 && y_dtype != W4A16_OUT_F32))
+        return W4A16_ERR_UNSUPPORTED;
+    int st = check_dims(M, N, K);
+    if (st != W4A16_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return W4A16_OK;
+    if (!X || !qweight || !scales || !qzeros || !Y)
+        return W4A16_ERR_NULL;
+    if (misaligned(X) || misaligned(qweight) || misaligned(scales) || misaligned(qzeros) || misaligned(Y) ||
+        misaligned(workspace))
+        return W4A16_ERR_ALIGN;
+    const size_t need = linear_ws(M, N, K);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return W4A16_ERR_WORKSPACE;
+
+    hipError_t e;
+    if (M <= kSkinnyMaxM) {
+        const SkinnyPlan p = plan_skinny(M, N, K, 0);
+        SkinnyArgs a{};
+        a.X = (const uint16_t *)X;
+        a.qw = qweight;
+        a.scales = (const uint16_t *)scales;
+        a.qz = qzeros;
+        a.M = M;
+        a.N = N;
+        a.K = K;
+        a.G = K / kGroup;
+        a.Y = Y;
+        a.y_f32 = y_dtype == W4A16_OUT_F32;
+        a.ws = (unsigned char *)workspace;
+        a.lmhead = 0;
+        e = launch_skinny(a, p, (hipStream_t)stream);
+    } else {
+        const TiledPlan p = plan_tiled(M, N, K);
+        TiledArgs a{};
+        a.X = (const uint16_t *)X;
+        a.qw = qweight;
+        a.scales = (const uint16_t *)scales;
+        a.qz = qzeros;
+        a.M = M;
+        a.N = N;
+        a.K = K;
+        a.G = K / kGroup;
+        a.Y = Y;
+        a.y_f32 = y_dtype == W4A16_OUT_F32;
+        a.ws = (unsigned char *)workspace;
+        e = launch_tiled(a, p, (hipStream_t)stream);
+    }
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+int w4a16_lmhead_verify(const void *X, const uint32_t *qweight, const void *scales,
+                        const uint32_t *qzeros, int M, int N, int K, int group,
+                        const int32_t *draft_ids, void *Y_or_null, int y_dtype,
+                        int32_t *argmax, int32_t *accept_len,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (group != kGroup || (y_dtype != W4A16_OUT_BF16 && y_dtype != W4A16_OUT_F32))
+        return W4A16_ERR_UNSUPPORTED;
+    int st = check_dims(M, N, K);
+    if (st != W4A16_OK)
+        return st;
+    if (M < 1 || M > 64 || N < 1)
+        return W4A16_ERR_SHAPE;
+    if (!X || !qweight || !scales || !qzeros || !draft_ids || !argmax || !accept_len || !workspace)
+        return W4A16_ERR_NULL;
+    if (misaligned(X) || misaligned(qweight) || misaligned(scales) || misaligned(qzeros) ||
+        misaligned(Y_or_null) || misaligned(draft_ids) || misaligned(argmax) || misaligned(accept_len) ||
+        misaligned(workspace))
+        return W4A16_ERR_ALIGN;
+    const SkinnyPlan p = plan_skinny(M, N, K, 1);
+    if (workspace_bytes < p.ws_bytes)
+        return W4A16_ERR_WORKSPACE;
+    SkinnyArgs a{};
+    a.X = (const uint16_t *)X;
+    a.qw = qweight;
+    a.scales = (const uint16_t *)scales;
+    a.qz = qzeros;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.G = K / kGroup;
+    a.Y = Y_or_null;
+    a.y_f32 = y_dtype == W4A16_OUT_F32;
+    a.ws = (unsigned char *)workspace;
+    a.lmhead = 1;
+    a.draft = draft_ids;
+    a.argmax_out = argmax;
+    a.accept_out = accept_len;
+    return launch_skinny(a, p, (hipStream_t)stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+} // extern "C"

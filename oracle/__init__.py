@@ -11,6 +11,7 @@ Functions (numpy in, numpy out):
   unpack(qweight, qzeros, N, K)                 -> (codes, zeros)
   linear(X bf16-bits u16[M,K], qweight, scales f16-bits u16[N,G], qzeros) -> Y f64[M,N]
   linear_at(..., rows, cols)                    -> Y[rows[i], cols[i]] f64
+  linear_matmul(X, qweight, scales, qzeros)     -> Y f64[M,N] (dequantize in fp64, then a library matmul)
   argmax_accept(Y f64[M,N], draft i32[M])       -> (argmax i32[M], gap f64[M], L int)
   bf16_to_f64 / f16_to_f64 (bit patterns -> exact values)
 """
@@ -116,6 +117,29 @@ def linear(X, qweight, scales, qzeros, group=GROUP):
     Y = np.zeros((M, N), np.float64)
     _load().oracle_linear_f64(px, pw, ps, pz, M, N, K, group, Y.ctypes.data_as(ctypes.c_void_p))
     return Y
+
+
+def dequantize(qweight, qzeros, scales, N, K, group=GROUP):
+    """W f64[N,K] = (q - z) * s per group, from the oracle's own unpack and fp16 decode."""
+    codes, zeros = unpack(qweight, qzeros, N, K, group)
+    s = np.asarray(scales, np.uint16).view(np.float16).astype(np.float64)  # exact widening
+    W = codes.astype(np.float64)
+    W -= np.repeat(zeros.astype(np.float64), group, axis=1)
+    W *= np.repeat(s, group, axis=1)
+    return W
+
+
+def linear_matmul(X, qweight, scales, qzeros, group=GROUP):
+    """The same definition as linear(), with the contraction done by a library fp64 matmul.
+
+    Dequantization is exact in fp64; only the summation order differs from the
+    naive loop (fp64 rounding, ~1e-13 relative).  Used for the full-size workloads."""
+    X = np.ascontiguousarray(X, np.uint16)
+    M, K = X.shape
+    N = qweight.shape[0]
+    W = dequantize(qweight, qzeros, scales, N, K, group)
+    x = (X.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x @ W.T
 
 
 def linear_at(X, qweight, scales, qzeros, rows, cols, group=GROUP):

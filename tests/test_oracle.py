@@ -324,3 +324,25 @@ def test_generator_rms_matches_closed_form(K):
     assert (d["codes"] < 16).all() and (d["zeros"] < 16).all()
     s = _f16(d["scales"])
     assert s.min() >= 0.002 - 1e-6 and s.max() <= 0.02 + 1e-5
+
+
+def test_matmul_variant_matches_naive_oracle():
+    d = synth.linear_inputs(41, 5, 96, 1280)
+    qw, qz = oracle.pack(d["codes"], d["zeros"])
+    Y = oracle.linear(d["X"], qw, d["scales"], qz)
+    Ym = oracle.linear_matmul(d["X"], qw, d["scales"], qz)
+    assert np.allclose(Ym, Y, rtol=1e-12, atol=1e-12 * float(np.abs(Y).max()))
+    # dyadic inputs: both are exact
+    rng = np.random.default_rng(42)
+    Xi = rng.integers(-8, 9, size=(4, 1280)).astype(np.float32)
+    sc = synth.f32_to_f16_bits((2.0 ** -rng.integers(6, 10, size=(96, 10))).astype(np.float32))
+    Xb = synth.f32_to_bf16_bits(Xi)
+    assert (oracle.linear_matmul(Xb, qw, sc, qz) == oracle.linear(Xb, qw, sc, qz)).all()
+
+
+def test_dequantize_matches_onehot_linear():
+    d = synth.linear_inputs(43, 1, 64, 384)
+    qw, qz = oracle.pack(d["codes"], d["zeros"])
+    W = oracle.dequantize(qw, qz, d["scales"], 64, 384)
+    eye = synth.f32_to_bf16_bits(np.eye(384, dtype=np.float32))
+    assert (oracle.linear(eye, qw, d["scales"], qz) == W.T).all()
