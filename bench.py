@@ -1,0 +1,339 @@
+#!/usr/bin/env python
+"""Benchmark of the gfx950 W4A16 group-quantized linear (INT4 weights, group 128, bf16 X).
+
+Default run (one GPU): the decode workload -- M = 1, the gate/up projection
+(K 2560 -> N 9728) and the down projection (K 9728 -> N 2560) of a 4B-class MLP;
+one step = both projections.  Prints ONE JSON line with:
+  value          algorithmic HBM GB/s of the whole step (inputs resident in HBM,
+                 weight copies rotated over > 768 MB so the 256 MB Infinity Cache
+                 cannot serve them), steps replayed from a HIP graph
+  roofline       the dominant kernel (skinny_kernel) against 8 TB/s: algorithmic
+                 bytes per launch / average launch time from HIP events on the
+                 launch stream; traffic from the committed rocprofv3 counter summary
+  cpu_baseline   the fp64 CPU oracle timed on this host on a bounded sample
+  workloads      the same measurements for the other shapes: a single 512x512
+                 linear, one decoder layer's seven projections at M = 16 (a draft
+                 block), the fused lm_head verify over a 151936 vocabulary, and
+                 prefill at M = 8192 (TFLOP/s against the bf16 MFMA peak)
+Options: --only WORKLOAD times one workload (for profiling runs), --calib runs a
+plain copy of known size (HBM counter calibration).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+CACHE_ROTATE_BYTES = 768 << 20
+METRIC = "W4A16 linear µs and HBM GB/s (% of peak) at M=1/16; TFLOP/s at M=8192"
+HEADLINE = "decode_gemv_m1"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def algo_bytes(M, N, K, out_bytes=2, lmhead=False):
+    G = K // 128
+    b = N * K // 2 + 2 * N * G + N * G // 2 + 2 * M * K + out_bytes * M * N
+    if lmhead:
+        b += 4 * M + 4 * M + 4  # draft ids in, argmax ids + accept length out
+    return b
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("common.h", "kernels.h", "skinny.hip", "tiled.hip", "api.hip"):
+        with open(os.path.join(ROOT, "int4_weight_only_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, launches_per_step):
+    """HBM bytes per launch from the committed counter summary, if it matches the current kernels."""
+    path = os.path.join(PROFILE_DIR, "skinny_kernel__%s__pmc.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Workload:
+    """Device tensors for one workload: R rotating copies of every projection."""
+
+    def __init__(self, name, dev, lmhead=False, max_copies=64):
+        import torch
+        import int4_weight_only_02_amd as w4
+        self.name = name
+        self.lmhead = lmhead
+        self.shapes = synth.WORKLOADS[name]
+        self.projs = []
+        per_copy = 0
+        for j, (label, M, K, N) in enumerate(self.shapes):
+            per_copy += algo_bytes(M, N, K)
+        self.R = int(min(max_copies, max(1, -(-CACHE_ROTATE_BYTES // per_copy))))
+        ws_need = 0
+        for j, (label, M, K, N) in enumerate(self.shapes):
+            d = synth.workload_inputs(name, j)
+            codes = torch.from_numpy(d["codes"]).to(dev)
+            zeros = torch.from_numpy(d["zeros"]).to(dev)
+            qw, qz = w4.w4a16_pack(codes, zeros)
+            del codes, zeros
+            X = torch.from_numpy(d["X"].view(np.int16)).to(dev).view(torch.bfloat16)
+            S = torch.from_numpy(d["scales"].view(np.int16)).to(dev).view(torch.float16)
+            copies = [(X, qw, S, qz)] + [(X.clone(), qw.clone(), S.clone(), qz.clone()) for _ in range(self.R - 1)]
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            p = {"label": label, "M": M, "K": K, "N": N, "copies": copies, "Y": Y, "host": d}
+            if lmhead:
+                draft, L0, rng = synth.draft_block(synth.seed_for(name, j), M, N)
+                p["draft"] = torch.from_numpy(draft).to(dev)
+                p["argmax"] = torch.empty((M,), dtype=torch.int32, device=dev)
+                p["accept"] = torch.empty((1,), dtype=torch.int32, device=dev)
+                ws_need = max(ws_need, w4.w4a16_workspace_bytes(w4.OP_LMHEAD, M, N, K))
+            else:
+                ws_need = max(ws_need, w4.w4a16_workspace_bytes(w4.OP_LINEAR, M, N, K))
+            self.projs.append(p)
+        self.ws = w4.Workspace(dev)
+        self.ws.get(ws_need)
+        self.bytes_per_step = sum(algo_bytes(p["M"], p["N"], p["K"], lmhead=lmhead) for p in self.projs)
+        self.flops_per_step = sum(2 * p["M"] * p["N"] * p["K"] for p in self.projs)
+
+    def launch(self, p, r):
+        import int4_weight_only_02_amd as w4
+        X, qw, S, qz = p["copies"][r]
+        if self.lmhead:
+            w4.w4a16_lmhead_verify(X, qw, S, qz, p["draft"], workspace=self.ws,
+                                   argmax_out=p["argmax"], accept_out=p["accept"])
+        else:
+            w4.w4a16_linear(X, qw, S, qz, out=p["Y"], workspace=self.ws)
+
+    def step(self, r):
+        for p in self.projs:
+            self.launch(p, r % self.R)
+
+    def check(self):
+        """Sanity check of one step against the oracle (sampled outputs)."""
+        import torch
+        import oracle
+        worst = 0.0
+        for p in self.projs:
+            self.launch(p, 0)
+            torch.cuda.synchronize()
+            d = p["host"]
+            qw, qz = oracle.pack(d["codes"], d["zeros"])
+            rng = np.random.default_rng(0)
+            rows = rng.integers(0, p["M"], 256)
+            cols = rng.integers(0, p["N"], 256)
+            ref = oracle.linear_at(d["X"], qw, d["scales"], qz, rows, cols)
+            if self.lmhead:
+                continue
+            got = p["Y"].float().cpu().numpy()[rows, cols]
+            rms = float(np.sqrt(np.mean(ref ** 2))) or 1.0
+            worst = max(worst, float(np.abs(got - ref).max()) / rms)
+        return worst
+
+
+def time_events(wl, reps):
+    """Per-launch kernel time (us) from HIP events around every launch, per projection."""
+    import torch
+    out = {}
+    for p in wl.projs:
+        evs = []
+        for i in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            wl.launch(p, i % wl.R)
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        t = [a.elapsed_time(b) * 1e3 for a, b in evs]
+        out[p["label"]] = float(np.mean(t))
+    return out
+
+
+def capture(wl, steps, start):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(2):  # warm the lazy initialisation outside the capture
+            wl.step(start + i)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                wl.step(start + i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_steps(wl, steps, warmup):
+    """Exactly `steps` steps replayed from HIP graphs (a cycle over the R copies plus
+    a remainder), bracketed by device synchronization.  Returns seconds per step."""
+    import torch
+    cyc = capture(wl, wl.R, 0)
+    rem_n = steps % wl.R
+    rem = capture(wl, rem_n, 0) if rem_n else None
+    for _ in range(max(1, -(-warmup // wl.R))):
+        cyc.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps // wl.R):
+        cyc.replay()
+    if rem is not None:
+        rem.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) / steps, e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def cpu_baseline(name, budget_s=10.0):
+    """The fp64 oracle (as it stands) on this host, on the headline step: repeat whole
+    steps (both projections at full size) until about budget_s seconds have passed."""
+    import oracle
+    data = []
+    for j, (label, M, K, N) in enumerate(synth.WORKLOADS[name]):
+        d = synth.workload_inputs(name, j)
+        qw, qz = oracle.pack(d["codes"], d["zeros"])
+        data.append((d["X"], qw, d["scales"], qz, algo_bytes(M, N, K)))
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for X, qw, S, qz, _ in data:
+            oracle.linear(X, qw, S, qz)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    gbs = sum(b for *_, b in data) / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d full decode steps (M=1, K2560xN9728 and K9728xN2560), fp64 naive loops, %.1f s"
+                      % (n, dt * n),
+            "ms_per_step": round(dt * 1e3, 3)}
+
+
+def measure(name, dev, steps, warmup, lmhead=False, ev_reps=200):
+    wl = Workload(name, dev, lmhead=lmhead)
+    err = wl.check()
+    ev = time_events(wl, ev_reps)
+    wall, gpu = time_steps(wl, steps, warmup)
+    res = {"copies": wl.R, "bytes_per_step": wl.bytes_per_step, "flops_per_step": wl.flops_per_step,
+           "us_per_step": round(wall * 1e6, 3), "us_per_step_gpu_events": round(gpu * 1e6, 3),
+           "GBps": round(wl.bytes_per_step / wall / 1e9, 2),
+           "hbm_frac": round(wl.bytes_per_step / wall / 1e9 / HBM_PEAK_GBS, 4),
+           "TFLOPs": round(wl.flops_per_step / wall / 1e12, 3),
+           "kernel_us": {k: round(v, 3) for k, v in ev.items()},
+           "sampled_max_err_over_rms": err}
+    per = {}
+    for p in wl.projs:
+        t = ev[p["label"]] * 1e-6
+        b = algo_bytes(p["M"], p["N"], p["K"], lmhead=lmhead)
+        f = 2 * p["M"] * p["N"] * p["K"]
+        per[p["label"]] = {"M": p["M"], "K": p["K"], "N": p["N"], "kernel_us": round(t * 1e6, 3),
+                           "GBps": round(b / t / 1e9, 1), "hbm_frac": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+                           "TFLOPs": round(f / t / 1e12, 2), "mfma_frac": round(f / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    res["per_launch"] = per
+    del wl
+    import torch
+    torch.cuda.empty_cache()
+    return res
+
+
+def calib_copy(dev, nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--only", default=None, help="time one workload only (profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the layer runs on one GPU's share; "
+              "multi-GPU sharding is described, not run); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import int4_weight_only_02_amd as w4
+    w4.lib()  # fails loudly if the HIP library is not built
+    dev = torch.device("cuda:0")
+    if args.calib:
+        calib_copy(dev)
+        return
+
+    names = [HEADLINE, "single_512", "verify_block_m16", "lmhead_verify_m16", "prefill_m8192"]
+    if args.only:
+        names = [args.only]
+    results = {}
+    for name in names:
+        steps = args.steps if name != "prefill_m8192" else max(4, min(args.steps, 40))
+        warm = args.warmup if name != "prefill_m8192" else 4
+        if name == "lmhead_verify_m16":
+            steps = max(10, min(args.steps, 400))
+        results[name] = measure(name, dev, steps, warm, lmhead=(name == "lmhead_verify_m16"))
+        print("[bench] %s: %s" % (name, json.dumps(results[name])), file=sys.stderr, flush=True)
+
+    head = results.get(HEADLINE) or results[names[0]]
+    head_name = HEADLINE if HEADLINE in results else names[0]
+    per = head["per_launch"]
+    b_launch = np.mean([algo_bytes(v["M"], v["N"], v["K"]) for v in per.values()])
+    t_launch = np.mean([v["kernel_us"] for v in per.values()]) * 1e-6
+    achieved = b_launch / t_launch / 1e9
+    traffic = load_traffic(head_name, len(per))
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "skinny_kernel", "algorithmic_bytes_per_launch": int(b_launch),
+            "avg_launch_us": round(t_launch * 1e6, 3)}
+    cpu = None
+    if not args.no_cpu_baseline and args.only is None:
+        cpu = cpu_baseline(HEADLINE)
+    steps_head = args.steps
+    line = {"metric": METRIC, "value": head["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": steps_head,
+            "warmup": args.warmup, "ms_per_step": round(head["us_per_step"] / 1e3, 6),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": head_name, "M": 1, "group": 128,
+                       "shapes": [[v["M"], v["K"], v["N"]] for v in per.values()],
+                       "cache": "cold: %d rotating weight copies (> 768 MB)" % head["copies"],
+                       "timing": "HIP graph replay of exactly `steps` steps, wall clock between device syncs"},
+            "roofline": roof, "cpu_baseline": cpu,
+            "workloads": results}
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -148,17 +148,21 @@ def w4a16_linear(X, qweight, scales, qzeros, out_dtype=None, group=GROUP, out=No
 
 
 def w4a16_lmhead_verify(X, qweight, scales, qzeros, draft_ids, return_logits=False,
-                        logits_dtype=None, group=GROUP, workspace=None, stream=None):
+                        logits_dtype=None, group=GROUP, workspace=None, stream=None,
+                        argmax_out=None, accept_out=None, logits_out=None):
     import torch
     M, K = X.shape
     N = qweight.shape[0]
     assert X.dtype == torch.bfloat16 and scales.dtype == torch.float16 and draft_ids.dtype == torch.int32
     assert X.is_contiguous() and draft_ids.is_contiguous()
-    argmax = torch.empty((M,), dtype=torch.int32, device=X.device)
-    accept = torch.empty((1,), dtype=torch.int32, device=X.device)
-    Y = None
+    argmax = argmax_out if argmax_out is not None else torch.empty((M,), dtype=torch.int32, device=X.device)
+    accept = accept_out if accept_out is not None else torch.empty((1,), dtype=torch.int32, device=X.device)
+    Y = logits_out
     ydt = OUT_BF16
-    if return_logits:
+    if Y is not None:
+        ydt = OUT_F32 if Y.dtype == torch.float32 else OUT_BF16
+        assert Y.shape == (M, N) and Y.is_contiguous()
+    elif return_logits:
         ldt = torch.float32 if logits_dtype is None else logits_dtype
         ydt = OUT_F32 if ldt == torch.float32 else OUT_BF16
         Y = torch.empty((M, N), dtype=ldt, device=X.device)

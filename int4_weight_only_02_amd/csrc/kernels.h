@@ -24,22 +24,27 @@ hipError_t launch_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K,
                        uint32_t *qweight, uint32_t *qzeros, hipStream_t stream);
 
 // ---------------------------------------------------------------- skinny (small M)
-// Work unit = one group (128 of K) of one 128-column block of one 16-row m-block.
-// Units are ordered (m-block, column block, group) and split into `grid`
-// contiguous, near-equal ranges, one per workgroup (stream-K).  A column block
-// whose K range spans several workgroups is summed by the last one to finish,
-// in workgroup order, from per-workgroup fp32 partials.  Its arrival counter is
-// indexed by the workgroup that owns its first unit (each workgroup owns the
-// first unit of at most one split column block), so grid counters suffice.
+// Every workgroup owns whole 16-column tiles (no partial sums cross workgroups).
+//   split mode  (stream == 0): item = (16-row m-block, group of tw tiles); a
+//               workgroup of tw * sk waves takes one item at a time, each tile's K
+//               split over sk waves and summed through LDS in slice order;
+//   stream mode (stream == 1): persistent workgroups of tw waves; each wave takes
+//               whole tiles (tile groups blockIdx.x, +grid, ...) over all of K.
+// X for the m-block is staged in LDS in chunks of `chunk` groups (all of K when it
+// fits).
 struct SkinnyPlan {
     int mblocks;   // ceil(M / 16)
-    int ncb;       // ceil(N / 128)
+    int nt;        // ceil(N / 16) column tiles
     int G;         // K / 128
-    long long units;
-    int grid;      // workgroups (<= kMaxGrid)
-    int chunk;     // max groups of X staged in LDS at once
+    int waves;     // waves per workgroup = tw * sk
+    int tw, sk;    // tiles per item, K slices per tile
+    int chunk;     // groups of X per LDS stage
+    int ntg;       // tile groups per m-block = ceil(nt / tw)
+    int items;     // mblocks * ntg
+    int grid;      // workgroups
+    int stream;    // 1: stream mode
     size_t lds_bytes;
-    size_t off_partial, ws_bytes; // partials start at kZeroRegion
+    size_t ws_bytes; // lm_head: the zero region (argmax keys, ticket); linear: 0
 };
 
 struct SkinnyArgs {
@@ -57,7 +62,7 @@ struct SkinnyArgs {
     int32_t *accept_out;
 };
 
-SkinnyPlan plan_skinny(int M, int N, int K, int lmhead);
+SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit = 0);
 hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &p, hipStream_t stream);
 
 // ---------------------------------------------------------------- tiled (large M)

@@ -3,19 +3,28 @@
 //
 // At M <= 16 per m-block the layer is bound by HBM: every packed weight byte is
 // read once and used for at most 16 rows.  The kernel streams the packed words
-// with 128-bit loads straight into MFMA B fragments (no LDS staging of weights):
-//   * one wave owns a 16-column tile; lane l holds column l%16 and, per group of
-//     128 codes, one 16-byte load = 32 codes = the B operand of four
-//     v_mfma_f32_16x16x32_bf16 (lane group l/16 covers codes 32*(l/16) .. +31);
-//   * the activations of the workgroup's K range sit in LDS, permuted to the
-//     fragment order, shared by the 8 waves (8 column tiles = a 128-column block);
-//   * per group, the four MFMAs give P = sum x * (128 + q) exactly in fp32, and
-//     the group is folded in fp32 as acc += s * (P - (128 + z) * sum x).
-// Work is split stream-K style: units (m-block, column block, group) in that
-// order are cut into one contiguous range per workgroup, so every shape spreads
-// evenly over the 256 CUs whatever its N and K.  A column block shared by
-// several workgroups is summed by the last to finish, in workgroup order, from
-// fp32 partials in the workspace: results are deterministic.
+// with 128-bit buffer loads straight into MFMA B fragments (no LDS staging of
+// weights):
+//   * a wave owns a 16-column tile (or a K slice of one); lane l holds column l%16
+//     and, per group of 128 codes, one 16-byte load = 32 codes = the B operand of
+//     four v_mfma_f32_16x16x32_bf16 (lane group l/16 covers codes 32*(l/16) .. +31);
+//   * the activations X[m-block][K] sit in LDS, permuted to the fragment order and
+//     shared by every wave of the workgroup;
+//   * per group, eight MFMAs accumulate P = sum x * (q - z) in fp32: four with the
+//     exact biased codes 128 + q and, interleaved, four with the column constant
+//     -(128 + z) (also exact in bf16: at most 8 significant bits), so the bias and
+//     the zero-point cancel inside the accumulator.  The group is then scaled in
+//     fp32: acc += s * P.  The matrix cores are otherwise idle in this
+//     memory-bound kernel, so the zero-point costs no VALU work beyond building
+//     its fragment.
+// Every workgroup owns whole output columns, so no partial sum crosses a workgroup:
+//   split mode   (few tiles: decode, the 7 projections of a decoder layer) -- a
+//                workgroup takes tw tiles and splits K over sk waves per tile; the
+//                sk partial accumulators are summed through LDS in a fixed order;
+//   stream mode  (many tiles: the 151936-column lm_head) -- persistent workgroups,
+//                each wave walks its own sequence of whole tiles with the next
+//                batch of loads always in flight, across tile boundaries.
+// Results are deterministic (fixed summation order everywhere).
 //
 // lm_head mode (the pages' greedy verifier: Pith review, Assumptions, "a correct
 // verifier is lossless"; draft blocks of 16 tokens, free parameters) keeps the
@@ -29,26 +38,14 @@ namespace w4a16 {
 
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBlockCols = kWaves * 16;     // columns per column block
-constexpr int kSlotFloats = 16 * kBlockCols; // one fp32 partial: 16 rows x 128 columns
-constexpr int kInner = 8;                    // groups whose weights are loaded together
+constexpr int kMaxWaves = 16;
+constexpr int kMaxThreads = kMaxWaves * 64;
+constexpr int kB = 4;           // groups per register batch (two batches in flight)
+constexpr int kStageUnrollWide = 8;  // X staging loads in flight per thread (512-thread workgroups)
+constexpr int kStageUnrollNarrow = 2; // (1024-thread workgroups: 128 VGPRs per lane)
 constexpr int kCUs = 256;
-constexpr size_t kLdsBudget = 160 * 1024 - 2048;
-
-__device__ __forceinline__ long long unit_start(long long U, int grid, int w)
-{
-    return (long long)w * U / grid;
-}
-
-__device__ __forceinline__ int unit_owner(long long U, int grid, long long u)
-{
-    int w = (int)((u * grid) / U);
-    while (w + 1 < grid && unit_start(U, grid, w + 1) <= u)
-        ++w;
-    return w;
-}
+constexpr size_t kLdsBudget = 160 * 1024 - 4096;
+constexpr uint32_t kOob = 0xFFFFFF00u; // an offset past the end of every tensor
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m)
 {
@@ -62,37 +59,168 @@ __device__ __forceinline__ unsigned long long max_u64(unsigned long long a, unsi
     return a > b ? a : b;
 }
 
-__device__ __forceinline__ float ld_agent(const float *p)
+// Cross-workgroup hand-off (lm_head keys and the finishing ticket).  They move
+// through device-scope atomics, which the gfx950 memory path keeps coherent across
+// the XCDs' L2s.  The only ordering needed is that a workgroup's device-scope
+// atomics have completed before it takes its ticket: s_waitcnt vmcnt(0) (vmcnt
+// counts stores and no-return atomics on gfx9).  Agent-scope fences would instead
+// write back and invalidate a whole L2 (buffer_wbl2 / buffer_inv).
+__device__ __forceinline__ void wait_device_writes()
 {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0), expcnt and lgkmcnt unconstrained
 }
 
-__device__ __forceinline__ void st_agent(float *p, float v)
+// Buffer resource word 3 for raw (untyped) loads on gfx9-class GPUs.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcWord3);
 }
 
-__global__ __launch_bounds__(kThreads) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
+// The lane's view of the packed grid for one 16-column tile: byte offsets of the
+// lane's column.  Group g of the lane's codes sits at wo + 64 g, its scale at
+// so + 2 g and its zero word at zo + 4 g.  A load past the end of a tensor (or at
+// kOob) returns 0 instead of faulting; groups past the lane's range read finite
+// neighbouring data or 0 and are masked in compute_batch.
+struct LaneGrid {
+    uint32_t wo, so, zo;
+    int zsh;
+};
+
+__device__ __forceinline__ LaneGrid lane_grid(int tile, int col, int h, int N, int K, int G, bool live)
+{
+    LaneGrid L;
+    int n = tile * 16 + col;
+    n = n < N ? n : N - 1;
+    L.wo = live ? (uint32_t)n * (uint32_t)(K / 2) + 16u * (uint32_t)h : kOob;
+    L.so = live ? (uint32_t)n * (uint32_t)(2 * G) : kOob;
+    L.zo = live ? (uint32_t)(n >> 3) * (uint32_t)(4 * G) : kOob;
+    L.zsh = (n & 7) * 4;
+    return L;
+}
+
+// kB consecutive groups of one lane's column: 16 bytes of codes, the fp16 scale and
+// the zero word for each
+struct Batch {
+    u32x4_t w[kB];
+    uint32_t s[kB];
+    uint32_t z[kB];
+};
+
+// Load groups gs .. gs+kB-1 (unconditionally: a batch starting at or past gend
+// loads from kOob and costs no memory traffic).
+__device__ __forceinline__ void load_batch(Batch &b, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rs,
+                                           __amdgpu_buffer_rsrc_t rz, const LaneGrid &L, int gs, int gend)
+{
+    const bool in = gs < gend;
+    const uint32_t wo = in ? L.wo + 64u * (uint32_t)gs : kOob;
+    const uint32_t so = in ? L.so + 2u * (uint32_t)gs : kOob;
+    const uint32_t zo = in ? L.zo + 4u * (uint32_t)gs : kOob;
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+        b.w[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 64u * i, 0, 0));
+        b.s[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, so + 2u * i, 0, 0);
+        b.z[i] = __builtin_amdgcn_raw_buffer_load_b32(rz, zo + 4u * i, 0, 0);
+    }
+}
+
+// 8 codes -> MFMA fragment, with the mask and the bias held in registers so that
+// each pair costs one v_and_or_b32 (plus a shift for the pairs 1..3)
+__device__ __forceinline__ bf16x8_t codes_to_frag_r(uint32_t w, uint32_t mask, uint32_t bias)
+{
+    u32x4_t r;
+    r.x = (w & mask) | bias;
+    r.y = ((w >> 4) & mask) | bias;
+    r.z = ((w >> 8) & mask) | bias;
+    r.w = ((w >> 12) & mask) | bias;
+    return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// Per group: P = sum x * (128 + q) + sum x * (-(128 + z)) = sum x * (q - z) for this
+// lane's column and the rows 4h .. 4h+3 (D layout), then acc += s * P.  Groups at
+// or past gend get s = 0 (their data is finite, so the product is exactly 0).
+// xlane points at the lane's X row in the staged chunk starting at group st_c0.
+// NR = the accumulator rows that can hold real output (1 for M = 1, 2 for M = 2).
+template <int NR>
+__device__ __forceinline__ void compute_batch(const Batch &b, f32x4_t &acc, const u32x4_t *xlane, int gs,
+                                              int gend, int st_c0, int Mb, int zsh, uint32_t mask,
+                                              uint32_t bias)
+{
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+        const int g = gs + i;
+        const int gl = (g < gend ? g : gend - 1) - st_c0;
+        const u32x4_t *xg = xlane + gl * 16 * Mb;
+        // -(128 + z) as a bf16 pair: sign | exponent of 128 | z in the mantissa
+        const uint32_t zb = (((b.z[i] >> zsh) & 15u) | 0xC300u) * 0x00010001u;
+        const bf16x8_t zfrag = __builtin_bit_cast(bf16x8_t, u32x4_t{zb, zb, zb, zb});
+        f32x4_t p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, xg[j * Mb]);
+            const uint32_t wj = j == 0 ? b.w[i].x : j == 1 ? b.w[i].y : j == 2 ? b.w[i].z : b.w[i].w;
+            p = mfma16x16x32(xa, codes_to_frag_r(wj, mask, bias), p);
+            p = mfma16x16x32(xa, zfrag, p);
+        }
+        const float s = g < gend ? f16_bits_to_f32((uint16_t)b.s[i]) : 0.f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+            acc[r] = fmaf(s, p[r], acc[r]);
+    }
+}
+
+// Stage X[m0 .. m0+Mb)[groups s0 .. s1) into LDS in fragment order: thread t takes
+// the 16-byte chunks kc = t, t + nthreads, ... of every row, so no index needs a
+// division; up to kStageUnroll rows' loads are in flight per thread.  Caller
+// synchronizes around it.
+template <int kStageUnroll>
+__device__ __forceinline__ void stage_x(const uint16_t *X, int K, int m0, int Mb, int s0, int s1,
+                                        u32x4_t *xs, int tid, int nthreads)
+{
+    const int R = (s1 - s0) * 16; // 16-byte chunks per row
+    for (int kc = tid; kc < R; kc += nthreads) {
+        const uint16_t *src = X + (size_t)m0 * K + (size_t)s0 * kGroup + kc * 8;
+        u32x4_t *dst = xs + kc * Mb; // chunk kc = (group kc/16, c = kc%16): [(gl*16 + c)*Mb + m]
+        for (int m = 0; m < Mb; m += kStageUnroll) {
+            u32x4_t v[kStageUnroll];
+#pragma unroll
+            for (int u = 0; u < kStageUnroll; ++u)
+                if (m + u < Mb)
+                    v[u] = *(const u32x4_t *)(src + (size_t)(m + u) * K);
+#pragma unroll
+            for (int u = 0; u < kStageUnroll; ++u)
+                if (m + u < Mb)
+                    dst[m + u] = x_permute8(v[u]);
+        }
+    }
+}
+
+template <int NR, bool STREAM>
+__global__ __launch_bounds__(STREAM ? 512 : kMaxThreads) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ unsigned long long red[kWaves][16];
-    __shared__ int s_first, s_last_w;
+    __shared__ unsigned long long kred[kMaxWaves][16];
+    __shared__ int s_flag;
 
     const int M = a.M, N = a.N, K = a.K, G = a.G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 4, col = lane & 15;
-    const int w = blockIdx.x;
-    const long long U = p.units;
-    const int grid = p.grid, ncb = p.ncb, chunk = p.chunk;
-    const long long u0 = unit_start(U, grid, w), u1 = unit_start(U, grid, w + 1);
+    const int nthreads = blockDim.x, nwaves = nthreads >> 6;
     const int mrows = M < 16 ? M : 16;
 
-    u32x4_t *xs = (u32x4_t *)smem;                                       // [g][chunk c][row]
-    float *ssum = (float *)(smem + (size_t)chunk * 256 * mrows);        // [g][16]
+    u32x4_t *xs = (u32x4_t *)smem;                              // [group][chunk c][row]
+    float *red = (float *)(smem + (size_t)p.chunk * 256 * mrows); // [wave][64 lanes][4]
     uint32_t *ticket = (uint32_t *)(a.ws + kOffTicket);
     unsigned long long *keys = (unsigned long long *)(a.ws + kOffKeys);
-    uint32_t *counters = (uint32_t *)(a.ws + kOffCounters);
-    float *partial = (float *)(a.ws + p.off_partial);
+
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.qw, (uint32_t)((size_t)N * K / 2));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales, (uint32_t)((size_t)N * G * 2));
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.qz, (uint32_t)((size_t)(N / 8) * G * 4));
+    // code-to-bf16 constants, pinned in VGPRs (see codes_to_frag_r)
+    uint32_t kmask = 0x000F000Fu, kbias = kBiasBits;
+    asm volatile("" : "+v"(kmask));
+    asm volatile("" : "+v"(kbias));
 
     unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
     int cur_mb = -1;
@@ -110,16 +238,15 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(SkinnyArgs a, SkinnyPl
         if (col == 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                red[wave][4 * h + r] = best[r];
+                kred[wave][4 * h + r] = best[r];
         }
         __syncthreads();
         if (tid < 16 && mb * 16 + tid < M) {
-            unsigned long long k = red[0][tid];
-#pragma unroll
-            for (int v = 1; v < kWaves; ++v)
-                k = max_u64(k, red[v][tid]);
+            unsigned long long k = kred[0][tid];
+            for (int v = 1; v < nwaves; ++v)
+                k = max_u64(k, kred[v][tid]);
             if (k)
-                atomicMax(&keys[mb * 16 + tid], k);
+                __hip_atomic_fetch_max(&keys[mb * 16 + tid], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
 #pragma unroll
@@ -127,181 +254,177 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(SkinnyArgs a, SkinnyPl
             best[r] = 0ull;
     };
 
-    long long u = u0;
-    while (u < u1) {
-        const long long per_mb = (long long)ncb * G;
-        const int mb = (int)(u / per_mb);
-        const long long rem = u - (long long)mb * per_mb;
-        const int cb = (int)(rem / G);
-        const int ga = (int)(rem - (long long)cb * G);
-        const int gb = (int)((long long)G < ga + (u1 - u) ? (long long)G : ga + (u1 - u));
-        const int m0 = mb * 16;
-        const int Mb = M - m0 < 16 ? M - m0 : 16;
-        const int ntile = cb * kBlockCols + wave * 16;
-        const int n = ntile + col;
-        const bool tile_live = ntile < N; // wave-uniform
-        const int nl = n < N ? n : N - 1; // clamped row for loads; never stored
+    // finished tile: store the rows < Mb of column n, or fold them into the argmax keys
+    auto finish_tile = [&](const f32x4_t &acc, int m0, int Mb, int n) {
+        if (n >= N)
+            return;
+        if (a.Y) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * h + r;
+                if (row < Mb) {
+                    const size_t o = (size_t)(m0 + row) * N + n;
+                    if (a.y_f32)
+                        ((float *)a.Y)[o] = acc[r];
+                    else
+                        ((uint16_t *)a.Y)[o] = f32_to_bf16_rne(acc[r]);
+                }
+            }
+        }
+        if (a.lmhead) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * h + r < Mb)
+                    best[r] = max_u64(best[r], argmax_key(acc[r], n));
+        }
+    };
 
-        if (a.lmhead && mb != cur_mb) {
-            if (cur_mb >= 0)
+    if constexpr (STREAM) {
+        // ---- stream mode: X of the m-block is staged once (all of K); each wave walks
+        // tile groups blockIdx.x, +grid, ... and takes tile tg * nwaves + wave of each.
+        for (int mb = 0; mb < p.mblocks; ++mb) {
+            const int m0 = mb * 16;
+            const int Mb = M - m0 < 16 ? M - m0 : 16;
+            const int xrow = col < Mb ? col : Mb - 1; // rows >= Mb feed outputs that are never stored
+            const u32x4_t *xlane = xs + (4 * h) * Mb + xrow;
+            if (a.lmhead && cur_mb >= 0)
                 flush_best(cur_mb);
             cur_mb = mb;
-        }
 
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int c0 = ga; c0 < gb; c0 += chunk) {
-            const int c1 = gb < c0 + chunk ? gb : c0 + chunk;
-            if (!(mb == st_mb && c0 >= st_c0 && c1 <= st_c1)) {
-                // stage X[m0 .. m0+Mb)[groups c0 .. c1) into LDS in fragment order,
-                // with the per-(row, group) sums S used by the fold
-                __syncthreads();
-                const int ng = c1 - c0;
-                const int total = Mb * ng * 16; // multiple of 16: one 16-lane team per (row, group)
-                for (int i = tid; i < total; i += kThreads) {
-                    const int c = i & 15;
-                    const int t = i >> 4;
-                    const int gl = t % ng;
-                    const int m = t / ng;
-                    const u32x4_t v = *(const u32x4_t *)(a.X + (size_t)(m0 + m) * K +
-                                                         (size_t)(c0 + gl) * kGroup + c * 8);
-                    float s = sum8_bf16(v);
-                    s += __shfl_xor(s, 1);
-                    s += __shfl_xor(s, 2);
-                    s += __shfl_xor(s, 4);
-                    s += __shfl_xor(s, 8);
-                    if (c == 0)
-                        ssum[gl * 16 + m] = s;
-                    xs[(gl * 16 + c) * Mb + m] = x_permute8(v);
-                }
-                __syncthreads();
-                st_mb = mb;
-                st_c0 = c0;
-                st_c1 = c1;
-            }
-            if (tile_live) {
-                const u32x4_t *wrow = (const u32x4_t *)(a.qw + (size_t)nl * (K / 8)) + h;
-                const uint16_t *srow = a.scales + (size_t)nl * G;
-                const uint32_t *zrow = a.qz + (size_t)(nl >> 3) * G;
-                const int zsh = (nl & 7) * 4;
-                for (int g = c0; g < c1; g += kInner) {
-                    u32x4_t wv[kInner];
-                    uint32_t sv[kInner], zv[kInner];
-#pragma unroll
-                    for (int i = 0; i < kInner; ++i) {
-                        if (g + i < c1) {
-                            wv[i] = wrow[4 * (g + i)];
-                            sv[i] = srow[g + i];
-                            zv[i] = zrow[g + i];
-                        }
-                    }
-#pragma unroll
-                    for (int i = 0; i < kInner; ++i) {
-                        if (g + i < c1) {
-                            const int gl = g + i - st_c0;
-                            f32x4_t pacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                u32x4_t xa = {0u, 0u, 0u, 0u};
-                                if (col < Mb)
-                                    xa = xs[(gl * 16 + 4 * h + j) * Mb + col];
-                                const uint32_t wj = j == 0 ? wv[i].x : j == 1 ? wv[i].y : j == 2 ? wv[i].z : wv[i].w;
-                                pacc = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xa), codes_to_frag(wj), pacc);
-                            }
-                            const float s = f16_bits_to_f32((uint16_t)sv[i]);
-                            const float cz = (float)(kCodeBias + ((zv[i] >> zsh) & 15u));
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                if (r < Mb) {
-                                    const float S = ssum[gl * 16 + 4 * h + r];
-                                    acc[r] = fmaf(s, fmaf(-cz, S, pacc[r]), acc[r]);
-                                }
-                            }
-                        }
-                    }
-                }
-            }
-        }
+            int tgA = blockIdx.x, gA = 0;
+            int tileA = tgA * nwaves + wave;
+            bool liveA = tgA < p.ntg && tileA * 16 < N;
+            LaneGrid LA = lane_grid(tileA, col, h, N, K, G, liveA);
+            Batch bA, bB;
+            load_batch(bA, rw, rs, rz, LA, gA, G); // in flight while X is staged
+            __syncthreads();
+            stage_x<kStageUnrollWide>(a.X, K, m0, Mb, 0, G, xs, tid, nthreads);
+            __syncthreads();
 
-        // ---- epilogue: finish the column block (directly, or by the last contributor)
-        bool have = true;
-        if (!(ga == 0 && gb == G)) {
-            const int slot = (u == u0) ? 0 : 1;
-            float *part = partial + ((size_t)w * 2 + slot) * kSlotFloats;
-            if (tile_live) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (4 * h + r < Mb)
-                        st_agent(&part[(4 * h + r) * kBlockCols + wave * 16 + col], acc[r]);
-            }
-            __threadfence();
-            __syncthreads();
-            if (tid == 0) {
-                const long long ub = ((long long)mb * ncb + cb) * G;
-                const int wf = unit_owner(U, grid, ub);
-                const int wl = unit_owner(U, grid, ub + G - 1);
-                const uint32_t old = atomicAdd(&counters[wf], 1u);
-                s_first = (old == (uint32_t)(wl - wf)) ? wf : -1;
-                s_last_w = wl;
-                if (s_first >= 0)
-                    __hip_atomic_store(&counters[wf], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            __syncthreads();
-            const int wf = s_first, wl = s_last_w;
-            have = wf >= 0;
-            if (have) {
-                __threadfence();
-                const long long ub = ((long long)mb * ncb + cb) * G;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[r] = 0.f;
-                for (int v = wf; v <= wl; ++v) {
-                    const int sl = unit_start(U, grid, v) < ub ? 1 : 0;
-                    const float *pv = partial + ((size_t)v * 2 + sl) * kSlotFloats;
-                    if (tile_live) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (4 * h + r < Mb)
-                                acc[r] += ld_agent(&pv[(4 * h + r) * kBlockCols + wave * 16 + col]);
-                    }
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            while (true) {
+                // phase A: prefetch the batch after A into bB, compute A
+                int tgB = tgA, gB = gA + kB;
+                if (gB >= G) {
+                    tgB += gridDim.x;
+                    gB = 0;
                 }
+                const int tileB = tgB * nwaves + wave;
+                const bool liveB = tgB < p.ntg && tileB * 16 < N;
+                const LaneGrid LB = lane_grid(tileB, col, h, N, K, G, liveB);
+                load_batch(bB, rw, rs, rz, LB, gB, G);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_batch<NR>(bA, acc, xlane, gA, G, 0, Mb, LA.zsh, kmask, kbias);
+                __builtin_amdgcn_sched_barrier(0);
+                if (gA + kB >= G) {
+                    if (liveA)
+                        finish_tile(acc, m0, Mb, tileA * 16 + col);
+                    acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+                if (tgB >= p.ntg)
+                    break;
+                // phase B: prefetch the batch after B into bA, compute B
+                int tgC = tgB, gC = gB + kB;
+                if (gC >= G) {
+                    tgC += gridDim.x;
+                    gC = 0;
+                }
+                const int tileC = tgC * nwaves + wave;
+                const bool liveC = tgC < p.ntg && tileC * 16 < N;
+                const LaneGrid LC = lane_grid(tileC, col, h, N, K, G, liveC);
+                load_batch(bA, rw, rs, rz, LC, gC, G);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_batch<NR>(bB, acc, xlane, gB, G, 0, Mb, LB.zsh, kmask, kbias);
+                __builtin_amdgcn_sched_barrier(0);
+                if (gB + kB >= G) {
+                    if (liveB)
+                        finish_tile(acc, m0, Mb, tileB * 16 + col);
+                    acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+                if (tgC >= p.ntg)
+                    break;
+                tgA = tgC;
+                gA = gC;
+                tileA = tileC;
+                liveA = liveC;
+                LA = LC;
             }
         }
-        if (have && tile_live && n < N) {
-            if (a.Y) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 4 * h + r;
-                    if (row < Mb) {
-                        const size_t o = (size_t)(m0 + row) * N + n;
-                        if (a.y_f32)
-                            ((float *)a.Y)[o] = acc[r];
-                        else
-                            ((uint16_t *)a.Y)[o] = f32_to_bf16_rne(acc[r]);
-                    }
+    } else {
+        // ---- split mode: item = (m-block, group of tw tiles); wave = (tile slot, K slice)
+        const int tslot = wave % p.tw, ks = wave / p.tw;
+        for (int it = blockIdx.x; it < p.items; it += gridDim.x) {
+            const int mb = it / p.ntg, tg = it - mb * p.ntg;
+            const int m0 = mb * 16;
+            const int Mb = M - m0 < 16 ? M - m0 : 16;
+            const int xrow = col < Mb ? col : Mb - 1;
+            const int tile = tg * p.tw + tslot;
+            const bool live = tile * 16 < N;
+            const LaneGrid L = lane_grid(tile, col, h, N, K, G, live);
+            if (a.lmhead && mb != cur_mb) {
+                if (cur_mb >= 0)
+                    flush_best(cur_mb);
+                cur_mb = mb;
+            }
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            for (int c0 = 0; c0 < G; c0 += p.chunk) {
+                const int c1 = G < c0 + p.chunk ? G : c0 + p.chunk;
+                const int per = (c1 - c0 + p.sk - 1) / p.sk;
+                const int g0 = c0 + ks * per;
+                const int g1 = c1 < g0 + per ? c1 : g0 + per;
+                Batch b0, b1;
+                load_batch(b0, rw, rs, rz, L, g0, g1); // in flight while X is staged
+                if (!(mb == st_mb && c0 == st_c0 && c1 == st_c1)) {
+                    __syncthreads();
+                    stage_x<kStageUnrollNarrow>(a.X, K, m0, Mb, c0, c1, xs, tid, nthreads);
+                    __syncthreads();
+                    st_mb = mb;
+                    st_c0 = c0;
+                    st_c1 = c1;
+                }
+                const u32x4_t *xlane = xs + (4 * h) * Mb + xrow;
+                for (int g = g0; g < g1; g += 2 * kB) {
+                    load_batch(b1, rw, rs, rz, L, g + kB, g1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute_batch<NR>(b0, acc, xlane, g, g1, c0, Mb, L.zsh, kmask, kbias);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_batch(b0, rw, rs, rz, L, g + 2 * kB, g1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute_batch<NR>(b1, acc, xlane, g + kB, g1, c0, Mb, L.zsh, kmask, kbias);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            if (a.lmhead) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (4 * h + r < Mb)
-                        best[r] = max_u64(best[r], argmax_key(acc[r], n));
+            if (p.sk > 1) {
+                // sum the K slices of each tile through LDS, slice 0 first, in slice order
+                *(f32x4_t *)(red + ((size_t)wave * 64 + lane) * 4) = acc;
+                __syncthreads();
+                if (ks == 0) {
+                    for (int s = 1; s < p.sk; ++s) {
+                        const f32x4_t o = *(const f32x4_t *)(red + ((size_t)(s * p.tw + tslot) * 64 + lane) * 4);
+                        acc[0] += o[0];
+                        acc[1] += o[1];
+                        acc[2] += o[2];
+                        acc[3] += o[3];
+                    }
+                }
+                __syncthreads();
             }
+            if (ks == 0 && live)
+                finish_tile(acc, m0, Mb, tile * 16 + col);
         }
-        u += gb - ga;
     }
 
     if (a.lmhead) {
         if (cur_mb >= 0)
             flush_best(cur_mb);
-        __threadfence();
+        wait_device_writes();
         __syncthreads();
         if (tid == 0) {
-            const uint32_t old = atomicAdd(ticket, 1u);
-            s_first = (old == (uint32_t)(grid - 1)) ? 1 : 0;
+            const uint32_t old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_flag = (old == (uint32_t)(gridDim.x - 1)) ? 1 : 0;
         }
         __syncthreads();
-        if (s_first && tid < 64) {
-            __threadfence();
+        if (s_flag && tid < 64) {
             int am = 0;
             bool mism = false;
             if (tid < M) {
@@ -321,37 +444,61 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(SkinnyArgs a, SkinnyPl
     }
 }
 
-} // namespace
-
-static void set_chunk(SkinnyPlan &p, int M, size_t lds_limit)
+size_t lds_for(const SkinnyPlan &p, int M)
 {
     const int mrows = M < 16 ? M : 16;
-    int chunk = (int)(lds_limit / ((size_t)mrows * 256 + 64));
-    if (chunk > p.G)
-        chunk = p.G;
-    if (chunk < 1)
-        chunk = 1;
-    p.chunk = chunk;
-    p.lds_bytes = (size_t)chunk * 256 * mrows + (size_t)chunk * 64;
+    const size_t red = p.sk > 1 ? (size_t)p.tw * p.sk * 1024 : 0;
+    return (size_t)p.chunk * 256 * mrows + red;
 }
 
-SkinnyPlan plan_skinny(int M, int N, int K, int lmhead)
+} // namespace
+
+SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit)
 {
-    (void)lmhead;
     SkinnyPlan p{};
+    if (lds_limit == 0 || lds_limit > kLdsBudget)
+        lds_limit = kLdsBudget;
     p.G = K / kGroup;
     p.mblocks = (M + 15) / 16;
-    p.ncb = (N + kBlockCols - 1) / kBlockCols;
-    p.units = (long long)p.mblocks * p.ncb * p.G;
-    set_chunk(p, M, kLdsBudget);
-    long long grid = kCUs;
-    if (grid > p.units)
-        grid = p.units;
-    if (grid > kMaxGrid)
-        grid = kMaxGrid;
-    p.grid = (int)grid;
-    p.off_partial = kZeroRegion;
-    p.ws_bytes = p.off_partial + (size_t)p.grid * 2 * kSlotFloats * sizeof(float);
+    p.nt = (N + 15) / 16;
+    const int mrows = M < 16 ? M : 16;
+    const size_t per_group = (size_t)mrows * 256;
+    const long long tiles = (long long)p.nt * p.mblocks;
+    const int stream_waves = 8;
+    if (tiles >= 16LL * kCUs && (size_t)p.G * per_group <= lds_limit) {
+        // many tiles (a vocabulary-sized lm_head): persistent workgroups, whole tiles per wave
+        p.stream = 1;
+        p.sk = 1;
+        p.tw = stream_waves;
+        p.chunk = p.G;
+        p.ntg = (p.nt + p.tw - 1) / p.tw;
+        p.items = p.mblocks * p.ntg;
+        const size_t lds = lds_for(p, M);
+        int per_cu = (int)(lds_limit / (lds ? lds : 1));
+        per_cu = per_cu < 1 ? 1 : per_cu > 2 ? 2 : per_cu;
+        p.grid = p.ntg < kCUs * per_cu ? p.ntg : kCUs * per_cu;
+    } else {
+        // few tiles: each workgroup takes tw tiles and splits K over sk waves per tile
+        p.stream = 0;
+        int tw = (int)((tiles + kCUs - 1) / kCUs);
+        tw = tw < 1 ? 1 : tw > kMaxWaves ? kMaxWaves : tw;
+        int sk = kMaxWaves / tw;
+        const int max_sk = p.G / 2 > 1 ? p.G / 2 : 1; // slices of at least two groups
+        sk = sk > max_sk ? max_sk : sk;
+        sk = sk < 1 ? 1 : sk;
+        p.tw = tw;
+        p.sk = sk;
+        const size_t red = sk > 1 ? (size_t)tw * sk * 1024 : 0;
+        int chunk = (int)((lds_limit - red) / per_group);
+        chunk = chunk > p.G ? p.G : chunk < 1 ? 1 : chunk;
+        p.chunk = chunk;
+        p.ntg = (p.nt + tw - 1) / tw;
+        p.items = p.mblocks * p.ntg;
+        p.grid = p.items;
+    }
+    p.waves = p.tw * p.sk;
+    p.lds_bytes = lds_for(p, M);
+    p.ws_bytes = lmhead ? kZeroRegion : 0; // only lm_head uses scratch (argmax keys, ticket)
     return p;
 }
 
@@ -366,16 +513,36 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, hipStream_
             e = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
         if (e != hipSuccess)
             return e;
-        size_t lim = (size_t)v > 2048 ? (size_t)v - 2048 : 0;
+        const size_t lim = (size_t)v > 4096 ? (size_t)v - 4096 : 0; // room for the static LDS
         lds_limit = lim < kLdsBudget ? lim : kLdsBudget;
-        if (lds_limit > 64 * 1024)
-            (void)hipFuncSetAttribute((const void *)skinny_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                      (int)lds_limit);
+        if (lds_limit > 64 * 1024) {
+            const void *fns[] = {(const void *)skinny_kernel<1, false>, (const void *)skinny_kernel<2, false>,
+                                 (const void *)skinny_kernel<4, false>, (const void *)skinny_kernel<1, true>,
+                                 (const void *)skinny_kernel<2, true>, (const void *)skinny_kernel<4, true>};
+            for (const void *f : fns)
+                (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_limit);
+        }
     }
-    SkinnyPlan p = plan;
+    const SkinnyPlan p = plan.lds_bytes > lds_limit ? plan_skinny(a.M, a.N, a.K, a.lmhead, lds_limit) : plan;
     if (p.lds_bytes > lds_limit)
-        set_chunk(p, a.M, lds_limit);
-    hipLaunchKernelGGL(skinny_kernel, dim3(p.grid), dim3(kThreads), p.lds_bytes, stream, a, p);
+        return hipErrorInvalidValue;
+    const dim3 block(64 * p.waves), grid(p.grid);
+    const int nr = a.M == 1 ? 1 : a.M == 2 ? 2 : 4;
+    if (p.stream) {
+        if (nr == 1)
+            hipLaunchKernelGGL((skinny_kernel<1, true>), grid, block, p.lds_bytes, stream, a, p);
+        else if (nr == 2)
+            hipLaunchKernelGGL((skinny_kernel<2, true>), grid, block, p.lds_bytes, stream, a, p);
+        else
+            hipLaunchKernelGGL((skinny_kernel<4, true>), grid, block, p.lds_bytes, stream, a, p);
+    } else {
+        if (nr == 1)
+            hipLaunchKernelGGL((skinny_kernel<1, false>), grid, block, p.lds_bytes, stream, a, p);
+        else if (nr == 2)
+            hipLaunchKernelGGL((skinny_kernel<2, false>), grid, block, p.lds_bytes, stream, a, p);
+        else
+            hipLaunchKernelGGL((skinny_kernel<4, false>), grid, block, p.lds_bytes, stream, a, p);
+    }
     return hipGetLastError();
 }
 

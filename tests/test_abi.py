@@ -63,7 +63,7 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_bytes_host_only(lib):
-    assert w4.w4a16_workspace_bytes(0, 1, 9728, 2560) > 0
+    assert w4.w4a16_workspace_bytes(0, 1, 9728, 2560) == 0  # small M owns whole columns: no scratch
     assert w4.w4a16_workspace_bytes(1, 16, 151936, 2560) > 0
     assert w4.w4a16_workspace_bytes(0, 8192, 2560, 9728) >= 8192 * 76 * 4  # group sums
     assert w4.w4a16_workspace_bytes(0, 1, 512, 512, group=64) == 0
@@ -99,11 +99,12 @@ def test_linear_rejections(lib):
     assert linear(lib, X=MIS) == ERR_ALIGN
     assert linear(lib, Y=MIS) == ERR_ALIGN
     assert linear(lib, qz=MIS) == ERR_ALIGN
-    assert linear(lib, ws=NUL) == ERR_WORKSPACE
-    assert linear(lib, wsb=16) == ERR_WORKSPACE
-    need = w4.w4a16_workspace_bytes(0, 1, 512, 512)
-    assert linear(lib, wsb=need - 1) == ERR_WORKSPACE
-    assert linear(lib, M=300, wsb=16) == ERR_WORKSPACE        # tiled path also needs scratch
+    # (only shapes that need scratch: a call that passes validation would launch)
+    need = w4.w4a16_workspace_bytes(0, 300, 512, 512)
+    assert need > 0
+    assert linear(lib, M=300, ws=NUL) == ERR_WORKSPACE
+    assert linear(lib, M=300, wsb=16) == ERR_WORKSPACE
+    assert linear(lib, M=300, wsb=need - 1) == ERR_WORKSPACE
 
 
 def test_linear_empty_is_a_noop(lib):
