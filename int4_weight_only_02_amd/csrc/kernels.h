@@ -30,19 +30,22 @@ hipError_t launch_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K,
 //               split over sk waves and summed through LDS in slice order;
 //   stream mode (stream == 1): persistent workgroups of tw waves; each wave takes
 //               whole tiles (tile groups blockIdx.x, +grid, ...) over all of K.
-// X for the m-block is staged in LDS in chunks of `chunk` groups (all of K when it
-// fits).
+// With xlds, X of the m-block is staged in LDS in chunks of `chunk` groups (all of
+// K when it fits; stream mode requires that); without it (split mode only) each
+// wave reads its K slice of X from global memory and chunk is 0.
 struct SkinnyPlan {
     int mblocks;   // ceil(M / 16)
     int nt;        // ceil(N / 16) column tiles
     int G;         // K / 128
     int waves;     // waves per workgroup = tw * sk
     int tw, sk;    // tiles per item, K slices per tile
-    int chunk;     // groups of X per LDS stage
+    int chunk;     // groups of X staged in LDS at once (all of K when it fits)
+    int per;       // groups per K slice (split mode; a multiple of 4)
     int ntg;       // tile groups per m-block = ceil(nt / tw)
     int items;     // mblocks * ntg
     int grid;      // workgroups
     int stream;    // 1: stream mode
+    int xlds;      // 1: X staged in LDS
     size_t lds_bytes;
     size_t ws_bytes; // lm_head: the zero region (argmax keys, ticket); linear: 0
 };

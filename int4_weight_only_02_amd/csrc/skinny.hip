@@ -8,19 +8,22 @@
 //   * a wave owns a 16-column tile (or a K slice of one); lane l holds column l%16
 //     and, per group of 128 codes, one 16-byte load = 32 codes = the B operand of
 //     four v_mfma_f32_16x16x32_bf16 (lane group l/16 covers codes 32*(l/16) .. +31);
-//   * the activations X[m-block][K] sit in LDS, permuted to the fragment order and
-//     shared by every wave of the workgroup;
+//   * the activations X[m-block][K] are staged once per workgroup in LDS, permuted
+//     to the fragment order and shared by all its waves;
 //   * per group, eight MFMAs accumulate P = sum x * (q - z) in fp32: four with the
-//     exact biased codes 128 + q and, interleaved, four with the column constant
-//     -(128 + z) (also exact in bf16: at most 8 significant bits), so the bias and
-//     the zero-point cancel inside the accumulator.  The group is then scaled in
-//     fp32: acc += s * P.  The matrix cores are otherwise idle in this
+//     exact biased codes 128 + q and four with the column constant -(128 + z) (also
+//     exact in bf16: at most 8 significant bits), in two independent chains, so the
+//     bias and the zero-point cancel inside the accumulators.  The group is then
+//     scaled in fp32: acc += s * P.  The matrix cores are otherwise idle in this
 //     memory-bound kernel, so the zero-point costs no VALU work beyond building
-//     its fragment.
+//     its fragment;
+//   * when K is a multiple of 512, the scales and zero words of four groups arrive
+//     in one 8-byte and one 16-byte load: 1.5 memory instructions per 1 KB of codes.
 // Every workgroup owns whole output columns, so no partial sum crosses a workgroup:
 //   split mode   (few tiles: decode, the 7 projections of a decoder layer) -- a
-//                workgroup takes tw tiles and splits K over sk waves per tile; the
-//                sk partial accumulators are summed through LDS in a fixed order;
+//                workgroup takes tw tiles and splits K over sk waves per tile; each
+//                wave requests its first three batches before X is staged; the sk
+//                partial accumulators are summed through LDS in a fixed order;
 //   stream mode  (many tiles: the 151936-column lm_head) -- persistent workgroups,
 //                each wave walks its own sequence of whole tiles with the next
 //                batch of loads always in flight, across tile boundaries.
@@ -31,6 +34,9 @@
 // fp32 logits, folds each finished column into a per-row (value, column) key,
 // reduces the keys with 64-bit atomic max (ties -> lowest column), and the last
 // workgroup turns them into argmax ids and the accepted-prefix length.
+#include <cstdio>
+#include <cstdlib>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -38,14 +44,15 @@ namespace w4a16 {
 
 namespace {
 
-constexpr int kMaxWaves = 16;
-constexpr int kMaxThreads = kMaxWaves * 64;
-constexpr int kB = 4;           // groups per register batch (two batches in flight)
-constexpr int kStageUnrollWide = 8;  // X staging loads in flight per thread (512-thread workgroups)
-constexpr int kStageUnrollNarrow = 2; // (1024-thread workgroups: 128 VGPRs per lane)
+constexpr int kMaxWaves = 8;           // up to 512 threads per workgroup (256 VGPRs per lane)
+constexpr int kStreamWaves = 8;
+constexpr int kB = 4;                  // groups per register batch
+constexpr int kStageUnrollStream = 8;  // X staging loads in flight per thread
+constexpr int kStageUnrollSplit = 4;
 constexpr int kCUs = 256;
 constexpr size_t kLdsBudget = 160 * 1024 - 4096;
 constexpr uint32_t kOob = 0xFFFFFF00u; // an offset past the end of every tensor
+constexpr int kSplitDirect = 0, kSplitLds = 1, kStream = 2;
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m)
 {
@@ -64,7 +71,7 @@ __device__ __forceinline__ unsigned long long max_u64(unsigned long long a, unsi
 // the XCDs' L2s.  The only ordering needed is that a workgroup's device-scope
 // atomics have completed before it takes its ticket: s_waitcnt vmcnt(0) (vmcnt
 // counts stores and no-return atomics on gfx9).  Agent-scope fences would instead
-// write back and invalidate a whole L2 (buffer_wbl2 / buffer_inv).
+// write back and invalidate a whole L2.
 __device__ __forceinline__ void wait_device_writes()
 {
     __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0), expcnt and lgkmcnt unconstrained
@@ -108,21 +115,45 @@ struct Batch {
     uint32_t z[kB];
 };
 
+// The scales and zero words of groups at byte offsets so, zo (kOob: none).  ALIGNED
+// (G and the first group multiples of 4): one 8-byte and one 16-byte load.
+template <bool ALIGNED>
+__device__ __forceinline__ void load_params(uint32_t (&sc)[kB], uint32_t (&zw)[kB], __amdgpu_buffer_rsrc_t rs,
+                                            __amdgpu_buffer_rsrc_t rz, uint32_t so, uint32_t zo)
+{
+    if constexpr (ALIGNED) {
+        typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+        const u32x2_t sv = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, so, 0, 0));
+        const u32x4_t zv = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rz, zo, 0, 0));
+        sc[0] = sv.x & 0xFFFFu;
+        sc[1] = sv.x >> 16;
+        sc[2] = sv.y & 0xFFFFu;
+        sc[3] = sv.y >> 16;
+        zw[0] = zv.x;
+        zw[1] = zv.y;
+        zw[2] = zv.z;
+        zw[3] = zv.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < kB; ++i) {
+            sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, so + 2u * i, 0, 0);
+            zw[i] = __builtin_amdgcn_raw_buffer_load_b32(rz, zo + 4u * i, 0, 0);
+        }
+    }
+}
+
 // Load groups gs .. gs+kB-1 (unconditionally: a batch starting at or past gend
-// loads from kOob and costs no memory traffic).
+// loads from kOob and costs no memory traffic)
+template <bool ALIGNED>
 __device__ __forceinline__ void load_batch(Batch &b, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rs,
                                            __amdgpu_buffer_rsrc_t rz, const LaneGrid &L, int gs, int gend)
 {
     const bool in = gs < gend;
     const uint32_t wo = in ? L.wo + 64u * (uint32_t)gs : kOob;
-    const uint32_t so = in ? L.so + 2u * (uint32_t)gs : kOob;
-    const uint32_t zo = in ? L.zo + 4u * (uint32_t)gs : kOob;
 #pragma unroll
-    for (int i = 0; i < kB; ++i) {
+    for (int i = 0; i < kB; ++i)
         b.w[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 64u * i, 0, 0));
-        b.s[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, so + 2u * i, 0, 0);
-        b.z[i] = __builtin_amdgcn_raw_buffer_load_b32(rz, zo + 4u * i, 0, 0);
-    }
+    load_params<ALIGNED>(b.s, b.z, rs, rz, in ? L.so + 2u * (uint32_t)gs : kOob, in ? L.zo + 4u * (uint32_t)gs : kOob);
 }
 
 // 8 codes -> MFMA fragment, with the mask and the bias held in registers so that
@@ -138,10 +169,12 @@ __device__ __forceinline__ bf16x8_t codes_to_frag_r(uint32_t w, uint32_t mask, u
 }
 
 // Per group: P = sum x * (128 + q) + sum x * (-(128 + z)) = sum x * (q - z) for this
-// lane's column and the rows 4h .. 4h+3 (D layout), then acc += s * P.  Groups at
-// or past gend get s = 0 (their data is finite, so the product is exactly 0).
-// xlane points at the lane's X row in the staged chunk starting at group st_c0.
-// NR = the accumulator rows that can hold real output (1 for M = 1, 2 for M = 2).
+// lane's column and the rows 4h .. 4h+3 (D layout), then acc += s * P.  Both halves
+// are exact products accumulated in fp32 (two independent chains, added before the
+// scale).  Groups at or past gend get s = 0 (their data is finite, so the product
+// is exactly 0).  xlane points at the lane's X row in the staged chunk starting at
+// group st_c0.  NR = the accumulator rows that can hold real output (1 for M = 1,
+// 2 for M = 2).
 template <int NR>
 __device__ __forceinline__ void compute_batch(const Batch &b, f32x4_t &acc, const u32x4_t *xlane, int gs,
                                               int gend, int st_c0, int Mb, int zsh, uint32_t mask,
@@ -155,50 +188,116 @@ __device__ __forceinline__ void compute_batch(const Batch &b, f32x4_t &acc, cons
         // -(128 + z) as a bf16 pair: sign | exponent of 128 | z in the mantissa
         const uint32_t zb = (((b.z[i] >> zsh) & 15u) | 0xC300u) * 0x00010001u;
         const bf16x8_t zfrag = __builtin_bit_cast(bf16x8_t, u32x4_t{zb, zb, zb, zb});
-        f32x4_t p = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t pq = {0.f, 0.f, 0.f, 0.f}, pz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, xg[j * Mb]);
             const uint32_t wj = j == 0 ? b.w[i].x : j == 1 ? b.w[i].y : j == 2 ? b.w[i].z : b.w[i].w;
-            p = mfma16x16x32(xa, codes_to_frag_r(wj, mask, bias), p);
-            p = mfma16x16x32(xa, zfrag, p);
+            pq = mfma16x16x32(xa, codes_to_frag_r(wj, mask, bias), pq);
+            pz = mfma16x16x32(xa, zfrag, pz);
         }
         const float s = g < gend ? f16_bits_to_f32((uint16_t)b.s[i]) : 0.f;
 #pragma unroll
         for (int r = 0; r < NR; ++r)
-            acc[r] = fmaf(s, p[r], acc[r]);
+            acc[r] = fmaf(s, pq[r] + pz[r], acc[r]);
     }
 }
 
-// Stage X[m0 .. m0+Mb)[groups s0 .. s1) into LDS in fragment order: thread t takes
-// the 16-byte chunks kc = t, t + nthreads, ... of every row, so no index needs a
-// division; up to kStageUnroll rows' loads are in flight per thread.  Caller
-// synchronizes around it.
+// Direct variant of the split mode, for shapes where every workgroup needs many
+// X rows and has few tiles to share them (M = 16 with one tile per workgroup): each
+// wave reads only its K slice of X, straight from global memory (L2), together with
+// its weights, so all of it is in flight at once instead of passing through a
+// staging round.  A BatchX holds kB groups of the lane's column and the lane's X
+// fragments for them (row m0 + xrow, codes 32h .. 32h+31 of each group).
+struct BatchX {
+    u32x4_t w[kB];
+    u32x4_t x[kB][4];
+    uint32_t s[kB];
+    uint32_t z[kB];
+};
+
+// xo = byte offset of the lane's X fragment for group 0 (row * 2K + 64 h)
+template <bool ALIGNED>
+__device__ __forceinline__ void load_batch_x(BatchX &b, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rs,
+                                             __amdgpu_buffer_rsrc_t rz, __amdgpu_buffer_rsrc_t rx,
+                                             const LaneGrid &L, uint32_t xo, int gs, int gend)
+{
+    const bool in = gs < gend;
+    const uint32_t wo = in ? L.wo + 64u * (uint32_t)gs : kOob;
+    const uint32_t xg = in ? xo + 256u * (uint32_t)gs : kOob;
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+        b.w[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, wo + 64u * i, 0, 0));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            b.x[i][j] =
+                __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, xg + 256u * i + 16u * j, 0, 0));
+    }
+    load_params<ALIGNED>(b.s, b.z, rs, rz, in ? L.so + 2u * (uint32_t)gs : kOob, in ? L.zo + 4u * (uint32_t)gs : kOob);
+}
+
+// compute_batch with the X fragments taken from the batch (permuted in registers)
+template <int NR>
+__device__ __forceinline__ void compute_batch_x(const BatchX &b, f32x4_t &acc, int gs, int gend, int zsh,
+                                                uint32_t mask, uint32_t bias)
+{
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+        const int g = gs + i;
+        const uint32_t zb = (((b.z[i] >> zsh) & 15u) | 0xC300u) * 0x00010001u;
+        const bf16x8_t zfrag = __builtin_bit_cast(bf16x8_t, u32x4_t{zb, zb, zb, zb});
+        f32x4_t pq = {0.f, 0.f, 0.f, 0.f}, pz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, x_permute8(b.x[i][j]));
+            const uint32_t wj = j == 0 ? b.w[i].x : j == 1 ? b.w[i].y : j == 2 ? b.w[i].z : b.w[i].w;
+            pq = mfma16x16x32(xa, codes_to_frag_r(wj, mask, bias), pq);
+            pz = mfma16x16x32(xa, zfrag, pz);
+        }
+        const float s = g < gend ? f16_bits_to_f32((uint16_t)b.s[i]) : 0.f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+            acc[r] = fmaf(s, pq[r] + pz[r], acc[r]);
+    }
+}
+
+// Stage X[m0 .. m0+Mb)[groups s0 .. s1) into LDS in fragment order.  LDS slot i holds
+// chunk kc = i / Mb (group kc/16, c = kc%16) of row m = i % Mb, so consecutive
+// threads write consecutive 16-byte slots (no bank conflicts); the quotient comes
+// from a multiply by ceil(2^32 / Mb).  kStageUnroll loads per thread are in flight
+// at once.  Caller synchronizes around it.
 template <int kStageUnroll>
 __device__ __forceinline__ void stage_x(const uint16_t *X, int K, int m0, int Mb, int s0, int s1,
                                         u32x4_t *xs, int tid, int nthreads)
 {
-    const int R = (s1 - s0) * 16; // 16-byte chunks per row
-    for (int kc = tid; kc < R; kc += nthreads) {
-        const uint16_t *src = X + (size_t)m0 * K + (size_t)s0 * kGroup + kc * 8;
-        u32x4_t *dst = xs + kc * Mb; // chunk kc = (group kc/16, c = kc%16): [(gl*16 + c)*Mb + m]
-        for (int m = 0; m < Mb; m += kStageUnroll) {
-            u32x4_t v[kStageUnroll];
+    const int total = Mb * (s1 - s0) * 16;
+    const unsigned long long magic = ((1ull << 32) + (unsigned)Mb - 1) / (unsigned)Mb;
+    const uint16_t *base = X + (size_t)m0 * K + (size_t)s0 * kGroup;
+    for (int i0 = 0; i0 < total; i0 += nthreads * kStageUnroll) {
+        u32x4_t v[kStageUnroll];
 #pragma unroll
-            for (int u = 0; u < kStageUnroll; ++u)
-                if (m + u < Mb)
-                    v[u] = *(const u32x4_t *)(src + (size_t)(m + u) * K);
+        for (int u = 0; u < kStageUnroll; ++u) {
+            const int i = i0 + u * nthreads + tid;
+            if (i < total) {
+                const int kc = (int)(((unsigned long long)(unsigned)i * magic) >> 32);
+                const int m = i - kc * Mb;
+                v[u] = *(const u32x4_t *)(base + (size_t)m * K + kc * 8);
+            }
+        }
 #pragma unroll
-            for (int u = 0; u < kStageUnroll; ++u)
-                if (m + u < Mb)
-                    dst[m + u] = x_permute8(v[u]);
+        for (int u = 0; u < kStageUnroll; ++u) {
+            const int i = i0 + u * nthreads + tid;
+            if (i < total)
+                xs[i] = x_permute8(v[u]);
         }
     }
 }
 
-template <int NR, bool STREAM>
-__global__ __launch_bounds__(STREAM ? 512 : kMaxThreads) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
+// MODE: kSplitDirect, kSplitLds or kStream (see the plan)
+template <int NR, int MODE, bool ALIGNED>
+__global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
 {
+    constexpr bool STREAM = MODE == kStream;
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ unsigned long long kred[kMaxWaves][16];
     __shared__ int s_flag;
@@ -209,7 +308,7 @@ __global__ __launch_bounds__(STREAM ? 512 : kMaxThreads) void skinny_kernel(Skin
     const int nthreads = blockDim.x, nwaves = nthreads >> 6;
     const int mrows = M < 16 ? M : 16;
 
-    u32x4_t *xs = (u32x4_t *)smem;                              // [group][chunk c][row]
+    u32x4_t *xs = (u32x4_t *)smem;                                // [group][chunk c][row]
     float *red = (float *)(smem + (size_t)p.chunk * 256 * mrows); // [wave][64 lanes][4]
     uint32_t *ticket = (uint32_t *)(a.ws + kOffTicket);
     unsigned long long *keys = (unsigned long long *)(a.ws + kOffKeys);
@@ -217,6 +316,7 @@ __global__ __launch_bounds__(STREAM ? 512 : kMaxThreads) void skinny_kernel(Skin
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.qw, (uint32_t)((size_t)N * K / 2));
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales, (uint32_t)((size_t)N * G * 2));
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.qz, (uint32_t)((size_t)(N / 8) * G * 4));
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X, (uint32_t)((size_t)M * K * 2));
     // code-to-bf16 constants, pinned in VGPRs (see codes_to_frag_r)
     uint32_t kmask = 0x000F000Fu, kbias = kBiasBits;
     asm volatile("" : "+v"(kmask));
@@ -224,7 +324,6 @@ __global__ __launch_bounds__(STREAM ? 512 : kMaxThreads) void skinny_kernel(Skin
 
     unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
     int cur_mb = -1;
-    int st_mb = -1, st_c0 = 0, st_c1 = 0; // X groups [st_c0, st_c1) of m-block st_mb are in LDS
 
     auto flush_best = [&](int mb) {
         // reduce (value, column) keys over the 16 columns of each wave, then the waves
@@ -296,9 +395,9 @@ __global__ __launch_bounds__(STREAM ? 512 : kMaxThreads) void skinny_kernel(Skin
             bool liveA = tgA < p.ntg && tileA * 16 < N;
             LaneGrid LA = lane_grid(tileA, col, h, N, K, G, liveA);
             Batch bA, bB;
-            load_batch(bA, rw, rs, rz, LA, gA, G); // in flight while X is staged
+            load_batch<ALIGNED>(bA, rw, rs, rz, LA, gA, G); // in flight while X is staged
             __syncthreads();
-            stage_x<kStageUnrollWide>(a.X, K, m0, Mb, 0, G, xs, tid, nthreads);
+            stage_x<kStageUnrollStream>(a.X, K, m0, Mb, 0, G, xs, tid, nthreads);
             __syncthreads();
 
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -312,7 +411,7 @@ __global__ __launch_bounds__(STREAM ? 512 : kMaxThreads) void skinny_kernel(Skin
                 const int tileB = tgB * nwaves + wave;
                 const bool liveB = tgB < p.ntg && tileB * 16 < N;
                 const LaneGrid LB = lane_grid(tileB, col, h, N, K, G, liveB);
-                load_batch(bB, rw, rs, rz, LB, gB, G);
+                load_batch<ALIGNED>(bB, rw, rs, rz, LB, gB, G);
                 __builtin_amdgcn_sched_barrier(0);
                 compute_batch<NR>(bA, acc, xlane, gA, G, 0, Mb, LA.zsh, kmask, kbias);
                 __builtin_amdgcn_sched_barrier(0);
@@ -332,7 +431,7 @@ __global__ __launch_bounds__(STREAM ? 512 : kMaxThreads) void skinny_kernel(Skin
                 const int tileC = tgC * nwaves + wave;
                 const bool liveC = tgC < p.ntg && tileC * 16 < N;
                 const LaneGrid LC = lane_grid(tileC, col, h, N, K, G, liveC);
-                load_batch(bA, rw, rs, rz, LC, gC, G);
+                load_batch<ALIGNED>(bA, rw, rs, rz, LC, gC, G);
                 __builtin_amdgcn_sched_barrier(0);
                 compute_batch<NR>(bB, acc, xlane, gB, G, 0, Mb, LB.zsh, kmask, kbias);
                 __builtin_amdgcn_sched_barrier(0);
@@ -353,6 +452,7 @@ __global__ __launch_bounds__(STREAM ? 512 : kMaxThreads) void skinny_kernel(Skin
     } else {
         // ---- split mode: item = (m-block, group of tw tiles); wave = (tile slot, K slice)
         const int tslot = wave % p.tw, ks = wave / p.tw;
+        int st_mb = -1, st_c0 = -1; // kSplitLds: X groups [st_c0, st_c0 + chunk) of m-block st_mb are in LDS
         for (int it = blockIdx.x; it < p.items; it += gridDim.x) {
             const int mb = it / p.ntg, tg = it - mb * p.ntg;
             const int m0 = mb * 16;
@@ -367,31 +467,65 @@ __global__ __launch_bounds__(STREAM ? 512 : kMaxThreads) void skinny_kernel(Skin
                 cur_mb = mb;
             }
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            for (int c0 = 0; c0 < G; c0 += p.chunk) {
-                const int c1 = G < c0 + p.chunk ? G : c0 + p.chunk;
-                const int per = (c1 - c0 + p.sk - 1) / p.sk;
-                const int g0 = c0 + ks * per;
-                const int g1 = c1 < g0 + per ? c1 : g0 + per;
-                Batch b0, b1;
-                load_batch(b0, rw, rs, rz, L, g0, g1); // in flight while X is staged
-                if (!(mb == st_mb && c0 == st_c0 && c1 == st_c1)) {
-                    __syncthreads();
-                    stage_x<kStageUnrollNarrow>(a.X, K, m0, Mb, c0, c1, xs, tid, nthreads);
-                    __syncthreads();
-                    st_mb = mb;
-                    st_c0 = c0;
-                    st_c1 = c1;
+            if constexpr (MODE == kSplitLds) {
+                for (int c0 = 0; c0 < G; c0 += p.chunk) {
+                    const int c1 = G < c0 + p.chunk ? G : c0 + p.chunk;
+                    // slices of p.per groups (a multiple of kB): batches stay 4-aligned
+                    const int g0 = c0 + ks * p.per;
+                    const int g1 = c1 < g0 + p.per ? c1 : g0 + p.per;
+                    // three register batches: up to 3 * kB groups of the slice are requested
+                    // before X is staged, so their HBM latency overlaps the staging
+                    Batch b0, b1, b2;
+                    load_batch<ALIGNED>(b0, rw, rs, rz, L, g0, g1);
+                    load_batch<ALIGNED>(b1, rw, rs, rz, L, g0 + kB, g1);
+                    load_batch<ALIGNED>(b2, rw, rs, rz, L, g0 + 2 * kB, g1);
+                    if (!(mb == st_mb && c0 == st_c0)) {
+                        __syncthreads();
+                        stage_x<kStageUnrollSplit>(a.X, K, m0, Mb, c0, c1, xs, tid, nthreads);
+                        __syncthreads();
+                        st_mb = mb;
+                        st_c0 = c0;
+                    }
+                    const u32x4_t *xlane = xs + (4 * h) * Mb + xrow;
+                    // rotate the three batches; loads stay unconditional (a batch past the
+                    // slice reads kOob), only fully masked computes are skipped (uniform
+                    // branches)
+                    for (int g = g0; g < g1; g += 3 * kB) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        compute_batch<NR>(b0, acc, xlane, g, g1, c0, Mb, L.zsh, kmask, kbias);
+                        __builtin_amdgcn_sched_barrier(0);
+                        load_batch<ALIGNED>(b0, rw, rs, rz, L, g + 3 * kB, g1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (g + kB < g1)
+                            compute_batch<NR>(b1, acc, xlane, g + kB, g1, c0, Mb, L.zsh, kmask, kbias);
+                        __builtin_amdgcn_sched_barrier(0);
+                        load_batch<ALIGNED>(b1, rw, rs, rz, L, g + 4 * kB, g1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (g + 2 * kB < g1)
+                            compute_batch<NR>(b2, acc, xlane, g + 2 * kB, g1, c0, Mb, L.zsh, kmask, kbias);
+                        __builtin_amdgcn_sched_barrier(0);
+                        load_batch<ALIGNED>(b2, rw, rs, rz, L, g + 5 * kB, g1);
+                    }
                 }
-                const u32x4_t *xlane = xs + (4 * h) * Mb + xrow;
+            } else {
+                const int g0 = ks * p.per;
+                const int g1 = G < g0 + p.per ? G : g0 + p.per;
+                const uint32_t xo = (uint32_t)(m0 + xrow) * (uint32_t)(2 * K) + 64u * (uint32_t)h;
+                // two register batches (weights, scales, zeros and X fragments): batch b+1 is
+                // in flight while batch b computes
+                BatchX b0, b1;
+                load_batch_x<ALIGNED>(b0, rw, rs, rz, rx, L, xo, g0, g1);
+                load_batch_x<ALIGNED>(b1, rw, rs, rz, rx, L, xo, g0 + kB, g1);
                 for (int g = g0; g < g1; g += 2 * kB) {
-                    load_batch(b1, rw, rs, rz, L, g + kB, g1);
                     __builtin_amdgcn_sched_barrier(0);
-                    compute_batch<NR>(b0, acc, xlane, g, g1, c0, Mb, L.zsh, kmask, kbias);
+                    compute_batch_x<NR>(b0, acc, g, g1, L.zsh, kmask, kbias);
                     __builtin_amdgcn_sched_barrier(0);
-                    load_batch(b0, rw, rs, rz, L, g + 2 * kB, g1);
+                    load_batch_x<ALIGNED>(b0, rw, rs, rz, rx, L, xo, g + 2 * kB, g1);
                     __builtin_amdgcn_sched_barrier(0);
-                    compute_batch<NR>(b1, acc, xlane, g + kB, g1, c0, Mb, L.zsh, kmask, kbias);
+                    if (g + kB < g1)
+                        compute_batch_x<NR>(b1, acc, g + kB, g1, L.zsh, kmask, kbias);
                     __builtin_amdgcn_sched_barrier(0);
+                    load_batch_x<ALIGNED>(b1, rw, rs, rz, rx, L, xo, g + 3 * kB, g1);
                 }
             }
             if (p.sk > 1) {
@@ -451,6 +585,24 @@ size_t lds_for(const SkinnyPlan &p, int M)
     return (size_t)p.chunk * 256 * mrows + red;
 }
 
+// Tuning override for the split-mode shape, read once from W4A16_SKINNY_SPLIT="tw,sk"
+// (tiles per workgroup, K slices per tile; tw * sk <= 8).  Unset: the heuristic.
+bool split_override(int *tw, int *sk)
+{
+    static int state = -1, otw = 0, osk = 0;
+    if (state < 0) {
+        state = 0;
+        const char *e = getenv("W4A16_SKINNY_SPLIT");
+        if (e && sscanf(e, "%d,%d", &otw, &osk) == 2 && otw >= 1 && osk >= 1 && otw * osk <= kMaxWaves)
+            state = 1;
+    }
+    *tw = otw;
+    *sk = osk;
+    return state == 1;
+}
+
+int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
 } // namespace
 
 SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit)
@@ -464,13 +616,14 @@ SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit)
     const int mrows = M < 16 ? M : 16;
     const size_t per_group = (size_t)mrows * 256;
     const long long tiles = (long long)p.nt * p.mblocks;
-    const int stream_waves = 8;
     if (tiles >= 16LL * kCUs && (size_t)p.G * per_group <= lds_limit) {
         // many tiles (a vocabulary-sized lm_head): persistent workgroups, whole tiles per wave
         p.stream = 1;
+        p.xlds = 1;
         p.sk = 1;
-        p.tw = stream_waves;
+        p.tw = kStreamWaves;
         p.chunk = p.G;
+        p.per = p.G;
         p.ntg = (p.nt + p.tw - 1) / p.tw;
         p.items = p.mblocks * p.ntg;
         const size_t lds = lds_for(p, M);
@@ -478,20 +631,32 @@ SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit)
         per_cu = per_cu < 1 ? 1 : per_cu > 2 ? 2 : per_cu;
         p.grid = p.ntg < kCUs * per_cu ? p.ntg : kCUs * per_cu;
     } else {
-        // few tiles: each workgroup takes tw tiles and splits K over sk waves per tile
+        // few tiles: each workgroup takes tw tiles and splits K over sk waves per tile;
+        // tw is the smallest count that keeps the grid within one workgroup per CU,
+        // sk gives each wave at least one batch of groups
         p.stream = 0;
         int tw = (int)((tiles + kCUs - 1) / kCUs);
         tw = tw < 1 ? 1 : tw > kMaxWaves ? kMaxWaves : tw;
+        const int batches = (p.G + kB - 1) / kB;
         int sk = kMaxWaves / tw;
-        const int max_sk = p.G / 2 > 1 ? p.G / 2 : 1; // slices of at least two groups
-        sk = sk > max_sk ? max_sk : sk;
+        sk = sk > batches ? batches : sk;
         sk = sk < 1 ? 1 : sk;
+        int otw = 0, osk = 0;
+        if (split_override(&otw, &osk)) {
+            tw = otw;
+            sk = osk;
+        }
+        const size_t red = sk > 1 ? (size_t)tw * sk * 1024 : 0;
+        // X in LDS when all of K fits and staging it is cheap next to the weights the
+        // workgroup streams: few rows, or several tiles sharing each staged row
+        const bool fits = (size_t)p.G * per_group + red <= lds_limit;
+        p.xlds = fits && (mrows <= 4 || tw >= 2);
+        p.chunk = p.xlds ? p.G : 0;
+        // whole batches per slice; drop the slices that rounding left empty
+        p.per = round_up((p.G + sk - 1) / sk, kB);
+        sk = (p.G + p.per - 1) / p.per;
         p.tw = tw;
         p.sk = sk;
-        const size_t red = sk > 1 ? (size_t)tw * sk * 1024 : 0;
-        int chunk = (int)((lds_limit - red) / per_group);
-        chunk = chunk > p.G ? p.G : chunk < 1 ? 1 : chunk;
-        p.chunk = chunk;
         p.ntg = (p.nt + tw - 1) / tw;
         p.items = p.mblocks * p.ntg;
         p.grid = p.items;
@@ -501,6 +666,43 @@ SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit)
     p.ws_bytes = lmhead ? kZeroRegion : 0; // only lm_head uses scratch (argmax keys, ticket)
     return p;
 }
+
+namespace {
+
+template <int MODE, bool ALIGNED>
+void launch_variant(int nr, dim3 grid, dim3 block, size_t lds, hipStream_t stream, const SkinnyArgs &a,
+                    const SkinnyPlan &p)
+{
+    if (nr == 1)
+        hipLaunchKernelGGL((skinny_kernel<1, MODE, ALIGNED>), grid, block, lds, stream, a, p);
+    else if (nr == 2)
+        hipLaunchKernelGGL((skinny_kernel<2, MODE, ALIGNED>), grid, block, lds, stream, a, p);
+    else
+        hipLaunchKernelGGL((skinny_kernel<4, MODE, ALIGNED>), grid, block, lds, stream, a, p);
+}
+
+template <int MODE, bool ALIGNED>
+void allow_lds(size_t bytes)
+{
+    (void)hipFuncSetAttribute((const void *)skinny_kernel<1, MODE, ALIGNED>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    (void)hipFuncSetAttribute((const void *)skinny_kernel<2, MODE, ALIGNED>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    (void)hipFuncSetAttribute((const void *)skinny_kernel<4, MODE, ALIGNED>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int MODE>
+void launch_mode(bool aligned, int nr, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                 const SkinnyArgs &a, const SkinnyPlan &p)
+{
+    if (aligned)
+        launch_variant<MODE, true>(nr, grid, block, lds, stream, a, p);
+    else
+        launch_variant<MODE, false>(nr, grid, block, lds, stream, a, p);
+}
+
+} // namespace
 
 hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, hipStream_t stream)
 {
@@ -516,11 +718,10 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, hipStream_
         const size_t lim = (size_t)v > 4096 ? (size_t)v - 4096 : 0; // room for the static LDS
         lds_limit = lim < kLdsBudget ? lim : kLdsBudget;
         if (lds_limit > 64 * 1024) {
-            const void *fns[] = {(const void *)skinny_kernel<1, false>, (const void *)skinny_kernel<2, false>,
-                                 (const void *)skinny_kernel<4, false>, (const void *)skinny_kernel<1, true>,
-                                 (const void *)skinny_kernel<2, true>, (const void *)skinny_kernel<4, true>};
-            for (const void *f : fns)
-                (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_limit);
+            allow_lds<kSplitLds, false>(lds_limit);
+            allow_lds<kSplitLds, true>(lds_limit);
+            allow_lds<kStream, false>(lds_limit);
+            allow_lds<kStream, true>(lds_limit);
         }
     }
     const SkinnyPlan p = plan.lds_bytes > lds_limit ? plan_skinny(a.M, a.N, a.K, a.lmhead, lds_limit) : plan;
@@ -528,21 +729,14 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, hipStream_
         return hipErrorInvalidValue;
     const dim3 block(64 * p.waves), grid(p.grid);
     const int nr = a.M == 1 ? 1 : a.M == 2 ? 2 : 4;
-    if (p.stream) {
-        if (nr == 1)
-            hipLaunchKernelGGL((skinny_kernel<1, true>), grid, block, p.lds_bytes, stream, a, p);
-        else if (nr == 2)
-            hipLaunchKernelGGL((skinny_kernel<2, true>), grid, block, p.lds_bytes, stream, a, p);
-        else
-            hipLaunchKernelGGL((skinny_kernel<4, true>), grid, block, p.lds_bytes, stream, a, p);
-    } else {
-        if (nr == 1)
-            hipLaunchKernelGGL((skinny_kernel<1, false>), grid, block, p.lds_bytes, stream, a, p);
-        else if (nr == 2)
-            hipLaunchKernelGGL((skinny_kernel<2, false>), grid, block, p.lds_bytes, stream, a, p);
-        else
-            hipLaunchKernelGGL((skinny_kernel<4, false>), grid, block, p.lds_bytes, stream, a, p);
-    }
+    // 4-group scale/zero loads need G and every slice start to be multiples of 4
+    const bool aligned = (a.G % 4) == 0 && (p.per % 4) == 0;
+    if (p.stream)
+        launch_mode<kStream>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
+    else if (p.xlds)
+        launch_mode<kSplitLds>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
+    else
+        launch_mode<kSplitDirect>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
     return hipGetLastError();
 }
 
