@@ -8,15 +8,19 @@ one step = both projections.  Prints ONE JSON line with:
                  weight copies rotated over > 768 MB so the 256 MB Infinity Cache
                  cannot serve them), steps replayed from a HIP graph
   roofline       the dominant kernel (skinny_kernel) against 8 TB/s: algorithmic
-                 bytes per launch / average launch time from HIP events on the
-                 launch stream; traffic from the committed rocprofv3 counter summary
+                 bytes per launch / average launch time, from HIP events recorded on
+                 the launch stream around the timed region (every launch in it is a
+                 skinny_kernel); traffic = HBM bytes per launch from the committed
+                 rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain
+                 copy of known size), or null if the kernel sources changed since
   cpu_baseline   the fp64 CPU oracle timed on this host on a bounded sample
   workloads      the same measurements for the other shapes: a single 512x512
                  linear, one decoder layer's seven projections at M = 16 (a draft
                  block), the fused lm_head verify over a 151936 vocabulary, and
                  prefill at M = 8192 (TFLOP/s against the bf16 MFMA peak)
 Options: --only WORKLOAD times one workload (for profiling runs), --calib runs a
-plain copy of known size (HBM counter calibration).
+plain copy of known size (HBM counter calibration), --pmc-summary writes the
+traffic summary from the counter CSVs of those runs (no GPU needed).
 """
 import argparse
 import hashlib
@@ -48,9 +52,14 @@ def algo_bytes(M, N, K, out_bytes=2, lmhead=False):
     return b
 
 
+SKINNY_SOURCES = ("common.h", "kernels.h", "skinny.hip", "api.hip")
+CALIB_BYTES = 1 << 30
+
+
 def kernel_source_sha():
+    """Hash of the sources that decide what skinny_kernel reads and writes."""
     h = hashlib.sha256()
-    for f in ("common.h", "kernels.h", "skinny.hip", "tiled.hip", "api.hip"):
+    for f in SKINNY_SOURCES:
         with open(os.path.join(ROOT, "int4_weight_only_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -128,29 +137,34 @@ class Workload:
             self.launch(p, r % self.R)
 
     def check(self):
-        """Sanity check of one step against the oracle (sampled outputs)."""
+        """Sanity check of one step against the oracle on sampled outputs: f32 Y, so the
+        figure is the arithmetic error alone (no bf16 output rounding)."""
         import torch
         import oracle
+        import int4_weight_only_02_amd as w4
         worst = 0.0
         for p in self.projs:
-            self.launch(p, 0)
+            if self.lmhead:
+                continue
+            X, qw, S, qz = p["copies"][0]
+            Y = w4.w4a16_linear(X, qw, S, qz, out_dtype=torch.float32, workspace=self.ws)
             torch.cuda.synchronize()
             d = p["host"]
-            qw, qz = oracle.pack(d["codes"], d["zeros"])
+            oqw, oqz = oracle.pack(d["codes"], d["zeros"])
             rng = np.random.default_rng(0)
             rows = rng.integers(0, p["M"], 256)
             cols = rng.integers(0, p["N"], 256)
-            ref = oracle.linear_at(d["X"], qw, d["scales"], qz, rows, cols)
-            if self.lmhead:
-                continue
-            got = p["Y"].float().cpu().numpy()[rows, cols]
+            ref = oracle.linear_at(d["X"], oqw, d["scales"], oqz, rows, cols)
+            got = Y.cpu().numpy()[rows, cols]
             rms = float(np.sqrt(np.mean(ref ** 2))) or 1.0
             worst = max(worst, float(np.abs(got - ref).max()) / rms)
+            del Y
         return worst
 
 
 def time_events(wl, reps):
-    """Per-launch kernel time (us) from HIP events around every launch, per projection."""
+    """Eager per-launch time (us, median) from HIP events around every launch, per
+    projection: back-to-back calls from the host, launch overhead included."""
     import torch
     out = {}
     for p in wl.projs:
@@ -164,7 +178,7 @@ def time_events(wl, reps):
             evs.append((e0, e1))
         torch.cuda.synchronize()
         t = [a.elapsed_time(b) * 1e3 for a, b in evs]
-        out[p["label"]] = float(np.mean(t))
+        out[p["label"]] = float(np.median(t))
     return out
 
 
@@ -244,14 +258,15 @@ def measure(name, dev, steps, warmup, lmhead=False, ev_reps=200):
            "GBps": round(wl.bytes_per_step / wall / 1e9, 2),
            "hbm_frac": round(wl.bytes_per_step / wall / 1e9 / HBM_PEAK_GBS, 4),
            "TFLOPs": round(wl.flops_per_step / wall / 1e12, 3),
-           "kernel_us": {k: round(v, 3) for k, v in ev.items()},
+           "launches_per_step": len(wl.projs),
+           "kernel_us_eager_median": {k: round(v, 3) for k, v in ev.items()},
            "sampled_max_err_over_rms": err}
     per = {}
     for p in wl.projs:
         t = ev[p["label"]] * 1e-6
         b = algo_bytes(p["M"], p["N"], p["K"], lmhead=lmhead)
         f = 2 * p["M"] * p["N"] * p["K"]
-        per[p["label"]] = {"M": p["M"], "K": p["K"], "N": p["N"], "kernel_us": round(t * 1e6, 3),
+        per[p["label"]] = {"M": p["M"], "K": p["K"], "N": p["N"], "eager_us": round(t * 1e6, 3),
                            "GBps": round(b / t / 1e9, 1), "hbm_frac": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
                            "TFLOPs": round(f / t / 1e12, 2), "mfma_frac": round(f / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
     res["per_launch"] = per
@@ -273,6 +288,52 @@ def calib_copy(dev, nbytes=1 << 30, reps=5):
     print(json.dumps({"calib_copy_bytes": nbytes, "reps": reps}))
 
 
+def _pmc_mean(path, counter, name_filter):
+    """Mean value of one counter per dispatch of the kernels whose name contains
+    name_filter, from a rocprofv3 counter_collection.csv."""
+    import csv
+    vals = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter and name_filter in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit("no %s rows for kernels matching %r in %s" % (counter, name_filter, path))
+    return float(np.mean(vals)), len(vals)
+
+
+def pmc_summary(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, commands):
+    """HBM traffic of skinny_kernel per launch: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) scaled by what the same counters read for a plain copy of CALIB_BYTES."""
+    fk, fn = _pmc_mean(fetch_csv, "FETCH_SIZE", "skinny_kernel")
+    wk, wn = _pmc_mean(write_csv, "WRITE_SIZE", "skinny_kernel")
+    cf, _ = _pmc_mean(calib_fetch_csv, "FETCH_SIZE", "copy")
+    cw, _ = _pmc_mean(calib_write_csv, "WRITE_SIZE", "copy")
+    f_scale = CALIB_BYTES / (cf * 1024.0)
+    w_scale = CALIB_BYTES / (cw * 1024.0)
+    fetch_b = fk * 1024.0 * f_scale
+    write_b = wk * 1024.0 * w_scale
+    launches = synth.WORKLOADS[workload]
+    algo = float(np.mean([algo_bytes(M, N, K) for _, M, K, N in launches]))
+    lines = ["# skinny_kernel HBM traffic per launch, workload %s" % workload,
+             "# shapes (label, M, K, N): %s" % (launches,),
+             "# commands (each counter in its own run):"] + ["#   %s" % c for c in commands] + [
+             "# calibration: a plain device copy of %d bytes (torch copy_) reads FETCH_SIZE %.1f KiB and"
+             " WRITE_SIZE %.1f KiB per dispatch -> scale fetch x%.4f, write x%.4f" % (CALIB_BYTES, cf, cw, f_scale, w_scale),
+             "fetch_kib_per_dispatch: %.1f" % fk, "fetch_dispatches: %d" % fn,
+             "write_kib_per_dispatch: %.1f" % wk, "write_dispatches: %d" % wn,
+             "hbm_fetch_bytes_per_launch: %.0f" % fetch_b, "hbm_write_bytes_per_launch: %.0f" % write_b,
+             "hbm_bytes_per_launch: %.0f" % (fetch_b + write_b),
+             "algorithmic_bytes_per_launch: %.0f" % algo,
+             "traffic_over_algorithmic: %.4f" % ((fetch_b + write_b) / algo),
+             "kernel_source_sha: %s" % kernel_source_sha()]
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    out = os.path.join(PROFILE_DIR, "skinny_kernel__%s__pmc.txt" % workload)
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,7 +342,13 @@ def main():
     ap.add_argument("--only", default=None, help="time one workload only (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV", "CALIB_WRITE_CSV"),
+                    help="write the traffic summary of --only WORKLOAD (default the headline) from counter CSVs")
+    ap.add_argument("--pmc-command", action="append", default=[], help="command line recorded in the summary")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.only or HEADLINE, *args.pmc_summary, commands=args.pmc_command)
+        return
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the layer runs on one GPU's share; "
               "multi-GPU sharding is described, not run); use --gpus 1", file=sys.stderr)
@@ -310,14 +377,16 @@ def main():
     head = results.get(HEADLINE) or results[names[0]]
     head_name = HEADLINE if HEADLINE in results else names[0]
     per = head["per_launch"]
-    b_launch = np.mean([algo_bytes(v["M"], v["N"], v["K"]) for v in per.values()])
-    t_launch = np.mean([v["kernel_us"] for v in per.values()]) * 1e-6
+    # every launch in the timed region is a skinny_kernel (one per projection)
+    b_launch = head["bytes_per_step"] / head["launches_per_step"]
+    t_launch = head["us_per_step_gpu_events"] * 1e-6 / head["launches_per_step"]
     achieved = b_launch / t_launch / 1e9
     traffic = load_traffic(head_name, len(per))
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": "skinny_kernel", "algorithmic_bytes_per_launch": int(b_launch),
-            "avg_launch_us": round(t_launch * 1e6, 3)}
+            "avg_launch_us": round(t_launch * 1e6, 3),
+            "timing": "HIP events on the launch stream around the timed graph replays / launches"}
     cpu = None
     if not args.no_cpu_baseline and args.only is None:
         cpu = cpu_baseline(HEADLINE)

@@ -10,9 +10,10 @@
  * review, Referee Report: Summary and Significance; Assumptions & free
  * parameters: frozen AWQ per-group scales).  The drafter is group-wise INT4
  * with group size 128 (Pith review, free parameters: GPTQ group size 128).
- * Each speculative step verifies a block of 16 draft tokens with a greedy,
- * lossless verifier (Pith review, free parameters: block size 16;
- * Assumptions: a correct verifier is lossless; mlsanity index page, Abstract).
+ * Each speculative step checks a block of 16 draft tokens against the target's
+ * own greedy choices, which leaves the target's output unchanged (Pith review,
+ * free parameters: block size 16; Assumptions & free parameters, first
+ * assumption; mlsanity index page, Abstract).
  *
  * Definitions (the pages print no formula; these are the plainest readings):
  *   G = K / group                        (group must be 128)
@@ -107,8 +108,8 @@ int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, con
 
 /*
  * w4a16_lmhead_verify -- the lm_head projection fused with greedy verification
- * of a draft block (Pith review, Assumptions: speculative decoding with a
- * correct verifier is lossless; free parameters: block size 16).
+ * of a draft block (Pith review, Assumptions & free parameters: the first
+ * assumption, on verification; free parameters: block size 16).
  * Computes the logits Y = X * W^T as w4a16_linear does (kept in fp32), then
  *   argmax[m]   = the smallest n attaining max_n Y[m,n]   (over the fp32 logits)
  *   accept_len  = the number of leading rows i with argmax[i] == draft_ids[i]

@@ -29,8 +29,8 @@
 //                batch of loads always in flight, across tile boundaries.
 // Results are deterministic (fixed summation order everywhere).
 //
-// lm_head mode (the pages' greedy verifier: Pith review, Assumptions, "a correct
-// verifier is lossless"; draft blocks of 16 tokens, free parameters) keeps the
+// lm_head mode (the pages' greedy verification of a draft block: Pith review,
+// Assumptions & free parameters, first assumption; blocks of 16 tokens) keeps the
 // fp32 logits, folds each finished column into a per-row (value, column) key,
 // reduces the keys with 64-bit atomic max (ties -> lowest column), and the last
 // workgroup turns them into argmax ids and the accepted-prefix length.

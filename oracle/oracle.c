@@ -9,16 +9,17 @@
  *
  * What is computed (sources, all about arXiv 2607.04244 "Quantize the Target,
  * Quantize the Drafter: Efficient Inference with Qwen3.5-4B"):
- *   - the target is served on an AWQ INT4 grid whose per-group scales are
- *     frozen, and weights are re-packed onto that same grid, so packing and
- *     serving stay as they were (Pith review, Referee Report: Summary and
- *     Significance; Assumptions: "Freezing the original AWQ per-group scales");
- *   - the drafter is group-wise INT4 with group size 128 (Pith review,
- *     Assumptions & free parameters: "GPTQ group size for drafter = 128");
- *   - speculative decoding with a correct verifier is lossless: draft tokens
- *     are kept while they equal the target's greedy choice (Pith review,
- *     Assumptions: "Speculative decoding with a correct verifier is
- *     lossless"; mlsanity index page, Abstract).
+ *   - the target model runs on an AWQ INT4 grid; distillation keeps its
+ *     per-group scales fixed and rounds the trained weights back onto that
+ *     grid, so the packed format and the serving path do not change (Pith
+ *     review, Referee Report: Summary and Significance; Assumptions & free
+ *     parameters, second assumption);
+ *   - the drafter's weights are INT4 in groups of 128 (Pith review,
+ *     Assumptions & free parameters: the drafter's GPTQ group size);
+ *   - verification by the target leaves the output unchanged, so a draft
+ *     token survives only while it matches the target's greedy choice (Pith
+ *     review, Assumptions & free parameters, first assumption; mlsanity index
+ *     page, Abstract).
  * The pages print no formula, layout or worked example.  The readings used
  * (all stated again at each function):
  *   W[n,k] = (q[n,k] - z[n,g]) * s[n,g],  g = floor(k / group)
@@ -72,7 +73,7 @@ double oracle_f16_to_f64(uint16_t h)
  * qweight u32[N][K/8]: nibble j (bits 4j..4j+3) of word w of row n holds
  * code (n, 8w + j).  Pack zeros u8[N][G] into qzeros u32[N/8][G]: nibble j of
  * word (r, g) holds the zero of row 8r + j, group g.
- * Reading: "packed 8 per uint32 along K" in the plainest order. */
+ * Reading: eight codes per 32-bit word along K, in the plainest order. */
 void oracle_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K, int group,
                  uint32_t *qweight, uint32_t *qzeros)
 {
@@ -191,7 +192,7 @@ void oracle_linear_at(const uint16_t *X, const uint32_t *qweight, const uint16_t
  *   gap[m]    = that maximum minus the largest logit at any other column
  *               (+inf when N == 1).
  * accept_len = the number of leading rows i with argmax[i] == draft[i]
- * (the lossless greedy verifier keeps draft tokens until the first one the
+ * (greedy verification keeps draft tokens up to the first one the
  * target would not have chosen). */
 void oracle_argmax_accept(const double *Y, int M, int N, const int32_t *draft,
                           int32_t *argmax, double *gap, int32_t *accept_len)
