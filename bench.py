@@ -57,11 +57,16 @@ CALIB_BYTES = 1 << 30
 
 
 def kernel_source_sha():
-    """Hash of the sources that decide what skinny_kernel reads and writes."""
+    """Hash of the code (comments and blank lines removed) of the sources that
+    decide what skinny_kernel reads and writes."""
+    import re
     h = hashlib.sha256()
     for f in SKINNY_SOURCES:
-        with open(os.path.join(ROOT, "int4_weight_only_02_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "int4_weight_only_02_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 
