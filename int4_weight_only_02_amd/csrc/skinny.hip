@@ -47,8 +47,6 @@ namespace {
 constexpr int kMaxWaves = 8;           // up to 512 threads per workgroup (256 VGPRs per lane)
 constexpr int kStreamWaves = 8;
 constexpr int kB = 4;                  // groups per register batch
-constexpr int kStageUnrollStream = 8;  // X staging loads in flight per thread
-constexpr int kStageUnrollSplit = 4;
 constexpr int kCUs = 256;
 constexpr size_t kLdsBudget = 160 * 1024 - 4096;
 constexpr uint32_t kOob = 0xFFFFFF00u; // an offset past the end of every tensor
@@ -168,38 +166,49 @@ __device__ __forceinline__ bf16x8_t codes_to_frag_r(uint32_t w, uint32_t mask, u
     return __builtin_bit_cast(bf16x8_t, r);
 }
 
-// Per group: P = sum x * (128 + q) + sum x * (-(128 + z)) = sum x * (q - z) for this
-// lane's column and the rows 4h .. 4h+3 (D layout), then acc += s * P.  Both halves
-// are exact products accumulated in fp32 (two independent chains, added before the
-// scale).  Groups at or past gend get s = 0 (their data is finite, so the product
-// is exactly 0).  xlane points at the lane's X row in the staged chunk starting at
-// group st_c0.  NR = the accumulator rows that can hold real output (1 for M = 1,
-// 2 for M = 2).
+// Per group, for this lane's column and the rows 4h .. 4h+3 (D layout):
+//   P = sum_k x * (128 + q)        four MFMAs on the exact biased codes (fp32 sums)
+//   acc += s * (P - (128 + z) * S)  S = sum_k x over the group, from LDS
+// which is s * sum_k x * (q - z).  Groups at or past gend get s = 0 (their data is
+// finite, so they add exactly 0).  xlane points at the lane's X row in the staged
+// chunk, sl at S of rows 4h .. 4h+3 of its first group.  NR = the accumulator rows
+// that can hold real output (1 for M = 1, 2 for M = 2).
 template <int NR>
-__device__ __forceinline__ void compute_batch(const Batch &b, f32x4_t &acc, const u32x4_t *xlane, int gs,
-                                              int gend, int st_c0, int Mb, int zsh, uint32_t mask,
-                                              uint32_t bias)
+__device__ __forceinline__ void compute_batch(const Batch &b, f32x4_t &acc, const u32x4_t *xlane,
+                                              const float *sl, int gs, int gend, int Mb, int zsh,
+                                              uint32_t mask, uint32_t bias)
 {
+    // the X fragments and S of group i + 1 are read from LDS while group i computes
+    u32x4_t xf[2][4];
+    f32x4_t sv[2];
+    auto fetch = [&](int i, int buf) {
+        const int g = gs + i;
+        const int gl = g < gend ? g : gend - 1;
+        const u32x4_t *xg = xlane + gl * 16 * Mb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            xf[buf][j] = xg[j * Mb];
+        sv[buf] = *(const f32x4_t *)(sl + gl * 16);
+    };
+    fetch(0, 0);
 #pragma unroll
     for (int i = 0; i < kB; ++i) {
+        const int cur = i & 1;
+        if (i + 1 < kB)
+            fetch(i + 1, cur ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
         const int g = gs + i;
-        const int gl = (g < gend ? g : gend - 1) - st_c0;
-        const u32x4_t *xg = xlane + gl * 16 * Mb;
-        // -(128 + z) as a bf16 pair: sign | exponent of 128 | z in the mantissa
-        const uint32_t zb = (((b.z[i] >> zsh) & 15u) | 0xC300u) * 0x00010001u;
-        const bf16x8_t zfrag = __builtin_bit_cast(bf16x8_t, u32x4_t{zb, zb, zb, zb});
-        f32x4_t pq = {0.f, 0.f, 0.f, 0.f}, pz = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t pq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, xg[j * Mb]);
             const uint32_t wj = j == 0 ? b.w[i].x : j == 1 ? b.w[i].y : j == 2 ? b.w[i].z : b.w[i].w;
-            pq = mfma16x16x32(xa, codes_to_frag_r(wj, mask, bias), pq);
-            pz = mfma16x16x32(xa, zfrag, pz);
+            pq = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[cur][j]), codes_to_frag_r(wj, mask, bias), pq);
         }
+        const float zc = (float)(kCodeBias + ((b.z[i] >> zsh) & 15u));
         const float s = g < gend ? f16_bits_to_f32((uint16_t)b.s[i]) : 0.f;
 #pragma unroll
         for (int r = 0; r < NR; ++r)
-            acc[r] = fmaf(s, pq[r] + pz[r], acc[r]);
+            acc[r] = fmaf(s, fmaf(-zc, sv[cur][r], pq[r]), acc[r]);
     }
 }
 
@@ -261,35 +270,92 @@ __device__ __forceinline__ void compute_batch_x(const BatchX &b, f32x4_t &acc, i
     }
 }
 
-// Stage X[m0 .. m0+Mb)[groups s0 .. s1) into LDS in fragment order.  LDS slot i holds
-// chunk kc = i / Mb (group kc/16, c = kc%16) of row m = i % Mb, so consecutive
-// threads write consecutive 16-byte slots (no bank conflicts); the quotient comes
-// from a multiply by ceil(2^32 / Mb).  kStageUnroll loads per thread are in flight
-// at once.  Caller synchronizes around it.
-template <int kStageUnroll>
-__device__ __forceinline__ void stage_x(const uint16_t *X, int K, int m0, int Mb, int s0, int s1,
-                                        u32x4_t *xs, int tid, int nthreads)
+// Staging of X[m0 .. m0+Mb)[all groups] into LDS, in fragment order.  LDS slot i
+// holds chunk kc = i / Mb (group kc/16, c = kc%16) of row m = i % Mb, so consecutive
+// threads write consecutive 16-byte slots (no bank conflicts); the quotient comes from
+// a multiply by ceil(2^32 / Mb).  Alongside each slot goes the sum of its 8
+// activations (part[i]), from which group_sums builds S.  A round is kStageU slots per
+// thread; the first round is issued before the weight loads, so that waiting for X
+// does not wait for the weights (loads complete in order).
+constexpr int kStageU = 4;
+
+struct XRound {
+    u32x4_t v[kStageU];
+};
+
+struct XStage {
+    __amdgpu_buffer_rsrc_t rx;
+    uint32_t base;             // byte offset of X[m0][0]
+    unsigned long long magic;  // ceil(2^32 / Mb)
+    int Mb, K, total;
+};
+
+__device__ __forceinline__ void stage_issue(XRound &xr, const XStage &st, int i0, int tid, int nthreads)
 {
-    const int total = Mb * (s1 - s0) * 16;
-    const unsigned long long magic = ((1ull << 32) + (unsigned)Mb - 1) / (unsigned)Mb;
-    const uint16_t *base = X + (size_t)m0 * K + (size_t)s0 * kGroup;
-    for (int i0 = 0; i0 < total; i0 += nthreads * kStageUnroll) {
-        u32x4_t v[kStageUnroll];
 #pragma unroll
-        for (int u = 0; u < kStageUnroll; ++u) {
-            const int i = i0 + u * nthreads + tid;
-            if (i < total) {
-                const int kc = (int)(((unsigned long long)(unsigned)i * magic) >> 32);
-                const int m = i - kc * Mb;
-                v[u] = *(const u32x4_t *)(base + (size_t)m * K + kc * 8);
-            }
-        }
+    for (int u = 0; u < kStageU; ++u) {
+        const int i = i0 + u * nthreads + tid;
+        const int kc = (int)(((unsigned long long)(unsigned)i * st.magic) >> 32);
+        const int m = i - kc * st.Mb;
+        const uint32_t off = i < st.total ? st.base + (uint32_t)(m * st.K + kc * 8) * 2u : kOob;
+        xr.v[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(st.rx, off, 0, 0));
+    }
+}
+
+__device__ __forceinline__ void stage_commit(const XRound &xr, const XStage &st, u32x4_t *xs, float *part, int i0,
+                                             int tid, int nthreads)
+{
+    // the loaded registers are used unconditionally (only the LDS writes are
+    // predicated), so no path leaves these loads pending behind the weight loads
 #pragma unroll
-        for (int u = 0; u < kStageUnroll; ++u) {
-            const int i = i0 + u * nthreads + tid;
-            if (i < total)
-                xs[i] = x_permute8(v[u]);
+    for (int u = 0; u < kStageU; ++u) {
+        const int i = i0 + u * nthreads + tid;
+        const u32x4_t pv = x_permute8(xr.v[u]);
+        const float ps = sum8_bf16(xr.v[u]);
+        if (i < st.total) {
+            xs[i] = pv;
+            part[i] = ps;
         }
+    }
+}
+
+// Rounds after the first (only when X exceeds one round: several rows with a long
+// K).  They are issued after the weight loads, so they wait for those too; the
+// closing vmcnt(0) makes that explicit, so that the single-round path, which skips
+// this, keeps its weight loads in flight into the compute loop.
+__device__ __forceinline__ void stage_rest(const XStage &st, u32x4_t *xs, float *part, int tid, int nthreads)
+{
+    if (st.total <= kStageU * nthreads)
+        return;
+    for (int i0 = kStageU * nthreads; i0 < st.total; i0 += kStageU * nthreads) {
+        XRound xr;
+        stage_issue(xr, st, i0, tid, nthreads);
+        stage_commit(xr, st, xs, part, i0, tid, nthreads);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0)
+}
+
+// S[g][r] = sum of the 128 activations of row min(r, Mb - 1) in group g: the 16 slot
+// sums of the group, c ascending (a fixed order).  Rows >= Mb repeat row Mb - 1, whose
+// activations the lanes of those rows also read.  Caller synchronizes around it.
+__device__ __forceinline__ void group_sums(const float *part, float *S, int Mb, int ng, int tid, int nthreads)
+{
+    for (int e = tid; e < ng * Mb; e += nthreads) {
+        const int g = e / Mb, m = e - g * Mb;
+        const float *pp = part + g * 16 * Mb + m;
+        float v[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            v[c] = pp[c * Mb];
+        __builtin_amdgcn_sched_barrier(0); // all 16 reads in flight before the sum
+        float t = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            t += v[c];
+        S[g * 16 + m] = t;
+        if (m == Mb - 1)
+            for (int r = Mb; r < 16; ++r)
+                S[g * 16 + r] = t;
     }
 }
 
@@ -303,13 +369,19 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
     __shared__ int s_flag;
 
     const int M = a.M, N = a.N, K = a.K, G = a.G;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // uniform: scalar loop control
     const int h = lane >> 4, col = lane & 15;
     const int nthreads = blockDim.x, nwaves = nthreads >> 6;
     const int mrows = M < 16 ? M : 16;
 
-    u32x4_t *xs = (u32x4_t *)smem;                                // [group][chunk c][row]
-    float *red = (float *)(smem + (size_t)p.chunk * 256 * mrows); // [wave][64 lanes][4]
+    // LDS: staged X [group][chunk c][row] (16 B each), the slot sums, S [group][16 rows],
+    // then the K-slice partial sums [wave][64 lanes][4]
+    const int nslot = p.chunk * 16 * mrows;
+    u32x4_t *xs = (u32x4_t *)smem;
+    float *part = (float *)(smem + (size_t)nslot * 16);
+    float *S = part + nslot;
+    float *red = S + p.chunk * 16;
     uint32_t *ticket = (uint32_t *)(a.ws + kOffTicket);
     unsigned long long *keys = (unsigned long long *)(a.ws + kOffKeys);
 
@@ -317,6 +389,16 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales, (uint32_t)((size_t)N * G * 2));
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.qz, (uint32_t)((size_t)(N / 8) * G * 4));
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X, (uint32_t)((size_t)M * K * 2));
+    auto x_stage = [&](int m0, int Mb) {
+        XStage st;
+        st.rx = rx;
+        st.base = (uint32_t)m0 * (uint32_t)K * 2u;
+        st.magic = ((1ull << 32) + (unsigned)Mb - 1) / (unsigned)Mb;
+        st.Mb = Mb;
+        st.K = K;
+        st.total = Mb * G * 16;
+        return st;
+    };
     // code-to-bf16 constants, pinned in VGPRs (see codes_to_frag_r)
     uint32_t kmask = 0x000F000Fu, kbias = kBiasBits;
     asm volatile("" : "+v"(kmask));
@@ -386,6 +468,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
             const int Mb = M - m0 < 16 ? M - m0 : 16;
             const int xrow = col < Mb ? col : Mb - 1; // rows >= Mb feed outputs that are never stored
             const u32x4_t *xlane = xs + (4 * h) * Mb + xrow;
+            const float *sl = S + 4 * h;
             if (a.lmhead && cur_mb >= 0)
                 flush_best(cur_mb);
             cur_mb = mb;
@@ -394,10 +477,17 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
             int tileA = tgA * nwaves + wave;
             bool liveA = tgA < p.ntg && tileA * 16 < N;
             LaneGrid LA = lane_grid(tileA, col, h, N, K, G, liveA);
+            // X first, then the first weight batch: both in flight together
+            const XStage st = x_stage(m0, Mb);
+            XRound xr;
+            stage_issue(xr, st, 0, tid, nthreads);
             Batch bA, bB;
-            load_batch<ALIGNED>(bA, rw, rs, rz, LA, gA, G); // in flight while X is staged
+            load_batch<ALIGNED>(bA, rw, rs, rz, LA, gA, G);
+            __syncthreads(); // the previous m-block's reads of X are done
+            stage_commit(xr, st, xs, part, 0, tid, nthreads);
+            stage_rest(st, xs, part, tid, nthreads);
             __syncthreads();
-            stage_x<kStageUnrollStream>(a.X, K, m0, Mb, 0, G, xs, tid, nthreads);
+            group_sums(part, S, Mb, G, tid, nthreads);
             __syncthreads();
 
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -413,7 +503,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
                 const LaneGrid LB = lane_grid(tileB, col, h, N, K, G, liveB);
                 load_batch<ALIGNED>(bB, rw, rs, rz, LB, gB, G);
                 __builtin_amdgcn_sched_barrier(0);
-                compute_batch<NR>(bA, acc, xlane, gA, G, 0, Mb, LA.zsh, kmask, kbias);
+                compute_batch<NR>(bA, acc, xlane, sl, gA, G, Mb, LA.zsh, kmask, kbias);
                 __builtin_amdgcn_sched_barrier(0);
                 if (gA + kB >= G) {
                     if (liveA)
@@ -433,7 +523,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
                 const LaneGrid LC = lane_grid(tileC, col, h, N, K, G, liveC);
                 load_batch<ALIGNED>(bA, rw, rs, rz, LC, gC, G);
                 __builtin_amdgcn_sched_barrier(0);
-                compute_batch<NR>(bB, acc, xlane, gB, G, 0, Mb, LB.zsh, kmask, kbias);
+                compute_batch<NR>(bB, acc, xlane, sl, gB, G, Mb, LB.zsh, kmask, kbias);
                 __builtin_amdgcn_sched_barrier(0);
                 if (gB + kB >= G) {
                     if (liveB)
@@ -452,7 +542,6 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
     } else {
         // ---- split mode: item = (m-block, group of tw tiles); wave = (tile slot, K slice)
         const int tslot = wave % p.tw, ks = wave / p.tw;
-        int st_mb = -1, st_c0 = -1; // kSplitLds: X groups [st_c0, st_c0 + chunk) of m-block st_mb are in LDS
         for (int it = blockIdx.x; it < p.items; it += gridDim.x) {
             const int mb = it / p.ntg, tg = it - mb * p.ntg;
             const int m0 = mb * 16;
@@ -468,44 +557,45 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
             }
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
             if constexpr (MODE == kSplitLds) {
-                for (int c0 = 0; c0 < G; c0 += p.chunk) {
-                    const int c1 = G < c0 + p.chunk ? G : c0 + p.chunk;
-                    // slices of p.per groups (a multiple of kB): batches stay 4-aligned
-                    const int g0 = c0 + ks * p.per;
-                    const int g1 = c1 < g0 + p.per ? c1 : g0 + p.per;
-                    // three register batches: up to 3 * kB groups of the slice are requested
-                    // before X is staged, so their HBM latency overlaps the staging
-                    Batch b0, b1, b2;
-                    load_batch<ALIGNED>(b0, rw, rs, rz, L, g0, g1);
-                    load_batch<ALIGNED>(b1, rw, rs, rz, L, g0 + kB, g1);
-                    load_batch<ALIGNED>(b2, rw, rs, rz, L, g0 + 2 * kB, g1);
-                    if (!(mb == st_mb && c0 == st_c0)) {
-                        __syncthreads();
-                        stage_x<kStageUnrollSplit>(a.X, K, m0, Mb, c0, c1, xs, tid, nthreads);
-                        __syncthreads();
-                        st_mb = mb;
-                        st_c0 = c0;
-                    }
-                    const u32x4_t *xlane = xs + (4 * h) * Mb + xrow;
-                    // rotate the three batches; loads stay unconditional (a batch past the
-                    // slice reads kOob), only fully masked computes are skipped (uniform
-                    // branches)
-                    for (int g = g0; g < g1; g += 3 * kB) {
-                        __builtin_amdgcn_sched_barrier(0);
-                        compute_batch<NR>(b0, acc, xlane, g, g1, c0, Mb, L.zsh, kmask, kbias);
-                        __builtin_amdgcn_sched_barrier(0);
-                        load_batch<ALIGNED>(b0, rw, rs, rz, L, g + 3 * kB, g1);
-                        __builtin_amdgcn_sched_barrier(0);
-                        if (g + kB < g1)
-                            compute_batch<NR>(b1, acc, xlane, g + kB, g1, c0, Mb, L.zsh, kmask, kbias);
-                        __builtin_amdgcn_sched_barrier(0);
-                        load_batch<ALIGNED>(b1, rw, rs, rz, L, g + 4 * kB, g1);
-                        __builtin_amdgcn_sched_barrier(0);
-                        if (g + 2 * kB < g1)
-                            compute_batch<NR>(b2, acc, xlane, g + 2 * kB, g1, c0, Mb, L.zsh, kmask, kbias);
-                        __builtin_amdgcn_sched_barrier(0);
-                        load_batch<ALIGNED>(b2, rw, rs, rz, L, g + 5 * kB, g1);
-                    }
+                // slices of p.per groups (a multiple of kB): batches stay 4-aligned
+                const int g0 = ks * p.per;
+                const int g1 = G < g0 + p.per ? G : g0 + p.per;
+                // X first, then three register batches (up to 3 * kB groups of the slice),
+                // all in flight together; X is committed to LDS as soon as it lands
+                const XStage st = x_stage(m0, Mb);
+                XRound xr;
+                stage_issue(xr, st, 0, tid, nthreads);
+                Batch b0, b1, b2;
+                load_batch<ALIGNED>(b0, rw, rs, rz, L, g0, g1);
+                load_batch<ALIGNED>(b1, rw, rs, rz, L, g0 + kB, g1);
+                load_batch<ALIGNED>(b2, rw, rs, rz, L, g0 + 2 * kB, g1);
+                if (it != (int)blockIdx.x)
+                    __syncthreads(); // the previous item's reads of X are done
+                stage_commit(xr, st, xs, part, 0, tid, nthreads);
+                stage_rest(st, xs, part, tid, nthreads);
+                __syncthreads();
+                group_sums(part, S, Mb, G, tid, nthreads);
+                __syncthreads();
+                const u32x4_t *xlane = xs + (4 * h) * Mb + xrow;
+                const float *sl = S + 4 * h;
+                // rotate the three batches; loads stay unconditional (a batch past the
+                // slice reads kOob), only fully masked computes are skipped (uniform
+                // branches)
+                for (int g = g0; g < g1; g += 3 * kB) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute_batch<NR>(b0, acc, xlane, sl, g, g1, Mb, L.zsh, kmask, kbias);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_batch<ALIGNED>(b0, rw, rs, rz, L, g + 3 * kB, g1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (g + kB < g1)
+                        compute_batch<NR>(b1, acc, xlane, sl, g + kB, g1, Mb, L.zsh, kmask, kbias);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_batch<ALIGNED>(b1, rw, rs, rz, L, g + 4 * kB, g1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (g + 2 * kB < g1)
+                        compute_batch<NR>(b2, acc, xlane, sl, g + 2 * kB, g1, Mb, L.zsh, kmask, kbias);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_batch<ALIGNED>(b2, rw, rs, rz, L, g + 5 * kB, g1);
                 }
             } else {
                 const int g0 = ks * p.per;
@@ -578,11 +668,17 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
     }
 }
 
-size_t lds_for(const SkinnyPlan &p, int M)
+// LDS per staged group: 16 slots of 16 B and their 4-byte sums per row, and S (16 rows)
+size_t lds_per_group(int M)
 {
     const int mrows = M < 16 ? M : 16;
+    return (size_t)mrows * 16 * (16 + 4) + 16 * 4;
+}
+
+size_t lds_for(const SkinnyPlan &p, int M)
+{
     const size_t red = p.sk > 1 ? (size_t)p.tw * p.sk * 1024 : 0;
-    return (size_t)p.chunk * 256 * mrows + red;
+    return (size_t)p.chunk * lds_per_group(M) + red;
 }
 
 // Tuning override for the split-mode shape, read once from W4A16_SKINNY_SPLIT="tw,sk"
@@ -614,7 +710,7 @@ SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit)
     p.mblocks = (M + 15) / 16;
     p.nt = (N + 15) / 16;
     const int mrows = M < 16 ? M : 16;
-    const size_t per_group = (size_t)mrows * 256;
+    const size_t per_group = lds_per_group(M);
     const long long tiles = (long long)p.nt * p.mblocks;
     if (tiles >= 16LL * kCUs && (size_t)p.G * per_group <= lds_limit) {
         // many tiles (a vocabulary-sized lm_head): persistent workgroups, whole tiles per wave
