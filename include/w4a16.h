@@ -100,7 +100,7 @@ int w4a16_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K, int gro
  *                      zero-filled), and every call leaves it that way.
  *                      May be NULL when that size is 0.
  * Shapes: M >= 0, N >= 0, N % 8 == 0, K >= group, K % group == 0, group == 128,
- *         M * N and N * K below 2^31.
+ *         M * N, N * K and M * K at most 2^31 - 256.
  */
 int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, const uint32_t *qzeros,
                  int M, int N, int K, int group, void *Y, int y_dtype,

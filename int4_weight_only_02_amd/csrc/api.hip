@@ -10,7 +10,7 @@ using namespace w4a16;
 
 namespace {
 
-constexpr long long kLimit = 0x7FFFFFFFll; // M*N and N*K stay below 2^31
+constexpr long long kLimit = 0x7FFFFF00ll; // element counts: byte offsets stay below the out-of-range offset the kernels use
 
 bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
 

@@ -72,7 +72,9 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &p, hipStream_t s
 struct TiledPlan {
     int G;
     int tiles_m, tiles_n;
-    size_t off_gsum, ws_bytes;  // per-row group sums of X, fp32 [G][M]
+    size_t off_xh;    // X as fp16, each row scaled by a power of two, [M][K]
+    size_t off_rs;    // the per-row scales (fp32, M)
+    size_t ws_bytes;
 };
 
 struct TiledArgs {

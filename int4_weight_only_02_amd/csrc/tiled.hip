@@ -1,18 +1,28 @@
-// tiled.hip -- W4A16 linear for large M (prefill) on gfx950: LDS-tiled bf16 MFMA.
+// tiled.hip -- W4A16 linear for large M (prefill) on gfx950: LDS-tiled fp16 MFMA.
 //
-// At M in the thousands the layer is bound by the matrix cores.  Each workgroup
-// computes a 128 x 128 tile of Y with 4 waves (64 x 64 each, 4 x 4 MFMA tiles of
-// 16 x 16).  K advances one group (128) at a time:
-//   * the X tile [128 rows x 128 k] is staged in LDS in fragment order, the
-//     packed weights [128 columns x 16 words] are staged raw (64 B per column);
-//   * every wave turns its words into exact bf16 codes 128 + q in registers
-//     (common.h) and runs 4 k-steps of v_mfma_f32_16x16x32_bf16 into a fresh
-//     per-group accumulator P;
-//   * the group is folded in fp32: acc += s * (P - (128 + z) * S), where
-//     S[m, g] = sum_{k in g} X[m, k] comes from a small pre-pass (gsum_kernel).
-// Nothing is rounded before the fp32 accumulation, so the result stays within a
-// few fp32 ulps of the exact product.  Global loads for group g+1 are issued
-// before the MFMAs of group g.
+// At M in the thousands the layer is bound by the matrix cores, and what limits a
+// kernel that keeps the codes exact is the per-group fp32 fold it then needs
+// (about six VALU instructions per MFMA).  This path instead feeds the matrix cores
+// fp16 operands and accumulates all of K in fp32 directly:
+//   * prep_kernel scales every row of X by a power of two 2^-e (chosen so the row's
+//     largest magnitude lands in [2^14, 2^15)) and stores it as fp16.  bf16 has 8
+//     significant bits and fp16 11, so the conversion is exact for every value
+//     within 2^29 of the row maximum; only values far below it lose bits.  The eight
+//     activations of each 16-byte chunk are stored in the order the code fragments
+//     use (k0 k4 k1 k5 k2 k6 k3 k7);
+//   * the weights are dequantized in registers, per packed word: the fp16 bias trick
+//     gives 1024 + q exactly (0x6400 | q), one packed fp16 add of -(1024 + z) gives
+//     q - z exactly, and one packed fp16 multiply by s rounds (q - z) * s once to
+//     fp16 (relative error at most 2^-11 per weight);
+//   * a workgroup of 8 waves (two per SIMD) computes a 256 x 256 tile of Y; each wave
+//     owns 128 x 64 (8 x 4 tiles of v_mfma_f32_16x16x32_f16, accumulators in AGPRs).  K advances
+//     one group (128) at a time through two LDS buffers filled by LDS DMA
+//     (buffer_load ... lds) one group ahead: the X tile [256 rows x 16 chunks], its
+//     16-byte slots XOR-swizzled by row (conflict-free fragment reads), and the
+//     packed words [256 columns x 64 B];
+//   * the epilogue multiplies each row by 2^e and stores bf16 (RNE) or fp32.
+// With X ~ N(0, 1) the rounding of the weights contributes about 3e-4 * rms(Y) (rms),
+// a few percent of the 1e-2 * rms(Y) bound at the largest shapes.
 #include "common.h"
 #include "kernels.h"
 
@@ -20,138 +30,249 @@ namespace w4a16 {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, kThreads = 256;
-constexpr int kWPad = 5; // 16-byte units per staged weight column (4 data + 1 pad)
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 
-// S^T[g][m] = sum of the 128 activations of row m in group g (fixed summation order)
-__global__ __launch_bounds__(256) void gsum_kernel(const uint16_t *X, int M, int K, int G, float *gsumT)
+constexpr int BM = 256, BN = 256, kThreads = 512;
+constexpr int kXBytes = BM * kGroup * 2; // 65536: X tile of one group (fp16)
+constexpr int kWBytes = BN * 64;         // 16384: packed words of one group
+constexpr int kBufBytes = kXBytes + kWBytes;
+constexpr int kLdsBytes = 2 * kBufBytes; // 163840
+constexpr uint32_t kOob = 0xFFFFFF00u;   // an offset past the end of every tensor
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kF16Bias = 0x64006400u; // fp16 1024 in both halves
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x; // one 16-byte chunk each
-    const long long total = (long long)M * G * 16;
-    if (i >= total)
-        return; // total is a multiple of 16, so whole 16-lane teams exit together
-    const int c = (int)(i & 15);
-    const long long t = i >> 4;
-    const int g = (int)(t % G);
-    const int m = (int)(t / G);
-    const u32x4_t v = *(const u32x4_t *)(X + (size_t)m * K + (size_t)g * kGroup + c * 8);
-    float s = sum8_bf16(v);
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
-    s += __shfl_xor(s, 8);
-    if (c == 0)
-        gsumT[(size_t)g * M + m] = s;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// 16 bytes per lane from global memory (offset off of r) into LDS at dst + 16 * lane;
+// dst must be the same for the whole wave
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned char *dst, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); } // vmcnt(0)
+
+// One row per workgroup: X[m] * 2^-e as fp16 (chunks permuted to the fragment order),
+// and 2^e into rowscale[m].
+__global__ __launch_bounds__(256) void prep_kernel(const uint16_t *X, int K, uint16_t *Xh, float *rowscale)
+{
+    __shared__ float wmax[4];
+    const int m = blockIdx.x, tid = threadIdx.x;
+    const u32x4_t *xr = (const u32x4_t *)(X + (size_t)m * K);
+    u32x4_t *hr = (u32x4_t *)(Xh + (size_t)m * K);
+    const int nc = K / 8;
+
+    float mx = 0.f;
+    for (int c = tid; c < nc; c += 256) {
+        const u32x4_t v = xr[c];
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))), fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))));
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))), fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((tid & 63) == 0)
+        wmax[tid >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+
+    // floor(log2(max)) = E - 127 for a normal max; the scaled maximum lands in
+    // [2^14, 2^15).  e is clamped so that 2^e and 2^-e are normal floats.
+    const int E = (int)((__float_as_uint(mx) >> 23) & 0xFFu);
+    int e = mx > 0.f ? E - 141 : 0;
+    e = e < -126 ? -126 : e > 113 ? 113 : e;
+    const float down = __uint_as_float((uint32_t)(127 - e) << 23); // 2^-e
+    if (tid == 0)
+        rowscale[m] = __uint_as_float((uint32_t)(127 + e) << 23); // 2^e
+
+    for (int c = tid; c < nc; c += 256) {
+        const u32x4_t v = xr[c];
+        const float f0 = bf16_lo(v.x) * down, f1 = bf16_hi(v.x) * down;
+        const float f2 = bf16_lo(v.y) * down, f3 = bf16_hi(v.y) * down;
+        const float f4 = bf16_lo(v.z) * down, f5 = bf16_hi(v.z) * down;
+        const float f6 = bf16_lo(v.w) * down, f7 = bf16_hi(v.w) * down;
+        // fragment order k0 k4 k1 k5 k2 k6 k3 k7
+        const f16x8_t o = {(_Float16)f0, (_Float16)f4, (_Float16)f1, (_Float16)f5,
+                           (_Float16)f2, (_Float16)f6, (_Float16)f3, (_Float16)f7};
+        hr[c] = __builtin_bit_cast(u32x4_t, o);
+    }
+}
+
+__device__ __forceinline__ f16x2_t as_h2(uint32_t u) { return __builtin_bit_cast(f16x2_t, u); }
+
+// one packed word (codes k0..k7 of a column) -> fp16 fragment (k0 k4 k1 k5 k2 k6 k3 k7)
+// of (q - z) * s: (1024 + q) exact, minus (1024 + z) exact, times s rounded once
+__device__ __forceinline__ f16x8_t dequant_word(uint32_t w, uint32_t mask, uint32_t bias, f16x2_t zn, f16x2_t s2)
+{
+    const f16x2_t d0 = as_h2((w & mask) | bias) + zn;
+    const f16x2_t d1 = as_h2(((w >> 4) & mask) | bias) + zn;
+    const f16x2_t d2 = as_h2(((w >> 8) & mask) | bias) + zn;
+    const f16x2_t d3 = as_h2(((w >> 12) & mask) | bias) + zn;
+    const f16x2_t r0 = d0 * s2, r1 = d1 * s2, r2 = d2 * s2, r3 = d3 * s2;
+    return f16x8_t{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
 }
 
 __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan p)
 {
-    __shared__ u32x4_t xs[16 * BM];      // [chunk c][row]: 8 activations in fragment order
-    __shared__ u32x4_t wsm[BN * kWPad];  // [column][quarter-group] packed words
-    __shared__ __align__(16) float gs[BM];
+    extern __shared__ __align__(16) unsigned char smem[];
 
     const int M = a.M, N = a.N, K = a.K, G = a.G;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3; // 2 x 4 waves of 128 x 64
     const int h = lane >> 4, col = lane & 15;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-    const float *gsumT = (const float *)(a.ws + p.off_gsum);
 
-    u32x4_t xr[8], wr[2];
-    float gr = 0.f;
+    // tiles are dealt out so that each XCD (blocks b, b + 8, ...) takes a contiguous
+    // run of tiles in n-fastest order: its CUs share X rows in their L2
+    const int ntiles = p.tiles_m * p.tiles_n;
+    const int b = blockIdx.x;
+    int t = (b & 7) * (ntiles / 8) + (b >> 3);
+    if ((ntiles & 7) != 0)
+        t = b; // uneven split: plain order
+    const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
+    const int m0 = tm * BM, n0 = tn * BN;
 
-    auto load_group = [&](int g) {
+    const uint16_t *xh = (const uint16_t *)(a.ws + p.off_xh);
+    const float *rowscale = (const float *)(a.ws + p.off_rs);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xh, (uint32_t)((size_t)M * K * 2));
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.qw, (uint32_t)((size_t)N * K / 2));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales, (uint32_t)((size_t)N * G * 2));
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.qz, (uint32_t)((size_t)(N / 8) * G * 4));
+
+    // DMA of group g into buffer bi: X 8 x 1 KB per wave, words 2 x 1 KB per wave.  The
+    // per-lane offsets of group 0 are computed once; group g adds g * 256 bytes (X) or
+    // g * 64 bytes (words) as the scalar offset.  Rows past M and columns past N start
+    // at kOob: with the scalar offset added the address may wrap to somewhere inside
+    // the tensor, which is harmless (those rows and columns are never stored).
+    uint32_t xoff[8], woff[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int u = tid + kThreads * i;
-            const int row = m0 + (u >> 4);
-            const int c = u & 15;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (row < M)
-                v = *(const u32x4_t *)(a.X + (size_t)row * K + (size_t)g * kGroup + c * 8);
-            xr[i] = v;
-        }
+    for (int i = 0; i < 8; ++i) {
+        const int s = (wave * 8 + i) * 64 + lane; // X slot: row s/16, swizzled chunk s%16
+        const int row = s >> 4, c = (s & 15) ^ (row & 15);
+        xoff[i] = m0 + row < M ? ((uint32_t)(m0 + row) * (uint32_t)K + (uint32_t)(c * 8)) * 2u : kOob;
+    }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int u = tid + kThreads * i;
-            int cn = n0 + (u >> 2);
-            cn = cn < N ? cn : N - 1;
-            wr[i] = *((const u32x4_t *)(a.qw + (size_t)cn * (K / 8)) + 4 * g + (u & 3));
-        }
-        if (tid < BM)
-            gr = (m0 + tid < M) ? gsumT[(size_t)g * M + m0 + tid] : 0.f;
+    for (int i = 0; i < 2; ++i) {
+        const int s = (wave * 2 + i) * 64 + lane; // word slot: column s/4, swizzled quarter s%4
+        const int cl = s >> 2, q = (s & 3) ^ ((cl >> 2) & 3);
+        woff[i] = n0 + cl < N ? (uint32_t)(n0 + cl) * (uint32_t)(K / 2) + (uint32_t)(q * 16) : kOob;
+    }
+    auto issue = [&](int g, int bi) {
+        unsigned char *base = smem + bi * kBufBytes;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            dma16(rx, base + (wave * 8 + i) * 1024, xoff[i], (uint32_t)g * (kGroup * 2));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            dma16(rw, base + kXBytes + (wave * 2 + i) * 1024, woff[i], (uint32_t)g * 64u);
     };
 
-    f32x4_t acc[4][4];
+    // per-lane scale and zero word of the wave's 4 column tiles for group g (offsets of
+    // group 0 once, + 2g / 4g bytes as the scalar offset)
+    uint32_t soff[4], zoff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int nt = 0; nt < 4; ++nt) {
+        const int n = n0 + wn * 64 + nt * 16 + col;
+        soff[nt] = n < N ? (uint32_t)(n * G) * 2u : kOob;
+        zoff[nt] = n < N ? (uint32_t)((n >> 3) * G) * 4u : kOob;
+    }
+    uint32_t sc_raw[4], zw_raw[4];
+    auto load_params = [&](int g) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            sc_raw[nt] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[nt], (uint32_t)g * 2u, 0);
+            zw_raw[nt] = __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[nt], (uint32_t)g * 4u, 0);
+        }
+    };
+
+    // dequantization constants pinned in VGPRs (one v_and_or_b32 per code pair)
+    uint32_t kmask = 0x000F000Fu, kbias = kF16Bias;
+    asm volatile("" : "+v"(kmask));
+    asm volatile("" : "+v"(kbias));
+
+    f32x4_t acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    load_group(0);
-    for (int g = 0; g < G; ++g) {
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int u = tid + kThreads * i;
-            xs[(u & 15) * BM + (u >> 4)] = x_permute8(xr[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int u = tid + kThreads * i;
-            wsm[(u >> 2) * kWPad + (u & 3)] = wr[i];
-        }
-        if (tid < BM)
-            gs[tid] = gr;
-        __syncthreads();
-        if (g + 1 < G)
-            load_group(g + 1);
+    issue(0, 0);
+    load_params(0);
+    wait_vmem();
+    __syncthreads();
 
-        float sc[4], cz[4];
-        u32x4_t wb[4];
+    for (int g = 0; g < G; ++g) {
+        const int bi = g & 1;
+        const unsigned char *base = smem + bi * kBufBytes;
+        f16x2_t s2[4], zn[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int zsh = ((n0 + wn * 64 + nt * 16 + col) & 7) * 4;
+            s2[nt] = as_h2((sc_raw[nt] & 0xFFFFu) * 0x00010001u);
+            zn[nt] = as_h2((0xE400u | ((zw_raw[nt] >> zsh) & 15u)) * 0x00010001u); // -(1024 + z)
+        }
+        if (g + 1 < G) {
+            issue(g + 1, bi ^ 1);
+            load_params(g + 1);
+        }
+
+        // the 4 words (k-steps 0..3) of each of the lane's 4 columns
+        u32x4_t wv[4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             const int cl = wn * 64 + nt * 16 + col;
-            int cn = n0 + cl;
-            cn = cn < N ? cn : N - 1;
-            sc[nt] = f16_bits_to_f32(a.scales[(size_t)cn * G + g]);
-            cz[nt] = (float)(kCodeBias + ((a.qz[(size_t)(cn >> 3) * G + g] >> ((cn & 7) * 4)) & 15u));
-            wb[nt] = wsm[cl * kWPad + h];
+            wv[nt] = *(const u32x4_t *)(base + kXBytes + (cl * 4 + (h ^ ((cl >> 2) & 3))) * 16);
         }
-
-        f32x4_t P[4][4];
+        // A fragments of k-step j (chunk 4h + j of lane group h) for the 8 row tiles; the
+        // next k-step's are read while this one computes.  B is dequantized one column
+        // tile at a time, between its 8 MFMAs.
+        auto read_a = [&](int j, f16x8_t (&af)[8]) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8_t bfr[4];
+            for (int mt = 0; mt < 8; ++mt) {
+                const int row = wm * 128 + mt * 16 + col;
+                af[mt] = *(const f16x8_t *)(base + (row * 16 + ((4 * h + j) ^ (row & 15))) * 16);
+            }
+        };
+        f16x8_t afa[8], afb[8];
+        read_a(0, afa);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f16x8_t(&cur)[8] = (j & 1) ? afb : afa;
+            f16x8_t(&nxt)[8] = (j & 1) ? afa : afb;
+            if (j < 3)
+                read_a(j + 1, nxt);
+            auto word = [&](int nt) { return j == 0 ? wv[nt].x : j == 1 ? wv[nt].y : j == 2 ? wv[nt].z : wv[nt].w; };
+            // B of column tile nt + 1 is dequantized while the MFMAs of tile nt run
+            f16x8_t bcur = dequant_word(word(0), kmask, kbias, zn[0], s2[0]);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                const uint32_t wj = ks == 0 ? wb[nt].x : ks == 1 ? wb[nt].y : ks == 2 ? wb[nt].z : wb[nt].w;
-                bfr[nt] = codes_to_frag(wj);
-            }
+                f16x8_t bnext = bcur;
+                if (nt < 3)
+                    bnext = dequant_word(word(nt + 1), kmask, kbias, zn[nt + 1], s2[nt + 1]);
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8_t af = __builtin_bit_cast(bf16x8_t, xs[(4 * h + ks) * BM + wm * 64 + mt * 16 + col]);
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    const f32x4_t cin = ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : P[mt][nt];
-                    P[mt][nt] = mfma16x16x32(af, bfr[nt], cin);
-                }
+                for (int mt = 0; mt < 8; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[mt], bcur, acc[mt][nt], 0, 0, 0);
+                bcur = bnext;
             }
         }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const f32x4_t S = *(const f32x4_t *)&gs[wm * 64 + mt * 16 + 4 * h];
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[mt][nt][r] = fmaf(sc[nt], fmaf(-cz[nt], S[r], P[mt][nt][r]), acc[mt][nt][r]);
-        }
+
+        wait_vmem(); // the next group's DMA and parameters have landed
+        __syncthreads();
     }
 
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 8; ++mt) {
+        float rsc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = m0 + wm * 128 + mt * 16 + 4 * h + r;
+            rsc[r] = row < M ? rowscale[row] : 0.f;
+        }
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             const int cn = n0 + wn * 64 + nt * 16 + col;
@@ -159,17 +280,21 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
                 continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm * 64 + mt * 16 + 4 * h + r;
+                const int row = m0 + wm * 128 + mt * 16 + 4 * h + r;
                 if (row < M) {
                     const size_t o = (size_t)row * N + cn;
+                    const float y = acc[mt][nt][r] * rsc[r];
                     if (a.y_f32)
-                        ((float *)a.Y)[o] = acc[mt][nt][r];
+                        ((float *)a.Y)[o] = y;
                     else
-                        ((uint16_t *)a.Y)[o] = f32_to_bf16_rne(acc[mt][nt][r]);
+                        ((uint16_t *)a.Y)[o] = f32_to_bf16_rne(y);
                 }
             }
         }
+    }
 }
+
+size_t round_up(size_t v, size_t m) { return (v + m - 1) / m * m; }
 
 } // namespace
 
@@ -179,20 +304,28 @@ TiledPlan plan_tiled(int M, int N, int K)
     p.G = K / kGroup;
     p.tiles_m = (M + BM - 1) / BM;
     p.tiles_n = (N + BN - 1) / BN;
-    p.off_gsum = kZeroRegion;
-    p.ws_bytes = p.off_gsum + (size_t)p.G * M * sizeof(float);
+    p.off_xh = kZeroRegion;
+    p.off_rs = round_up(p.off_xh + (size_t)M * K * 2, 256);
+    p.ws_bytes = p.off_rs + (size_t)M * sizeof(float);
     return p;
 }
 
 hipError_t launch_tiled(const TiledArgs &a, const TiledPlan &p, hipStream_t stream)
 {
-    const long long chunks = (long long)a.M * p.G * 16;
-    hipLaunchKernelGGL(gsum_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, a.X, a.M, a.K, p.G,
-                       (float *)(a.ws + p.off_gsum));
+    static bool lds_set = false;
+    if (!lds_set) {
+        const hipError_t e = hipFuncSetAttribute((const void *)tiled_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 kLdsBytes);
+        if (e != hipSuccess)
+            return e;
+        lds_set = true;
+    }
+    hipLaunchKernelGGL(prep_kernel, dim3(a.M), dim3(256), 0, stream, a.X, a.K, (uint16_t *)(a.ws + p.off_xh),
+                       (float *)(a.ws + p.off_rs));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(tiled_kernel, dim3(p.tiles_n, p.tiles_m), dim3(kThreads), 0, stream, a, p);
+    hipLaunchKernelGGL(tiled_kernel, dim3(p.tiles_m * p.tiles_n), dim3(kThreads), kLdsBytes, stream, a, p);
     return hipGetLastError();
 }
 
