@@ -72,8 +72,11 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &p, hipStream_t s
 struct TiledPlan {
     int G;
     int tiles_m, tiles_n;
+    int ksplit;       // K slices per tile (1: the tile kernel stores Y itself)
+    int gper;         // groups per K slice
     size_t off_xh;    // X as fp16, each row scaled by a power of two, [M][K]
     size_t off_rs;    // the per-row scales (fp32, M)
+    size_t off_part;  // ksplit > 1: fp32 partial sums [ksplit][M][N]
     size_t ws_bytes;
 };
 

@@ -20,7 +20,10 @@
 //     (buffer_load ... lds) one group ahead: the X tile [256 rows x 16 chunks], its
 //     16-byte slots XOR-swizzled by row (conflict-free fragment reads), and the
 //     packed words [256 columns x 64 B];
-//   * the epilogue multiplies each row by 2^e and stores bf16 (RNE) or fp32.
+//   * the epilogue multiplies each row by 2^e and stores bf16 (RNE) or fp32.  When
+//     the tiles alone would leave most CUs idle in the last round, K is split into
+//     slices: each slice stores its fp32 partial sums and reduce_kernel adds them in
+//     slice order (deterministic), scales the row and stores Y.
 // With X ~ N(0, 1) the rounding of the weights contributes about 3e-4 * rms(Y) (rms),
 // a few percent of the 1e-2 * rms(Y) bound at the largest shapes.
 #include "common.h"
@@ -128,12 +131,16 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
 
     // tiles are dealt out so that each XCD (blocks b, b + 8, ...) takes a contiguous
     // run of tiles in n-fastest order: its CUs share X rows in their L2
+    // (K slices are the outermost index: unit u = slice * ntiles + tile)
     const int ntiles = p.tiles_m * p.tiles_n;
+    const int nunits = ntiles * p.ksplit;
     const int b = blockIdx.x;
-    int t = (b & 7) * (ntiles / 8) + (b >> 3);
-    if ((ntiles & 7) != 0)
-        t = b; // uneven split: plain order
+    int u = (b & 7) * (nunits / 8) + (b >> 3);
+    if ((nunits & 7) != 0)
+        u = b; // uneven split: plain order
+    const int ks = u / ntiles, t = u - ks * ntiles;
     const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
+    const int g0 = ks * p.gper, g1 = G < g0 + p.gper ? G : g0 + p.gper;
     const int m0 = tm * BM, n0 = tn * BN;
 
     const uint16_t *xh = (const uint16_t *)(a.ws + p.off_xh);
@@ -201,13 +208,13 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
         for (int j = 0; j < 4; ++j)
             acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    issue(0, 0);
-    load_params(0);
+    issue(g0, 0);
+    load_params(g0);
     wait_vmem();
     __syncthreads();
 
-    for (int g = 0; g < G; ++g) {
-        const int bi = g & 1;
+    for (int g = g0; g < g1; ++g) {
+        const int bi = (g - g0) & 1;
         const unsigned char *base = smem + bi * kBufBytes;
         f16x2_t s2[4], zn[4];
 #pragma unroll
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
             s2[nt] = as_h2((sc_raw[nt] & 0xFFFFu) * 0x00010001u);
             zn[nt] = as_h2((0xE400u | ((zw_raw[nt] >> zsh) & 15u)) * 0x00010001u); // -(1024 + z)
         }
-        if (g + 1 < G) {
+        if (g + 1 < g1) {
             issue(g + 1, bi ^ 1);
             load_params(g + 1);
         }
@@ -265,6 +272,25 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
         __syncthreads();
     }
 
+    if (p.ksplit > 1) {
+        // fp32 partial sums of this K slice; reduce_kernel finishes the rows
+        float *part = (float *)(a.ws + p.off_part) + (size_t)ks * M * N;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int cn = n0 + wn * 64 + nt * 16 + col;
+                if (cn >= N)
+                    continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = m0 + wm * 128 + mt * 16 + 4 * h + r;
+                    if (row < M)
+                        part[(size_t)row * N + cn] = acc[mt][nt][r];
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
         float rsc[4];
@@ -294,6 +320,35 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
     }
 }
 
+// Y[m, 4c .. 4c+3] = 2^e_m * sum over slices s (in order) of part[s][m][4c ..]; N % 8 == 0
+__global__ __launch_bounds__(256) void reduce_kernel(const float *part, const float *rowscale, int M, int N, int ksplit,
+                                                     void *Y, int y_f32)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x; // 4 outputs each
+    const long long total = (long long)M * N / 4;
+    if (i >= total)
+        return;
+    const int m = (int)(i * 4 / N);
+    const size_t stride = (size_t)M * N;
+    f32x4_t s = *(const f32x4_t *)(part + i * 4);
+    for (int k = 1; k < ksplit; ++k) {
+        const f32x4_t v = *(const f32x4_t *)(part + (size_t)k * stride + i * 4);
+        s[0] += v[0];
+        s[1] += v[1];
+        s[2] += v[2];
+        s[3] += v[3];
+    }
+    const float sc = rowscale[m];
+    if (y_f32) {
+        *(f32x4_t *)((float *)Y + i * 4) = f32x4_t{s[0] * sc, s[1] * sc, s[2] * sc, s[3] * sc};
+    } else {
+        const uint32_t lo = f32_to_bf16_rne(s[0] * sc) | ((uint32_t)f32_to_bf16_rne(s[1] * sc) << 16);
+        const uint32_t hi = f32_to_bf16_rne(s[2] * sc) | ((uint32_t)f32_to_bf16_rne(s[3] * sc) << 16);
+        typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+        *(u32x2_t *)((uint16_t *)Y + i * 4) = u32x2_t{lo, hi};
+    }
+}
+
 size_t round_up(size_t v, size_t m) { return (v + m - 1) / m * m; }
 
 } // namespace
@@ -304,9 +359,29 @@ TiledPlan plan_tiled(int M, int N, int K)
     p.G = K / kGroup;
     p.tiles_m = (M + BM - 1) / BM;
     p.tiles_n = (N + BN - 1) / BN;
+    // K slices: estimated time = rounds * groups per round (one tile-group ~ 3.5 us on a
+    // CU) plus the traffic of the partial sums (~5 TB/s) for ksplit > 1
+    const long long ntiles = (long long)p.tiles_m * p.tiles_n;
+    const int kCUs = 256;
+    double best = 1e30;
+    p.ksplit = 1;
+    for (int ks = 1; ks <= 4 && ks <= p.G; ++ks) {
+        const int gper = (p.G + ks - 1) / ks;
+        const double rounds = (double)((ntiles * ks + kCUs - 1) / kCUs);
+        double t = rounds * gper * 3.5e-6;
+        if (ks > 1)
+            t += (double)(ks * 4 + 2) * M * N / 5e12;
+        if (t < best * 0.97) { // prefer fewer slices unless clearly faster
+            best = t;
+            p.ksplit = ks;
+        }
+    }
+    p.gper = (p.G + p.ksplit - 1) / p.ksplit;
+    p.ksplit = (p.G + p.gper - 1) / p.gper; // no empty slices
     p.off_xh = kZeroRegion;
     p.off_rs = round_up(p.off_xh + (size_t)M * K * 2, 256);
-    p.ws_bytes = p.off_rs + (size_t)M * sizeof(float);
+    p.off_part = round_up(p.off_rs + (size_t)M * sizeof(float), 256);
+    p.ws_bytes = p.off_part + (p.ksplit > 1 ? (size_t)p.ksplit * M * N * sizeof(float) : 0);
     return p;
 }
 
@@ -325,7 +400,14 @@ hipError_t launch_tiled(const TiledArgs &a, const TiledPlan &p, hipStream_t stre
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(tiled_kernel, dim3(p.tiles_m * p.tiles_n), dim3(kThreads), kLdsBytes, stream, a, p);
+    hipLaunchKernelGGL(tiled_kernel, dim3(p.tiles_m * p.tiles_n * p.ksplit), dim3(kThreads), kLdsBytes, stream, a, p);
+    e = hipGetLastError();
+    if (e != hipSuccess || p.ksplit == 1)
+        return e;
+    const long long quads = (long long)a.M * a.N / 4;
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream,
+                       (const float *)(a.ws + p.off_part), (const float *)(a.ws + p.off_rs), a.M, a.N, p.ksplit, a.Y,
+                       a.y_f32);
     return hipGetLastError();
 }
 
