@@ -39,13 +39,13 @@ struct SkinnyPlan {
     int G;         // K / 128
     int waves;     // waves per workgroup = tw * sk
     int tw, sk;    // tiles per item, K slices per tile
-    int chunk;     // groups of X staged in LDS at once (all of K when it fits)
+    int chunk;     // groups of X staged in LDS at once (all of K; xlds == 2: one slice)
     int per;       // groups per K slice (split mode; a multiple of 4)
     int ntg;       // tile groups per m-block = ceil(nt / tw)
     int items;     // mblocks * ntg
     int grid;      // workgroups
     int stream;    // 1: stream mode
-    int xlds;      // 1: X staged in LDS
+    int xlds;      // 1: X staged in LDS by the workgroup; 2: each wave stages its own slice
     size_t lds_bytes;
     size_t ws_bytes; // lm_head: the zero region (argmax keys, ticket); linear: 0
 };

@@ -50,7 +50,7 @@ constexpr int kB = 4;                  // groups per register batch
 constexpr int kCUs = 256;
 constexpr size_t kLdsBudget = 160 * 1024 - 4096;
 constexpr uint32_t kOob = 0xFFFFFF00u; // an offset past the end of every tensor
-constexpr int kSplitDirect = 0, kSplitLds = 1, kStream = 2;
+constexpr int kSplitDirect = 0, kSplitLds = 1, kStream = 2, kSplitPriv = 3;
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m)
 {
@@ -375,13 +375,17 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
     const int nthreads = blockDim.x, nwaves = nthreads >> 6;
     const int mrows = M < 16 ? M : 16;
 
-    // LDS: staged X [group][chunk c][row] (16 B each), the slot sums, S [group][16 rows],
-    // then the K-slice partial sums [wave][64 lanes][4]
+    // LDS: staged X [group][chunk c][row] (16 B each), the slot sums, S [group][16 rows]
+    // -- shared by the workgroup, or (kSplitPriv) one such region per wave holding
+    // p.chunk groups of its own K slice -- then the K-slice partial sums
+    // [wave][64 lanes][4]
     const int nslot = p.chunk * 16 * mrows;
-    u32x4_t *xs = (u32x4_t *)smem;
-    float *part = (float *)(smem + (size_t)nslot * 16);
+    const size_t region = (size_t)nslot * 20 + (size_t)p.chunk * 64;
+    unsigned char *xbase = MODE == kSplitPriv ? smem + (size_t)wave * region : smem;
+    u32x4_t *xs = (u32x4_t *)xbase;
+    float *part = (float *)(xbase + (size_t)nslot * 16);
     float *S = part + nslot;
-    float *red = S + p.chunk * 16;
+    float *red = (float *)(smem + (MODE == kSplitPriv ? (size_t)nwaves * region : region));
     uint32_t *ticket = (uint32_t *)(a.ws + kOffTicket);
     unsigned long long *keys = (unsigned long long *)(a.ws + kOffKeys);
 
@@ -556,7 +560,44 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
                 cur_mb = mb;
             }
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (MODE == kSplitLds) {
+            if constexpr (MODE == kSplitPriv) {
+                // each wave stages only its own K slice of X (few rows), in its own LDS
+                // region: the loads, the commit, the row sums and the compute of one wave
+                // need no workgroup barrier (LDS operations of a wave complete in order)
+                const int g0 = ks * p.per;
+                const int g1 = G < g0 + p.per ? G : g0 + p.per;
+                XStage st = x_stage(m0, Mb);
+                st.base += (uint32_t)(g0 * kGroup) * 2u;
+                st.total = Mb * (g1 - g0) * 16;
+                XRound xr;
+                stage_issue(xr, st, 0, lane, 64);
+                Batch b0, b1, b2;
+                load_batch<ALIGNED>(b0, rw, rs, rz, L, g0, g1);
+                load_batch<ALIGNED>(b1, rw, rs, rz, L, g0 + kB, g1);
+                load_batch<ALIGNED>(b2, rw, rs, rz, L, g0 + 2 * kB, g1);
+                stage_commit(xr, st, xs, part, 0, lane, 64);
+                stage_rest(st, xs, part, lane, 64);
+                group_sums(part, S, Mb, g1 - g0, lane, 64);
+                // compute_batch indexes by absolute group: shift the bases by g0
+                const u32x4_t *xlane = xs + (4 * h) * Mb + xrow - (size_t)g0 * 16 * Mb;
+                const float *sl = S + 4 * h - (size_t)g0 * 16;
+                for (int g = g0; g < g1; g += 3 * kB) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute_batch<NR>(b0, acc, xlane, sl, g, g1, Mb, L.zsh, kmask, kbias);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_batch<ALIGNED>(b0, rw, rs, rz, L, g + 3 * kB, g1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (g + kB < g1)
+                        compute_batch<NR>(b1, acc, xlane, sl, g + kB, g1, Mb, L.zsh, kmask, kbias);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_batch<ALIGNED>(b1, rw, rs, rz, L, g + 4 * kB, g1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (g + 2 * kB < g1)
+                        compute_batch<NR>(b2, acc, xlane, sl, g + 2 * kB, g1, Mb, L.zsh, kmask, kbias);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_batch<ALIGNED>(b2, rw, rs, rz, L, g + 5 * kB, g1);
+                }
+            } else if constexpr (MODE == kSplitLds) {
                 // slices of p.per groups (a multiple of kB): batches stay 4-aligned
                 const int g0 = ks * p.per;
                 const int g1 = G < g0 + p.per ? G : g0 + p.per;
@@ -678,7 +719,8 @@ size_t lds_per_group(int M)
 size_t lds_for(const SkinnyPlan &p, int M)
 {
     const size_t red = p.sk > 1 ? (size_t)p.tw * p.sk * 1024 : 0;
-    return (size_t)p.chunk * lds_per_group(M) + red;
+    const size_t xs = (size_t)p.chunk * lds_per_group(M);
+    return (p.xlds == 2 ? xs * p.tw * p.sk : xs) + red;
 }
 
 // Tuning override for the split-mode shape, read once from W4A16_SKINNY_SPLIT="tw,sk"
@@ -743,14 +785,16 @@ SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit)
             sk = osk;
         }
         const size_t red = sk > 1 ? (size_t)tw * sk * 1024 : 0;
-        // X in LDS when all of K fits and staging it is cheap next to the weights the
-        // workgroup streams: few rows, or several tiles sharing each staged row
-        const bool fits = (size_t)p.G * per_group + red <= lds_limit;
-        p.xlds = fits && (mrows <= 4 || tw >= 2);
-        p.chunk = p.xlds ? p.G : 0;
         // whole batches per slice; drop the slices that rounding left empty
         p.per = round_up((p.G + sk - 1) / sk, kB);
         sk = (p.G + p.per - 1) / p.per;
+        // X in LDS: per wave (its own slice) for up to 4 rows, else shared by the
+        // workgroup when all of K fits and staging it is cheap next to the weights the
+        // workgroup streams (several tiles sharing each staged row); else from L2
+        const bool priv = mrows <= 4 && (size_t)tw * sk * p.per * per_group + red <= lds_limit;
+        const bool fits = (size_t)p.G * per_group + red <= lds_limit;
+        p.xlds = priv ? 2 : (fits && (mrows <= 4 || tw >= 2)) ? 1 : 0;
+        p.chunk = p.xlds == 2 ? p.per : p.xlds == 1 ? p.G : 0;
         p.tw = tw;
         p.sk = sk;
         p.ntg = (p.nt + tw - 1) / tw;
@@ -818,6 +862,8 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, hipStream_
             allow_lds<kSplitLds, true>(lds_limit);
             allow_lds<kStream, false>(lds_limit);
             allow_lds<kStream, true>(lds_limit);
+            allow_lds<kSplitPriv, false>(lds_limit);
+            allow_lds<kSplitPriv, true>(lds_limit);
         }
     }
     const SkinnyPlan p = plan.lds_bytes > lds_limit ? plan_skinny(a.M, a.N, a.K, a.lmhead, lds_limit) : plan;
@@ -829,7 +875,9 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, hipStream_
     const bool aligned = (a.G % 4) == 0 && (p.per % 4) == 0;
     if (p.stream)
         launch_mode<kStream>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
-    else if (p.xlds)
+    else if (p.xlds == 2)
+        launch_mode<kSplitPriv>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
+    else if (p.xlds == 1)
         launch_mode<kSplitLds>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
     else
         launch_mode<kSplitDirect>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
