@@ -91,11 +91,12 @@ def load_traffic(workload, launches_per_step):
 class Workload:
     """Device tensors for one workload: R rotating copies of every projection."""
 
-    def __init__(self, name, dev, lmhead=False, max_copies=64):
+    def __init__(self, name, dev, lmhead=False, max_copies=64, batched=False):
         import torch
         import int4_weight_only_02_amd as w4
         self.name = name
         self.lmhead = lmhead
+        self.batched = batched
         self.shapes = synth.WORKLOADS[name]
         self.projs = []
         per_copy = 0
@@ -138,6 +139,12 @@ class Workload:
             w4.w4a16_linear(X, qw, S, qz, out=p["Y"], workspace=self.ws)
 
     def step(self, r):
+        if self.batched:
+            # every projection of the step in one launch (w4a16_linear_batch)
+            import int4_weight_only_02_amd as w4
+            w4.w4a16_linear_batch([p["copies"][r % self.R] for p in self.projs], workspace=self.ws,
+                                  outs=[p["Y"] for p in self.projs])
+            return
         for p in self.projs:
             self.launch(p, r % self.R)
 
@@ -148,11 +155,16 @@ class Workload:
         import oracle
         import int4_weight_only_02_amd as w4
         worst = 0.0
-        for p in self.projs:
+        ys = None
+        if self.batched:
+            ys = w4.w4a16_linear_batch([p["copies"][0] for p in self.projs], out_dtype=torch.float32,
+                                       workspace=self.ws)
+        for q, p in enumerate(self.projs):
             if self.lmhead:
                 continue
             X, qw, S, qz = p["copies"][0]
-            Y = w4.w4a16_linear(X, qw, S, qz, out_dtype=torch.float32, workspace=self.ws)
+            Y = ys[q] if ys is not None else w4.w4a16_linear(X, qw, S, qz, out_dtype=torch.float32,
+                                                              workspace=self.ws)
             torch.cuda.synchronize()
             d = p["host"]
             oqw, oqz = oracle.pack(d["codes"], d["zeros"])
@@ -169,9 +181,22 @@ class Workload:
 
 def time_events(wl, reps):
     """Eager per-launch time (us, median) from HIP events around every launch, per
-    projection: back-to-back calls from the host, launch overhead included."""
+    projection (or per batch launch): back-to-back calls from the host, launch
+    overhead included."""
     import torch
     out = {}
+    if wl.batched:
+        evs = []
+        for i in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            wl.step(i)
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        out["batch"] = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+        return out
     for p in wl.projs:
         evs = []
         for i in range(reps):
@@ -253,8 +278,8 @@ def cpu_baseline(name, budget_s=10.0):
             "ms_per_step": round(dt * 1e3, 3)}
 
 
-def measure(name, dev, steps, warmup, lmhead=False, ev_reps=200):
-    wl = Workload(name, dev, lmhead=lmhead)
+def measure(name, dev, steps, warmup, lmhead=False, ev_reps=200, batched=False):
+    wl = Workload(name, dev, lmhead=lmhead, batched=batched)
     err = wl.check()
     ev = time_events(wl, ev_reps)
     wall, gpu = time_steps(wl, steps, warmup)
@@ -263,11 +288,14 @@ def measure(name, dev, steps, warmup, lmhead=False, ev_reps=200):
            "GBps": round(wl.bytes_per_step / wall / 1e9, 2),
            "hbm_frac": round(wl.bytes_per_step / wall / 1e9 / HBM_PEAK_GBS, 4),
            "TFLOPs": round(wl.flops_per_step / wall / 1e12, 3),
-           "launches_per_step": len(wl.projs),
+           "launches_per_step": 1 if batched else len(wl.projs),
+           "batched": batched,
            "kernel_us_eager_median": {k: round(v, 3) for k, v in ev.items()},
            "sampled_max_err_over_rms": err}
     per = {}
     for p in wl.projs:
+        if batched:
+            continue
         t = ev[p["label"]] * 1e-6
         b = algo_bytes(p["M"], p["N"], p["K"], lmhead=lmhead)
         f = 2 * p["M"] * p["N"] * p["K"]
@@ -367,17 +395,19 @@ def main():
         calib_copy(dev)
         return
 
-    names = [HEADLINE, "single_512", "verify_block_m16", "lmhead_verify_m16", "prefill_m8192"]
+    names = [HEADLINE, "single_512", "verify_block_m16", "lmhead_verify_m16", "prefill_m8192",
+             "decode_gemv_m1+batch", "verify_block_m16+batch"]
     if args.only:
         names = [args.only]
     results = {}
-    for name in names:
+    for key in names:
+        name, batched = key.split("+")[0], key.endswith("+batch")
         steps = args.steps if name != "prefill_m8192" else max(4, min(args.steps, 40))
         warm = args.warmup if name != "prefill_m8192" else 4
         if name == "lmhead_verify_m16":
             steps = max(10, min(args.steps, 400))
-        results[name] = measure(name, dev, steps, warm, lmhead=(name == "lmhead_verify_m16"))
-        print("[bench] %s: %s" % (name, json.dumps(results[name])), file=sys.stderr, flush=True)
+        results[key] = measure(name, dev, steps, warm, lmhead=(name == "lmhead_verify_m16"), batched=batched)
+        print("[bench] %s: %s" % (key, json.dumps(results[key])), file=sys.stderr, flush=True)
 
     head = results.get(HEADLINE) or results[names[0]]
     head_name = HEADLINE if HEADLINE in results else names[0]

@@ -107,6 +107,38 @@ int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, con
                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * w4a16_linear_batch -- several projections of the same rows in one launch.
+ * Verifying a draft block of 16 tokens runs every projection of a decoder layer on
+ * 16 rows (Pith review, free parameters: block size 16), and a decode step runs
+ * them on one row; each projection alone is too small to fill the GPU or to hide a
+ * launch.  This call computes Y_q = X_q * W_q^T for every entry of
+ * problems[0 .. count) as w4a16_linear would (same grid, same reading, same
+ * accuracy bound), in one launch when M <= 64 (one after another when M > 64).
+ *   problems  host array of count descriptors (read during the call only); each
+ *             names its own device tensors X [M][K] bf16, qweight, scales, qzeros,
+ *             Y [M][N], and its N and K (the layouts of w4a16_linear)
+ *   count     0 .. W4A16_MAX_BATCH
+ *   M, group, y_dtype   shared by all entries
+ *   workspace at least the largest w4a16_workspace_bytes(W4A16_OP_LINEAR, M, N_q, K_q)
+ *             over the entries (0 when M <= 64); the rules of w4a16_linear
+ * Errors: as w4a16_linear, checked for every entry before anything is launched;
+ * W4A16_ERR_SHAPE also for count outside 0 .. W4A16_MAX_BATCH.  Entries with N == 0
+ * and calls with M == 0 do nothing.  Outputs must not alias each other or inputs.
+ */
+#define W4A16_MAX_BATCH 8
+typedef struct w4a16_problem {
+    const void *X;            /* bf16 [M][K] */
+    const uint32_t *qweight;  /* [N][K/8] */
+    const void *scales;       /* fp16 [N][K/group] */
+    const uint32_t *qzeros;   /* [N/8][K/group] */
+    void *Y;                  /* [M][N], bf16 or fp32 */
+    int N, K;
+} w4a16_problem;
+
+int w4a16_linear_batch(const w4a16_problem *problems, int count, int M, int group, int y_dtype,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * w4a16_lmhead_verify -- the lm_head projection fused with greedy verification
  * of a draft block (Pith review, Assumptions & free parameters: the first
  * assumption, on verification; free parameters: block size 16).

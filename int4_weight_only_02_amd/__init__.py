@@ -11,6 +11,8 @@ Calls (same names as the C ABI):
   w4a16_linear(X bf16[M,K], qweight, scales f16[N,G], qzeros, out_dtype) -> Y[M,N]
   w4a16_lmhead_verify(X, qweight, scales, qzeros, draft i32[M], return_logits) ->
         (argmax i32[M], accept_len i32[1], logits or None)
+  w4a16_linear_batch([(X, qweight, scales, qzeros), ...], out_dtype) -> [Y, ...]
+        (up to 8 projections with the same M in one launch)
   w4a16_workspace_bytes(op, M, N, K)
 Packed words travel as int32 tensors (same bits as uint32).
 """
@@ -25,8 +27,15 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw4a16.so")
 _lib = None
 
-EXPORTED = ("w4a16_pack", "w4a16_linear", "w4a16_lmhead_verify", "w4a16_workspace_bytes",
-            "w4a16_status_string", "w4a16_abi_version")
+EXPORTED = ("w4a16_pack", "w4a16_linear", "w4a16_linear_batch", "w4a16_lmhead_verify",
+            "w4a16_workspace_bytes", "w4a16_status_string", "w4a16_abi_version")
+MAX_BATCH = 8
+
+
+class Problem(ctypes.Structure):
+    """w4a16_problem: the device tensors of one projection of a batch call."""
+    _fields_ = [("X", ctypes.c_void_p), ("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("qzeros", ctypes.c_void_p), ("Y", ctypes.c_void_p), ("N", ctypes.c_int), ("K", ctypes.c_int)]
 
 
 class W4A16Error(RuntimeError):
@@ -49,6 +58,8 @@ def lib():
     L.w4a16_pack.restype = I
     L.w4a16_linear.argtypes = [P, P, P, P, I, I, I, I, P, I, P, S, P]
     L.w4a16_linear.restype = I
+    L.w4a16_linear_batch.argtypes = [P, I, I, I, I, P, S, P]
+    L.w4a16_linear_batch.restype = I
     L.w4a16_lmhead_verify.argtypes = [P, P, P, P, I, I, I, I, P, P, I, P, P, P, S, P]
     L.w4a16_lmhead_verify.restype = I
     L.w4a16_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -145,6 +156,35 @@ def w4a16_linear(X, qweight, scales, qzeros, out_dtype=None, group=GROUP, out=No
                             _ptr(Y), ydt, _ptr(ws), nbytes, _stream(stream))
     _check(st, "w4a16_linear")
     return Y
+
+
+def w4a16_linear_batch(problems, out_dtype=None, group=GROUP, outs=None, workspace=None, stream=None):
+    """problems: list of (X, qweight, scales, qzeros) sharing M; returns the list of Y."""
+    import torch
+    if len(problems) == 0:
+        return []
+    M = problems[0][0].shape[0]
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if outs is None else outs[0].dtype
+    ydt = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    arr = (Problem * len(problems))()
+    ys = []
+    need = 0
+    for q, (X, qweight, scales, qzeros) in enumerate(problems):
+        assert X.dtype == torch.bfloat16 and scales.dtype == torch.float16 and X.shape[0] == M
+        assert X.is_contiguous() and qweight.is_contiguous() and scales.is_contiguous() and qzeros.is_contiguous()
+        K = X.shape[1]
+        N = qweight.shape[0]
+        Y = outs[q] if outs is not None else torch.empty((M, N), dtype=out_dtype, device=X.device)
+        assert Y.shape == (M, N) and Y.dtype == out_dtype and Y.is_contiguous()
+        arr[q] = Problem(X.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(), Y.data_ptr(), N, K)
+        need = max(need, w4a16_workspace_bytes(OP_LINEAR, M, N, K, group))
+        ys.append(Y)
+    ws = _workspace(workspace, problems[0][0].device).get(need)
+    st = lib().w4a16_linear_batch(ctypes.cast(arr, ctypes.c_void_p), len(problems), M, group, ydt, _ptr(ws), need,
+                                  _stream(stream))
+    _check(st, "w4a16_linear_batch")
+    return ys
 
 
 def w4a16_lmhead_verify(X, qweight, scales, qzeros, draft_ids, return_logits=False,

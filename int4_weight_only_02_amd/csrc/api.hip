@@ -136,6 +136,78 @@ int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, con
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
+int w4a16_linear_batch(const w4a16_problem *problems, int count, int M, int group, int y_dtype,
+                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (group != kGroup || (y_dtype != W4A16_OUT_BF16 && y_dtype != W4A16_OUT_F32))
+        return W4A16_ERR_UNSUPPORTED;
+    if (count < 0 || count > W4A16_MAX_BATCH || M < 0)
+        return W4A16_ERR_SHAPE;
+    if (count > 0 && !problems)
+        return W4A16_ERR_NULL;
+    size_t need = 0;
+    for (int q = 0; q < count; ++q) {
+        const w4a16_problem &pr = problems[q];
+        const int st = check_dims(M, pr.N, pr.K);
+        if (st != W4A16_OK)
+            return st;
+        if (M == 0 || pr.N == 0)
+            continue;
+        if (!pr.X || !pr.qweight || !pr.scales || !pr.qzeros || !pr.Y)
+            return W4A16_ERR_NULL;
+        if (misaligned(pr.X) || misaligned(pr.qweight) || misaligned(pr.scales) || misaligned(pr.qzeros) ||
+            misaligned(pr.Y))
+            return W4A16_ERR_ALIGN;
+        const size_t n = linear_ws(M, pr.N, pr.K);
+        need = n > need ? n : need;
+    }
+    if (M == 0)
+        return W4A16_OK;
+    if (misaligned(workspace))
+        return W4A16_ERR_ALIGN;
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return W4A16_ERR_WORKSPACE;
+
+    if (M > kSkinnyMaxM) {
+        // large M: the matrix cores are busy within each projection; run them in turn
+        for (int q = 0; q < count; ++q) {
+            const w4a16_problem &pr = problems[q];
+            const int st = w4a16_linear(pr.X, pr.qweight, pr.scales, pr.qzeros, M, pr.N, pr.K, group, pr.Y,
+                                        y_dtype, workspace, workspace_bytes, stream);
+            if (st != W4A16_OK)
+                return st;
+        }
+        return W4A16_OK;
+    }
+    SkinnyMulti mp{};
+    int c = 0;
+    for (int q = 0; q < count; ++q) {
+        const w4a16_problem &pr = problems[q];
+        if (pr.N == 0)
+            continue;
+        SkinnyArgs &a = mp.args[c];
+        a.X = (const uint16_t *)pr.X;
+        a.qw = pr.qweight;
+        a.scales = (const uint16_t *)pr.scales;
+        a.qz = pr.qzeros;
+        a.M = M;
+        a.N = pr.N;
+        a.K = pr.K;
+        a.G = pr.K / kGroup;
+        a.Y = pr.Y;
+        a.y_f32 = y_dtype == W4A16_OUT_F32;
+        a.ws = (unsigned char *)workspace;
+        a.lmhead = 0;
+        mp.plan[c] = plan_skinny_fixed(M, pr.N, pr.K);
+        ++c;
+    }
+    mp.count = c;
+    if (c == 0)
+        return W4A16_OK;
+    const hipError_t e = launch_skinny_multi(mp, M, (hipStream_t)stream);
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
 int w4a16_lmhead_verify(const void *X, const uint32_t *qweight, const void *scales,
                         const uint32_t *qzeros, int M, int N, int K, int group,
                         const int32_t *draft_ids, void *Y_or_null, int y_dtype,

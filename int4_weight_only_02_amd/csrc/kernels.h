@@ -68,6 +68,17 @@ struct SkinnyArgs {
 SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit = 0);
 hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &p, hipStream_t stream);
 
+// several linear projections with the same M in one launch (split mode, 8 waves each)
+constexpr int kMaxProblems = 8;
+struct SkinnyMulti {
+    int count;
+    int begin[kMaxProblems + 1]; // first workgroup of each projection; begin[count] = grid
+    SkinnyArgs args[kMaxProblems];
+    SkinnyPlan plan[kMaxProblems];
+};
+SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit = 0);
+hipError_t launch_skinny_multi(SkinnyMulti &mp, int M, hipStream_t stream);
+
 // ---------------------------------------------------------------- tiled (large M)
 struct TiledPlan {
     int G;

@@ -359,14 +359,14 @@ __device__ __forceinline__ void group_sums(const float *part, float *S, int Mb, 
     }
 }
 
-// MODE: kSplitDirect, kSplitLds or kStream (see the plan)
+// The work of one workgroup on one projection.  MODE: kSplitDirect, kSplitLds,
+// kSplitPriv or kStream (see the plan).  The workgroup takes items first, first +
+// stride, ... (split mode) or tile groups first, first + stride, ... (stream mode).
 template <int NR, int MODE, bool ALIGNED>
-__global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
+__device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPlan &p, int first, int stride,
+                                            unsigned char *smem, unsigned long long (*kred)[16], int &s_flag)
 {
     constexpr bool STREAM = MODE == kStream;
-    extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ unsigned long long kred[kMaxWaves][16];
-    __shared__ int s_flag;
 
     const int M = a.M, N = a.N, K = a.K, G = a.G;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
                 flush_best(cur_mb);
             cur_mb = mb;
 
-            int tgA = blockIdx.x, gA = 0;
+            int tgA = first, gA = 0;
             int tileA = tgA * nwaves + wave;
             bool liveA = tgA < p.ntg && tileA * 16 < N;
             LaneGrid LA = lane_grid(tileA, col, h, N, K, G, liveA);
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
                 // phase A: prefetch the batch after A into bB, compute A
                 int tgB = tgA, gB = gA + kB;
                 if (gB >= G) {
-                    tgB += gridDim.x;
+                    tgB += stride;
                     gB = 0;
                 }
                 const int tileB = tgB * nwaves + wave;
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
                 // phase B: prefetch the batch after B into bA, compute B
                 int tgC = tgB, gC = gB + kB;
                 if (gC >= G) {
-                    tgC += gridDim.x;
+                    tgC += stride;
                     gC = 0;
                 }
                 const int tileC = tgC * nwaves + wave;
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
     } else {
         // ---- split mode: item = (m-block, group of tw tiles); wave = (tile slot, K slice)
         const int tslot = wave % p.tw, ks = wave / p.tw;
-        for (int it = blockIdx.x; it < p.items; it += gridDim.x) {
+        for (int it = first; it < p.items; it += stride) {
             const int mb = it / p.ntg, tg = it - mb * p.ntg;
             const int m0 = mb * 16;
             const int Mb = M - m0 < 16 ? M - m0 : 16;
@@ -566,9 +566,10 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
                 // need no workgroup barrier (LDS operations of a wave complete in order)
                 const int g0 = ks * p.per;
                 const int g1 = G < g0 + p.per ? G : g0 + p.per;
+                const int ng = g1 > g0 ? g1 - g0 : 0; // slices past K are empty
                 XStage st = x_stage(m0, Mb);
-                st.base += (uint32_t)(g0 * kGroup) * 2u;
-                st.total = Mb * (g1 - g0) * 16;
+                st.base += (uint32_t)(g0 < G ? g0 * kGroup : 0) * 2u;
+                st.total = Mb * ng * 16;
                 XRound xr;
                 stage_issue(xr, st, 0, lane, 64);
                 Batch b0, b1, b2;
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
                 load_batch<ALIGNED>(b2, rw, rs, rz, L, g0 + 2 * kB, g1);
                 stage_commit(xr, st, xs, part, 0, lane, 64);
                 stage_rest(st, xs, part, lane, 64);
-                group_sums(part, S, Mb, g1 - g0, lane, 64);
+                group_sums(part, S, Mb, ng, lane, 64);
                 // compute_batch indexes by absolute group: shift the bases by g0
                 const u32x4_t *xlane = xs + (4 * h) * Mb + xrow - (size_t)g0 * 16 * Mb;
                 const float *sl = S + 4 * h - (size_t)g0 * 16;
@@ -610,7 +611,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
                 load_batch<ALIGNED>(b0, rw, rs, rz, L, g0, g1);
                 load_batch<ALIGNED>(b1, rw, rs, rz, L, g0 + kB, g1);
                 load_batch<ALIGNED>(b2, rw, rs, rz, L, g0 + 2 * kB, g1);
-                if (it != (int)blockIdx.x)
+                if (it != first)
                     __syncthreads(); // the previous item's reads of X are done
                 stage_commit(xr, st, xs, part, 0, tid, nthreads);
                 stage_rest(st, xs, part, tid, nthreads);
@@ -707,6 +708,41 @@ __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
             }
         }
     }
+}
+
+template <int NR, int MODE, bool ALIGNED>
+__global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ unsigned long long kred[kMaxWaves][16];
+    __shared__ int s_flag;
+    skinny_body<NR, MODE, ALIGNED>(a, p, blockIdx.x, gridDim.x, smem, kred, s_flag);
+}
+
+// Several projections (same M) in one launch: workgroup b works on item
+// b - begin[q] of projection q, with that projection's own plan (all plans use the
+// same number of waves).  Consecutive projections overlap: no launch gap, and the
+// tail of one is filled by the next.
+template <int NR, bool ALIGNED>
+__global__ __launch_bounds__(512) void skinny_multi_kernel(SkinnyMulti mp)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ unsigned long long kred[kMaxWaves][16];
+    __shared__ int s_flag;
+    const int b = blockIdx.x;
+    int q = 0;
+    for (int i = 1; i < mp.count; ++i)
+        if (b >= mp.begin[i])
+            q = i;
+    const SkinnyArgs a = mp.args[q];
+    const SkinnyPlan p = mp.plan[q];
+    const int it = b - mp.begin[q];
+    if (p.xlds == 2)
+        skinny_body<NR, kSplitPriv, ALIGNED>(a, p, it, 1 << 30, smem, kred, s_flag);
+    else if (p.xlds == 1)
+        skinny_body<NR, kSplitLds, ALIGNED>(a, p, it, 1 << 30, smem, kred, s_flag);
+    else
+        skinny_body<NR, kSplitDirect, ALIGNED>(a, p, it, 1 << 30, smem, kred, s_flag);
 }
 
 // LDS per staged group: 16 slots of 16 B and their 4-byte sums per row, and S (16 rows)
@@ -807,6 +843,41 @@ SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit)
     return p;
 }
 
+// Split-mode plan with exactly kMaxWaves waves (for projections sharing one launch):
+// tw a power of two, sk = kMaxWaves / tw (slices past K stay empty).
+SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit)
+{
+    SkinnyPlan p{};
+    if (lds_limit == 0 || lds_limit > kLdsBudget)
+        lds_limit = kLdsBudget;
+    p.G = K / kGroup;
+    p.mblocks = (M + 15) / 16;
+    p.nt = (N + 15) / 16;
+    const int mrows = M < 16 ? M : 16;
+    const size_t per_group = lds_per_group(M);
+    const long long tiles = (long long)p.nt * p.mblocks;
+    int tw = 1;
+    while (tw < kMaxWaves && (long long)tw * kCUs < tiles)
+        tw *= 2;
+    const int sk = kMaxWaves / tw;
+    const size_t red = sk > 1 ? (size_t)kMaxWaves * 1024 : 0;
+    p.stream = 0;
+    p.tw = tw;
+    p.sk = sk;
+    p.per = round_up((p.G + sk - 1) / sk, kB);
+    const bool priv = mrows <= 4 && (size_t)kMaxWaves * p.per * per_group + red <= lds_limit;
+    const bool fits = (size_t)p.G * per_group + red <= lds_limit;
+    p.xlds = priv ? 2 : (fits && (mrows <= 4 || tw >= 2)) ? 1 : 0;
+    p.chunk = p.xlds == 2 ? p.per : p.xlds == 1 ? p.G : 0;
+    p.ntg = (p.nt + tw - 1) / tw;
+    p.items = p.mblocks * p.ntg;
+    p.grid = p.items;
+    p.waves = kMaxWaves;
+    p.lds_bytes = lds_for(p, M);
+    p.ws_bytes = 0;
+    return p;
+}
+
 namespace {
 
 template <int MODE, bool ALIGNED>
@@ -842,11 +913,20 @@ void launch_mode(bool aligned, int nr, dim3 grid, dim3 block, size_t lds, hipStr
         launch_variant<MODE, false>(nr, grid, block, lds, stream, a, p);
 }
 
-} // namespace
-
-hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, hipStream_t stream)
+template <bool ALIGNED>
+void allow_lds_multi(size_t bytes)
 {
-    // LDS per workgroup: whatever the device allows, up to the budget the plan assumed
+    (void)hipFuncSetAttribute((const void *)skinny_multi_kernel<1, ALIGNED>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    (void)hipFuncSetAttribute((const void *)skinny_multi_kernel<2, ALIGNED>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    (void)hipFuncSetAttribute((const void *)skinny_multi_kernel<4, ALIGNED>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+// LDS per workgroup: whatever the device allows, up to the budget the plans assume
+hipError_t device_lds_limit(size_t *limit)
+{
     static size_t lds_limit = 0;
     if (lds_limit == 0) {
         int dev = 0, v = 0;
@@ -864,8 +944,64 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, hipStream_
             allow_lds<kStream, true>(lds_limit);
             allow_lds<kSplitPriv, false>(lds_limit);
             allow_lds<kSplitPriv, true>(lds_limit);
+            allow_lds_multi<false>(lds_limit);
+            allow_lds_multi<true>(lds_limit);
         }
     }
+    *limit = lds_limit;
+    return hipSuccess;
+}
+
+} // namespace
+
+hipError_t launch_skinny_multi(SkinnyMulti &mp, int M, hipStream_t stream)
+{
+    size_t lds_limit = 0;
+    hipError_t e = device_lds_limit(&lds_limit);
+    if (e != hipSuccess)
+        return e;
+    size_t lds = 0;
+    bool aligned = true;
+    int grid = 0;
+    for (int q = 0; q < mp.count; ++q) {
+        if (mp.plan[q].lds_bytes > lds_limit)
+            mp.plan[q] = plan_skinny_fixed(M, mp.args[q].N, mp.args[q].K, lds_limit);
+        if (mp.plan[q].lds_bytes > lds_limit)
+            return hipErrorInvalidValue;
+        lds = mp.plan[q].lds_bytes > lds ? mp.plan[q].lds_bytes : lds;
+        aligned = aligned && (mp.args[q].G % 4) == 0 && (mp.plan[q].per % 4) == 0;
+        mp.begin[q] = grid;
+        grid += mp.plan[q].grid;
+    }
+    mp.begin[mp.count] = grid;
+    if (grid == 0)
+        return hipSuccess;
+    const dim3 block(64 * kMaxWaves), g(grid);
+    const int nr = M == 1 ? 1 : M == 2 ? 2 : 4;
+    if (aligned) {
+        if (nr == 1)
+            hipLaunchKernelGGL((skinny_multi_kernel<1, true>), g, block, lds, stream, mp);
+        else if (nr == 2)
+            hipLaunchKernelGGL((skinny_multi_kernel<2, true>), g, block, lds, stream, mp);
+        else
+            hipLaunchKernelGGL((skinny_multi_kernel<4, true>), g, block, lds, stream, mp);
+    } else {
+        if (nr == 1)
+            hipLaunchKernelGGL((skinny_multi_kernel<1, false>), g, block, lds, stream, mp);
+        else if (nr == 2)
+            hipLaunchKernelGGL((skinny_multi_kernel<2, false>), g, block, lds, stream, mp);
+        else
+            hipLaunchKernelGGL((skinny_multi_kernel<4, false>), g, block, lds, stream, mp);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, hipStream_t stream)
+{
+    size_t lds_limit = 0;
+    const hipError_t le = device_lds_limit(&lds_limit);
+    if (le != hipSuccess)
+        return le;
     const SkinnyPlan p = plan.lds_bytes > lds_limit ? plan_skinny(a.M, a.N, a.K, a.lmhead, lds_limit) : plan;
     if (p.lds_bytes > lds_limit)
         return hipErrorInvalidValue;

@@ -128,6 +128,32 @@ def test_lmhead_rejections(lib):
     assert lmhead(lib, wsb=8) == ERR_WORKSPACE
 
 
+def batch(lib, probs, count=None, M=4, group=128, ydt=0, ws=None, wsb=0):
+    arr = (w4.Problem * max(1, len(probs)))(*probs)
+    n = len(probs) if count is None else count
+    return lib.w4a16_linear_batch(ctypes.cast(arr, ctypes.c_void_p), n, M, group, ydt, ws, wsb, None)
+
+
+def test_batch_rejections(lib):
+    good = w4.Problem(A.value, A.value, A.value, A.value, A2.value, 512, 512)
+    assert batch(lib, [good], group=64) == ERR_UNSUPPORTED
+    assert batch(lib, [good], ydt=3) == ERR_UNSUPPORTED
+    assert batch(lib, [good], count=-1) == ERR_SHAPE
+    assert batch(lib, [good] * 9) == ERR_SHAPE
+    assert batch(lib, [good], M=-1) == ERR_SHAPE
+    assert lib.w4a16_linear_batch(None, 2, 4, 128, 0, None, 0, None) == ERR_NULL
+    assert batch(lib, [good, w4.Problem(A.value, A.value, A.value, A.value, A2.value, 12, 512)]) == ERR_SHAPE
+    assert batch(lib, [good, w4.Problem(A.value, A.value, A.value, A.value, A2.value, 512, 500)]) == ERR_SHAPE
+    assert batch(lib, [good, w4.Problem(A.value, None, A.value, A.value, A2.value, 512, 512)]) == ERR_NULL
+    assert batch(lib, [good, w4.Problem(A.value, A.value, A.value, A.value, MIS.value, 512, 512)]) == ERR_ALIGN
+    # large M needs the prefill workspace of the largest entry
+    assert batch(lib, [good], M=300) == ERR_WORKSPACE
+    # nothing to do: no launch
+    assert batch(lib, [], count=0) == OK
+    assert batch(lib, [good], M=0) == OK
+    assert batch(lib, [w4.Problem(A.value, None, None, None, None, 0, 512)]) == OK
+
+
 def test_pack_rejections(lib):
     f = lib.w4a16_pack
     assert f(A, A, 512, 512, 64, A, A, None) == ERR_UNSUPPORTED
