@@ -88,6 +88,16 @@ def load_traffic(workload, launches_per_step):
         return None
 
 
+# Projections of one step that read the same activations, so that nothing in the
+# group waits for another's output: they may share one launch.  In a decoder layer q,
+# k and v read the layer input and gate and up the MLP input, while o reads the
+# attention output and down the gated MLP activation; a decode step's MLP (gate/up,
+# then down) is a chain.
+BATCH_GROUPS = {
+    "verify_block_m16": [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]],
+}
+
+
 class Workload:
     """Device tensors for one workload: R rotating copies of every projection."""
 
@@ -124,6 +134,13 @@ class Workload:
             else:
                 ws_need = max(ws_need, w4.w4a16_workspace_bytes(w4.OP_LINEAR, M, N, K))
             self.projs.append(p)
+        self.groups = None
+        if batched:
+            idx = {p["label"]: q for q, p in enumerate(self.projs)}
+            self.groups = [[idx[l] for l in g] for g in BATCH_GROUPS[name]]
+            ws_need = max(ws_need, max(sum(w4.w4a16_workspace_bytes(w4.OP_LINEAR, self.projs[q]["M"],
+                                                                   self.projs[q]["N"], self.projs[q]["K"])
+                                           for q in g) for g in self.groups))
         self.ws = w4.Workspace(dev)
         self.ws.get(ws_need)
         self.bytes_per_step = sum(algo_bytes(p["M"], p["N"], p["K"], lmhead=lmhead) for p in self.projs)
@@ -138,12 +155,19 @@ class Workload:
         else:
             w4.w4a16_linear(X, qw, S, qz, out=p["Y"], workspace=self.ws)
 
+    def launch_group(self, g, r):
+        """One launch for the projections g (w4a16_linear_batch), or the plain call."""
+        import int4_weight_only_02_amd as w4
+        if len(g) == 1:
+            self.launch(self.projs[g[0]], r)
+            return
+        w4.w4a16_linear_batch([self.projs[q]["copies"][r] for q in g], workspace=self.ws,
+                              outs=[self.projs[q]["Y"] for q in g])
+
     def step(self, r):
         if self.batched:
-            # every projection of the step in one launch (w4a16_linear_batch)
-            import int4_weight_only_02_amd as w4
-            w4.w4a16_linear_batch([p["copies"][r % self.R] for p in self.projs], workspace=self.ws,
-                                  outs=[p["Y"] for p in self.projs])
+            for g in self.groups:
+                self.launch_group(g, r % self.R)
             return
         for p in self.projs:
             self.launch(p, r % self.R)
@@ -157,8 +181,12 @@ class Workload:
         worst = 0.0
         ys = None
         if self.batched:
-            ys = w4.w4a16_linear_batch([p["copies"][0] for p in self.projs], out_dtype=torch.float32,
-                                       workspace=self.ws)
+            ys = [None] * len(self.projs)
+            for g in self.groups:
+                out = w4.w4a16_linear_batch([self.projs[q]["copies"][0] for q in g], out_dtype=torch.float32,
+                                            workspace=self.ws)
+                for q, y in zip(g, out):
+                    ys[q] = y
         for q, p in enumerate(self.projs):
             if self.lmhead:
                 continue
@@ -186,16 +214,18 @@ def time_events(wl, reps):
     import torch
     out = {}
     if wl.batched:
-        evs = []
-        for i in range(reps):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            wl.step(i)
-            e1.record()
-            evs.append((e0, e1))
-        torch.cuda.synchronize()
-        out["batch"] = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+        for g in wl.groups:
+            evs = []
+            for i in range(reps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                wl.launch_group(g, i % wl.R)
+                e1.record()
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            out["+".join(wl.projs[q]["label"] for q in g)] = float(np.median([a.elapsed_time(b) * 1e3
+                                                                              for a, b in evs]))
         return out
     for p in wl.projs:
         evs = []
@@ -288,7 +318,7 @@ def measure(name, dev, steps, warmup, lmhead=False, ev_reps=200, batched=False):
            "GBps": round(wl.bytes_per_step / wall / 1e9, 2),
            "hbm_frac": round(wl.bytes_per_step / wall / 1e9 / HBM_PEAK_GBS, 4),
            "TFLOPs": round(wl.flops_per_step / wall / 1e12, 3),
-           "launches_per_step": 1 if batched else len(wl.projs),
+           "launches_per_step": len(wl.groups) if batched else len(wl.projs),
            "batched": batched,
            "kernel_us_eager_median": {k: round(v, 3) for k, v in ev.items()},
            "sampled_max_err_over_rms": err}
@@ -396,7 +426,7 @@ def main():
         return
 
     names = [HEADLINE, "single_512", "verify_block_m16", "lmhead_verify_m16", "prefill_m8192",
-             "decode_gemv_m1+batch", "verify_block_m16+batch"]
+             "verify_block_m16+batch"]
     if args.only:
         names = [args.only]
     results = {}

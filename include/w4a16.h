@@ -96,8 +96,9 @@ int w4a16_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K, int gro
  *   Y        [M][N]    row-major, bf16 (W4A16_OUT_BF16) or fp32 (W4A16_OUT_F32)
  *   workspace          device scratch of at least
  *                      w4a16_workspace_bytes(W4A16_OP_LINEAR, M, N, K, group) bytes;
- *                      it must hold zeros before its first use (allocate it
- *                      zero-filled), and every call leaves it that way.
+ *                      its counter region must hold zeros before its first
+ *                      use (allocate it zero-filled); every call returns that
+ *                      region to zero.
  *                      May be NULL when that size is 0.
  * Shapes: M >= 0, N >= 0, N % 8 == 0, K >= group, K % group == 0, group == 128,
  *         M * N, N * K and M * K at most 2^31 - 256.
@@ -119,8 +120,10 @@ int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, con
  *             Y [M][N], and its N and K (the layouts of w4a16_linear)
  *   count     0 .. W4A16_MAX_BATCH
  *   M, group, y_dtype   shared by all entries
- *   workspace at least the largest w4a16_workspace_bytes(W4A16_OP_LINEAR, M, N_q, K_q)
- *             over the entries (0 when M <= 64); the rules of w4a16_linear
+ *   workspace at least the sum over the entries of
+ *             w4a16_workspace_bytes(W4A16_OP_LINEAR, M, N_q, K_q, group) (projections
+ *             that split K across workgroups keep their partial sums side by side);
+ *             the rules of w4a16_linear
  * Errors: as w4a16_linear, checked for every entry before anything is launched;
  * W4A16_ERR_SHAPE also for count outside 0 .. W4A16_MAX_BATCH.  Entries with N == 0
  * and calls with M == 0 do nothing.  Outputs must not alias each other or inputs.

@@ -178,7 +178,7 @@ def w4a16_linear_batch(problems, out_dtype=None, group=GROUP, outs=None, workspa
         Y = outs[q] if outs is not None else torch.empty((M, N), dtype=out_dtype, device=X.device)
         assert Y.shape == (M, N) and Y.dtype == out_dtype and Y.is_contiguous()
         arr[q] = Problem(X.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(), Y.data_ptr(), N, K)
-        need = max(need, w4a16_workspace_bytes(OP_LINEAR, M, N, K, group))
+        need += w4a16_workspace_bytes(OP_LINEAR, M, N, K, group)
         ys.append(Y)
     ws = _workspace(workspace, problems[0][0].device).get(need)
     st = lib().w4a16_linear_batch(ctypes.cast(arr, ctypes.c_void_p), len(problems), M, group, ydt, _ptr(ws), need,

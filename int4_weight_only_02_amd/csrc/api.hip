@@ -24,10 +24,14 @@ int check_dims(int M, int N, int K)
     return W4A16_OK;
 }
 
+// covers both the single-call plan and the plan the same projection gets inside a
+// batched launch, so that the sum over a batch's projections always suffices
 size_t linear_ws(int M, int N, int K)
 {
-    if (M <= kSkinnyMaxM)
-        return plan_skinny(M, N, K, 0).ws_bytes;
+    if (M <= kSkinnyMaxM) {
+        const size_t a = plan_skinny(M, N, K, 0).ws_bytes, b = plan_skinny_fixed(M, N, K).ws_bytes;
+        return a > b ? a : b;
+    }
     return plan_tiled(M, N, K).ws_bytes;
 }
 
@@ -204,7 +208,10 @@ int w4a16_linear_batch(const w4a16_problem *problems, int count, int M, int grou
     mp.count = c;
     if (c == 0)
         return W4A16_OK;
-    const hipError_t e = launch_skinny_multi(mp, M, (hipStream_t)stream);
+    const size_t scratch = skinny_multi_scratch(mp, M);
+    if (scratch > 0 && (!workspace || workspace_bytes < scratch))
+        return W4A16_ERR_WORKSPACE;
+    const hipError_t e = launch_skinny_multi(mp, M, workspace ? workspace_bytes : 0, (hipStream_t)stream);
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 

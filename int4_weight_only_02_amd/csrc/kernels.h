@@ -15,8 +15,7 @@ namespace w4a16 {
 // path can share one workspace.
 constexpr size_t kOffTicket = 0;          // u32: workgroups finished (lm_head)
 constexpr size_t kOffKeys = 256;          // u64[64]: per-row argmax keys (lm_head)
-constexpr size_t kOffCounters = 1024;     // u32[kMaxGrid]: split column-block arrivals
-constexpr int kMaxGrid = 1024;
+constexpr size_t kOffCounters = 1024;     // u32[]: arrivals of K-chunked tile groups (small M)
 constexpr size_t kZeroRegion = 8192;
 
 // ---------------------------------------------------------------- pack
@@ -45,9 +44,13 @@ struct SkinnyPlan {
     int items;     // mblocks * ntg
     int grid;      // workgroups
     int stream;    // 1: stream mode
-    int xlds;      // 1: X staged in LDS by the workgroup; 2: each wave stages its own slice
+    int xlds;      // 1: X staged in LDS by the workgroup; 2: each wave stages its own slice;
+                   // 3: chunked (X of one K chunk in LDS by DMA, chunks meet in the workspace)
+    int C, cg;     // xlds 3: K chunks per tile group, groups per chunk (a multiple of 4 if C > 1)
+    int tkt;       // xlds 3, C > 1: first arrival counter (u32 at kOffCounters) of this projection
+    size_t part_off; // xlds 3, C > 1: workspace offset of the fp32 partial sums [C][M][N]
     size_t lds_bytes;
-    size_t ws_bytes; // lm_head: the zero region (argmax keys, ticket); linear: 0
+    size_t ws_bytes; // lm_head: the zero region (argmax keys, ticket); linear: the partials (xlds 3) or 0
 };
 
 struct SkinnyArgs {
@@ -77,7 +80,10 @@ struct SkinnyMulti {
     SkinnyPlan plan[kMaxProblems];
 };
 SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit = 0);
-hipError_t launch_skinny_multi(SkinnyMulti &mp, int M, hipStream_t stream);
+// gives every chunked projection its own arrival counters and partial-sum region;
+// returns the workspace bytes the launch needs (0: none)
+size_t skinny_multi_scratch(SkinnyMulti &mp, int M);
+hipError_t launch_skinny_multi(SkinnyMulti &mp, int M, size_t ws_bytes, hipStream_t stream);
 
 // ---------------------------------------------------------------- tiled (large M)
 struct TiledPlan {

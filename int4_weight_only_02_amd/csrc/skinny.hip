@@ -50,7 +50,8 @@ constexpr int kB = 4;                  // groups per register batch
 constexpr int kCUs = 256;
 constexpr size_t kLdsBudget = 160 * 1024 - 4096;
 constexpr uint32_t kOob = 0xFFFFFF00u; // an offset past the end of every tensor
-constexpr int kSplitDirect = 0, kSplitLds = 1, kStream = 2, kSplitPriv = 3;
+constexpr int kSplitDirect = 0, kSplitLds = 1, kStream = 2, kSplitPriv = 3, kSplitChunk = 4;
+constexpr int kMaxTickets = (int)((kZeroRegion - kOffCounters) / 4); // arrival counters of chunked tiles
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m)
 {
@@ -270,6 +271,68 @@ __device__ __forceinline__ void compute_batch_x(const BatchX &b, f32x4_t &acc, i
     }
 }
 
+// 16 bytes per lane from global memory (offset voff of r) into LDS at dst + 16 * lane
+// (dst the same for the whole wave): LDS DMA, no registers involved
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned char *dst, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N): all but the N most recent vector memory loads of the wave have
+// completed (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt, lgkmcnt unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vm_below()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// vector memory loads per register batch (codes, scales, zero words)
+template <bool ALIGNED>
+constexpr int batch_loads() { return ALIGNED ? kB + 2 : 3 * kB; }
+
+// compute_batch for the chunked mode: the X fragments come from LDS in natural order
+// (as the DMA left them; permuted in registers) and the zero-point is folded by a
+// second MFMA chain on the column constant -(128 + z), as in compute_batch_x.
+// xlane points at the lane's X row in the first staged group (group gbase).
+template <int NR>
+__device__ __forceinline__ void compute_batch_lx(const Batch &b, f32x4_t &acc, const u32x4_t *xlane, int gs,
+                                                 int gend, int gbase, int Mb, int zsh, uint32_t mask, uint32_t bias)
+{
+    u32x4_t xf[2][4];
+    auto fetch = [&](int i, int buf) {
+        const int g = gs + i;
+        const int gl = (g < gend ? g : gend - 1) - gbase;
+        const u32x4_t *xg = xlane + gl * 16 * Mb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            xf[buf][j] = xg[j * Mb];
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+        const int cur = i & 1;
+        if (i + 1 < kB)
+            fetch(i + 1, cur ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int g = gs + i;
+        const uint32_t zb = (((b.z[i] >> zsh) & 15u) | 0xC300u) * 0x00010001u;
+        const bf16x8_t zfrag = __builtin_bit_cast(bf16x8_t, u32x4_t{zb, zb, zb, zb});
+        f32x4_t pq = {0.f, 0.f, 0.f, 0.f}, pz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, x_permute8(xf[cur][j]));
+            const uint32_t wj = j == 0 ? b.w[i].x : j == 1 ? b.w[i].y : j == 2 ? b.w[i].z : b.w[i].w;
+            pq = mfma16x16x32(xa, codes_to_frag_r(wj, mask, bias), pq);
+            pz = mfma16x16x32(xa, zfrag, pz);
+        }
+        const float s = g < gend ? f16_bits_to_f32((uint16_t)b.s[i]) : 0.f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+            acc[r] = fmaf(s, pq[r] + pz[r], acc[r]);
+    }
+}
+
 // Staging of X[m0 .. m0+Mb)[all groups] into LDS, in fragment order.  LDS slot i
 // holds chunk kc = i / Mb (group kc/16, c = kc%16) of row m = i % Mb, so consecutive
 // threads write consecutive 16-byte slots (no bank conflicts); the quotient comes from
@@ -385,7 +448,12 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
     u32x4_t *xs = (u32x4_t *)xbase;
     float *part = (float *)(xbase + (size_t)nslot * 16);
     float *S = part + nslot;
-    float *red = (float *)(smem + (MODE == kSplitPriv ? (size_t)nwaves * region : region));
+    // kSplitChunk: the raw X of the item's K chunk (DMA slots, whole 1 KB rounds), then
+    // the K-slice partial sums
+    const size_t xchunk = (size_t)((p.cg * 16 * mrows + 63) & ~63) * 16;
+    float *red = (float *)(smem + (MODE == kSplitPriv    ? (size_t)nwaves * region
+                                   : MODE == kSplitChunk ? xchunk
+                                                         : region));
     uint32_t *ticket = (uint32_t *)(a.ws + kOffTicket);
     unsigned long long *keys = (unsigned long long *)(a.ws + kOffKeys);
 
@@ -547,7 +615,10 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
         // ---- split mode: item = (m-block, group of tw tiles); wave = (tile slot, K slice)
         const int tslot = wave % p.tw, ks = wave / p.tw;
         for (int it = first; it < p.items; it += stride) {
-            const int mb = it / p.ntg, tg = it - mb * p.ntg;
+            // kSplitChunk: item = (tile group, K chunk), the chunk index fastest
+            const int chunk = MODE == kSplitChunk ? it % p.C : 0;
+            const int rest = MODE == kSplitChunk ? it / p.C : it;
+            const int mb = rest / p.ntg, tg = rest - mb * p.ntg;
             const int m0 = mb * 16;
             const int Mb = M - m0 < 16 ? M - m0 : 16;
             const int xrow = col < Mb ? col : Mb - 1;
@@ -597,6 +668,53 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
                         compute_batch<NR>(b2, acc, xlane, sl, g + 2 * kB, g1, Mb, L.zsh, kmask, kbias);
                     __builtin_amdgcn_sched_barrier(0);
                     load_batch<ALIGNED>(b2, rw, rs, rz, L, g + 5 * kB, g1);
+                }
+            } else if constexpr (MODE == kSplitChunk) {
+                // X of the chunk's groups [ga, gb) arrives in LDS by DMA, all of it in
+                // flight together with the first three weight batches of each wave; the
+                // waves' K slices of the chunk are [s0, s1)
+                const int ga = chunk * p.cg;
+                const int gb = G < ga + p.cg ? G : ga + p.cg;
+                const int s0 = ga + ks * p.per;
+                const int s1 = gb < s0 + p.per ? gb : s0 + p.per; // s1 <= s0: empty slice
+                if (it != first)
+                    __syncthreads(); // the previous item's reads of X are done
+                // the previous item's last (unused) batch loads have landed: nothing older
+                // than the DMA is pending, so the batch registers need no wait below
+                wait_vm_below<0>();
+                const int total = (gb - ga) * 16 * Mb;
+                const uint32_t xb = ((uint32_t)m0 * (uint32_t)K + (uint32_t)ga * kGroup) * 2u;
+                const unsigned long long magic = 0xFFFFFFFFull / (uint32_t)Mb + 1ull; // ceil(2^32 / Mb)
+                for (int i = wave; i * 64 < total; i += nwaves) {
+                    // slot q = (group, chunk c) * Mb + row, as in the register staging
+                    const int q = i * 64 + lane;
+                    const int kc = (int)(((unsigned long long)(uint32_t)q * magic) >> 32);
+                    const int m = q - kc * Mb;
+                    dma16(rx, smem + (size_t)i * 1024, q < total ? xb + (uint32_t)(m * K + kc * 8) * 2u : kOob);
+                }
+                asm volatile("" ::: "memory"); // the weight loads stay behind the DMA
+                Batch b0, b1, b2;
+                load_batch<ALIGNED>(b0, rw, rs, rz, L, s0, s1);
+                load_batch<ALIGNED>(b1, rw, rs, rz, L, s0 + kB, s1);
+                load_batch<ALIGNED>(b2, rw, rs, rz, L, s0 + 2 * kB, s1);
+                wait_vm_below<3 * batch_loads<ALIGNED>()>(); // this wave's DMA has landed
+                __syncthreads();                              // and every other wave's
+                const u32x4_t *xlane = xs + (4 * h) * Mb + xrow;
+                for (int g = s0; g < s1; g += 3 * kB) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute_batch_lx<NR>(b0, acc, xlane, g, s1, ga, Mb, L.zsh, kmask, kbias);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_batch<ALIGNED>(b0, rw, rs, rz, L, g + 3 * kB, s1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (g + kB < s1)
+                        compute_batch_lx<NR>(b1, acc, xlane, g + kB, s1, ga, Mb, L.zsh, kmask, kbias);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_batch<ALIGNED>(b1, rw, rs, rz, L, g + 4 * kB, s1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (g + 2 * kB < s1)
+                        compute_batch_lx<NR>(b2, acc, xlane, g + 2 * kB, s1, ga, Mb, L.zsh, kmask, kbias);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_batch<ALIGNED>(b2, rw, rs, rz, L, g + 5 * kB, s1);
                 }
             } else if constexpr (MODE == kSplitLds) {
                 // slices of p.per groups (a multiple of kB): batches stay 4-aligned
@@ -675,6 +793,47 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
                 }
                 __syncthreads();
             }
+            if (MODE == kSplitChunk && p.C > 1) {
+                // K chunks of one tile group meet in the workspace: each workgroup stores
+                // its fp32 partial sums [chunk][row][column] (device-coherent stores), then
+                // takes an arrival ticket; the last to arrive adds the C partials in chunk
+                // order (its own from registers) and finishes the tiles, so the result
+                // does not depend on the arrival order
+                float *pbuf = (float *)(a.ws + p.part_off);
+                uint32_t *tk = (uint32_t *)(a.ws + kOffCounters) + p.tkt + rest;
+                const int n = tile * 16 + col;
+                if (ks == 0 && live && n < N) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * h + r < Mb)
+                            __hip_atomic_store(pbuf + ((size_t)chunk * M + m0 + 4 * h + r) * N + n, acc[r],
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                wait_device_writes();
+                __syncthreads();
+                if (tid == 0) {
+                    const uint32_t old = __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    s_flag = old == (uint32_t)(p.C - 1) ? 1 : 0;
+                }
+                __syncthreads();
+                if (!s_flag)
+                    continue; // uniform over the workgroup
+                if (ks == 0 && live && n < N) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (4 * h + r >= Mb)
+                            continue;
+                        float t = 0.f;
+                        for (int cc = 0; cc < p.C; ++cc)
+                            t += cc == chunk ? acc[r]
+                                             : __hip_atomic_load(pbuf + ((size_t)cc * M + m0 + 4 * h + r) * N + n,
+                                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        acc[r] = t;
+                    }
+                }
+                if (tid == 0)
+                    __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
             if (ks == 0 && live)
                 finish_tile(acc, m0, Mb, tile * 16 + col);
         }
@@ -737,7 +896,9 @@ __global__ __launch_bounds__(512) void skinny_multi_kernel(SkinnyMulti mp)
     const SkinnyArgs a = mp.args[q];
     const SkinnyPlan p = mp.plan[q];
     const int it = b - mp.begin[q];
-    if (p.xlds == 2)
+    if (p.xlds == 3)
+        skinny_body<NR, kSplitChunk, ALIGNED>(a, p, it, 1 << 30, smem, kred, s_flag);
+    else if (p.xlds == 2)
         skinny_body<NR, kSplitPriv, ALIGNED>(a, p, it, 1 << 30, smem, kred, s_flag);
     else if (p.xlds == 1)
         skinny_body<NR, kSplitLds, ALIGNED>(a, p, it, 1 << 30, smem, kred, s_flag);
@@ -755,6 +916,10 @@ size_t lds_per_group(int M)
 size_t lds_for(const SkinnyPlan &p, int M)
 {
     const size_t red = p.sk > 1 ? (size_t)p.tw * p.sk * 1024 : 0;
+    if (p.xlds == 3) {
+        const int mrows = M < 16 ? M : 16;
+        return (size_t)((p.cg * 16 * mrows + 63) & ~63) * 16 + red;
+    }
     const size_t xs = (size_t)p.chunk * lds_per_group(M);
     return (p.xlds == 2 ? xs * p.tw * p.sk : xs) + red;
 }
@@ -776,6 +941,95 @@ bool split_override(int *tw, int *sk)
 }
 
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+// Tuning override for the chunked mode, read once from W4A16_SKINNY_CHUNK="tw,cg"
+// (tiles per workgroup, groups per K chunk; cg 0 = all of K).  Unset: the heuristic.
+bool chunk_override(int *tw, int *cg)
+{
+    static int state = -1, otw = 0, ocg = 0;
+    if (state < 0) {
+        state = 0;
+        const char *e = getenv("W4A16_SKINNY_CHUNK");
+        if (e && sscanf(e, "%d,%d", &otw, &ocg) == 2 && otw >= 1 && otw <= kMaxWaves && ocg >= 0)
+            state = 1;
+    }
+    *tw = otw;
+    *cg = ocg;
+    return state == 1;
+}
+
+// Chunked split mode: tw tiles per workgroup share X, whose K range is cut into C
+// chunks of cg groups (one workgroup per tile group and chunk).  Fills p.tw, sk, per,
+// cg, C, ntg, items, grid; with fixed, sk = kMaxWaves / tw (slices past the chunk stay
+// empty).  Returns false when the chunk does not fit in LDS or there are too many
+// arrival counters.
+bool plan_chunk(SkinnyPlan &p, int M, size_t lds_limit, int tw, int cg, bool fixed)
+{
+    const int mrows = M < 16 ? M : 16;
+    const int G = p.G;
+    const int ntg = (p.nt + tw - 1) / tw;
+    if (cg <= 0 || cg >= G)
+        cg = G;
+    else
+        cg = round_up(cg, kB);
+    if (cg >= G)
+        cg = G;
+    const int C = (G + cg - 1) / cg;
+    // a launch of several projections gives each its own share of the counters
+    if (C > 1 && (long long)p.mblocks * ntg > (fixed ? kMaxTickets / kMaxProblems : kMaxTickets))
+        return false;
+    // K slices of the chunk over the remaining waves: whole batches each
+    int sk = kMaxWaves / tw;
+    if (!fixed) {
+        const int batches = (cg + kB - 1) / kB;
+        sk = sk > batches ? batches : sk;
+        sk = sk < 1 ? 1 : sk;
+    }
+    p.per = round_up((cg + sk - 1) / sk, kB);
+    if (!fixed)
+        sk = (cg + p.per - 1) / p.per;
+    p.tw = tw;
+    p.sk = sk;
+    p.cg = cg;
+    p.C = C;
+    p.ntg = ntg;
+    p.items = p.mblocks * ntg * C;
+    p.grid = p.items;
+    p.xlds = 3;
+    p.chunk = 0;
+    p.tkt = 0;
+    p.part_off = kZeroRegion;
+    return lds_for(p, M) <= lds_limit && mrows > 0;
+}
+
+// The chunked mode's choice for one m-block of 5..16 rows (measured on MI355X at
+// M = 5, 8, 16 and K = 2560 .. 9728): when every tile can have its own workgroup
+// (at most one tile per CU), one tile per workgroup with X of all of K in LDS, or,
+// when that does not fit, two tiles per workgroup and chunks of 32 groups.  With
+// more tiles than CUs the workgroup-shared staging of the other split modes wins.
+bool choose_chunk(SkinnyPlan &p, int M, size_t lds_limit, bool fixed)
+{
+    int tw = 0, cg = 0;
+    SkinnyPlan c = p;
+    if (chunk_override(&tw, &cg)) {
+        if (!plan_chunk(c, M, lds_limit, tw, cg, fixed))
+            return false;
+        p = c;
+        return true;
+    }
+    if (p.mblocks != 1 || M <= 4 || p.nt > kCUs)
+        return false;
+    if (plan_chunk(c, M, lds_limit, 1, 0, fixed)) {
+        p = c;
+        return true;
+    }
+    c = p;
+    if (plan_chunk(c, M, lds_limit, 2, 32, fixed)) {
+        p = c;
+        return true;
+    }
+    return false;
+}
 
 } // namespace
 
@@ -836,10 +1090,15 @@ SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit)
         p.ntg = (p.nt + tw - 1) / tw;
         p.items = p.mblocks * p.ntg;
         p.grid = p.items;
+        if (!lmhead)
+            choose_chunk(p, M, lds_limit, false);
     }
     p.waves = p.tw * p.sk;
     p.lds_bytes = lds_for(p, M);
-    p.ws_bytes = lmhead ? kZeroRegion : 0; // only lm_head uses scratch (argmax keys, ticket)
+    // lm_head: the zero region (argmax keys, ticket); chunked: counters and partial sums
+    p.ws_bytes = lmhead ? kZeroRegion
+                 : (p.xlds == 3 && p.C > 1) ? kZeroRegion + (size_t)p.C * M * N * 4
+                                             : 0;
     return p;
 }
 
@@ -872,9 +1131,10 @@ SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit)
     p.ntg = (p.nt + tw - 1) / tw;
     p.items = p.mblocks * p.ntg;
     p.grid = p.items;
+    choose_chunk(p, M, lds_limit, true);
     p.waves = kMaxWaves;
     p.lds_bytes = lds_for(p, M);
-    p.ws_bytes = 0;
+    p.ws_bytes = (p.xlds == 3 && p.C > 1) ? kZeroRegion + (size_t)p.C * M * N * 4 : 0;
     return p;
 }
 
@@ -944,6 +1204,8 @@ hipError_t device_lds_limit(size_t *limit)
             allow_lds<kStream, true>(lds_limit);
             allow_lds<kSplitPriv, false>(lds_limit);
             allow_lds<kSplitPriv, true>(lds_limit);
+            allow_lds<kSplitChunk, false>(lds_limit);
+            allow_lds<kSplitChunk, true>(lds_limit);
             allow_lds_multi<false>(lds_limit);
             allow_lds_multi<true>(lds_limit);
         }
@@ -954,7 +1216,23 @@ hipError_t device_lds_limit(size_t *limit)
 
 } // namespace
 
-hipError_t launch_skinny_multi(SkinnyMulti &mp, int M, hipStream_t stream)
+size_t skinny_multi_scratch(SkinnyMulti &mp, int M)
+{
+    int tkt = 0;
+    size_t off = kZeroRegion;
+    for (int q = 0; q < mp.count; ++q) {
+        SkinnyPlan &p = mp.plan[q];
+        if (p.xlds != 3 || p.C <= 1)
+            continue;
+        p.tkt = tkt;
+        p.part_off = off;
+        tkt += p.mblocks * p.ntg;
+        off += (size_t)p.C * M * mp.args[q].N * 4;
+    }
+    return off == kZeroRegion ? 0 : off;
+}
+
+hipError_t launch_skinny_multi(SkinnyMulti &mp, int M, size_t ws_bytes, hipStream_t stream)
 {
     size_t lds_limit = 0;
     hipError_t e = device_lds_limit(&lds_limit);
@@ -963,9 +1241,12 @@ hipError_t launch_skinny_multi(SkinnyMulti &mp, int M, hipStream_t stream)
     size_t lds = 0;
     bool aligned = true;
     int grid = 0;
+    bool replanned = false;
     for (int q = 0; q < mp.count; ++q) {
-        if (mp.plan[q].lds_bytes > lds_limit)
+        if (mp.plan[q].lds_bytes > lds_limit) {
             mp.plan[q] = plan_skinny_fixed(M, mp.args[q].N, mp.args[q].K, lds_limit);
+            replanned = true;
+        }
         if (mp.plan[q].lds_bytes > lds_limit)
             return hipErrorInvalidValue;
         lds = mp.plan[q].lds_bytes > lds ? mp.plan[q].lds_bytes : lds;
@@ -974,6 +1255,8 @@ hipError_t launch_skinny_multi(SkinnyMulti &mp, int M, hipStream_t stream)
         grid += mp.plan[q].grid;
     }
     mp.begin[mp.count] = grid;
+    if (replanned && skinny_multi_scratch(mp, M) > ws_bytes)
+        return hipErrorInvalidValue;
     if (grid == 0)
         return hipSuccess;
     const dim3 block(64 * kMaxWaves), g(grid);
@@ -1011,6 +1294,8 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, hipStream_
     const bool aligned = (a.G % 4) == 0 && (p.per % 4) == 0;
     if (p.stream)
         launch_mode<kStream>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
+    else if (p.xlds == 3)
+        launch_mode<kSplitChunk>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
     else if (p.xlds == 2)
         launch_mode<kSplitPriv>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
     else if (p.xlds == 1)

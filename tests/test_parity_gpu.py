@@ -262,15 +262,25 @@ def test_shared_workspace_across_paths_and_shapes(dev):
         d = synth.linear_inputs(500 + i, M, N, K)
         t, qw, qz, oqw, oqz = _prep(d, dev)
         fresh = w4.w4a16_linear(t["X"], qw, t["scales"], qz, out_dtype=torch.float32, workspace=w4.Workspace(dev))
-        cases.append((t, qw, qz, fresh))
+        fresh_lm = None
+        if M <= 64:
+            draft = torch.zeros(M, dtype=torch.int32, device=dev)
+            fresh_lm = w4.w4a16_lmhead_verify(t["X"], qw, t["scales"], qz, draft, return_logits=True,
+                                              workspace=w4.Workspace(dev))[2]
+        cases.append((t, qw, qz, fresh, fresh_lm))
     for rep in range(2):
-        for t, qw, qz, fresh in cases:
+        for t, qw, qz, fresh, fresh_lm in cases:
             Y = w4.w4a16_linear(t["X"], qw, t["scales"], qz, out_dtype=torch.float32, workspace=ws)
             assert torch.equal(Y, fresh)
-            if t["X"].shape[0] <= 64:
+            if fresh_lm is not None:
                 draft = torch.zeros(t["X"].shape[0], dtype=torch.int32, device=dev)
                 am, acc, logits = w4.w4a16_lmhead_verify(t["X"], qw, t["scales"], qz, draft,
                                                          return_logits=True, workspace=ws)
-                assert torch.equal(logits, fresh)
+                assert torch.equal(logits, fresh_lm)
+                # the lm_head logits are the layer's output (its own launch shape, so only
+                # to the accuracy bound when the linear call takes another path)
+                ref = fresh.double()
+                tol = 1e-2 * float(ref.pow(2).mean().sqrt())
+                assert float((logits.double() - ref).abs().max()) <= tol
                 # ties aside, the fused argmax equals the first maximum of the logits
-                assert torch.equal(am.long(), fresh.argmax(dim=1))
+                assert torch.equal(am.long(), fresh_lm.argmax(dim=1))
