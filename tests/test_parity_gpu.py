@@ -56,7 +56,10 @@ def test_pack_bit_exact(dev, N, K):
 
 SMALL = [(1, 8, 128), (1, 512, 512), (2, 136, 384), (3, 1032, 1280), (5, 264, 2560), (16, 1024, 2560),
          (16, 264, 9728), (17, 264, 640), (33, 520, 1024), (64, 136, 256), (65, 136, 384),
-         (128, 256, 256), (200, 392, 1280), (257, 1032, 640)]
+         (128, 256, 256), (200, 392, 1280), (257, 1032, 640),
+         # K chunked across workgroups: 41 groups (not a multiple of 4) for 7 rows in one
+         # chunk; 45 groups in two chunks; three chunks over 161 tiles (ragged last tile)
+         (7, 520, 5248), (16, 264, 5760), (12, 2568, 9728)]
 
 
 @pytest.mark.parametrize("M,N,K", SMALL)
@@ -101,7 +104,8 @@ def _dyadic(seed, M, N, K):
 
 
 DYADIC = [(1, 9728, 2560), (1, 2560, 9728), (16, 4096, 2560), (16, 2560, 9728), (16, 1000, 640),
-          (37, 520, 1280), (300, 1032, 2560), (8192, 9728, 2560), (8192, 2560, 9728)]
+          (16, 264, 9728), (7, 520, 5248), (37, 520, 1280), (300, 1032, 2560), (8192, 9728, 2560),
+          (8192, 2560, 9728)]
 
 
 @pytest.mark.parametrize("M,N,K", DYADIC)
