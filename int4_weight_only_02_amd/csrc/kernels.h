@@ -46,6 +46,7 @@ struct SkinnyPlan {
     int stream;    // 1: stream mode
     int xlds;      // 1: X staged in LDS by the workgroup; 2: each wave stages its own slice;
                    // 3: chunked (X of one K chunk in LDS by DMA, chunks meet in the workspace)
+    int xdma;      // xlds 2: X arrives by LDS DMA and the zero-point is folded by MFMA
     int C, cg;     // xlds 3: K chunks per tile group, groups per chunk (a multiple of 4 if C > 1)
     int tkt;       // xlds 3, C > 1: first arrival counter (u32 at kOffCounters) of this projection
     size_t part_off; // xlds 3, C > 1: workspace offset of the fp32 partial sums [C][M][N]

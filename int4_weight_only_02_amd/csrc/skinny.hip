@@ -50,7 +50,7 @@ constexpr int kB = 4;                  // groups per register batch
 constexpr int kCUs = 256;
 constexpr size_t kLdsBudget = 160 * 1024 - 4096;
 constexpr uint32_t kOob = 0xFFFFFF00u; // an offset past the end of every tensor
-constexpr int kSplitDirect = 0, kSplitLds = 1, kStream = 2, kSplitPriv = 3, kSplitChunk = 4;
+constexpr int kSplitDirect = 0, kSplitLds = 1, kStream = 2, kSplitPriv = 3, kSplitChunk = 4, kSplitPrivDma = 5;
 constexpr int kMaxTickets = (int)((kZeroRegion - kOffCounters) / 4); // arrival counters of chunked tiles
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m)
@@ -133,11 +133,16 @@ __device__ __forceinline__ void load_params(uint32_t (&sc)[kB], uint32_t (&zw)[k
         zw[2] = zv.z;
         zw[3] = zv.w;
     } else {
+        // the four zero words are consecutive (4-byte aligned): one 16-byte load, each
+        // word range-checked on its own
+        const u32x4_t zv = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rz, zo, 0, 0));
 #pragma unroll
-        for (int i = 0; i < kB; ++i) {
+        for (int i = 0; i < kB; ++i)
             sc[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, so + 2u * i, 0, 0);
-            zw[i] = __builtin_amdgcn_raw_buffer_load_b32(rz, zo + 4u * i, 0, 0);
-        }
+        zw[0] = zv.x;
+        zw[1] = zv.y;
+        zw[2] = zv.z;
+        zw[3] = zv.w;
     }
 }
 
@@ -287,9 +292,10 @@ __device__ __forceinline__ void wait_vm_below()
     __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-// vector memory loads per register batch (codes, scales, zero words)
+// vector memory loads per register batch (codes, scales, zero words), as written in
+// load_batch / load_params: the waits for the X DMA below count on this
 template <bool ALIGNED>
-constexpr int batch_loads() { return ALIGNED ? kB + 2 : 3 * kB; }
+constexpr int batch_loads() { return ALIGNED ? kB + 2 : 2 * kB + 1; }
 
 // compute_batch for the chunked mode: the X fragments come from LDS in natural order
 // (as the DMA left them; permuted in registers) and the zero-point is folded by a
@@ -423,7 +429,7 @@ __device__ __forceinline__ void group_sums(const float *part, float *S, int Mb, 
 }
 
 // The work of one workgroup on one projection.  MODE: kSplitDirect, kSplitLds,
-// kSplitPriv or kStream (see the plan).  The workgroup takes items first, first +
+// kSplitPriv, kSplitPrivDma, kSplitChunk or kStream (see the plan).  The workgroup takes items first, first +
 // stride, ... (split mode) or tile groups first, first + stride, ... (stream mode).
 template <int NR, int MODE, bool ALIGNED>
 __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPlan &p, int first, int stride,
@@ -444,14 +450,15 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
     // [wave][64 lanes][4]
     const int nslot = p.chunk * 16 * mrows;
     const size_t region = (size_t)nslot * 20 + (size_t)p.chunk * 64;
-    unsigned char *xbase = MODE == kSplitPriv ? smem + (size_t)wave * region : smem;
+    constexpr bool PRIV = MODE == kSplitPriv || MODE == kSplitPrivDma;
+    unsigned char *xbase = PRIV ? smem + (size_t)wave * region : smem;
     u32x4_t *xs = (u32x4_t *)xbase;
     float *part = (float *)(xbase + (size_t)nslot * 16);
     float *S = part + nslot;
     // kSplitChunk: the raw X of the item's K chunk (DMA slots, whole 1 KB rounds), then
     // the K-slice partial sums
     const size_t xchunk = (size_t)((p.cg * 16 * mrows + 63) & ~63) * 16;
-    float *red = (float *)(smem + (MODE == kSplitPriv    ? (size_t)nwaves * region
+    float *red = (float *)(smem + (PRIV                  ? (size_t)nwaves * region
                                    : MODE == kSplitChunk ? xchunk
                                                          : region));
     uint32_t *ticket = (uint32_t *)(a.ws + kOffTicket);
@@ -631,43 +638,88 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
                 cur_mb = mb;
             }
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (MODE == kSplitPriv) {
+            if constexpr (PRIV) {
                 // each wave stages only its own K slice of X (few rows), in its own LDS
                 // region: the loads, the commit, the row sums and the compute of one wave
                 // need no workgroup barrier (LDS operations of a wave complete in order)
                 const int g0 = ks * p.per;
                 const int g1 = G < g0 + p.per ? G : g0 + p.per;
                 const int ng = g1 > g0 ? g1 - g0 : 0; // slices past K are empty
-                XStage st = x_stage(m0, Mb);
-                st.base += (uint32_t)(g0 < G ? g0 * kGroup : 0) * 2u;
-                st.total = Mb * ng * 16;
-                XRound xr;
-                stage_issue(xr, st, 0, lane, 64);
-                Batch b0, b1, b2;
-                load_batch<ALIGNED>(b0, rw, rs, rz, L, g0, g1);
-                load_batch<ALIGNED>(b1, rw, rs, rz, L, g0 + kB, g1);
-                load_batch<ALIGNED>(b2, rw, rs, rz, L, g0 + 2 * kB, g1);
-                stage_commit(xr, st, xs, part, 0, lane, 64);
-                stage_rest(st, xs, part, lane, 64);
-                group_sums(part, S, Mb, ng, lane, 64);
-                // compute_batch indexes by absolute group: shift the bases by g0
-                const u32x4_t *xlane = xs + (4 * h) * Mb + xrow - (size_t)g0 * 16 * Mb;
-                const float *sl = S + 4 * h - (size_t)g0 * 16;
-                for (int g = g0; g < g1; g += 3 * kB) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    compute_batch<NR>(b0, acc, xlane, sl, g, g1, Mb, L.zsh, kmask, kbias);
-                    __builtin_amdgcn_sched_barrier(0);
-                    load_batch<ALIGNED>(b0, rw, rs, rz, L, g + 3 * kB, g1);
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (g + kB < g1)
-                        compute_batch<NR>(b1, acc, xlane, sl, g + kB, g1, Mb, L.zsh, kmask, kbias);
-                    __builtin_amdgcn_sched_barrier(0);
-                    load_batch<ALIGNED>(b1, rw, rs, rz, L, g + 4 * kB, g1);
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (g + 2 * kB < g1)
-                        compute_batch<NR>(b2, acc, xlane, sl, g + 2 * kB, g1, Mb, L.zsh, kmask, kbias);
-                    __builtin_amdgcn_sched_barrier(0);
-                    load_batch<ALIGNED>(b2, rw, rs, rz, L, g + 5 * kB, g1);
+                if constexpr (MODE == kSplitPrivDma) {
+                    // X by LDS DMA and the zero-point folded by MFMA (no row sums): the
+                    // shorter chain wins for 2..4 rows and for slices of one batch; one row
+                    // over many groups keeps the register staging and the row-sum fold,
+                    // which leaves the matrix cores half the work in the compute tail.
+                    // The previous item's LDS reads and loads are done before the region and
+                    // the batch registers are reused.
+                    wait_vm_below<0>();
+                    __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
+                    const int total = ng * 16 * Mb;
+                    const uint32_t xb = ((uint32_t)m0 * (uint32_t)K + (uint32_t)(g0 < G ? g0 : 0) * kGroup) * 2u;
+                    const unsigned long long magic = 0xFFFFFFFFull / (uint32_t)Mb + 1ull; // ceil(2^32 / Mb)
+                    for (int i = 0; i * 64 < total; ++i) {
+                        // slot q = (group, chunk c) * Mb + row, as in the register staging
+                        const int q = i * 64 + lane;
+                        const int kc = (int)(((unsigned long long)(uint32_t)q * magic) >> 32);
+                        const int m = q - kc * Mb;
+                        dma16(rx, xbase + (size_t)i * 1024, q < total ? xb + (uint32_t)(m * K + kc * 8) * 2u : kOob);
+                    }
+                    asm volatile("" ::: "memory"); // the weight loads stay behind the DMA
+                    Batch b0, b1, b2;
+                    load_batch<ALIGNED>(b0, rw, rs, rz, L, g0, g1);
+                    load_batch<ALIGNED>(b1, rw, rs, rz, L, g0 + kB, g1);
+                    load_batch<ALIGNED>(b2, rw, rs, rz, L, g0 + 2 * kB, g1);
+                    asm volatile("" ::: "memory"); // ... and ahead of the wait
+                    wait_vm_below<3 * batch_loads<ALIGNED>()>(); // this wave's X has landed
+                    const u32x4_t *xlane = xs + (4 * h) * Mb + xrow;
+                    for (int g = g0; g < g1; g += 3 * kB) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        compute_batch_lx<NR>(b0, acc, xlane, g, g1, g0, Mb, L.zsh, kmask, kbias);
+                        __builtin_amdgcn_sched_barrier(0);
+                        load_batch<ALIGNED>(b0, rw, rs, rz, L, g + 3 * kB, g1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (g + kB < g1)
+                            compute_batch_lx<NR>(b1, acc, xlane, g + kB, g1, g0, Mb, L.zsh, kmask, kbias);
+                        __builtin_amdgcn_sched_barrier(0);
+                        load_batch<ALIGNED>(b1, rw, rs, rz, L, g + 4 * kB, g1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (g + 2 * kB < g1)
+                            compute_batch_lx<NR>(b2, acc, xlane, g + 2 * kB, g1, g0, Mb, L.zsh, kmask, kbias);
+                        __builtin_amdgcn_sched_barrier(0);
+                        load_batch<ALIGNED>(b2, rw, rs, rz, L, g + 5 * kB, g1);
+                    }
+                } else {
+                    XStage st = x_stage(m0, Mb);
+                    st.base += (uint32_t)(g0 < G ? g0 * kGroup : 0) * 2u;
+                    st.total = Mb * ng * 16;
+                    XRound xr;
+                    stage_issue(xr, st, 0, lane, 64);
+                    Batch b0, b1, b2;
+                    load_batch<ALIGNED>(b0, rw, rs, rz, L, g0, g1);
+                    load_batch<ALIGNED>(b1, rw, rs, rz, L, g0 + kB, g1);
+                    load_batch<ALIGNED>(b2, rw, rs, rz, L, g0 + 2 * kB, g1);
+                    stage_commit(xr, st, xs, part, 0, lane, 64);
+                    stage_rest(st, xs, part, lane, 64);
+                    group_sums(part, S, Mb, ng, lane, 64);
+                    // compute_batch indexes by absolute group: shift the bases by g0
+                    const u32x4_t *xlane = xs + (4 * h) * Mb + xrow - (size_t)g0 * 16 * Mb;
+                    const float *sl = S + 4 * h - (size_t)g0 * 16;
+                    for (int g = g0; g < g1; g += 3 * kB) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        compute_batch<NR>(b0, acc, xlane, sl, g, g1, Mb, L.zsh, kmask, kbias);
+                        __builtin_amdgcn_sched_barrier(0);
+                        load_batch<ALIGNED>(b0, rw, rs, rz, L, g + 3 * kB, g1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (g + kB < g1)
+                            compute_batch<NR>(b1, acc, xlane, sl, g + kB, g1, Mb, L.zsh, kmask, kbias);
+                        __builtin_amdgcn_sched_barrier(0);
+                        load_batch<ALIGNED>(b1, rw, rs, rz, L, g + 4 * kB, g1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (g + 2 * kB < g1)
+                            compute_batch<NR>(b2, acc, xlane, sl, g + 2 * kB, g1, Mb, L.zsh, kmask, kbias);
+                        __builtin_amdgcn_sched_barrier(0);
+                        load_batch<ALIGNED>(b2, rw, rs, rz, L, g + 5 * kB, g1);
+                    }
                 }
             } else if constexpr (MODE == kSplitChunk) {
                 // X of the chunk's groups [ga, gb) arrives in LDS by DMA, all of it in
@@ -697,6 +749,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
                 load_batch<ALIGNED>(b0, rw, rs, rz, L, s0, s1);
                 load_batch<ALIGNED>(b1, rw, rs, rz, L, s0 + kB, s1);
                 load_batch<ALIGNED>(b2, rw, rs, rz, L, s0 + 2 * kB, s1);
+                asm volatile("" ::: "memory"); // ... and ahead of the wait
                 wait_vm_below<3 * batch_loads<ALIGNED>()>(); // this wave's DMA has landed
                 __syncthreads();                              // and every other wave's
                 const u32x4_t *xlane = xs + (4 * h) * Mb + xrow;
@@ -898,6 +951,8 @@ __global__ __launch_bounds__(512) void skinny_multi_kernel(SkinnyMulti mp)
     const int it = b - mp.begin[q];
     if (p.xlds == 3)
         skinny_body<NR, kSplitChunk, ALIGNED>(a, p, it, 1 << 30, smem, kred, s_flag);
+    else if (p.xlds == 2 && p.xdma)
+        skinny_body<NR, kSplitPrivDma, ALIGNED>(a, p, it, 1 << 30, smem, kred, s_flag);
     else if (p.xlds == 2)
         skinny_body<NR, kSplitPriv, ALIGNED>(a, p, it, 1 << 30, smem, kred, s_flag);
     else if (p.xlds == 1)
@@ -1085,6 +1140,7 @@ SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit)
         const bool fits = (size_t)p.G * per_group + red <= lds_limit;
         p.xlds = priv ? 2 : (fits && (mrows <= 4 || tw >= 2)) ? 1 : 0;
         p.chunk = p.xlds == 2 ? p.per : p.xlds == 1 ? p.G : 0;
+        p.xdma = priv && (M >= 2 || p.per <= kB); // measured on MI355X at M = 1..4
         p.tw = tw;
         p.sk = sk;
         p.ntg = (p.nt + tw - 1) / tw;
@@ -1128,6 +1184,7 @@ SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit)
     const bool fits = (size_t)p.G * per_group + red <= lds_limit;
     p.xlds = priv ? 2 : (fits && (mrows <= 4 || tw >= 2)) ? 1 : 0;
     p.chunk = p.xlds == 2 ? p.per : p.xlds == 1 ? p.G : 0;
+    p.xdma = priv && (M >= 2 || p.per <= kB);
     p.ntg = (p.nt + tw - 1) / tw;
     p.items = p.mblocks * p.ntg;
     p.grid = p.items;
@@ -1204,6 +1261,8 @@ hipError_t device_lds_limit(size_t *limit)
             allow_lds<kStream, true>(lds_limit);
             allow_lds<kSplitPriv, false>(lds_limit);
             allow_lds<kSplitPriv, true>(lds_limit);
+            allow_lds<kSplitPrivDma, false>(lds_limit);
+            allow_lds<kSplitPrivDma, true>(lds_limit);
             allow_lds<kSplitChunk, false>(lds_limit);
             allow_lds<kSplitChunk, true>(lds_limit);
             allow_lds_multi<false>(lds_limit);
@@ -1296,6 +1355,8 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, hipStream_
         launch_mode<kStream>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
     else if (p.xlds == 3)
         launch_mode<kSplitChunk>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
+    else if (p.xlds == 2 && p.xdma)
+        launch_mode<kSplitPrivDma>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
     else if (p.xlds == 2)
         launch_mode<kSplitPriv>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
     else if (p.xlds == 1)
