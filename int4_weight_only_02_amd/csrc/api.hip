@@ -29,7 +29,7 @@ int check_dims(int M, int N, int K)
 size_t linear_ws(int M, int N, int K)
 {
     if (M <= kSkinnyMaxM) {
-        const size_t a = plan_skinny(M, N, K, 0).ws_bytes, b = plan_skinny_fixed(M, N, K).ws_bytes;
+        const size_t a = plan_skinny(M, N, K, 0).ws_bytes, b = skinny_chunk_ws_bound(M, N, K);
         return a > b ? a : b;
     }
     return plan_tiled(M, N, K).ws_bytes;
@@ -184,6 +184,14 @@ int w4a16_linear_batch(const w4a16_problem *problems, int count, int M, int grou
         return W4A16_OK;
     }
     SkinnyMulti mp{};
+    int bn[W4A16_MAX_BATCH], bk[W4A16_MAX_BATCH], btw[W4A16_MAX_BATCH], nb = 0;
+    for (int q = 0; q < count; ++q)
+        if (problems[q].N != 0) {
+            bn[nb] = problems[q].N;
+            bk[nb] = problems[q].K;
+            ++nb;
+        }
+    balance_multi(bn, bk, nb, M, btw);
     int c = 0;
     for (int q = 0; q < count; ++q) {
         const w4a16_problem &pr = problems[q];
@@ -202,7 +210,7 @@ int w4a16_linear_batch(const w4a16_problem *problems, int count, int M, int grou
         a.y_f32 = y_dtype == W4A16_OUT_F32;
         a.ws = (unsigned char *)workspace;
         a.lmhead = 0;
-        mp.plan[c] = plan_skinny_fixed(M, pr.N, pr.K);
+        mp.plan[c] = plan_skinny_fixed(M, pr.N, pr.K, 0, btw[c]);
         ++c;
     }
     mp.count = c;

@@ -80,7 +80,11 @@ struct SkinnyMulti {
     SkinnyArgs args[kMaxProblems];
     SkinnyPlan plan[kMaxProblems];
 };
-SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit = 0);
+SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit = 0, int tw_hint = 0);
+// tiles per workgroup that spread the projections of one launch evenly over the CUs
+void balance_multi(const int *N, const int *K, int count, int M, int *tw);
+// upper bound of the partial-sum scratch any chunked plan of this shape needs
+size_t skinny_chunk_ws_bound(int M, int N, int K);
 // gives every chunked projection its own arrival counters and partial-sum region;
 // returns the workspace bytes the launch needs (0: none)
 size_t skinny_multi_scratch(SkinnyMulti &mp, int M);

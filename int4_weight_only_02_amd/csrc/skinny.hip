@@ -968,15 +968,17 @@ size_t lds_per_group(int M)
     return (size_t)mrows * 16 * (16 + 4) + 16 * 4;
 }
 
+// LDS of a plan: X (shared, per wave, or one chunk) and the K-slice partial sums of
+// every wave the workgroup launches with (p.waves; waves past tw * sk stay idle)
 size_t lds_for(const SkinnyPlan &p, int M)
 {
-    const size_t red = p.sk > 1 ? (size_t)p.tw * p.sk * 1024 : 0;
+    const size_t red = p.sk > 1 ? (size_t)p.waves * 1024 : 0;
     if (p.xlds == 3) {
         const int mrows = M < 16 ? M : 16;
         return (size_t)((p.cg * 16 * mrows + 63) & ~63) * 16 + red;
     }
     const size_t xs = (size_t)p.chunk * lds_per_group(M);
-    return (p.xlds == 2 ? xs * p.tw * p.sk : xs) + red;
+    return (p.xlds == 2 ? xs * p.waves : xs) + red;
 }
 
 // Tuning override for the split-mode shape, read once from W4A16_SKINNY_SPLIT="tw,sk"
@@ -1054,6 +1056,7 @@ bool plan_chunk(SkinnyPlan &p, int M, size_t lds_limit, int tw, int cg, bool fix
     p.chunk = 0;
     p.tkt = 0;
     p.part_off = kZeroRegion;
+    p.waves = fixed ? kMaxWaves : tw * sk;
     return lds_for(p, M) <= lds_limit && mrows > 0;
 }
 
@@ -1062,7 +1065,7 @@ bool plan_chunk(SkinnyPlan &p, int M, size_t lds_limit, int tw, int cg, bool fix
 // (at most one tile per CU), one tile per workgroup with X of all of K in LDS, or,
 // when that does not fit, two tiles per workgroup and chunks of 32 groups.  With
 // more tiles than CUs the workgroup-shared staging of the other split modes wins.
-bool choose_chunk(SkinnyPlan &p, int M, size_t lds_limit, bool fixed)
+bool choose_chunk(SkinnyPlan &p, int M, size_t lds_limit, bool fixed, int tw_hint)
 {
     int tw = 0, cg = 0;
     SkinnyPlan c = p;
@@ -1072,14 +1075,15 @@ bool choose_chunk(SkinnyPlan &p, int M, size_t lds_limit, bool fixed)
         p = c;
         return true;
     }
-    if (p.mblocks != 1 || M <= 4 || p.nt > kCUs)
+    if (p.mblocks != 1 || M <= 4 || (tw_hint <= 0 && p.nt > kCUs))
         return false;
-    if (plan_chunk(c, M, lds_limit, 1, 0, fixed)) {
+    tw = tw_hint > 0 ? tw_hint : 1;
+    if (plan_chunk(c, M, lds_limit, tw, 0, fixed)) {
         p = c;
         return true;
     }
     c = p;
-    if (plan_chunk(c, M, lds_limit, 2, 32, fixed)) {
+    if (plan_chunk(c, M, lds_limit, tw > 2 ? tw : 2, 32, fixed)) {
         p = c;
         return true;
     }
@@ -1147,7 +1151,7 @@ SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit)
         p.items = p.mblocks * p.ntg;
         p.grid = p.items;
         if (!lmhead)
-            choose_chunk(p, M, lds_limit, false);
+            choose_chunk(p, M, lds_limit, false, 0);
     }
     p.waves = p.tw * p.sk;
     p.lds_bytes = lds_for(p, M);
@@ -1159,8 +1163,10 @@ SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit)
 }
 
 // Split-mode plan with exactly kMaxWaves waves (for projections sharing one launch):
-// tw a power of two, sk = kMaxWaves / tw (slices past K stay empty).
-SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit)
+// tw from the caller (tw_hint, balancing the launch) or the smallest power of two that
+// keeps the projection within one workgroup per CU; sk = kMaxWaves / tw (waves and
+// slices past K stay empty).
+SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit, int tw_hint)
 {
     SkinnyPlan p{};
     if (lds_limit == 0 || lds_limit > kLdsBudget)
@@ -1174,6 +1180,8 @@ SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit)
     int tw = 1;
     while (tw < kMaxWaves && (long long)tw * kCUs < tiles)
         tw *= 2;
+    if (tw_hint > 0)
+        tw = tw_hint < kMaxWaves ? tw_hint : kMaxWaves;
     const int sk = kMaxWaves / tw;
     const size_t red = sk > 1 ? (size_t)kMaxWaves * 1024 : 0;
     p.stream = 0;
@@ -1188,8 +1196,8 @@ SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit)
     p.ntg = (p.nt + tw - 1) / tw;
     p.items = p.mblocks * p.ntg;
     p.grid = p.items;
-    choose_chunk(p, M, lds_limit, true);
     p.waves = kMaxWaves;
+    choose_chunk(p, M, lds_limit, true, tw_hint);
     p.lds_bytes = lds_for(p, M);
     p.ws_bytes = (p.xlds == 3 && p.C > 1) ? kZeroRegion + (size_t)p.C * M * N * 4 : 0;
     return p;
@@ -1275,6 +1283,34 @@ hipError_t device_lds_limit(size_t *limit)
 
 } // namespace
 
+void balance_multi(const int *N, const int *K, int count, int M, int *tw)
+{
+    // the same amount of packed weights per workgroup for every projection, sized so
+    // that the launch fits one workgroup per CU: tw = ceil(work per CU / groups per tile)
+    const long long mb = (M + 15) / 16;
+    long long work = 0;
+    for (int q = 0; q < count; ++q)
+        work += (long long)((N[q] + 15) / 16) * mb * (K[q] / kGroup);
+    for (int q = 0; q < count; ++q) {
+        const long long g = K[q] / kGroup > 0 ? K[q] / kGroup : 1;
+        long long t = (work + (long long)kCUs * g - 1) / ((long long)kCUs * g);
+        tw[q] = (int)(t < 1 ? 1 : t > kMaxWaves ? kMaxWaves : t);
+    }
+}
+
+size_t skinny_chunk_ws_bound(int M, int N, int K)
+{
+    // a chunked plan splits K only when X of all of K does not fit in LDS, and then
+    // into chunks of 32 groups (any tiles-per-workgroup choice)
+    const int G = K / kGroup;
+    if (M <= 4 || M > 16 || G <= 32)
+        return 0;
+    const size_t all = (size_t)((G * 16 * M + 63) & ~63) * 16 + (size_t)kMaxWaves * 1024;
+    if (all <= kLdsBudget)
+        return 0;
+    return kZeroRegion + (size_t)((G + 31) / 32) * M * N * 4;
+}
+
 size_t skinny_multi_scratch(SkinnyMulti &mp, int M)
 {
     int tkt = 0;
@@ -1303,7 +1339,7 @@ hipError_t launch_skinny_multi(SkinnyMulti &mp, int M, size_t ws_bytes, hipStrea
     bool replanned = false;
     for (int q = 0; q < mp.count; ++q) {
         if (mp.plan[q].lds_bytes > lds_limit) {
-            mp.plan[q] = plan_skinny_fixed(M, mp.args[q].N, mp.args[q].K, lds_limit);
+            mp.plan[q] = plan_skinny_fixed(M, mp.args[q].N, mp.args[q].K, lds_limit, mp.plan[q].tw);
             replanned = true;
         }
         if (mp.plan[q].lds_bytes > lds_limit)
