@@ -13,6 +13,7 @@ Functions (numpy in, numpy out):
   linear_at(..., rows, cols)                    -> Y[rows[i], cols[i]] f64
   linear_matmul(X, qweight, scales, qzeros)     -> Y f64[M,N] (dequantize in fp64, then a library matmul)
   argmax_accept(Y f64[M,N], draft i32[M])       -> (argmax i32[M], gap f64[M], L int)
+  quantize(W bf16-bits u16[N,K], scales f16-bits u16[N,G], zeros u8[N,G]) -> codes u8[N,K]
   bf16_to_f64 / f16_to_f64 (bit patterns -> exact values)
 """
 import ctypes
@@ -49,6 +50,7 @@ def _bind(path):
     lib.oracle_linear_f64.argtypes = [P, P, P, P, I, I, I, I, P]
     lib.oracle_linear_at.argtypes = [P, P, P, P, I, I, I, I, P, P, I, P]
     lib.oracle_argmax_accept.argtypes = [P, I, I, P, P, P, P]
+    lib.oracle_quantize.argtypes = [P, P, P, I, I, I, P]
     lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_f64.restype = ctypes.c_double
     lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
@@ -170,3 +172,15 @@ def argmax_accept(Y, draft):
     _load().oracle_argmax_accept(py, M, N, pd, am.ctypes.data_as(ctypes.c_void_p),
                                  gap.ctypes.data_as(ctypes.c_void_p), ctypes.byref(L))
     return am, gap, int(L.value)
+
+
+def quantize(W, scales, zeros, group=GROUP):
+    """Round W back onto the grid with frozen scales and zeros (oracle_quantize)."""
+    W, pw = _c(W, np.uint16)
+    scales, ps = _c(scales, np.uint16)
+    zeros, pz = _c(zeros, np.uint8)
+    N, K = W.shape
+    assert K % group == 0 and scales.shape == (N, K // group) and zeros.shape == (N, K // group)
+    codes = np.zeros((N, K), np.uint8)
+    _load().oracle_quantize(pw, ps, pz, N, K, group, codes.ctypes.data_as(ctypes.c_void_p))
+    return codes

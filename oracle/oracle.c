@@ -216,6 +216,40 @@ void oracle_argmax_accept(const double *Y, int M, int N, const int32_t *draft,
     *accept_len = L;
 }
 
+/* ---- re-quantization onto a frozen grid ----------------------------------- */
+
+/* Round a weight matrix back onto the grid, keeping the grid's per-group scales
+ * and zero-points (Pith review, Referee Report: Summary and Significance, and
+ * Assumptions & free parameters, second assumption: distillation keeps the INT4
+ * grid's scales fixed and rounds the trained weights back onto it, so the packed
+ * format does not change).  The pages give no formula; the reading is the usual
+ * asymmetric one, the inverse of W = (q - z) * s:
+ *     q[n,k] = clamp(round(W[n,k] / s[n,g]) + z[n,g], 0, 15),  g = floor(k / group)
+ * where round is to the nearest integer, ties to even, and is applied to the
+ * quotient before z is added (the order matters at exact ties).  The quotient is
+ * an IEEE binary32 division of the exact binary32 values of W (bfloat16) and s
+ * (binary16), the precision the GPU takes the same decision in; rintf rounds in
+ * the default mode (nearest, ties to even).
+ * W u16[N][K] bfloat16 bits, scales u16[N][G] binary16 bits, zeros u8[N][G]
+ * (0..15), codes out u8[N][K]. */
+void oracle_quantize(const uint16_t *W, const uint16_t *scales, const uint8_t *zeros, int N, int K,
+                     int group, uint8_t *codes)
+{
+    int G = K / group;
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k) {
+            int g = k / group;
+            float w = (float)oracle_bf16_to_f64(W[(size_t)n * K + k]);
+            float sc = (float)oracle_f16_to_f64(scales[(size_t)n * G + g]);
+            float r = rintf(w / sc) + (float)(zeros[(size_t)n * G + g] & 15u);
+            if (!(r >= 0.0f)) /* below 0 (or NaN): the lowest code */
+                r = 0.0f;
+            if (r > 15.0f)
+                r = 15.0f;
+            codes[(size_t)n * K + k] = (uint8_t)r;
+        }
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

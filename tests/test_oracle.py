@@ -15,6 +15,9 @@ Each pin is chosen so that a plausible mistake in the oracle fails it:
   permutation      permuting weight rows permutes Y columns bit-exactly
   verify goldens   hand-worked argmax / accepted-prefix cases, ties to the lowest id
   statistics       rms(Y) of the synthetic workloads against its closed form
+  re-quantization  hand-worked round-to-grid cases (ties to even, clamping, overflow);
+                   on-grid weights come back as their own codes; agreement with exact
+                   rational rounding away from binary32 near-ties
 """
 import math
 import os
@@ -346,3 +349,77 @@ def test_dequantize_matches_onehot_linear():
     W = oracle.dequantize(qw, qz, d["scales"], 64, 384)
     eye = synth.f32_to_bf16_bits(np.eye(384, dtype=np.float32))
     assert (oracle.linear(eye, qw, d["scales"], qz) == W.T).all()
+
+
+# ------------------------------------------------------------------ re-quantization
+
+
+def _read_quantize_cases():
+    rows = []
+    with open(os.path.join(GOLDEN, "quantize_cases.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                w, sc, z, q = line.split()
+                rows.append((int(w, 16), int(sc, 16), int(z), int(q)))
+    return rows
+
+
+def test_quantize_worked_by_hand():
+    cases = _read_quantize_cases()
+    assert len(cases) >= 12
+    # one group of 128 per case (the case's weight repeated), so the group index matters
+    W = np.array([[w] * 128 for w, _, _, _ in cases], np.uint16)
+    S = np.array([[sc] for _, sc, _, _ in cases], np.uint16)
+    Z = np.array([[z] for _, _, z, _ in cases], np.uint8)
+    codes = oracle.quantize(W, S, Z)
+    for i, (_, _, _, q) in enumerate(cases):
+        assert (codes[i] == q).all(), (i, cases[i], codes[i, 0])
+
+
+def _bf16_rne(x):
+    """fp64 -> bfloat16 bits, round to nearest even (via fp32; the values here are
+    far from fp32 rounding boundaries)."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_quantize_returns_on_grid_weights_to_their_codes(seed):
+    # W = (q - z) * s rounded to bfloat16 is within 2^-9 |W| <= 0.03 s of the grid
+    # point, so rounding W / s back gives q - z exactly: every code must come back
+    rng = np.random.default_rng(seed)
+    N, K, G = 16, 512, 4
+    q = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    z = rng.integers(0, 16, (N, G)).astype(np.uint8)
+    s = rng.uniform(0.002, 0.02, (N, G)).astype(np.float16)
+    Wf = (q.astype(np.float64) - np.repeat(z, 128, axis=1)) * np.repeat(s.astype(np.float64), 128, axis=1)
+    codes = oracle.quantize(_bf16_rne(Wf), s.view(np.uint16), z)
+    assert (codes == q).all()
+
+
+def test_quantize_matches_exact_rational_rounding():
+    # exact W / s (Fractions), round half to even, + z, clamp; the oracle's binary32
+    # quotient may only differ where the exact quotient is within one binary32 ulp of
+    # a half-integer (a near-tie), which these random values almost never hit
+    rng = np.random.default_rng(7)
+    N, K, G = 8, 256, 2
+    s = rng.uniform(0.002, 0.02, (N, G)).astype(np.float16)
+    z = rng.integers(0, 16, (N, G)).astype(np.uint8)
+    Wf = rng.normal(0.0, 1.0, (N, K)) * np.repeat(s.astype(np.float64), 128, axis=1) * 6.0
+    Wb = _bf16_rne(Wf)
+    codes = oracle.quantize(Wb, s.view(np.uint16), z)
+    w_exact = (Wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    near = 0
+    for n in range(N):
+        for k in range(K):
+            g = k // 128
+            x = Fraction(float(w_exact[n, k])) / Fraction(float(s[n, g]))
+            r = round(x)  # Fraction: nearest, ties to even
+            want = min(15, max(0, r + int(z[n, g])))
+            frac = x - math.floor(x)
+            if abs(frac - Fraction(1, 2)) * 2 ** 24 <= abs(x) + 1:
+                near += 1
+                continue
+            assert codes[n, k] == want, (n, k, float(x), codes[n, k], want)
+    assert near <= 2

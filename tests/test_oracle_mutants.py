@@ -36,6 +36,13 @@ MUTANTS = [
      "for (int i = 0; i < M; ++i)\n        L += argmax[i] == draft[i];"),
     ("f16_bias_off_by_one", "v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
     ("bf16_low_half", "uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h;"),
+    ("quantize_ties_away", "float r = rintf(w / sc) + (float)", "float r = roundf(w / sc) + (float)"),
+    ("quantize_round_after_zero", "float r = rintf(w / sc) + (float)(zeros[(size_t)n * G + g] & 15u);",
+     "float r = rintf(w / sc + (float)(zeros[(size_t)n * G + g] & 15u));"),
+    ("quantize_truncates", "float r = rintf(w / sc) + (float)", "float r = truncf(w / sc) + (float)"),
+    ("quantize_no_low_clamp", "if (!(r >= 0.0f)) /* below 0 (or NaN): the lowest code */\n                r = 0.0f;",
+     "if (r != r)\n                r = 0.0f;"),
+    ("quantize_group_of_64", "int g = k / group;\n            float w", "int g = k / 64 % G;\n            float w"),
 ]
 
 PIN_TESTS = [
@@ -47,6 +54,9 @@ PIN_TESTS = [
     lambda: pins.test_equal_codes_closed_form(),
     lambda: pins.test_dyadic_inputs_exact(),
     lambda: pins.test_verify_golden_cases(),
+    lambda: pins.test_quantize_worked_by_hand(),
+    lambda: pins.test_quantize_returns_on_grid_weights_to_their_codes(0),
+    lambda: pins.test_quantize_matches_exact_rational_rounding(),
 ]
 
 
