@@ -86,6 +86,28 @@ int w4a16_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K, int gro
                uint32_t *qweight, uint32_t *qzeros, void *stream);
 
 /*
+ * w4a16_quantize -- round a weight matrix back onto the grid, keeping the grid's
+ * per-group scales and zero-points: the re-packing step of the pages'
+ * distillation, which keeps the INT4 grid's scales fixed so that the packed format
+ * and the serving path do not change (Pith review, Referee Report: Summary and
+ * Significance; Assumptions & free parameters, second assumption).  The pages give
+ * no formula; this is the asymmetric reading, the inverse of W = (q - z) * s:
+ *     q[n,k] = clamp(round(W[n,k] / s[n,g]) + z[n,g], 0, 15),  g = k / group
+ * round = to nearest, ties to even, applied to the IEEE binary32 quotient before z
+ * is added.  The codes are written packed (no unpacked copy is made).
+ *   W        [N][K]    bf16 weights, row-major (device)
+ *   scales   [N][G]    fp16 (device, frozen)
+ *   qzeros   [N/8][G]  uint32, layout of w4a16_pack (device, frozen)
+ *   qweight  [N][K/8]  uint32 out, layout of w4a16_pack (device; must not alias)
+ * Shapes: N >= 0, N % 8 == 0, K >= group, K % group == 0, group == 128,
+ *         N * K at most 2^31 - 256.  N == 0 enqueues nothing.
+ * Errors: W4A16_ERR_SHAPE, W4A16_ERR_UNSUPPORTED (group), W4A16_ERR_NULL,
+ *         W4A16_ERR_ALIGN (16-byte alignment), W4A16_ERR_HIP.
+ */
+int w4a16_quantize(const void *W, const void *scales, const uint32_t *qzeros, int N, int K, int group,
+                   uint32_t *qweight, void *stream);
+
+/*
  * w4a16_linear -- Y[M][N] = X[M][K] * W^T on the grid defined above.
  * The layer the pages' INT4 target and GPTQ-INT4 drafter spend their forward
  * passes in (Pith review, Referee Report: Summary; free parameters: group 128).

@@ -27,7 +27,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw4a16.so")
 _lib = None
 
-EXPORTED = ("w4a16_pack", "w4a16_linear", "w4a16_linear_batch", "w4a16_lmhead_verify",
+EXPORTED = ("w4a16_pack", "w4a16_quantize", "w4a16_linear", "w4a16_linear_batch", "w4a16_lmhead_verify",
             "w4a16_workspace_bytes", "w4a16_status_string", "w4a16_abi_version")
 MAX_BATCH = 8
 
@@ -56,6 +56,8 @@ def lib():
     P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     L.w4a16_pack.argtypes = [P, P, I, I, I, P, P, P]
     L.w4a16_pack.restype = I
+    L.w4a16_quantize.argtypes = [P, P, P, I, I, I, P, P]
+    L.w4a16_quantize.restype = I
     L.w4a16_linear.argtypes = [P, P, P, P, I, I, I, I, P, I, P, S, P]
     L.w4a16_linear.restype = I
     L.w4a16_linear_batch.argtypes = [P, I, I, I, I, P, S, P]
@@ -136,6 +138,20 @@ def w4a16_pack(codes, zeros, group=GROUP, stream=None):
                           _ptr(qweight), _ptr(qzeros), _stream(stream))
     _check(st, "w4a16_pack")
     return qweight, qzeros
+
+
+def w4a16_quantize(W, scales, qzeros, group=GROUP, out=None, stream=None):
+    """Round bf16 W [N,K] onto the grid with frozen fp16 scales [N,G] and packed qzeros
+    [N/8,G]; returns the packed qweight [N,K/8] (int32 view of the uint32 words)."""
+    import torch
+    N, K = W.shape
+    assert W.dtype == torch.bfloat16 and scales.dtype == torch.float16
+    assert W.is_contiguous() and scales.is_contiguous() and qzeros.is_contiguous()
+    qweight = out if out is not None else torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
+    assert qweight.shape == (N, K // 8) and qweight.dtype == torch.int32 and qweight.is_contiguous()
+    st = lib().w4a16_quantize(_ptr(W), _ptr(scales), _ptr(qzeros), N, K, group, _ptr(qweight), _stream(stream))
+    _check(st, "w4a16_quantize")
+    return qweight
 
 
 def w4a16_linear(X, qweight, scales, qzeros, out_dtype=None, group=GROUP, out=None,

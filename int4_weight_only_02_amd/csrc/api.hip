@@ -84,6 +84,25 @@ int w4a16_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K, int gro
     return W4A16_OK;
 }
 
+int w4a16_quantize(const void *W, const void *scales, const uint32_t *qzeros, int N, int K, int group,
+                   uint32_t *qweight, void *stream)
+{
+    if (group != kGroup)
+        return W4A16_ERR_UNSUPPORTED;
+    const int st = check_dims(0, N, K);
+    if (st != W4A16_OK)
+        return st;
+    if (N == 0)
+        return W4A16_OK;
+    if (!W || !scales || !qzeros || !qweight)
+        return W4A16_ERR_NULL;
+    if (misaligned(W) || misaligned(scales) || misaligned(qzeros) || misaligned(qweight))
+        return W4A16_ERR_ALIGN;
+    const hipError_t e = launch_quantize((const uint16_t *)W, (const uint16_t *)scales, qzeros, N, K, qweight,
+                                         (hipStream_t)stream);
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
 int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, const uint32_t *qzeros,
                  int M, int N, int K, int group, void *Y, int y_dtype,
                  void *workspace, size_t workspace_bytes, void *stream)

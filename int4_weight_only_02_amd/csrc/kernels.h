@@ -22,6 +22,10 @@ constexpr size_t kZeroRegion = 8192;
 hipError_t launch_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K, int G,
                        uint32_t *qweight, uint32_t *qzeros, hipStream_t stream);
 
+// ---------------------------------------------------------------- re-quantization
+hipError_t launch_quantize(const uint16_t *W, const uint16_t *scales, const uint32_t *qzeros, int N, int K,
+                           uint32_t *qweight, hipStream_t stream);
+
 // ---------------------------------------------------------------- skinny (small M)
 // Every workgroup owns whole 16-column tiles (no partial sums cross workgroups).
 //   split mode  (stream == 0): item = (16-row m-block, group of tw tiles); a

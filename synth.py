@@ -57,6 +57,22 @@ def linear_inputs(seed, M, N, K, group=GROUP):
     return {"codes": codes, "zeros": zeros, "scales": scales, "X": X}
 
 
+def requant_inputs(seed, N, K, group=GROUP):
+    """Weights near a frozen grid, as after distillation: W = (q - z + e) * s with
+    e ~ N(0, 0.5) (most weights land near their old code, some cross to a neighbour,
+    the extremes fall off the 4-bit range), rounded to bfloat16; scales and zeros as
+    in linear_inputs.  Returns W (bf16 bits), scales (fp16 bits), zeros u8."""
+    rng = np.random.default_rng(seed)
+    G = K // group
+    codes = rng.integers(0, 16, size=(N, K)).astype(np.float32)
+    zeros = rng.integers(0, 16, size=(N, G), dtype=np.uint8)
+    scales = f32_to_f16_bits(rng.uniform(0.002, 0.02, size=(N, G)).astype(np.float32))
+    s = np.repeat(scales.view(np.float16).astype(np.float32), group, axis=1)
+    e = rng.normal(0.0, 0.5, size=(N, K)).astype(np.float32)
+    W = (codes - np.repeat(zeros.astype(np.float32), group, axis=1) + e) * s
+    return {"W": f32_to_bf16_bits(W), "scales": scales, "zeros": zeros}
+
+
 def workload_inputs(workload, j, group=GROUP):
     label, M, K, N = WORKLOADS[workload][j]
     return linear_inputs(seed_for(workload, j), M, N, K, group)
