@@ -339,6 +339,59 @@ def measure(name, dev, steps, warmup, lmhead=False, ev_reps=200, batched=False):
     return res
 
 
+def measure_requant(dev, steps, warmup, N=9728, K=2560):
+    """w4a16_quantize on one gate/up-shaped matrix: rounding weights near the grid back
+    onto it (frozen scales and zeros), bf16 in, packed words out.  HBM-bound; bytes per
+    launch = 2NK (W) + NK/2 (codes) + 2NG + NG/2 (scales, zeros)."""
+    import torch
+    import int4_weight_only_02_amd as w4
+    import oracle
+    G = K // 128
+    d = synth.requant_inputs(4242, N, K)
+    W = torch.from_numpy(d["W"].view(np.int16)).to(dev).view(torch.bfloat16)
+    S = torch.from_numpy(d["scales"].view(np.int16)).to(dev).view(torch.float16)
+    qz = w4.w4a16_pack(torch.zeros((N, K), dtype=torch.uint8, device=dev), torch.from_numpy(d["zeros"]).to(dev))[1]
+    nbytes = 2 * N * K + N * K // 2 + 2 * N * G + N * G // 2
+    R = int(max(1, min(32, -(-CACHE_ROTATE_BYTES // nbytes))))
+    copies = [W] + [W.clone() for _ in range(R - 1)]
+    out = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    # check: a sample of rows bit-exact against the oracle
+    w4.w4a16_quantize(W, S, qz, out=out)
+    torch.cuda.synchronize()
+    rows = np.arange(0, N, max(1, N // 64))
+    codes = oracle.quantize(d["W"][rows], d["scales"][rows], d["zeros"][rows])
+    want = np.zeros((len(rows), K // 8), np.uint32)
+    for j in range(8):
+        want |= codes[:, j::8].astype(np.uint32) << (4 * j)
+    exact = bool((out.cpu().numpy().view(np.uint32)[rows] == want).all())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        w4.w4a16_quantize(copies[0], S, qz, out=out)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for r in range(R):
+                w4.w4a16_quantize(copies[r], S, qz, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for _ in range(max(1, warmup // R)):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // R)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * R)
+    return {"N": N, "K": K, "copies": R, "launches": reps * R, "bytes_per_launch": nbytes,
+            "us_per_launch": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
+            "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4), "bit_exact_sample": exact}
+
+
 def calib_copy(dev, nbytes=1 << 30, reps=5):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -426,11 +479,15 @@ def main():
         return
 
     names = [HEADLINE, "single_512", "verify_block_m16", "lmhead_verify_m16", "prefill_m8192",
-             "verify_block_m16+batch"]
+             "verify_block_m16+batch", "requantize_9728x2560"]
     if args.only:
         names = [args.only]
     results = {}
     for key in names:
+        if key == "requantize_9728x2560":
+            results[key] = measure_requant(dev, max(64, min(args.steps, 1000)), 32)
+            print("[bench] %s: %s" % (key, json.dumps(results[key])), file=sys.stderr, flush=True)
+            continue
         name, batched = key.split("+")[0], key.endswith("+batch")
         steps = args.steps if name != "prefill_m8192" else max(4, min(args.steps, 40))
         warm = args.warmup if name != "prefill_m8192" else 4
@@ -440,6 +497,9 @@ def main():
         print("[bench] %s: %s" % (key, json.dumps(results[key])), file=sys.stderr, flush=True)
 
     head = results.get(HEADLINE) or results[names[0]]
+    if "per_launch" not in head:  # --only requantize_9728x2560
+        print(json.dumps({"workloads": results}))
+        return
     head_name = HEADLINE if HEADLINE in results else names[0]
     per = head["per_launch"]
     # every launch in the timed region is a skinny_kernel (one per projection)

@@ -93,7 +93,7 @@ int w4a16_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K, int gro
  * Significance; Assumptions & free parameters, second assumption).  The pages give
  * no formula; this is the asymmetric reading, the inverse of W = (q - z) * s:
  *     q[n,k] = clamp(round(W[n,k] / s[n,g]) + z[n,g], 0, 15),  g = k / group
- * round = to nearest, ties to even, applied to the IEEE binary32 quotient before z
+ * round = the exact quotient to the nearest integer, ties to even, applied before z
  * is added.  The codes are written packed (no unpacked copy is made).
  *   W        [N][K]    bf16 weights, row-major (device)
  *   scales   [N][G]    fp16 (device, frozen)

@@ -14,7 +14,6 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-fhip-fp32-correctly-rounded-divide-sqrt",
          "-Wall", "-Wno-unused-function",
          "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
 

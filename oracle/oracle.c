@@ -225,13 +225,27 @@ void oracle_argmax_accept(const double *Y, int M, int N, const int32_t *draft,
  * format does not change).  The pages give no formula; the reading is the usual
  * asymmetric one, the inverse of W = (q - z) * s:
  *     q[n,k] = clamp(round(W[n,k] / s[n,g]) + z[n,g], 0, 15),  g = floor(k / group)
- * where round is to the nearest integer, ties to even, and is applied to the
- * quotient before z is added (the order matters at exact ties).  The quotient is
- * an IEEE binary32 division of the exact binary32 values of W (bfloat16) and s
- * (binary16), the precision the GPU takes the same decision in; rintf rounds in
- * the default mode (nearest, ties to even).
+ * where round takes the exact quotient to the nearest integer, ties to even, and
+ * is applied before z is added (the order matters at exact ties).
  * W u16[N][K] bfloat16 bits, scales u16[N][G] binary16 bits, zeros u8[N][G]
  * (0..15), codes out u8[N][K]. */
+
+/* round(w / s), ties to even, for |w / s| < 32, from exact fp64 arithmetic: w has 8
+ * significant bits and s 11, so r * s, w - r * s and 2 (w - r s) - s are exact for
+ * the small integers r used here; the fp64 quotient only picks the starting r. */
+static double round_quotient(double w, double s)
+{
+    double r = floor(w / s);
+    while (r * s > w) /* make r * s <= w < (r + 1) * s hold exactly */
+        r -= 1.0;
+    while ((r + 1.0) * s <= w)
+        r += 1.0;
+    double d = 2.0 * (w - r * s) - s; /* < 0: r is nearer; > 0: r + 1; = 0: a tie */
+    if (d > 0.0 || (d == 0.0 && fmod(r, 2.0) != 0.0))
+        r += 1.0;
+    return r;
+}
+
 void oracle_quantize(const uint16_t *W, const uint16_t *scales, const uint8_t *zeros, int N, int K,
                      int group, uint8_t *codes)
 {
@@ -239,14 +253,24 @@ void oracle_quantize(const uint16_t *W, const uint16_t *scales, const uint8_t *z
     for (int n = 0; n < N; ++n)
         for (int k = 0; k < K; ++k) {
             int g = k / group;
-            float w = (float)oracle_bf16_to_f64(W[(size_t)n * K + k]);
-            float sc = (float)oracle_f16_to_f64(scales[(size_t)n * G + g]);
-            float r = rintf(w / sc) + (float)(zeros[(size_t)n * G + g] & 15u);
-            if (!(r >= 0.0f)) /* below 0 (or NaN): the lowest code */
-                r = 0.0f;
-            if (r > 15.0f)
-                r = 15.0f;
-            codes[(size_t)n * K + k] = (uint8_t)r;
+            double w = oracle_bf16_to_f64(W[(size_t)n * K + k]);
+            double s = oracle_f16_to_f64(scales[(size_t)n * G + g]);
+            double z = (double)(zeros[(size_t)n * G + g] & 15u);
+            double x = w / s;
+            double q;
+            if (x != x)            /* NaN weight: the lowest code */
+                q = 0.0;
+            else if (x >= 32.0)    /* far above the grid (z <= 15): the top code */
+                q = 15.0;
+            else if (x <= -32.0)   /* far below: the lowest code */
+                q = 0.0;
+            else
+                q = round_quotient(w, s) + z;
+            if (q < 0.0)
+                q = 0.0;
+            if (q > 15.0)
+                q = 15.0;
+            codes[(size_t)n * K + k] = (uint8_t)q;
         }
 }
 

@@ -17,7 +17,7 @@ Each pin is chosen so that a plausible mistake in the oracle fails it:
   statistics       rms(Y) of the synthetic workloads against its closed form
   re-quantization  hand-worked round-to-grid cases (ties to even, clamping, overflow);
                    on-grid weights come back as their own codes; agreement with exact
-                   rational rounding away from binary32 near-ties
+                   rational rounding everywhere, ties and their neighbours included
 """
 import math
 import os
@@ -399,27 +399,25 @@ def test_quantize_returns_on_grid_weights_to_their_codes(seed):
 
 
 def test_quantize_matches_exact_rational_rounding():
-    # exact W / s (Fractions), round half to even, + z, clamp; the oracle's binary32
-    # quotient may only differ where the exact quotient is within one binary32 ulp of
-    # a half-integer (a near-tie), which these random values almost never hit
+    # exact W / s (Fractions), round half to even (Python's round on a Fraction), + z,
+    # clamp: the oracle must agree on every weight, near-ties included
     rng = np.random.default_rng(7)
     N, K, G = 8, 256, 2
     s = rng.uniform(0.002, 0.02, (N, G)).astype(np.float16)
     z = rng.integers(0, 16, (N, G)).astype(np.uint8)
     Wf = rng.normal(0.0, 1.0, (N, K)) * np.repeat(s.astype(np.float64), 128, axis=1) * 6.0
     Wb = _bf16_rne(Wf)
+    # plus exact ties and values one bfloat16 step either side of them
+    for i in range(64):
+        n, g = i % N, (i // N) % G
+        t = Fraction(int(rng.integers(-12, 12)) * 2 + 1, 2) * Fraction(float(s[n, g]))
+        tb = _bf16_rne(np.array([float(t)]))[0]
+        Wb[n, g * 128 + i] = (int(tb) + int(rng.integers(-1, 2))) & 0xFFFF
     codes = oracle.quantize(Wb, s.view(np.uint16), z)
     w_exact = (Wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    near = 0
     for n in range(N):
         for k in range(K):
             g = k // 128
             x = Fraction(float(w_exact[n, k])) / Fraction(float(s[n, g]))
-            r = round(x)  # Fraction: nearest, ties to even
-            want = min(15, max(0, r + int(z[n, g])))
-            frac = x - math.floor(x)
-            if abs(frac - Fraction(1, 2)) * 2 ** 24 <= abs(x) + 1:
-                near += 1
-                continue
+            want = min(15, max(0, round(x) + int(z[n, g])))
             assert codes[n, k] == want, (n, k, float(x), codes[n, k], want)
-    assert near <= 2

@@ -36,13 +36,13 @@ MUTANTS = [
      "for (int i = 0; i < M; ++i)\n        L += argmax[i] == draft[i];"),
     ("f16_bias_off_by_one", "v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
     ("bf16_low_half", "uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h;"),
-    ("quantize_ties_away", "float r = rintf(w / sc) + (float)", "float r = roundf(w / sc) + (float)"),
-    ("quantize_round_after_zero", "float r = rintf(w / sc) + (float)(zeros[(size_t)n * G + g] & 15u);",
-     "float r = rintf(w / sc + (float)(zeros[(size_t)n * G + g] & 15u));"),
-    ("quantize_truncates", "float r = rintf(w / sc) + (float)", "float r = truncf(w / sc) + (float)"),
-    ("quantize_no_low_clamp", "if (!(r >= 0.0f)) /* below 0 (or NaN): the lowest code */\n                r = 0.0f;",
-     "if (r != r)\n                r = 0.0f;"),
-    ("quantize_group_of_64", "int g = k / group;\n            float w", "int g = k / 64 % G;\n            float w"),
+    ("quantize_ties_away", "if (d > 0.0 || (d == 0.0 && fmod(r, 2.0) != 0.0))", "if (d >= 0.0)"),
+    ("quantize_round_after_zero", "q = round_quotient(w, s) + z;", "q = round_quotient(w + z * s, s);"),
+    ("quantize_truncates", "if (d > 0.0 || (d == 0.0 && fmod(r, 2.0) != 0.0))\n        r += 1.0;",
+     "if (0)\n        r += 1.0;"),
+    ("quantize_no_low_clamp", "if (q < 0.0)\n                q = 0.0;", "if (q < -100.0)\n                q = 0.0;"),
+    ("quantize_group_of_64", "int g = k / group;\n            double w = oracle_bf16_to_f64(W",
+     "int g = k / 64 % G;\n            double w = oracle_bf16_to_f64(W"),
 ]
 
 PIN_TESTS = [

@@ -1,6 +1,6 @@
 """GPU parity of w4a16_quantize (round-to-grid with frozen scales and zeros) with the
-CPU oracle: the codes are integers decided by the same binary32 quotient on both
-sides, so the packed words must match bit for bit."""
+CPU oracle: both round the exact quotient W / s (ties to even), so the packed words
+must match bit for bit."""
 import os
 
 import numpy as np
@@ -101,3 +101,21 @@ def test_quantize_empty_and_errors(dev):
     with pytest.raises(w4.W4A16Error) as e:
         w4.w4a16_quantize(Wmis, S, Z)
     assert e.value.status == 3
+
+
+def test_every_bf16_value_against_the_oracle(dev):
+    # all 65536 bfloat16 patterns (zeros, subnormals, normals, infinities, NaNs) under
+    # 64 scales and zero-points: 4.2M codes, every near-tie of these scales included
+    rng = np.random.default_rng(11)
+    n_s = 64
+    allw = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(8, 8192)
+    W = np.tile(allw, (n_s, 1))                       # [512, 8192]
+    s_row = np.concatenate([synth.f32_to_f16_bits(np.array([0.002, 0.02, 0.25, 0.75, 1.0, 3.0], np.float32)),
+                            synth.f32_to_f16_bits(rng.uniform(0.002, 0.02, n_s - 6).astype(np.float32))])
+    S = np.repeat(s_row, 8)[:, None].repeat(8192 // 128, axis=1)
+    Z = np.repeat(rng.integers(0, 16, n_s).astype(np.uint8), 8)[:, None].repeat(8192 // 128, axis=1)
+    codes = oracle.quantize(W, S, Z)
+    want, _ = oracle.pack(codes, Z)
+    got = _gpu_quantize(W, S, Z, dev)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, "%d words differ, first at %s" % (len(bad), bad[:3].tolist())
