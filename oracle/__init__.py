@@ -14,6 +14,7 @@ Functions (numpy in, numpy out):
   linear_matmul(X, qweight, scales, qzeros)     -> Y f64[M,N] (dequantize in fp64, then a library matmul)
   argmax_accept(Y f64[M,N], draft i32[M])       -> (argmax i32[M], gap f64[M], L int)
   quantize(W bf16-bits u16[N,K], scales f16-bits u16[N,G], zeros u8[N,G]) -> codes u8[N,K]
+  linear_gidx(X, qweight, scales, qzeros, g_idx i32[K]) -> Y f64[M,N] (GPTQ act-order groups)
   bf16_to_f64 / f16_to_f64 (bit patterns -> exact values)
 """
 import ctypes
@@ -51,6 +52,7 @@ def _bind(path):
     lib.oracle_linear_at.argtypes = [P, P, P, P, I, I, I, I, P, P, I, P]
     lib.oracle_argmax_accept.argtypes = [P, I, I, P, P, P, P]
     lib.oracle_quantize.argtypes = [P, P, P, I, I, I, P]
+    lib.oracle_linear_gidx.argtypes = [P, P, P, P, P, I, I, I, I, P]
     lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_f64.restype = ctypes.c_double
     lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
@@ -184,3 +186,20 @@ def quantize(W, scales, zeros, group=GROUP):
     codes = np.zeros((N, K), np.uint8)
     _load().oracle_quantize(pw, ps, pz, N, K, group, codes.ctypes.data_as(ctypes.c_void_p))
     return codes
+
+
+def linear_gidx(X, qweight, scales, qzeros, g_idx, group=GROUP):
+    """Y = X W^T with column k of W in group g_idx[k] (oracle_linear_gidx)."""
+    X, px = _c(X, np.uint16)
+    qweight, pw = _c(qweight, np.uint32)
+    scales, ps = _c(scales, np.uint16)
+    qzeros, pz = _c(qzeros, np.uint32)
+    g_idx, pg = _c(g_idx, np.int32)
+    M, K = X.shape
+    N = qweight.shape[0]
+    G = K // group
+    assert qweight.shape == (N, K // 8) and scales.shape == (N, G) and qzeros.shape == (N // 8, G)
+    assert g_idx.shape == (K,) and (g_idx >= 0).all() and (g_idx < G).all()
+    Y = np.zeros((M, N), np.float64)
+    _load().oracle_linear_gidx(px, pw, ps, pz, pg, M, N, K, group, Y.ctypes.data_as(ctypes.c_void_p))
+    return Y

@@ -162,6 +162,39 @@ void oracle_linear_f64(const uint16_t *X, const uint32_t *qweight, const uint16_
     }
 }
 
+/* GPTQ act-order ("desc_act") variant: column k of the weight belongs to group
+ * g_idx[k] instead of floor(k / group), so the groups are sets of columns, not runs
+ * (the pages' drafter is GPTQ INT4 with groups of 128: Pith review, Assumptions &
+ * free parameters; whether it uses act-order is not said, so both are supported).
+ *     Y[m,n] = sum_{k ascending} X[m,k] * (q[n,k] - z[n,g_idx[k]]) * s[n,g_idx[k]]
+ * The codes stay in their natural k order in qweight; g_idx i32[K], 0 <= g < K/group.
+ * Symmetric GPTQ is the case z = 8 everywhere. */
+void oracle_linear_gidx(const uint16_t *X, const uint32_t *qweight, const uint16_t *scales,
+                        const uint32_t *qzeros, const int32_t *g_idx, int M, int N, int K, int group,
+                        double *Y)
+{
+    int G = K / group;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(static)
+        for (int n = 0; n < N; ++n) {
+            for (int k = 0; k < K; ++k) {
+                int g = g_idx[k];
+                w[k] = (double)(q_at(qweight, K, n, k) - z_at(qzeros, G, n, g)) *
+                       oracle_f16_to_f64(scales[(size_t)n * G + g]);
+            }
+            for (int m = 0; m < M; ++m) {
+                double acc = 0.0;
+                for (int k = 0; k < K; ++k)
+                    acc += oracle_bf16_to_f64(X[(size_t)m * K + k]) * w[k];
+                Y[(size_t)m * N + n] = acc;
+            }
+        }
+        free(w);
+    }
+}
+
 /* The same definition evaluated only at the listed (row, col) pairs:
  * out[i] = Y[rows[i], cols[i]].  Used where the full product is too large. */
 void oracle_linear_at(const uint16_t *X, const uint32_t *qweight, const uint16_t *scales,

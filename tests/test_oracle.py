@@ -15,6 +15,9 @@ Each pin is chosen so that a plausible mistake in the oracle fails it:
   permutation      permuting weight rows permutes Y columns bit-exactly
   verify goldens   hand-worked argmax / accepted-prefix cases, ties to the lowest id
   statistics       rms(Y) of the synthetic workloads against its closed form
+  act-order        GPTQ column groups (g_idx): sequential g_idx is the plain oracle bit
+                   for bit; one-hot X picks (q - z[g_idx[k]]) * s[g_idx[k]]; permuting
+                   the columns (X, codes and g_idx together) leaves dyadic Y unchanged
   re-quantization  hand-worked round-to-grid cases (ties to even, clamping, overflow);
                    on-grid weights come back as their own codes; agreement with exact
                    rational rounding everywhere, ties and their neighbours included
@@ -421,3 +424,64 @@ def test_quantize_matches_exact_rational_rounding():
             x = Fraction(float(w_exact[n, k])) / Fraction(float(s[n, g]))
             want = min(15, max(0, round(x) + int(z[n, g])))
             assert codes[n, k] == want, (n, k, float(x), codes[n, k], want)
+
+
+# ------------------------------------------------------------------ GPTQ act-order
+
+
+def _actorder_gidx(rng, K, group=128):
+    """GPTQ act-order groups: columns in a random order, consecutive blocks of `group`
+    of that order share a group."""
+    order = rng.permutation(K)
+    g_idx = np.empty(K, np.int32)
+    g_idx[order] = np.arange(K) // group
+    return g_idx
+
+
+def test_gidx_sequential_is_the_plain_oracle():
+    d = synth.linear_inputs(21, 5, 24, 384)
+    qw, qz = oracle.pack(d["codes"], d["zeros"])
+    g_idx = (np.arange(384) // 128).astype(np.int32)
+    Y1 = oracle.linear(d["X"], qw, d["scales"], qz)
+    Y2 = oracle.linear_gidx(d["X"], qw, d["scales"], qz, g_idx)
+    assert (Y1 == Y2).all()
+
+
+def test_gidx_onehot_picks_its_group():
+    rng = np.random.default_rng(3)
+    N, K = 16, 512
+    d = synth.linear_inputs(22, 1, N, K)
+    g_idx = _actorder_gidx(rng, K)
+    qw, qz = oracle.pack(d["codes"], d["zeros"])
+    ks = [0, 1, 127, 128, 300, 511]
+    X = np.zeros((len(ks), K), np.uint16)
+    for m, k in enumerate(ks):
+        X[m, k] = 0x3F80  # bf16 1.0
+    Y = oracle.linear_gidx(X, qw, d["scales"], qz, g_idx)
+    s = d["scales"].view(np.float16).astype(np.float64)
+    for m, k in enumerate(ks):
+        g = g_idx[k]
+        want = (d["codes"][:, k].astype(np.float64) - d["zeros"][:, g]) * s[:, g]
+        assert (Y[m] == want).all(), (m, k, g)
+
+
+def test_gidx_column_permutation_invariance():
+    # dyadic X and power-of-two scales: Y is exact, so permuting the columns of X, the
+    # codes and g_idx together must give the same Y bit for bit
+    rng = np.random.default_rng(4)
+    M, N, K = 3, 8, 256
+    codes = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    zeros = rng.integers(0, 16, (N, 2)).astype(np.uint8)
+    scales = (2.0 ** -rng.integers(3, 8, (N, 2))).astype(np.float16).view(np.uint16)
+    Xf = rng.integers(-8, 9, (M, K)).astype(np.float32)
+    X = (Xf.view(np.uint32) >> 16).astype(np.uint16)
+    g_idx = _actorder_gidx(rng, K)
+    p = rng.permutation(K)
+    qw, qz = oracle.pack(codes, zeros)
+    qwp, _ = oracle.pack(codes[:, p], zeros)
+    Y1 = oracle.linear_gidx(X, qw, scales, qz, g_idx)
+    Y2 = oracle.linear_gidx(np.ascontiguousarray(X[:, p]), qwp, scales, qz, np.ascontiguousarray(g_idx[p]))
+    assert (Y1 == Y2).all()
+    # and a grouping other than the sequential one changes the result
+    Y3 = oracle.linear(X, qw, scales, qz)
+    assert not (Y1 == Y3).all()

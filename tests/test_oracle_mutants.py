@@ -36,6 +36,9 @@ MUTANTS = [
      "for (int i = 0; i < M; ++i)\n        L += argmax[i] == draft[i];"),
     ("f16_bias_off_by_one", "v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
     ("bf16_low_half", "uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h;"),
+    ("gidx_ignored", "int g = g_idx[k];", "int g = k / group;"),
+    ("gidx_zero_from_k", "w[k] = (double)(q_at(qweight, K, n, k) - z_at(qzeros, G, n, g)) *\n                       oracle_f16_to_f64(scales[(size_t)n * G + g]);",
+     "w[k] = (double)(q_at(qweight, K, n, k) - z_at(qzeros, G, n, k / group)) *\n                       oracle_f16_to_f64(scales[(size_t)n * G + g]);"),
     ("quantize_ties_away", "if (d > 0.0 || (d == 0.0 && fmod(r, 2.0) != 0.0))", "if (d >= 0.0)"),
     ("quantize_round_after_zero", "q = round_quotient(w, s) + z;", "q = round_quotient(w + z * s, s);"),
     ("quantize_truncates", "if (d > 0.0 || (d == 0.0 && fmod(r, 2.0) != 0.0))\n        r += 1.0;",
@@ -54,6 +57,9 @@ PIN_TESTS = [
     lambda: pins.test_equal_codes_closed_form(),
     lambda: pins.test_dyadic_inputs_exact(),
     lambda: pins.test_verify_golden_cases(),
+    lambda: pins.test_gidx_sequential_is_the_plain_oracle(),
+    lambda: pins.test_gidx_onehot_picks_its_group(),
+    lambda: pins.test_gidx_column_permutation_invariance(),
     lambda: pins.test_quantize_worked_by_hand(),
     lambda: pins.test_quantize_returns_on_grid_weights_to_their_codes(0),
     lambda: pins.test_quantize_matches_exact_rational_rounding(),
