@@ -68,8 +68,9 @@ enum w4a16_out_dtype {
 };
 
 enum w4a16_op {
-    W4A16_OP_LINEAR = 0, /* w4a16_linear */
-    W4A16_OP_LMHEAD = 1  /* w4a16_lmhead_verify */
+    W4A16_OP_LINEAR = 0,          /* w4a16_linear */
+    W4A16_OP_LMHEAD = 1,          /* w4a16_lmhead_verify */
+    W4A16_OP_LINEAR_ACTORDER = 2  /* w4a16_linear_actorder */
 };
 
 /*
@@ -84,6 +85,43 @@ enum w4a16_op {
  */
 int w4a16_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K, int group,
                uint32_t *qweight, uint32_t *qzeros, void *stream);
+
+/*
+ * GPTQ act-order ("desc_act") support.  With act-order, column k of the weight
+ * belongs to group g_idx[k] instead of k / group (the pages' drafter is GPTQ INT4
+ * with groups of 128: Pith review, Assumptions & free parameters; the pages do not
+ * say whether it uses act-order).  Reading: W[n,k] = (q[n,k] - z[n,g_idx[k]]) *
+ * s[n,g_idx[k]]; symmetric GPTQ is z = 8 everywhere.  A permutation of the K axis
+ * makes every group's columns consecutive, after which the grid is the plain one:
+ *   perm[j] = the j-th column in (group, column) order, g_idx[perm[j]] = j / group.
+ *
+ * w4a16_actorder_perm -- the permutation, on the host (host pointers g_idx[K],
+ * perm[K]).  W4A16_ERR_SHAPE unless K % group == 0, every g_idx is in
+ * [0, K/group) and every group holds exactly `group` columns; W4A16_ERR_NULL.
+ */
+int w4a16_actorder_perm(const int32_t *g_idx, int K, int group, int32_t *perm);
+
+/*
+ * w4a16_pack_actorder -- w4a16_pack of the columns in perm order:
+ * qweight[n][j/8] nibble j%8 holds codes[n][perm[j]]; qzeros as w4a16_pack.
+ * codes u8[N][K] and zeros u8[N][K/group] in natural column order; perm i32[K]
+ * from w4a16_actorder_perm (device copy).  Shapes and errors as w4a16_pack; perm
+ * must be 16-byte aligned (an index outside [0, K) is clamped, never followed).
+ */
+int w4a16_pack_actorder(const uint8_t *codes, const uint8_t *zeros, const int32_t *perm, int N, int K,
+                        int group, uint32_t *qweight, uint32_t *qzeros, void *stream);
+
+/*
+ * w4a16_linear_actorder -- Y = X * W^T for an act-order grid packed by
+ * w4a16_pack_actorder: X [M][K] bf16 in natural column order is gathered by perm
+ * into the workspace, then the call proceeds as w4a16_linear (same kernels, same
+ * accuracy bound).  workspace: at least
+ * w4a16_workspace_bytes(W4A16_OP_LINEAR_ACTORDER, M, N, K, group).  Shapes and
+ * errors as w4a16_linear; perm (device) must be 16-byte aligned.
+ */
+int w4a16_linear_actorder(const void *X, const int32_t *perm, const uint32_t *qweight, const void *scales,
+                          const uint32_t *qzeros, int M, int N, int K, int group, void *Y, int y_dtype,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * w4a16_quantize -- round a weight matrix back onto the grid, keeping the grid's

@@ -21,13 +21,14 @@ import os
 
 GROUP = 128
 OUT_BF16, OUT_F32 = 0, 1
-OP_LINEAR, OP_LMHEAD = 0, 1
+OP_LINEAR, OP_LMHEAD, OP_LINEAR_ACTORDER = 0, 1, 2
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw4a16.so")
 _lib = None
 
 EXPORTED = ("w4a16_pack", "w4a16_quantize", "w4a16_linear", "w4a16_linear_batch", "w4a16_lmhead_verify",
+            "w4a16_actorder_perm", "w4a16_pack_actorder", "w4a16_linear_actorder",
             "w4a16_workspace_bytes", "w4a16_status_string", "w4a16_abi_version")
 MAX_BATCH = 8
 
@@ -58,6 +59,12 @@ def lib():
     L.w4a16_pack.restype = I
     L.w4a16_quantize.argtypes = [P, P, P, I, I, I, P, P]
     L.w4a16_quantize.restype = I
+    L.w4a16_actorder_perm.argtypes = [P, I, I, P]
+    L.w4a16_actorder_perm.restype = I
+    L.w4a16_pack_actorder.argtypes = [P, P, P, I, I, I, P, P, P]
+    L.w4a16_pack_actorder.restype = I
+    L.w4a16_linear_actorder.argtypes = [P, P, P, P, P, I, I, I, I, P, I, P, S, P]
+    L.w4a16_linear_actorder.restype = I
     L.w4a16_linear.argtypes = [P, P, P, P, I, I, I, I, P, I, P, S, P]
     L.w4a16_linear.restype = I
     L.w4a16_linear_batch.argtypes = [P, I, I, I, I, P, S, P]
@@ -138,6 +145,51 @@ def w4a16_pack(codes, zeros, group=GROUP, stream=None):
                           _ptr(qweight), _ptr(qzeros), _stream(stream))
     _check(st, "w4a16_pack")
     return qweight, qzeros
+
+
+def w4a16_actorder_perm(g_idx, group=GROUP):
+    """Host: the column permutation that makes every act-order group consecutive."""
+    import numpy as np
+    g = np.ascontiguousarray(g_idx, dtype=np.int32)
+    perm = np.zeros(g.shape[0], np.int32)
+    st = lib().w4a16_actorder_perm(g.ctypes.data_as(ctypes.c_void_p), g.shape[0], group,
+                                   perm.ctypes.data_as(ctypes.c_void_p))
+    _check(st, "w4a16_actorder_perm")
+    return perm
+
+
+def w4a16_pack_actorder(codes, zeros, perm, group=GROUP, stream=None):
+    """Pack u8 codes [N,K] (natural column order) in perm order; zeros as w4a16_pack."""
+    import torch
+    N, K = codes.shape
+    G = K // group
+    assert codes.dtype == torch.uint8 and zeros.dtype == torch.uint8 and zeros.shape == (N, G)
+    assert perm.dtype == torch.int32 and perm.shape == (K,)
+    qweight = torch.empty((N, K // 8), dtype=torch.int32, device=codes.device)
+    qzeros = torch.empty((N // 8, G), dtype=torch.int32, device=codes.device)
+    st = lib().w4a16_pack_actorder(_ptr(codes.contiguous()), _ptr(zeros.contiguous()), _ptr(perm.contiguous()),
+                                   N, K, group, _ptr(qweight), _ptr(qzeros), _stream(stream))
+    _check(st, "w4a16_pack_actorder")
+    return qweight, qzeros
+
+
+def w4a16_linear_actorder(X, perm, qweight, scales, qzeros, out_dtype=None, group=GROUP, out=None,
+                          workspace=None, stream=None):
+    """Y = X W^T for an act-order grid packed by w4a16_pack_actorder; X in natural order."""
+    import torch
+    M, K = X.shape
+    N = qweight.shape[0]
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    ydt = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    assert X.dtype == torch.bfloat16 and X.is_contiguous() and perm.dtype == torch.int32
+    Y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=X.device)
+    nbytes = w4a16_workspace_bytes(OP_LINEAR_ACTORDER, M, N, K, group)
+    ws = _workspace(workspace, X.device).get(nbytes)
+    st = lib().w4a16_linear_actorder(_ptr(X), _ptr(perm), _ptr(qweight), _ptr(scales), _ptr(qzeros), M, N, K,
+                                     group, _ptr(Y), ydt, _ptr(ws), nbytes, _stream(stream))
+    _check(st, "w4a16_linear_actorder")
+    return Y
 
 
 def w4a16_quantize(W, scales, qzeros, group=GROUP, out=None, stream=None):

@@ -35,6 +35,15 @@ size_t linear_ws(int M, int N, int K)
     return plan_tiled(M, N, K).ws_bytes;
 }
 
+// the gathered X of an act-order call sits after the workspace of the linear call,
+// and never in the zero region (a linear call that needs no workspace has base 0)
+size_t actorder_x_offset(int M, int N, int K)
+{
+    size_t base = linear_ws(M, N, K);
+    base = base > kZeroRegion ? base : kZeroRegion;
+    return (base + 255) / 256 * 256;
+}
+
 } // namespace
 
 extern "C" {
@@ -61,6 +70,8 @@ size_t w4a16_workspace_bytes(int op, int M, int N, int K, int group)
         return 0;
     if (op == W4A16_OP_LINEAR)
         return (M == 0 || N == 0) ? 0 : linear_ws(M, N, K);
+    if (op == W4A16_OP_LINEAR_ACTORDER)
+        return (M == 0 || N == 0) ? 0 : actorder_x_offset(M, N, K) + (size_t)M * K * 2;
     if (op == W4A16_OP_LMHEAD)
         return (M < 1 || M > 64 || N < 1) ? 0 : plan_skinny(M, N, K, 1).ws_bytes;
     return 0;
@@ -82,6 +93,65 @@ int w4a16_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K, int gro
     if (launch_pack(codes, zeros, N, K, K / kGroup, qweight, qzeros, (hipStream_t)stream) != hipSuccess)
         return W4A16_ERR_HIP;
     return W4A16_OK;
+}
+
+int w4a16_actorder_perm(const int32_t *g_idx, int K, int group, int32_t *perm)
+{
+    if (group != kGroup)
+        return W4A16_ERR_UNSUPPORTED;
+    if (K < group || K % group != 0 || (long long)K > kLimit)
+        return W4A16_ERR_SHAPE;
+    if (!g_idx || !perm)
+        return W4A16_ERR_NULL;
+    return actorder_perm_host(g_idx, K, group, perm) ? W4A16_OK : W4A16_ERR_SHAPE;
+}
+
+int w4a16_pack_actorder(const uint8_t *codes, const uint8_t *zeros, const int32_t *perm, int N, int K,
+                        int group, uint32_t *qweight, uint32_t *qzeros, void *stream)
+{
+    if (group != kGroup)
+        return W4A16_ERR_UNSUPPORTED;
+    const int st = check_dims(0, N, K);
+    if (st != W4A16_OK)
+        return st;
+    if (N == 0)
+        return W4A16_OK;
+    if (!codes || !zeros || !perm || !qweight || !qzeros)
+        return W4A16_ERR_NULL;
+    if (misaligned(codes) || misaligned(perm) || misaligned(qweight))
+        return W4A16_ERR_ALIGN;
+    const hipError_t e = launch_pack_perm(codes, zeros, perm, N, K, K / kGroup, qweight, qzeros,
+                                          (hipStream_t)stream);
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+int w4a16_linear_actorder(const void *X, const int32_t *perm, const uint32_t *qweight, const void *scales,
+                          const uint32_t *qzeros, int M, int N, int K, int group, void *Y, int y_dtype,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (group != kGroup || (y_dtype != W4A16_OUT_BF16 && y_dtype != W4A16_OUT_F32))
+        return W4A16_ERR_UNSUPPORTED;
+    const int st = check_dims(M, N, K);
+    if (st != W4A16_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return W4A16_OK;
+    if (!X || !perm || !workspace)
+        return W4A16_ERR_NULL;
+    if (misaligned(X) || misaligned(perm) || misaligned(workspace))
+        return W4A16_ERR_ALIGN;
+    const size_t off = actorder_x_offset(M, N, K);
+    if (workspace_bytes < off + (size_t)M * K * 2)
+        return W4A16_ERR_WORKSPACE;
+    // everything w4a16_linear checks is checked before the gather is enqueued
+    if (!qweight || !scales || !qzeros || !Y)
+        return W4A16_ERR_NULL;
+    if (misaligned(qweight) || misaligned(scales) || misaligned(qzeros) || misaligned(Y))
+        return W4A16_ERR_ALIGN;
+    void *xg = (unsigned char *)workspace + off;
+    if (launch_gather_k(X, perm, M, K, 2, xg, (hipStream_t)stream) != hipSuccess)
+        return W4A16_ERR_HIP;
+    return w4a16_linear(xg, qweight, scales, qzeros, M, N, K, group, Y, y_dtype, workspace, off, stream);
 }
 
 int w4a16_quantize(const void *W, const void *scales, const uint32_t *qzeros, int N, int K, int group,

@@ -21,6 +21,17 @@ constexpr size_t kZeroRegion = 8192;
 // ---------------------------------------------------------------- pack
 hipError_t launch_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K, int G,
                        uint32_t *qweight, uint32_t *qzeros, hipStream_t stream);
+hipError_t launch_pack_zeros(const uint8_t *zeros, int N, int G, uint32_t *qzeros, hipStream_t stream);
+
+// ---------------------------------------------------------------- GPTQ act-order
+// perm (host) from g_idx (host): false unless every group holds exactly `group` columns
+bool actorder_perm_host(const int32_t *g_idx, int K, int group, int32_t *perm);
+// codes gathered by perm and packed, zeros packed as by launch_pack (device)
+hipError_t launch_pack_perm(const uint8_t *codes, const uint8_t *zeros, const int32_t *perm, int N, int K, int G,
+                            uint32_t *qweight, uint32_t *qzeros, hipStream_t stream);
+// dst[r][j] = src[r][perm[j]] for 1- or 2-byte elements (device), K % 8 == 0
+hipError_t launch_gather_k(const void *src, const int32_t *perm, int rows, int K, int elem_bytes, void *dst,
+                           hipStream_t stream);
 
 // ---------------------------------------------------------------- re-quantization
 hipError_t launch_quantize(const uint16_t *W, const uint16_t *scales, const uint32_t *qzeros, int N, int K,

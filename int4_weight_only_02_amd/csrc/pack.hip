@@ -60,10 +60,17 @@ hipError_t launch_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
+    return launch_pack_zeros(zeros, N, G, qzeros, stream);
+}
+
+hipError_t launch_pack_zeros(const uint8_t *zeros, int N, int G, uint32_t *qzeros, hipStream_t stream)
+{
     const long long nz = (long long)(N / 8) * G;
     long long zb = (nz + 255) / 256;
     if (zb > 4096)
         zb = 4096;
+    if (zb == 0)
+        return hipSuccess;
     hipLaunchKernelGGL(pack_zeros_kernel, dim3((unsigned)zb), dim3(256), 0, stream, zeros, N, G, qzeros);
     return hipGetLastError();
 }
