@@ -392,6 +392,75 @@ def measure_requant(dev, steps, warmup, N=9728, K=2560):
             "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4), "bit_exact_sample": exact}
 
 
+def measure_actorder(dev, steps, warmup, M=16, N=9728, K=2560):
+    """One gate/up-shaped projection at M = 16 with GPTQ act-order groups
+    (w4a16_linear_actorder: gather X by the column permutation, then the ordinary
+    kernels), next to the same call on the plain grid; graph replay over rotating
+    weight copies.  The difference is the cost of act-order."""
+    import torch
+    import int4_weight_only_02_amd as w4
+    import oracle
+    rng = np.random.default_rng(4343)
+    d = synth.linear_inputs(4343, M, N, K)
+    order = rng.permutation(K)
+    g_idx = np.empty(K, np.int32)
+    g_idx[order] = np.arange(K) // 128
+    perm = torch.from_numpy(w4.w4a16_actorder_perm(g_idx)).to(dev)
+    codes = torch.from_numpy(d["codes"]).to(dev)
+    zeros = torch.from_numpy(d["zeros"]).to(dev)
+    qw, qz = w4.w4a16_pack_actorder(codes, zeros, perm)
+    X = torch.from_numpy(d["X"].view(np.int16)).to(dev).view(torch.bfloat16)
+    S = torch.from_numpy(d["scales"].view(np.int16)).to(dev).view(torch.float16)
+    nbytes = algo_bytes(M, N, K)
+    R = int(max(1, min(32, -(-CACHE_ROTATE_BYTES // nbytes))))
+    copies = [(qw, S, qz)] + [(qw.clone(), S.clone(), qz.clone()) for _ in range(R - 1)]
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = w4.Workspace(dev)
+    ws.get(w4.w4a16_workspace_bytes(w4.OP_LINEAR_ACTORDER, M, N, K))
+    # check: sampled outputs against the oracle's act-order definition
+    Yf = w4.w4a16_linear_actorder(X, perm, qw, S, qz, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    oqw, oqz = oracle.pack(d["codes"], d["zeros"])
+    cols = np.arange(0, N, max(1, N // 256))
+    sub = oracle.linear_gidx(d["X"], oqw[cols], d["scales"][cols], oracle.pack(d["codes"][cols], d["zeros"][cols])[1],
+                             g_idx) if len(cols) % 8 == 0 else None
+    err = None
+    if sub is not None:
+        got = Yf.cpu().numpy()[:, cols].astype(np.float64)
+        err = float(np.abs(got - sub).max() / np.sqrt((sub ** 2).mean()))
+
+    def timed(fn):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            fn(0)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                for r in range(R):
+                    fn(r)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for _ in range(max(1, warmup // R)):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // R)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * R)
+
+    t_act = timed(lambda r: w4.w4a16_linear_actorder(X, perm, *copies[r], out=Y, workspace=ws))
+    t_plain = timed(lambda r: w4.w4a16_linear(X, *copies[r], out=Y, workspace=ws))
+    return {"M": M, "N": N, "K": K, "copies": R, "bytes_per_call": nbytes,
+            "us_per_call_actorder": round(t_act, 3), "us_per_call_plain": round(t_plain, 3),
+            "GBps_actorder": round(nbytes / t_act / 1e3, 1), "sampled_max_err_over_rms": err}
+
+
 def calib_copy(dev, nbytes=1 << 30, reps=5):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -479,13 +548,14 @@ def main():
         return
 
     names = [HEADLINE, "single_512", "verify_block_m16", "lmhead_verify_m16", "prefill_m8192",
-             "verify_block_m16+batch", "requantize_9728x2560"]
+             "verify_block_m16+batch", "requantize_9728x2560", "actorder_gate_m16"]
     if args.only:
         names = [args.only]
     results = {}
     for key in names:
-        if key == "requantize_9728x2560":
-            results[key] = measure_requant(dev, max(64, min(args.steps, 1000)), 32)
+        if key in ("requantize_9728x2560", "actorder_gate_m16"):
+            fn = measure_requant if key == "requantize_9728x2560" else measure_actorder
+            results[key] = fn(dev, max(64, min(args.steps, 1000)), 32)
             print("[bench] %s: %s" % (key, json.dumps(results[key])), file=sys.stderr, flush=True)
             continue
         name, batched = key.split("+")[0], key.endswith("+batch")
@@ -497,7 +567,7 @@ def main():
         print("[bench] %s: %s" % (key, json.dumps(results[key])), file=sys.stderr, flush=True)
 
     head = results.get(HEADLINE) or results[names[0]]
-    if "per_launch" not in head:  # --only requantize_9728x2560
+    if "per_launch" not in head:  # --only requantize_9728x2560 / actorder_gate_m16
         print(json.dumps({"workloads": results}))
         return
     head_name = HEADLINE if HEADLINE in results else names[0]
