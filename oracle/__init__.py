@@ -15,6 +15,7 @@ Functions (numpy in, numpy out):
   argmax_accept(Y f64[M,N], draft i32[M])       -> (argmax i32[M], gap f64[M], L int)
   quantize(W bf16-bits u16[N,K], scales f16-bits u16[N,G], zeros u8[N,G]) -> codes u8[N,K]
   linear_gidx(X, qweight, scales, qzeros, g_idx i32[K]) -> Y f64[M,N] (GPTQ act-order groups)
+  swa(Q u16[M,Hq,D], K u16[T,Hkv,D], Vt u16[Hkv,D,T], window) -> O f64[M,Hq,D] (sliding-window attention)
   bf16_to_f64 / f16_to_f64 (bit patterns -> exact values)
 """
 import ctypes
@@ -53,6 +54,7 @@ def _bind(path):
     lib.oracle_argmax_accept.argtypes = [P, I, I, P, P, P, P]
     lib.oracle_quantize.argtypes = [P, P, P, I, I, I, P]
     lib.oracle_linear_gidx.argtypes = [P, P, P, P, P, I, I, I, I, P]
+    lib.oracle_swa.argtypes = [P, P, P, I, I, I, I, I, I, P]
     lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_f64.restype = ctypes.c_double
     lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
@@ -203,3 +205,16 @@ def linear_gidx(X, qweight, scales, qzeros, g_idx, group=GROUP):
     Y = np.zeros((M, N), np.float64)
     _load().oracle_linear_gidx(px, pw, ps, pz, pg, M, N, K, group, Y.ctypes.data_as(ctypes.c_void_p))
     return Y
+
+
+def swa(Q, K, Vt, window):
+    """Causal sliding-window attention of the last M tokens (oracle_swa)."""
+    Q, pq = _c(Q, np.uint16)
+    K, pk = _c(K, np.uint16)
+    Vt, pv = _c(Vt, np.uint16)
+    M, Hq, D = Q.shape
+    T, Hkv, D2 = K.shape
+    assert D2 == D and Vt.shape == (Hkv, D, T) and Hq % Hkv == 0 and M <= T and window >= 1
+    O = np.zeros((M, Hq, D), np.float64)
+    _load().oracle_swa(pq, pk, pv, M, T, Hq, Hkv, D, window, O.ctypes.data_as(ctypes.c_void_p))
+    return O

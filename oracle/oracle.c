@@ -307,6 +307,57 @@ void oracle_quantize(const uint16_t *W, const uint16_t *scales, const uint8_t *z
         }
 }
 
+/* ---- sliding-window attention of a query block (the drafter) ------------- */
+
+/* The drafter attends over a sliding window of the context (the pages' long-context
+ * lever: a window of 1024 or 2048 tokens at 8192 context).  The pages give no kernel
+ * or formula; the reading is standard scaled-dot-product attention, causal, over a
+ * window, with grouped key/value heads:
+ *   queries: the last M tokens of a context of T tokens, query i at position
+ *            p_i = T - M + i; head h reads key/value head h / (Hq / Hkv);
+ *   keys:    j with p_i - window < j <= p_i (and j >= 0);
+ *   O[i,h,:] = sum_j softmax_j(Q[i,h,:] . K[j,kv,:] / sqrt(D)) V[j,kv,:].
+ * Layouts: Q [M][Hq][D], K [T][Hkv][D] (token-major), V transposed [Hkv][D][T],
+ * all bfloat16 bits; O f64 [M][Hq][D].  fp64 throughout, the softmax shifted by its
+ * maximum before the exponentials (exact in real arithmetic). */
+void oracle_swa(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt, int M, int T, int Hq, int Hkv, int D,
+                int window, double *O)
+{
+    int grp = Hq / Hkv;
+    double scale = 1.0 / sqrt((double)D);
+#pragma omp parallel for schedule(static) collapse(2)
+    for (int i = 0; i < M; ++i)
+        for (int h = 0; h < Hq; ++h) {
+            int kv = h / grp;
+            int p = T - M + i;
+            int j0 = p - window + 1 > 0 ? p - window + 1 : 0;
+            int n = p - j0 + 1;
+            double *sc = (double *)malloc(sizeof(double) * (size_t)n);
+            double mx = -INFINITY;
+            for (int j = j0; j <= p; ++j) {
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d)
+                    dot += oracle_bf16_to_f64(Q[((size_t)i * Hq + h) * D + d]) *
+                           oracle_bf16_to_f64(K[((size_t)j * Hkv + kv) * D + d]);
+                sc[j - j0] = dot * scale;
+                if (sc[j - j0] > mx)
+                    mx = sc[j - j0];
+            }
+            double sum = 0.0;
+            for (int t = 0; t < n; ++t) {
+                sc[t] = exp(sc[t] - mx);
+                sum += sc[t];
+            }
+            for (int d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (int j = j0; j <= p; ++j)
+                    acc += sc[j - j0] * oracle_bf16_to_f64(Vt[((size_t)kv * D + d) * T + j]);
+                O[((size_t)i * Hq + h) * D + d] = acc / sum;
+            }
+            free(sc);
+        }
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

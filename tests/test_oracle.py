@@ -18,6 +18,9 @@ Each pin is chosen so that a plausible mistake in the oracle fails it:
   act-order        GPTQ column groups (g_idx): sequential g_idx is the plain oracle bit
                    for bit; one-hot X picks (q - z[g_idx[k]]) * s[g_idx[k]]; permuting
                    the columns (X, codes and g_idx together) leaves dyadic Y unchanged
+  attention        a window of one gives V of the query's own position exactly; equal
+                   keys give the window mean of V; an independent numpy formulation
+                   (masked score matrix, library softmax) agrees on small shapes
   re-quantization  hand-worked round-to-grid cases (ties to even, clamping, overflow);
                    on-grid weights come back as their own codes; agreement with exact
                    rational rounding everywhere, ties and their neighbours included
@@ -485,3 +488,65 @@ def test_gidx_column_permutation_invariance():
     # and a grouping other than the sequential one changes the result
     Y3 = oracle.linear(X, qw, scales, qz)
     assert not (Y1 == Y3).all()
+
+
+# ------------------------------------------------------------------ sliding-window attention
+
+
+def _bf16_bits(a):
+    return _bf16_rne(np.asarray(a, np.float64))
+
+
+def _bits_to_f64(b):
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _swa_inputs(rng, M, T, Hq, Hkv, D):
+    Q = _bf16_bits(rng.normal(0, 1, (M, Hq, D)))
+    K = _bf16_bits(rng.normal(0, 1, (T, Hkv, D)))
+    Vt = _bf16_bits(rng.normal(0, 1, (Hkv, D, T)))
+    return Q, K, Vt
+
+
+def test_swa_window_of_one_returns_own_value():
+    rng = np.random.default_rng(0)
+    M, T, Hq, Hkv, D = 4, 40, 4, 2, 16
+    Q, K, Vt = _swa_inputs(rng, M, T, Hq, Hkv, D)
+    O = oracle.swa(Q, K, Vt, 1)
+    V = _bits_to_f64(Vt)
+    for i in range(M):
+        for h in range(Hq):
+            assert (O[i, h] == V[h // 2, :, T - M + i]).all()
+
+
+def test_swa_equal_keys_give_the_window_mean():
+    rng = np.random.default_rng(1)
+    M, T, Hq, Hkv, D, W = 3, 50, 2, 1, 8, 7
+    Q, K, Vt = _swa_inputs(rng, M, T, Hq, Hkv, D)
+    K[:] = K[0]  # every key the same: uniform weights over the window
+    O = oracle.swa(Q, K, Vt, W)
+    V = _bits_to_f64(Vt)
+    for i in range(M):
+        p = T - M + i
+        want = V[0, :, p - W + 1:p + 1].mean(axis=1)
+        assert np.abs(O[i, 0] - want).max() < 1e-12
+
+
+@pytest.mark.parametrize("W", [1, 5, 64, 1000])
+def test_swa_matches_masked_softmax_formulation(W):
+    rng = np.random.default_rng(2 + W)
+    M, T, Hq, Hkv, D = 5, 70, 6, 2, 32
+    Q, K, Vt = _swa_inputs(rng, M, T, Hq, Hkv, D)
+    O = oracle.swa(Q, K, Vt, W)
+    q, k, v = _bits_to_f64(Q), _bits_to_f64(K), _bits_to_f64(Vt)
+    pos = np.arange(T - M, T)
+    j = np.arange(T)
+    mask = (j[None, :] <= pos[:, None]) & (j[None, :] > pos[:, None] - W)  # [M, T]
+    for h in range(Hq):
+        kv = h // (Hq // Hkv)
+        s = q[:, h, :] @ k[:, kv, :].T / np.sqrt(D)  # [M, T]
+        s = np.where(mask, s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        want = p @ v[kv].T  # [M, D]
+        assert np.abs(O[:, h, :] - want).max() < 1e-12

@@ -39,6 +39,11 @@ MUTANTS = [
     ("gidx_ignored", "int g = g_idx[k];", "int g = k / group;"),
     ("gidx_zero_from_k", "w[k] = (double)(q_at(qweight, K, n, k) - z_at(qzeros, G, n, g)) *\n                       oracle_f16_to_f64(scales[(size_t)n * G + g]);",
      "w[k] = (double)(q_at(qweight, K, n, k) - z_at(qzeros, G, n, k / group)) *\n                       oracle_f16_to_f64(scales[(size_t)n * G + g]);"),
+    ("swa_unscaled", "double scale = 1.0 / sqrt((double)D);", "double scale = 1.0;"),
+    ("swa_window_off_by_one", "int j0 = p - window + 1 > 0 ? p - window + 1 : 0;", "int j0 = p - window > 0 ? p - window : 0;"),
+    ("swa_kv_head_modulo", "int kv = h / grp;", "int kv = h % Hkv;"),
+    ("swa_v_untransposed", "acc += sc[j - j0] * oracle_bf16_to_f64(Vt[((size_t)kv * D + d) * T + j]);",
+     "acc += sc[j - j0] * oracle_bf16_to_f64(Vt[((size_t)j * Hkv + kv) * D + d]);"),
     ("quantize_ties_away", "if (d > 0.0 || (d == 0.0 && fmod(r, 2.0) != 0.0))", "if (d >= 0.0)"),
     ("quantize_round_after_zero", "q = round_quotient(w, s) + z;", "q = round_quotient(w + z * s, s);"),
     ("quantize_truncates", "if (d > 0.0 || (d == 0.0 && fmod(r, 2.0) != 0.0))\n        r += 1.0;",
@@ -60,6 +65,9 @@ PIN_TESTS = [
     lambda: pins.test_gidx_sequential_is_the_plain_oracle(),
     lambda: pins.test_gidx_onehot_picks_its_group(),
     lambda: pins.test_gidx_column_permutation_invariance(),
+    lambda: pins.test_swa_window_of_one_returns_own_value(),
+    lambda: pins.test_swa_equal_keys_give_the_window_mean(),
+    lambda: pins.test_swa_matches_masked_softmax_formulation(5),
     lambda: pins.test_quantize_worked_by_hand(),
     lambda: pins.test_quantize_returns_on_grid_weights_to_their_codes(0),
     lambda: pins.test_quantize_matches_exact_rational_rounding(),
