@@ -124,6 +124,32 @@ int w4a16_linear_actorder(const void *X, const int32_t *perm, const uint32_t *qw
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * w4a16_swa_attention -- causal sliding-window attention of a block of M query tokens
+ * at the end of a context of T tokens: the drafter's long-context lever (Pith review,
+ * Assumptions & free parameters: an SWA window of 1024 tokens on the leaderboard, 1024
+ * or 2048 in the window study; the pages' Figure 1: inputs of up to 8192 tokens).  The
+ * pages give no formula; reading:
+ *   query i (0 <= i < M) sits at position p_i = T - M + i; head h reads key/value
+ *   head h / (Hq / Hkv); it attends to keys p_i - window < j <= p_i (j >= 0):
+ *   O[i,h,:] = sum_j softmax_j(Q[i,h,:] . K[j,kv,:] / sqrt(D)) V[j,kv,:]
+ * fp32 scores and sums; the softmax weights enter the value product as bf16.
+ *   Q   [M][Hq][D]         bf16 (device)
+ *   K   [T][Hkv][D]        bf16 key cache, token-major (device)
+ *   Vt  [Hkv][D][t_stride] bf16 value cache, transposed: row (kv, d) holds the values
+ *                          of dimension d for tokens 0 .. T-1 (device); t_stride >= T,
+ *                          a multiple of 8; entries past T are never used
+ *   O   [M][Hq][D]         bf16 or fp32 (o_dtype as y_dtype of w4a16_linear)
+ *   workspace              at least w4a16_swa_workspace_bytes(M, T, Hq, Hkv, window)
+ * Shapes: D == 128 (else W4A16_ERR_UNSUPPORTED), 1 <= M <= 16, M <= T, Hq a multiple
+ * of Hkv with Hq / Hkv <= 16, window >= 1; element counts at most 2^31 - 256.
+ * Errors: W4A16_ERR_SHAPE, _UNSUPPORTED, _NULL, _ALIGN (16 bytes), _WORKSPACE, _HIP.
+ */
+int w4a16_swa_attention(const void *Q, const void *K, const void *Vt, int M, int T, int Hq, int Hkv, int D,
+                        int window, int t_stride, void *O, int o_dtype, void *workspace, size_t workspace_bytes,
+                        void *stream);
+size_t w4a16_swa_workspace_bytes(int M, int T, int Hq, int Hkv, int window);
+
+/*
  * w4a16_quantize -- round a weight matrix back onto the grid, keeping the grid's
  * per-group scales and zero-points: the re-packing step of the pages'
  * distillation, which keeps the INT4 grid's scales fixed so that the packed format

@@ -29,6 +29,7 @@ _lib = None
 
 EXPORTED = ("w4a16_pack", "w4a16_quantize", "w4a16_linear", "w4a16_linear_batch", "w4a16_lmhead_verify",
             "w4a16_actorder_perm", "w4a16_pack_actorder", "w4a16_linear_actorder",
+            "w4a16_swa_attention", "w4a16_swa_workspace_bytes",
             "w4a16_workspace_bytes", "w4a16_status_string", "w4a16_abi_version")
 MAX_BATCH = 8
 
@@ -59,6 +60,10 @@ def lib():
     L.w4a16_pack.restype = I
     L.w4a16_quantize.argtypes = [P, P, P, I, I, I, P, P]
     L.w4a16_quantize.restype = I
+    L.w4a16_swa_attention.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, P, S, P]
+    L.w4a16_swa_attention.restype = I
+    L.w4a16_swa_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.w4a16_swa_workspace_bytes.restype = S
     L.w4a16_actorder_perm.argtypes = [P, I, I, P]
     L.w4a16_actorder_perm.restype = I
     L.w4a16_pack_actorder.argtypes = [P, P, P, I, I, I, P, P, P]
@@ -190,6 +195,27 @@ def w4a16_linear_actorder(X, perm, qweight, scales, qzeros, out_dtype=None, grou
                                      group, _ptr(Y), ydt, _ptr(ws), nbytes, _stream(stream))
     _check(st, "w4a16_linear_actorder")
     return Y
+
+
+def w4a16_swa_attention(Q, K, Vt, T, window, out_dtype=None, out=None, workspace=None, stream=None):
+    """Causal sliding-window attention of Q [M,Hq,128] over K [T_alloc,Hkv,128] and the
+    transposed values Vt [Hkv,128,t_stride] (the first T tokens are the context)."""
+    import torch
+    M, Hq, D = Q.shape
+    Hkv = K.shape[1]
+    t_stride = Vt.shape[2]
+    assert Q.dtype == K.dtype == Vt.dtype == torch.bfloat16
+    assert Q.is_contiguous() and K.is_contiguous() and Vt.is_contiguous() and K.shape[0] >= T
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    odt = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    O = out if out is not None else torch.empty((M, Hq, D), dtype=out_dtype, device=Q.device)
+    nbytes = lib().w4a16_swa_workspace_bytes(M, T, Hq, Hkv, window)
+    ws = _workspace(workspace, Q.device).get(nbytes)
+    st = lib().w4a16_swa_attention(_ptr(Q), _ptr(K), _ptr(Vt), M, T, Hq, Hkv, D, window, t_stride, _ptr(O), odt,
+                                   _ptr(ws), nbytes, _stream(stream))
+    _check(st, "w4a16_swa_attention")
+    return O
 
 
 def w4a16_quantize(W, scales, qzeros, group=GROUP, out=None, stream=None):

@@ -154,6 +154,58 @@ int w4a16_linear_actorder(const void *X, const int32_t *perm, const uint32_t *qw
     return w4a16_linear(xg, qweight, scales, qzeros, M, N, K, group, Y, y_dtype, workspace, off, stream);
 }
 
+static int swa_check(int M, int T, int Hq, int Hkv, int D, int window, int t_stride)
+{
+    if (D != 128)
+        return W4A16_ERR_UNSUPPORTED;
+    if (M < 1 || M > 16 || T < M || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || Hq / Hkv > 16 || window < 1 ||
+        t_stride < T || t_stride % 8 != 0)
+        return W4A16_ERR_SHAPE;
+    if ((long long)T * Hkv * D > kLimit || (long long)Hkv * D * t_stride > kLimit || (long long)M * Hq * D > kLimit)
+        return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+
+size_t w4a16_swa_workspace_bytes(int M, int T, int Hq, int Hkv, int window)
+{
+    if (swa_check(M, T, Hq, Hkv, 128, window, (T + 7) / 8 * 8) != W4A16_OK)
+        return 0;
+    return plan_swa(M, T, Hq, Hkv, window).ws_bytes;
+}
+
+int w4a16_swa_attention(const void *Q, const void *K, const void *Vt, int M, int T, int Hq, int Hkv, int D,
+                        int window, int t_stride, void *O, int o_dtype, void *workspace, size_t workspace_bytes,
+                        void *stream)
+{
+    if (o_dtype != W4A16_OUT_BF16 && o_dtype != W4A16_OUT_F32)
+        return W4A16_ERR_UNSUPPORTED;
+    const int st = swa_check(M, T, Hq, Hkv, D, window, t_stride);
+    if (st != W4A16_OK)
+        return st;
+    if (!Q || !K || !Vt || !O || !workspace)
+        return W4A16_ERR_NULL;
+    if (misaligned(Q) || misaligned(K) || misaligned(Vt) || misaligned(O) || misaligned(workspace))
+        return W4A16_ERR_ALIGN;
+    const SwaPlan p = plan_swa(M, T, Hq, Hkv, window);
+    if (workspace_bytes < p.ws_bytes)
+        return W4A16_ERR_WORKSPACE;
+    SwaArgs a{};
+    a.Q = (const uint16_t *)Q;
+    a.K = (const uint16_t *)K;
+    a.Vt = (const uint16_t *)Vt;
+    a.M = M;
+    a.T = T;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.window = window;
+    a.t_stride = t_stride;
+    a.scale = 0.08838834764831845f; // 1 / sqrt(128)
+    a.O = O;
+    a.o_f32 = o_dtype == W4A16_OUT_F32;
+    const hipError_t e = launch_swa(a, p, (unsigned char *)workspace, (hipStream_t)stream);
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
 int w4a16_quantize(const void *W, const void *scales, const uint32_t *qzeros, int N, int K, int group,
                    uint32_t *qweight, void *stream)
 {

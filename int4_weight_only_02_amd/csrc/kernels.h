@@ -33,6 +33,24 @@ hipError_t launch_pack_perm(const uint8_t *codes, const uint8_t *zeros, const in
 hipError_t launch_gather_k(const void *src, const int32_t *perm, int rows, int K, int elem_bytes, void *dst,
                            hipStream_t stream);
 
+// ---------------------------------------------------------------- sliding-window attention
+struct SwaArgs {
+    const uint16_t *Q, *K, *Vt; // bf16: [M][Hq][128], [T][Hkv][128], [Hkv][128][t_stride]
+    int M, T, Hq, Hkv, window;
+    int t_stride;               // row length of V^T (>= T, a multiple of 8)
+    float scale;                // 1 / sqrt(128)
+    void *O;                    // [M][Hq][128], bf16 or fp32
+    int o_f32;
+    int j_lo;                   // first key any query sees
+    float *ml, *part;           // workspace: per (chunk, head, query) (max, sum) and O~
+};
+struct SwaPlan {
+    int j_lo, chunks;
+    size_t ml_off, part_off, ws_bytes;
+};
+SwaPlan plan_swa(int M, int T, int Hq, int Hkv, int window);
+hipError_t launch_swa(SwaArgs a, const SwaPlan &p, unsigned char *ws, hipStream_t stream);
+
 // ---------------------------------------------------------------- re-quantization
 hipError_t launch_quantize(const uint16_t *W, const uint16_t *scales, const uint32_t *qzeros, int N, int K,
                            uint32_t *qweight, hipStream_t stream);

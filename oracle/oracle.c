@@ -309,10 +309,11 @@ void oracle_quantize(const uint16_t *W, const uint16_t *scales, const uint8_t *z
 
 /* ---- sliding-window attention of a query block (the drafter) ------------- */
 
-/* The drafter attends over a sliding window of the context (the pages' long-context
- * lever: a window of 1024 or 2048 tokens at 8192 context).  The pages give no kernel
- * or formula; the reading is standard scaled-dot-product attention, causal, over a
- * window, with grouped key/value heads:
+/* The drafter attends over a sliding window of the context (Pith review, Assumptions
+ * & free parameters: an SWA window of 1024 tokens on the leaderboard, 1024 or 2048 in
+ * the window study; inputs of up to 8192 tokens in the pages' Figure 1).  The pages
+ * give no kernel or formula; the reading is standard scaled-dot-product attention,
+ * causal, over a window, with grouped key/value heads:
  *   queries: the last M tokens of a context of T tokens, query i at position
  *            p_i = T - M + i; head h reads key/value head h / (Hq / Hkv);
  *   keys:    j with p_i - window < j <= p_i (and j >= 0);
