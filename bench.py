@@ -461,6 +461,64 @@ def measure_actorder(dev, steps, warmup, M=16, N=9728, K=2560):
             "GBps_actorder": round(nbytes / t_act / 1e3, 1), "sampled_max_err_over_rms": err}
 
 
+def measure_swa(dev, steps, warmup, M=16, T=8192, Hq=32, Hkv=8, window=1024):
+    """The drafter's sliding-window attention for one verify block: M = 16 queries at
+    the end of an 8192-token context, 32 query heads over 8 key/value heads of 128,
+    window 1024 (the pages' leaderboard setting) and 2048.  Algorithmic bytes: the keys
+    and values of the union of the windows, Q and O (bf16)."""
+    import torch
+    import int4_weight_only_02_amd as w4
+    import oracle
+    D = 128
+    rng = np.random.default_rng(5151)
+    bits = lambda a: synth.f32_to_bf16_bits(np.asarray(a, np.float32))
+    Q = bits(rng.normal(0, 1, (M, Hq, D)))
+    K = bits(rng.normal(0, 1, (T, Hkv, D)))
+    Vt = bits(rng.normal(0, 1, (Hkv, D, T)))
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    out = {}
+    for W in (window, 2 * window):
+        nkeys = min(T, W + M - 1)
+        nbytes = 2 * nkeys * Hkv * D * 2 + 2 * M * Hq * D * 2
+        R = int(max(1, min(32, -(-CACHE_ROTATE_BYTES // (2 * T * Hkv * D * 2)))))
+        caches = [(t(K), t(Vt)) for _ in range(R)]
+        Qd = t(Q)
+        O = torch.empty((M, Hq, D), dtype=torch.bfloat16, device=dev)
+        ws = w4.Workspace(dev)
+        Of = w4.w4a16_swa_attention(Qd, *caches[0], T, W, out_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        Oo = oracle.swa(Q, K, Vt, W)
+        err = float(np.abs(Of.cpu().numpy() - Oo).max() / np.sqrt((Oo ** 2).mean()))
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            w4.w4a16_swa_attention(Qd, *caches[0], T, W, out=O, workspace=ws)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                for r in range(R):
+                    w4.w4a16_swa_attention(Qd, *caches[r], T, W, out=O, workspace=ws)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for _ in range(max(1, warmup // R)):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // R)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * R)
+        out["window_%d" % W] = {"us_per_call": round(us, 3), "bytes_per_call": nbytes,
+                                "GBps": round(nbytes / us / 1e3, 1), "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                                "max_err_over_rms": err, "copies": R}
+    out.update({"M": M, "T": T, "Hq": Hq, "Hkv": Hkv, "D": D})
+    return out
+
+
 def calib_copy(dev, nbytes=1 << 30, reps=5):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     import torch
@@ -548,13 +606,14 @@ def main():
         return
 
     names = [HEADLINE, "single_512", "verify_block_m16", "lmhead_verify_m16", "prefill_m8192",
-             "verify_block_m16+batch", "requantize_9728x2560", "actorder_gate_m16"]
+             "verify_block_m16+batch", "requantize_9728x2560", "actorder_gate_m16", "swa_verify_m16_t8192"]
     if args.only:
         names = [args.only]
     results = {}
     for key in names:
-        if key in ("requantize_9728x2560", "actorder_gate_m16"):
-            fn = measure_requant if key == "requantize_9728x2560" else measure_actorder
+        if key in ("requantize_9728x2560", "actorder_gate_m16", "swa_verify_m16_t8192"):
+            fn = {"requantize_9728x2560": measure_requant, "actorder_gate_m16": measure_actorder,
+                  "swa_verify_m16_t8192": measure_swa}[key]
             results[key] = fn(dev, max(64, min(args.steps, 1000)), 32)
             print("[bench] %s: %s" % (key, json.dumps(results[key])), file=sys.stderr, flush=True)
             continue
