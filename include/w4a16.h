@@ -141,7 +141,7 @@ int w4a16_linear_actorder(const void *X, const int32_t *perm, const uint32_t *qw
  *   O   [M][Hq][D]         bf16 or fp32 (o_dtype as y_dtype of w4a16_linear)
  *   workspace              at least w4a16_swa_workspace_bytes(M, T, Hq, Hkv, window)
  * Shapes: D == 128 (else W4A16_ERR_UNSUPPORTED), 1 <= M <= 16, M <= T, Hq a multiple
- * of Hkv with Hq / Hkv <= 16, window >= 1; element counts at most 2^31 - 256.
+ * of Hkv with Hq / Hkv <= 16, 1 <= window <= 65536; element counts at most 2^31 - 256.
  * Errors: W4A16_ERR_SHAPE, _UNSUPPORTED, _NULL, _ALIGN (16 bytes), _WORKSPACE, _HIP.
  */
 int w4a16_swa_attention(const void *Q, const void *K, const void *Vt, int M, int T, int Hq, int Hkv, int D,

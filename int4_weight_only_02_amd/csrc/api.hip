@@ -159,7 +159,7 @@ static int swa_check(int M, int T, int Hq, int Hkv, int D, int window, int t_str
     if (D != 128)
         return W4A16_ERR_UNSUPPORTED;
     if (M < 1 || M > 16 || T < M || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || Hq / Hkv > 16 || window < 1 ||
-        t_stride < T || t_stride % 8 != 0)
+        window > 65536 || t_stride < T || t_stride % 8 != 0)
         return W4A16_ERR_SHAPE;
     if ((long long)T * Hkv * D > kLimit || (long long)Hkv * D * t_stride > kLimit || (long long)M * Hq * D > kLimit)
         return W4A16_ERR_SHAPE;

@@ -35,6 +35,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t b
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// 16 bytes per lane from global memory (offset voff of r) into LDS at dst + 16 * lane
+// (dst the same for the whole wave)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned char *dst, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -60,6 +67,27 @@ __global__ __launch_bounds__(1024) void swa_partial_kernel(SwaArgs a)
     const __amdgpu_buffer_rsrc_t rk = rsrc(a.K, (uint32_t)((size_t)a.T * a.Hkv * kD * 2));
     const __amdgpu_buffer_rsrc_t rv = rsrc(a.Vt, (uint32_t)((size_t)a.Hkv * kD * a.t_stride * 2));
 
+    // The chunk's keys and values, shared by the group's waves, arrive in LDS by DMA:
+    //   Kl: 128 keys x 16 units of 16 bytes (8 d each), unit c of key k at c ^ (k & 15)
+    //   Vl: 128 d    x 16 units (8 keys each),          unit c of row d at c ^ (d & 15)
+    // so that the 16 lanes of a fragment read hit 16 different units.
+    __shared__ __align__(16) unsigned char Kl[kChunk * kD * 2];
+    __shared__ __align__(16) unsigned char Vl[kD * kChunk * 2];
+    const int nwaves = blockDim.x >> 6;
+    for (int ins = wave; ins < 2 * (kChunk * kD * 2 / 1024); ins += nwaves) {
+        const int kv_part = ins >= kChunk * kD * 2 / 1024; // 0: keys, 1: values
+        const int slot = (ins - kv_part * (kChunk * kD * 2 / 1024)) * 64 + lane; // 16-byte slot
+        const int row = slot >> 4, unit = (slot & 15) ^ (row & 15);
+        if (!kv_part) {
+            const int j = j0 + row;
+            const uint32_t off = j < a.T ? (uint32_t)((j * a.Hkv + kv) * kD + 8 * unit) * 2u : kOob;
+            dma16(rk, Kl + (slot - lane) * 16, off);
+        } else {
+            const uint32_t off = (uint32_t)((kv * kD + row) * a.t_stride + j0 + 8 * unit) * 2u;
+            dma16(rv, Vl + (slot - lane) * 16, off);
+        }
+    }
+
     // Q^T as the B operand: lane (col = query, h4) holds d = 32 s + 8 h4 .. +7
     u32x4_t qf[4];
     const uint32_t qoff = col < a.M ? (uint32_t)((col * a.Hq + head) * kD + 8 * h4) * 2u : kOob;
@@ -69,16 +97,17 @@ __global__ __launch_bounds__(1024) void swa_partial_kernel(SwaArgs a)
 
     // S^T for the chunk: key tile t, lane (col = key 16 t + col, h4) as the A operand;
     // result lane l: keys 16 t + 4 h4 + r of query col
+    __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): this wave's DMA and Q have landed
+    __syncthreads();                    // and every wave's DMA
     constexpr int kTiles = kChunk / 16;
     f32x4_t st[kTiles];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-        const int j = j0 + 16 * t + col;
-        const uint32_t koff = j < a.T ? (uint32_t)((j * a.Hkv + kv) * kD + 8 * h4) * 2u : kOob;
+        const int key = 16 * t + col;
         u32x4_t kf[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            kf[s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 64u * s, 0));
+            kf[s] = *(const u32x4_t *)(Kl + (key * 16 + ((4 * s + h4) ^ (key & 15))) * 16);
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -133,15 +162,15 @@ __global__ __launch_bounds__(1024) void swa_partial_kernel(SwaArgs a)
             const int j = (e < 2 ? ja : jb) + 2 * (e & 1);
             keep[e] = (j < a.T ? 0x0000FFFFu : 0u) | (j + 1 < a.T ? 0xFFFF0000u : 0u);
         }
+        // keys ja - j0 = 32 u + 4 h4 (.. +3) and + 16: half of unit 4 u + h4 / 2 and of unit
+        // 4 u + 2 + h4 / 2 of row d
+        const int ua = 4 * u + (h4 >> 1), ub = ua + 2, half = (h4 & 1) * 8;
 #pragma unroll
         for (int dt = 0; dt < kD / 16; ++dt) {
             const int d = dt * 16 + col;
-            const uint32_t vrow = (uint32_t)((kv * kD + d) * a.t_stride);
             typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
-            const u32x2_t va = __builtin_bit_cast(
-                u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, (vrow + (uint32_t)ja) * 2u, 0, 0));
-            const u32x2_t vb = __builtin_bit_cast(
-                u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, (vrow + (uint32_t)jb) * 2u, 0, 0));
+            const u32x2_t va = *(const u32x2_t *)(Vl + (d * 16 + (ua ^ (d & 15))) * 16 + half);
+            const u32x2_t vb = *(const u32x2_t *)(Vl + (d * 16 + (ub ^ (d & 15))) * 16 + half);
             o[dt] = mfma(pf, u32x4_t{va.x & keep[0], va.y & keep[1], vb.x & keep[2], vb.y & keep[3]}, o[dt]);
         }
     }
@@ -159,22 +188,56 @@ __global__ __launch_bounds__(1024) void swa_partial_kernel(SwaArgs a)
             a.part[(slot + 4 * h4 + r) * kD + dt * 16 + col] = o[dt][r];
 }
 
-// O[i][h][:] from the chunks in order; one workgroup of kD threads per (i, h)
+// O[i][h][:] from the chunks in order; one workgroup of kD threads per (i, h).  The
+// chunks' (m, l) pairs go through LDS once (all loads in flight together), then each
+// thread adds its column of the chunk partials in chunk order, eight loads at a time.
+constexpr int kCombineMax = 1024; // chunks per query handled by one pass of the LDS table
+
 __global__ __launch_bounds__(kD) void swa_combine_kernel(SwaArgs a, int chunks)
 {
+    __shared__ float sm[kCombineMax], sw[kCombineMax];
+    __shared__ float red[kD / 64];
     const int i = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-    float m = -INFINITY;
-    for (int c = 0; c < chunks; ++c)
-        m = fmaxf(m, a.ml[(((size_t)c * a.Hq + h) * 16 + i) * 2]);
+    const int n = chunks < kCombineMax ? chunks : kCombineMax;
+    float mx = -INFINITY;
+    for (int c = d; c < n; c += kD) {
+        sm[c] = a.ml[(((size_t)c * a.Hq + h) * 16 + i) * 2];
+        mx = fmaxf(mx, sm[c]);
+    }
+    // workgroup max: within each wave, then across the two waves
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((d & 63) == 0)
+        red[d >> 6] = mx;
+    __syncthreads();
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < kD / 64; ++w)
+        m = fmaxf(m, red[w]);
+    for (int c = d; c < n; c += kD) // weight of each chunk (0 for chunks without keys)
+        sw[c] = sm[c] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[c] - m);
+    __syncthreads();
     float num = 0.f, den = 0.f;
-    for (int c = 0; c < chunks; ++c) {
+    int c = 0;
+    for (; c + 8 <= n; c += 8) {
+        float pv[8], lv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const size_t slot = ((size_t)(c + u) * a.Hq + h) * 16 + i;
+            pv[u] = a.part[slot * kD + d];
+            lv[u] = a.ml[slot * 2 + 1];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            num += sw[c + u] * pv[u];
+            den += sw[c + u] * lv[u];
+        }
+    }
+    for (; c < n; ++c) {
         const size_t slot = ((size_t)c * a.Hq + h) * 16 + i;
-        const float mc = a.ml[slot * 2];
-        if (mc == -INFINITY)
-            continue; // no key of this query in the chunk
-        const float w = __builtin_amdgcn_exp2f(mc - m);
-        den += w * a.ml[slot * 2 + 1];
-        num += w * a.part[slot * kD + d];
+        num += sw[c] * a.part[slot * kD + d];
+        den += sw[c] * a.ml[slot * 2 + 1];
     }
     const float y = num / den;
     const size_t o = ((size_t)i * a.Hq + h) * kD + d;
