@@ -44,7 +44,7 @@ def _run(dev, Q, K, Vp, T, window, dtype=torch.float32):
 
 @pytest.mark.parametrize("M,T,Hq,Hkv,W", [(16, 8192, 32, 8, 1024), (16, 8192, 32, 8, 2048), (1, 300, 4, 1, 64),
                                           (5, 77, 8, 2, 1000), (16, 16, 2, 2, 4), (3, 2049, 16, 1, 2048),
-                                          (16, 1000, 8, 8, 1)])
+                                          (16, 1000, 8, 8, 1), (2, 5000, 4, 2, 3500), (4, 8192, 2, 1, 6000)])
 def test_swa_matches_oracle(dev, M, T, Hq, Hkv, W):
     print("swa", M, T, Hq, Hkv, W, flush=True)
     Q, K, Vt, Vp = _inputs(M * 7 + T + W, M, T, Hq, Hkv)
