@@ -16,6 +16,8 @@ Functions (numpy in, numpy out):
   quantize(W bf16-bits u16[N,K], scales f16-bits u16[N,G], zeros u8[N,G]) -> codes u8[N,K]
   linear_gidx(X, qweight, scales, qzeros, g_idx i32[K]) -> Y f64[M,N] (GPTQ act-order groups)
   swa(Q u16[M,Hq,D], K u16[T,Hkv,D], Vt u16[Hkv,D,T], window) -> O f64[M,Hq,D] (sliding-window attention)
+  silu_mul(G f64, U f64)                        -> silu(G) * U elementwise (oracle_silu_mul)
+  gated(X, gate, up)                            -> silu(X Wg^T) * (X Wu^T) f64[M,N]; gate/up = (qweight, scales, qzeros)
   bf16_to_f64 / f16_to_f64 (bit patterns -> exact values)
 """
 import ctypes
@@ -55,6 +57,7 @@ def _bind(path):
     lib.oracle_quantize.argtypes = [P, P, P, I, I, I, P]
     lib.oracle_linear_gidx.argtypes = [P, P, P, P, P, I, I, I, I, P]
     lib.oracle_swa.argtypes = [P, P, P, I, I, I, I, I, I, P]
+    lib.oracle_silu_mul.argtypes = [P, P, ctypes.c_longlong, P]
     lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_f64.restype = ctypes.c_double
     lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
@@ -218,3 +221,18 @@ def swa(Q, K, Vt, window):
     O = np.zeros((M, Hq, D), np.float64)
     _load().oracle_swa(pq, pk, pv, M, T, Hq, Hkv, D, window, O.ctypes.data_as(ctypes.c_void_p))
     return O
+
+
+def silu_mul(G, U):
+    """Y = silu(G) * U elementwise, silu(g) = g / (1 + exp(-g)) (oracle_silu_mul)."""
+    G, pg = _c(G, np.float64)
+    U, pu = _c(U, np.float64)
+    assert G.shape == U.shape
+    Y = np.zeros(G.shape, np.float64)
+    _load().oracle_silu_mul(pg, pu, G.size, Y.ctypes.data_as(ctypes.c_void_p))
+    return Y
+
+
+def gated(X, gate, up, group=GROUP):
+    """The gated MLP activation of two projections of X: silu(X Wg^T) * (X Wu^T)."""
+    return silu_mul(linear(X, *gate, group=group), linear(X, *up, group=group))

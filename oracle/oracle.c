@@ -359,6 +359,19 @@ void oracle_swa(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt, int M,
         }
 }
 
+/* ---- gated MLP activation -------------------------------------------------- */
+
+/* The pages serve a Qwen3.5-4B target (Pith review, Referee Report: Summary) and do
+ * not spell out its MLP; the reading is that family's gated form, whose gate and
+ * up projections are two of the layer's INT4 linears:
+ *   Y[i] = silu(G[i]) * U[i],  silu(g) = g / (1 + exp(-g)) = g * sigmoid(g),
+ * with G and U the fp64 results of those projections (oracle_linear_f64). */
+void oracle_silu_mul(const double *G, const double *U, long long n, double *Y)
+{
+    for (long long i = 0; i < n; ++i)
+        Y[i] = G[i] / (1.0 + exp(-G[i])) * U[i];
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

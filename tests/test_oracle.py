@@ -550,3 +550,45 @@ def test_swa_matches_masked_softmax_formulation(W):
         p /= p.sum(axis=1, keepdims=True)
         want = p @ v[kv].T  # [M, D]
         assert np.abs(O[:, h, :] - want).max() < 1e-12
+
+
+# ---- gated MLP activation (oracle_silu_mul, gated) ----------------------------
+
+def test_silu_closed_forms():
+    # sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4; silu(0) = 0; silu(g) -> g for large g
+    ln3 = np.log(3.0)
+    Y = oracle.silu_mul(np.array([0.0, ln3, -ln3, 40.0, -40.0]), np.ones(5))
+    assert Y[0] == 0.0
+    assert abs(Y[1] - 0.75 * ln3) <= 1e-15
+    assert abs(Y[2] + 0.25 * ln3) <= 1e-15
+    assert abs(Y[3] - 40.0) <= 1e-12
+    assert abs(Y[4] - (-40.0 * np.exp(-40.0))) <= 1e-25
+
+
+def test_silu_odd_part_identity():
+    # silu(g) - silu(-g) = g (sigmoid(g) + sigmoid(-g) = 1), and the product is linear in U
+    rng = np.random.default_rng(71)
+    g = rng.normal(0, 3, 1000)
+    u = rng.normal(0, 1, 1000)
+    d = oracle.silu_mul(g, np.ones_like(g)) - oracle.silu_mul(-g, np.ones_like(g))
+    assert np.abs(d - g).max() <= 1e-12
+    assert np.abs(oracle.silu_mul(g, u) - oracle.silu_mul(g, np.ones_like(g)) * u).max() <= 1e-12
+
+
+def test_gated_applies_silu_to_the_gate_and_scales_by_up():
+    # one-hot X on k = 0 with s = 1: gate column n gives q - z = 2, up gives -3, so
+    # Y = silu(2) * (-3) = -6 / (1 + e^-2) (swapping gate and up would give 2 silu(-3))
+    N, K = 16, 128
+    X = np.zeros((1, K), np.float32)
+    X[0, 0] = 1.0
+    Xb = synth.f32_to_bf16_bits(X)
+    s = synth.f32_to_f16_bits(np.ones((N, 1), np.float32))
+    z = np.full((N, 1), 8, np.uint8)
+    cg = np.full((N, K), 8, np.uint8)
+    cg[:, 0] = 10
+    cu = np.full((N, K), 8, np.uint8)
+    cu[:, 0] = 5
+    qg, zg = oracle.pack(cg, z)
+    qu, zu = oracle.pack(cu, z)
+    Y = oracle.gated(Xb, (qg, s, zg), (qu, s, zu))
+    assert np.abs(Y - (-6.0 / (1.0 + np.exp(-2.0)))).max() <= 1e-15

@@ -51,6 +51,9 @@ MUTANTS = [
     ("quantize_no_low_clamp", "if (q < 0.0)\n                q = 0.0;", "if (q < -100.0)\n                q = 0.0;"),
     ("quantize_group_of_64", "int g = k / group;\n            double w = oracle_bf16_to_f64(W",
      "int g = k / 64 % G;\n            double w = oracle_bf16_to_f64(W"),
+    ("silu_sign_of_exponent", "Y[i] = G[i] / (1.0 + exp(-G[i])) * U[i];", "Y[i] = G[i] / (1.0 + exp(G[i])) * U[i];"),
+    ("silu_without_gate_factor", "Y[i] = G[i] / (1.0 + exp(-G[i])) * U[i];", "Y[i] = 1.0 / (1.0 + exp(-G[i])) * U[i];"),
+    ("gated_up_dropped", "Y[i] = G[i] / (1.0 + exp(-G[i])) * U[i];", "Y[i] = G[i] / (1.0 + exp(-G[i]));"),
 ]
 
 PIN_TESTS = [
@@ -71,6 +74,9 @@ PIN_TESTS = [
     lambda: pins.test_quantize_worked_by_hand(),
     lambda: pins.test_quantize_returns_on_grid_weights_to_their_codes(0),
     lambda: pins.test_quantize_matches_exact_rational_rounding(),
+    lambda: pins.test_silu_closed_forms(),
+    lambda: pins.test_silu_odd_part_identity(),
+    lambda: pins.test_gated_applies_silu_to_the_gate_and_scales_by_up(),
 ]
 
 
