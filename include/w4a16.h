@@ -70,7 +70,8 @@ enum w4a16_out_dtype {
 enum w4a16_op {
     W4A16_OP_LINEAR = 0,          /* w4a16_linear */
     W4A16_OP_LMHEAD = 1,          /* w4a16_lmhead_verify */
-    W4A16_OP_LINEAR_ACTORDER = 2  /* w4a16_linear_actorder */
+    W4A16_OP_LINEAR_ACTORDER = 2, /* w4a16_linear_actorder */
+    W4A16_OP_LINEAR_GATED = 3     /* w4a16_linear_gated */
 };
 
 /*
@@ -192,6 +193,34 @@ int w4a16_quantize(const void *W, const void *scales, const uint32_t *qzeros, in
 int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, const uint32_t *qzeros,
                  int M, int N, int K, int group, void *Y, int y_dtype,
                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * w4a16_linear_gated -- the gate and up projections of a gated MLP and its
+ * activation in one call: Y = silu(X * Wg^T) * (X * Wu^T), elementwise, with
+ * silu(g) = g / (1 + exp(-g)).  The pages serve a Qwen3.5-4B target (Pith review,
+ * Referee Report: Summary) and do not spell out its MLP; the gated form, with the
+ * activation applied to the fp32 sums of both projections, is that family's MLP
+ * (a reading).  Wg and Wu are two grids of the layouts of w4a16_linear over the
+ * same N columns.  For M <= 64 one launch computes both projections (each
+ * workgroup holds a gate tile and the up tile of the same columns) and applies the
+ * activation in its epilogue, so neither projection's output reaches memory; for
+ * M > 64 the two projections run in turn into the workspace (fp32) and a third
+ * kernel applies the activation.
+ *   X                                     [M][K] bf16, row-major
+ *   qweight_gate, scales_gate, qzeros_gate   the gate grid (layouts of w4a16_linear)
+ *   qweight_up, scales_up, qzeros_up         the up grid, same N and K
+ *   Y                                     [M][N] row-major, bf16 or fp32
+ *   workspace   at least w4a16_workspace_bytes(W4A16_OP_LINEAR_GATED, M, N, K, group)
+ *               bytes (M > 64: the fp32 outputs of both projections); the
+ *               counter-region rule of w4a16_linear; may be NULL when that size is 0
+ * Shapes: as w4a16_linear, and N % 16 == 0, 2 * M * N at most 2^31 - 256.
+ * Errors: as w4a16_linear (W4A16_ERR_SHAPE also for N % 16 != 0).  Y must not
+ * alias any input.
+ */
+int w4a16_linear_gated(const void *X, const uint32_t *qweight_gate, const void *scales_gate,
+                       const uint32_t *qzeros_gate, const uint32_t *qweight_up, const void *scales_up,
+                       const uint32_t *qzeros_up, int M, int N, int K, int group, void *Y, int y_dtype,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * w4a16_linear_batch -- several projections of the same rows in one launch.

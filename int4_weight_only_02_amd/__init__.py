@@ -21,13 +21,14 @@ import os
 
 GROUP = 128
 OUT_BF16, OUT_F32 = 0, 1
-OP_LINEAR, OP_LMHEAD, OP_LINEAR_ACTORDER = 0, 1, 2
+OP_LINEAR, OP_LMHEAD, OP_LINEAR_ACTORDER, OP_LINEAR_GATED = 0, 1, 2, 3
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw4a16.so")
 _lib = None
 
-EXPORTED = ("w4a16_pack", "w4a16_quantize", "w4a16_linear", "w4a16_linear_batch", "w4a16_lmhead_verify",
+EXPORTED = ("w4a16_pack", "w4a16_quantize", "w4a16_linear", "w4a16_linear_gated", "w4a16_linear_batch",
+            "w4a16_lmhead_verify",
             "w4a16_actorder_perm", "w4a16_pack_actorder", "w4a16_linear_actorder",
             "w4a16_swa_attention", "w4a16_swa_workspace_bytes",
             "w4a16_workspace_bytes", "w4a16_status_string", "w4a16_abi_version")
@@ -72,6 +73,8 @@ def lib():
     L.w4a16_linear_actorder.restype = I
     L.w4a16_linear.argtypes = [P, P, P, P, I, I, I, I, P, I, P, S, P]
     L.w4a16_linear.restype = I
+    L.w4a16_linear_gated.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, I, P, S, P]
+    L.w4a16_linear_gated.restype = I
     L.w4a16_linear_batch.argtypes = [P, I, I, I, I, P, S, P]
     L.w4a16_linear_batch.restype = I
     L.w4a16_lmhead_verify.argtypes = [P, P, P, P, I, I, I, I, P, P, I, P, P, P, S, P]
@@ -249,6 +252,29 @@ def w4a16_linear(X, qweight, scales, qzeros, out_dtype=None, group=GROUP, out=No
     st = lib().w4a16_linear(_ptr(X), _ptr(qweight), _ptr(scales), _ptr(qzeros), M, N, K, group,
                             _ptr(Y), ydt, _ptr(ws), nbytes, _stream(stream))
     _check(st, "w4a16_linear")
+    return Y
+
+
+def w4a16_linear_gated(X, gate, up, out_dtype=None, group=GROUP, out=None, workspace=None, stream=None):
+    """Y = silu(X Wg^T) * (X Wu^T); gate and up are (qweight, scales, qzeros) over the same N."""
+    import torch
+    M, K = X.shape
+    (qg, sg, zg), (qu, su, zu) = gate, up
+    N = qg.shape[0]
+    assert X.dtype == torch.bfloat16 and sg.dtype == torch.float16 and su.dtype == torch.float16
+    assert qu.shape == qg.shape and su.shape == sg.shape and zu.shape == zg.shape
+    for t in (X, qg, sg, zg, qu, su, zu):
+        assert t.is_contiguous()
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    ydt = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    Y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=X.device)
+    assert Y.shape == (M, N) and Y.dtype == out_dtype and Y.is_contiguous()
+    nbytes = w4a16_workspace_bytes(OP_LINEAR_GATED, M, N, K, group)
+    ws = _workspace(workspace, X.device).get(nbytes)
+    st = lib().w4a16_linear_gated(_ptr(X), _ptr(qg), _ptr(sg), _ptr(zg), _ptr(qu), _ptr(su), _ptr(zu), M, N, K,
+                                  group, _ptr(Y), ydt, _ptr(ws), nbytes, _stream(stream))
+    _check(st, "w4a16_linear_gated")
     return Y
 
 

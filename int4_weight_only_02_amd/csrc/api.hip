@@ -44,6 +44,20 @@ size_t actorder_x_offset(int M, int N, int K)
     return (base + 255) / 256 * 256;
 }
 
+// gated pair: the partial sums of the paired small-M plan, or (large M) the tiled
+// call's workspace followed by the two fp32 outputs [M][N] of gate and up
+size_t gated_gu_offset(int M, int N, int K)
+{
+    return (linear_ws(M, N, K) + 255) / 256 * 256;
+}
+
+size_t gated_ws(int M, int N, int K)
+{
+    if (M <= kSkinnyMaxM)
+        return plan_skinny_pair(M, N, K).ws_bytes;
+    return gated_gu_offset(M, N, K) + 2 * (size_t)M * N * 4;
+}
+
 } // namespace
 
 extern "C" {
@@ -74,6 +88,8 @@ size_t w4a16_workspace_bytes(int op, int M, int N, int K, int group)
         return (M == 0 || N == 0) ? 0 : actorder_x_offset(M, N, K) + (size_t)M * K * 2;
     if (op == W4A16_OP_LMHEAD)
         return (M < 1 || M > 64 || N < 1) ? 0 : plan_skinny(M, N, K, 1).ws_bytes;
+    if (op == W4A16_OP_LINEAR_GATED)
+        return (M == 0 || N == 0 || N % 16 != 0) ? 0 : gated_ws(M, N, K);
     return 0;
 }
 
@@ -277,6 +293,71 @@ int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, con
         a.y_f32 = y_dtype == W4A16_OUT_F32;
         a.ws = (unsigned char *)workspace;
         e = launch_tiled(a, p, (hipStream_t)stream);
+    }
+    return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+int w4a16_linear_gated(const void *X, const uint32_t *qweight_gate, const void *scales_gate,
+                       const uint32_t *qzeros_gate, const uint32_t *qweight_up, const void *scales_up,
+                       const uint32_t *qzeros_up, int M, int N, int K, int group, void *Y, int y_dtype,
+                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (group != kGroup || (y_dtype != W4A16_OUT_BF16 && y_dtype != W4A16_OUT_F32))
+        return W4A16_ERR_UNSUPPORTED;
+    int st = check_dims(M, N, K);
+    if (st != W4A16_OK)
+        return st;
+    if (N % 16 != 0 || (long long)M * N * 2 > kLimit)
+        return W4A16_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return W4A16_OK;
+    if (!X || !qweight_gate || !scales_gate || !qzeros_gate || !qweight_up || !scales_up || !qzeros_up || !Y)
+        return W4A16_ERR_NULL;
+    if (misaligned(X) || misaligned(qweight_gate) || misaligned(scales_gate) || misaligned(qzeros_gate) ||
+        misaligned(qweight_up) || misaligned(scales_up) || misaligned(qzeros_up) || misaligned(Y) ||
+        misaligned(workspace))
+        return W4A16_ERR_ALIGN;
+    const size_t need = gated_ws(M, N, K);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return W4A16_ERR_WORKSPACE;
+
+    hipError_t e;
+    if (M <= kSkinnyMaxM) {
+        // one launch: each workgroup holds gate and up tiles of the same columns
+        const SkinnyPlan p = plan_skinny_pair(M, N, K);
+        SkinnyArgs a{};
+        a.X = (const uint16_t *)X;
+        a.qw = qweight_gate;
+        a.scales = (const uint16_t *)scales_gate;
+        a.qz = qzeros_gate;
+        a.qw2 = qweight_up;
+        a.scales2 = (const uint16_t *)scales_up;
+        a.qz2 = qzeros_up;
+        a.gated = 1;
+        a.M = M;
+        a.N = N;
+        a.K = K;
+        a.G = K / kGroup;
+        a.Y = Y;
+        a.y_f32 = y_dtype == W4A16_OUT_F32;
+        a.ws = (unsigned char *)workspace;
+        a.lmhead = 0;
+        e = launch_skinny(a, p, (hipStream_t)stream);
+    } else {
+        // large M: the two projections in turn (fp32, into the workspace), then the
+        // elementwise activation
+        unsigned char *ws = (unsigned char *)workspace;
+        const size_t off = gated_gu_offset(M, N, K);
+        float *G = (float *)(ws + off), *U = G + (size_t)M * N;
+        st = w4a16_linear(X, qweight_gate, scales_gate, qzeros_gate, M, N, K, group, G, W4A16_OUT_F32, workspace,
+                          off, stream);
+        if (st != W4A16_OK)
+            return st;
+        st = w4a16_linear(X, qweight_up, scales_up, qzeros_up, M, N, K, group, U, W4A16_OUT_F32, workspace, off,
+                          stream);
+        if (st != W4A16_OK)
+            return st;
+        e = launch_silu_mul(G, U, (long long)M * N, Y, y_dtype == W4A16_OUT_F32, (hipStream_t)stream);
     }
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }

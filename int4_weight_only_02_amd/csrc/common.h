@@ -74,6 +74,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
+// silu(g) = g * sigmoid(g) = g / (1 + e^-g), fp32 (e^-g by the hardware exp2; -inf
+// at g -> -inf gives -0, large g gives g)
+__device__ __forceinline__ float silu_f32(float g)
+{
+    return g / (1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h)
 {
     return (float)__builtin_bit_cast(_Float16, h);

@@ -83,6 +83,7 @@ struct SkinnyPlan {
     int C, cg;     // xlds 3: K chunks per tile group, groups per chunk (a multiple of 4 if C > 1)
     int tkt;       // xlds 3, C > 1: first arrival counter (u32 at kOffCounters) of this projection
     size_t part_off; // xlds 3, C > 1: workspace offset of the fp32 partial sums [C][M][N]
+    int pair;      // gated pairs: tile slot 2i holds a gate tile, 2i + 1 the up tile of the same columns (tw even)
     size_t lds_bytes;
     size_t ws_bytes; // lm_head: the zero region (argmax keys, ticket); linear: the partials (xlds 3) or 0
 };
@@ -100,6 +101,12 @@ struct SkinnyArgs {
     const int32_t *draft;
     int32_t *argmax_out;
     int32_t *accept_out;
+    // gated (plan.pair): qw/scales/qz are the gate projection, these the up projection
+    // of the same N columns; Y = silu(gate) * up
+    const uint32_t *qw2;
+    const uint16_t *scales2;
+    const uint32_t *qz2;
+    int gated;
 };
 
 SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit = 0);
@@ -113,7 +120,9 @@ struct SkinnyMulti {
     SkinnyArgs args[kMaxProblems];
     SkinnyPlan plan[kMaxProblems];
 };
-SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit = 0, int tw_hint = 0);
+SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit = 0, int tw_hint = 0, bool pair = false);
+// gated gate/up pair of N columns each (N % 16 == 0): 2N/16 tiles, an even tw
+SkinnyPlan plan_skinny_pair(int M, int N, int K, size_t lds_limit = 0);
 // tiles per workgroup that spread the projections of one launch evenly over the CUs
 void balance_multi(const int *N, const int *K, int count, int M, int *tw);
 // upper bound of the partial-sum scratch any chunked plan of this shape needs
@@ -151,5 +160,8 @@ hipError_t launch_tiled(const TiledArgs &a, const TiledPlan &p, hipStream_t stre
 
 // path choice for w4a16_linear: small M streams the weights once per 16 rows
 constexpr int kSkinnyMaxM = 64;
+
+// Y[i] = silu(G[i]) * U[i] for n fp32 values (n % 4 == 0, 16-byte aligned)
+hipError_t launch_silu_mul(const float *G, const float *U, long long n, void *Y, int y_f32, hipStream_t stream);
 
 } // namespace w4a16

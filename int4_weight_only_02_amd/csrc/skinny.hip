@@ -431,7 +431,7 @@ __device__ __forceinline__ void group_sums(const float *part, float *S, int Mb, 
 // The work of one workgroup on one projection.  MODE: kSplitDirect, kSplitLds,
 // kSplitPriv, kSplitPrivDma, kSplitChunk or kStream (see the plan).  The workgroup takes items first, first +
 // stride, ... (split mode) or tile groups first, first + stride, ... (stream mode).
-template <int NR, int MODE, bool ALIGNED>
+template <int NR, int MODE, bool ALIGNED, bool GATED = false>
 __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPlan &p, int first, int stride,
                                             unsigned char *smem, unsigned long long (*kred)[16], int &s_flag)
 {
@@ -464,9 +464,11 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
     uint32_t *ticket = (uint32_t *)(a.ws + kOffTicket);
     unsigned long long *keys = (unsigned long long *)(a.ws + kOffKeys);
 
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.qw, (uint32_t)((size_t)N * K / 2));
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales, (uint32_t)((size_t)N * G * 2));
-    const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.qz, (uint32_t)((size_t)(N / 8) * G * 4));
+    // gated pairs: the waves of odd tile slots stream the up projection
+    const bool upw = !STREAM && GATED && ((wave % p.tw) & 1);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(upw ? a.qw2 : a.qw, (uint32_t)((size_t)N * K / 2));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(upw ? a.scales2 : a.scales, (uint32_t)((size_t)N * G * 2));
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(upw ? a.qz2 : a.qz, (uint32_t)((size_t)(N / 8) * G * 4));
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X, (uint32_t)((size_t)M * K * 2));
     auto x_stage = [&](int m0, int Mb) {
         XStage st;
@@ -630,8 +632,9 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
             const int Mb = M - m0 < 16 ? M - m0 : 16;
             const int xrow = col < Mb ? col : Mb - 1;
             const int tile = tg * p.tw + tslot;
-            const bool live = tile * 16 < N;
-            const LaneGrid L = lane_grid(tile, col, h, N, K, G, live);
+            const int ptile = GATED ? tile >> 1 : tile; // the tile in the wave's own projection
+            const bool live = ptile * 16 < N;
+            const LaneGrid L = lane_grid(ptile, col, h, N, K, G, live);
             if (a.lmhead && mb != cur_mb) {
                 if (cur_mb >= 0)
                     flush_best(cur_mb);
@@ -852,14 +855,16 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
                 // takes an arrival ticket; the last to arrive adds the C partials in chunk
                 // order (its own from registers) and finishes the tiles, so the result
                 // does not depend on the arrival order
+                // (gated: over the 2N columns of the pair, gate and up tiles alternating)
                 float *pbuf = (float *)(a.ws + p.part_off);
                 uint32_t *tk = (uint32_t *)(a.ws + kOffCounters) + p.tkt + rest;
+                const int Nv = GATED ? 2 * N : N;
                 const int n = tile * 16 + col;
-                if (ks == 0 && live && n < N) {
+                if (ks == 0 && live && n < Nv) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         if (4 * h + r < Mb)
-                            __hip_atomic_store(pbuf + ((size_t)chunk * M + m0 + 4 * h + r) * N + n, acc[r],
+                            __hip_atomic_store(pbuf + ((size_t)chunk * M + m0 + 4 * h + r) * Nv + n, acc[r],
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
                 wait_device_writes();
@@ -871,7 +876,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
                 __syncthreads();
                 if (!s_flag)
                     continue; // uniform over the workgroup
-                if (ks == 0 && live && n < N) {
+                if (ks == 0 && live && n < Nv) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         if (4 * h + r >= Mb)
@@ -879,7 +884,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
                         float t = 0.f;
                         for (int cc = 0; cc < p.C; ++cc)
                             t += cc == chunk ? acc[r]
-                                             : __hip_atomic_load(pbuf + ((size_t)cc * M + m0 + 4 * h + r) * N + n,
+                                             : __hip_atomic_load(pbuf + ((size_t)cc * M + m0 + 4 * h + r) * Nv + n,
                                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         acc[r] = t;
                     }
@@ -887,8 +892,25 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
                 if (tid == 0)
                     __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            if (ks == 0 && live)
+            if constexpr (GATED) {
+                // the gate tile's sums (even slot) meet the up tile's (the next slot)
+                // through LDS: Y = silu(gate) * up.  Every wave of the workgroup passes
+                // both barriers (the branch is uniform).
+                if (ks == 0 && !(tslot & 1))
+                    *(f32x4_t *)(red + ((size_t)tslot * 64 + lane) * 4) = acc;
+                __syncthreads();
+                if (ks == 0 && (tslot & 1) && live) {
+                    const f32x4_t gv = *(const f32x4_t *)(red + ((size_t)(tslot - 1) * 64 + lane) * 4);
+                    f32x4_t y;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        y[r] = silu_f32(gv[r]) * acc[r];
+                    finish_tile(y, m0, Mb, ptile * 16 + col);
+                }
+                __syncthreads(); // before the next item reuses the exchange region
+            } else if (ks == 0 && live) {
                 finish_tile(acc, m0, Mb, tile * 16 + col);
+            }
         }
     }
 
@@ -922,13 +944,13 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
     }
 }
 
-template <int NR, int MODE, bool ALIGNED>
+template <int NR, int MODE, bool ALIGNED, bool GATED = false>
 __global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs a, SkinnyPlan p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ unsigned long long kred[kMaxWaves][16];
     __shared__ int s_flag;
-    skinny_body<NR, MODE, ALIGNED>(a, p, blockIdx.x, gridDim.x, smem, kred, s_flag);
+    skinny_body<NR, MODE, ALIGNED, GATED>(a, p, blockIdx.x, gridDim.x, smem, kred, s_flag);
 }
 
 // Several projections (same M) in one launch: workgroup b works on item
@@ -972,7 +994,7 @@ size_t lds_per_group(int M)
 // every wave the workgroup launches with (p.waves; waves past tw * sk stay idle)
 size_t lds_for(const SkinnyPlan &p, int M)
 {
-    const size_t red = p.sk > 1 ? (size_t)p.waves * 1024 : 0;
+    const size_t red = (p.sk > 1 || p.pair) ? (size_t)p.waves * 1024 : 0;
     if (p.xlds == 3) {
         const int mrows = M < 16 ? M : 16;
         return (size_t)((p.cg * 16 * mrows + 63) & ~63) * 16 + red;
@@ -1069,7 +1091,7 @@ bool choose_chunk(SkinnyPlan &p, int M, size_t lds_limit, bool fixed, int tw_hin
 {
     int tw = 0, cg = 0;
     SkinnyPlan c = p;
-    if (chunk_override(&tw, &cg)) {
+    if (chunk_override(&tw, &cg) && !(p.pair && (tw & 1))) {
         if (!plan_chunk(c, M, lds_limit, tw, cg, fixed))
             return false;
         p = c;
@@ -1166,9 +1188,10 @@ SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit)
 // tw from the caller (tw_hint, balancing the launch) or the smallest power of two that
 // keeps the projection within one workgroup per CU; sk = kMaxWaves / tw (waves and
 // slices past K stay empty).
-SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit, int tw_hint)
+SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit, int tw_hint, bool pair)
 {
     SkinnyPlan p{};
+    p.pair = pair ? 1 : 0;
     if (lds_limit == 0 || lds_limit > kLdsBudget)
         lds_limit = kLdsBudget;
     p.G = K / kGroup;
@@ -1183,7 +1206,7 @@ SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit, int tw_hint)
     if (tw_hint > 0)
         tw = tw_hint < kMaxWaves ? tw_hint : kMaxWaves;
     const int sk = kMaxWaves / tw;
-    const size_t red = sk > 1 ? (size_t)kMaxWaves * 1024 : 0;
+    const size_t red = (sk > 1 || pair) ? (size_t)kMaxWaves * 1024 : 0;
     p.stream = 0;
     p.tw = tw;
     p.sk = sk;
@@ -1203,39 +1226,51 @@ SkinnyPlan plan_skinny_fixed(int M, int N, int K, size_t lds_limit, int tw_hint)
     return p;
 }
 
+// Gated gate/up pair: the 2N / 16 tiles of both projections, alternating, in the
+// fixed-wave split plan with an even tw (each pair in one workgroup), sized so the
+// launch fits one workgroup per CU.
+SkinnyPlan plan_skinny_pair(int M, int N, int K, size_t lds_limit)
+{
+    const long long tiles = 2LL * ((N + 15) / 16) * ((M + 15) / 16);
+    int tw = (int)((tiles + kCUs - 1) / kCUs);
+    tw = (tw + 1) & ~1;
+    tw = tw < 2 ? 2 : tw > kMaxWaves ? kMaxWaves : tw;
+    return plan_skinny_fixed(M, 2 * N, K, lds_limit, tw, true);
+}
+
 namespace {
 
-template <int MODE, bool ALIGNED>
+template <int MODE, bool ALIGNED, bool GATED>
 void launch_variant(int nr, dim3 grid, dim3 block, size_t lds, hipStream_t stream, const SkinnyArgs &a,
                     const SkinnyPlan &p)
 {
     if (nr == 1)
-        hipLaunchKernelGGL((skinny_kernel<1, MODE, ALIGNED>), grid, block, lds, stream, a, p);
+        hipLaunchKernelGGL((skinny_kernel<1, MODE, ALIGNED, GATED>), grid, block, lds, stream, a, p);
     else if (nr == 2)
-        hipLaunchKernelGGL((skinny_kernel<2, MODE, ALIGNED>), grid, block, lds, stream, a, p);
+        hipLaunchKernelGGL((skinny_kernel<2, MODE, ALIGNED, GATED>), grid, block, lds, stream, a, p);
     else
-        hipLaunchKernelGGL((skinny_kernel<4, MODE, ALIGNED>), grid, block, lds, stream, a, p);
+        hipLaunchKernelGGL((skinny_kernel<4, MODE, ALIGNED, GATED>), grid, block, lds, stream, a, p);
 }
 
-template <int MODE, bool ALIGNED>
+template <int MODE, bool ALIGNED, bool GATED = false>
 void allow_lds(size_t bytes)
 {
-    (void)hipFuncSetAttribute((const void *)skinny_kernel<1, MODE, ALIGNED>,
+    (void)hipFuncSetAttribute((const void *)skinny_kernel<1, MODE, ALIGNED, GATED>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    (void)hipFuncSetAttribute((const void *)skinny_kernel<2, MODE, ALIGNED>,
+    (void)hipFuncSetAttribute((const void *)skinny_kernel<2, MODE, ALIGNED, GATED>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    (void)hipFuncSetAttribute((const void *)skinny_kernel<4, MODE, ALIGNED>,
+    (void)hipFuncSetAttribute((const void *)skinny_kernel<4, MODE, ALIGNED, GATED>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <int MODE>
+template <int MODE, bool GATED = false>
 void launch_mode(bool aligned, int nr, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
                  const SkinnyArgs &a, const SkinnyPlan &p)
 {
     if (aligned)
-        launch_variant<MODE, true>(nr, grid, block, lds, stream, a, p);
+        launch_variant<MODE, true, GATED>(nr, grid, block, lds, stream, a, p);
     else
-        launch_variant<MODE, false>(nr, grid, block, lds, stream, a, p);
+        launch_variant<MODE, false, GATED>(nr, grid, block, lds, stream, a, p);
 }
 
 template <bool ALIGNED>
@@ -1273,6 +1308,14 @@ hipError_t device_lds_limit(size_t *limit)
             allow_lds<kSplitPrivDma, true>(lds_limit);
             allow_lds<kSplitChunk, false>(lds_limit);
             allow_lds<kSplitChunk, true>(lds_limit);
+            allow_lds<kSplitLds, false, true>(lds_limit);
+            allow_lds<kSplitLds, true, true>(lds_limit);
+            allow_lds<kSplitPriv, false, true>(lds_limit);
+            allow_lds<kSplitPriv, true, true>(lds_limit);
+            allow_lds<kSplitPrivDma, false, true>(lds_limit);
+            allow_lds<kSplitPrivDma, true, true>(lds_limit);
+            allow_lds<kSplitChunk, false, true>(lds_limit);
+            allow_lds<kSplitChunk, true, true>(lds_limit);
             allow_lds_multi<false>(lds_limit);
             allow_lds_multi<true>(lds_limit);
         }
@@ -1380,13 +1423,31 @@ hipError_t launch_skinny(const SkinnyArgs &a, const SkinnyPlan &plan, hipStream_
     const hipError_t le = device_lds_limit(&lds_limit);
     if (le != hipSuccess)
         return le;
-    const SkinnyPlan p = plan.lds_bytes > lds_limit ? plan_skinny(a.M, a.N, a.K, a.lmhead, lds_limit) : plan;
+    const SkinnyPlan p = plan.lds_bytes <= lds_limit ? plan
+                         : a.gated               ? plan_skinny_pair(a.M, a.N, a.K, lds_limit)
+                                                 : plan_skinny(a.M, a.N, a.K, a.lmhead, lds_limit);
     if (p.lds_bytes > lds_limit)
         return hipErrorInvalidValue;
     const dim3 block(64 * p.waves), grid(p.grid);
     const int nr = a.M == 1 ? 1 : a.M == 2 ? 2 : 4;
     // 4-group scale/zero loads need G and every slice start to be multiples of 4
     const bool aligned = (a.G % 4) == 0 && (p.per % 4) == 0;
+    if (a.gated) {
+        // a pair plan is never in stream mode
+        if (p.stream || !p.pair || (p.tw & 1))
+            return hipErrorInvalidValue;
+        if (p.xlds == 3)
+            launch_mode<kSplitChunk, true>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
+        else if (p.xlds == 2 && p.xdma)
+            launch_mode<kSplitPrivDma, true>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
+        else if (p.xlds == 2)
+            launch_mode<kSplitPriv, true>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
+        else if (p.xlds == 1)
+            launch_mode<kSplitLds, true>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
+        else
+            launch_mode<kSplitDirect, true>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
+        return hipGetLastError();
+    }
     if (p.stream)
         launch_mode<kStream>(aligned, nr, grid, block, p.lds_bytes, stream, a, p);
     else if (p.xlds == 3)

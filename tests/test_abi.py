@@ -107,6 +107,28 @@ def test_linear_rejections(lib):
     assert linear(lib, M=300, wsb=need - 1) == ERR_WORKSPACE
 
 
+def gated(lib, X=A, qg=A, sg=A, zg=A, qu=A, su=A, zu=A, M=1, N=512, K=512, group=128, Y=A2, ydt=0, ws=A,
+          wsb=1 << 30):
+    return lib.w4a16_linear_gated(X, qg, sg, zg, qu, su, zu, M, N, K, group, Y, ydt, ws, wsb, None)
+
+
+def test_gated_rejections(lib):
+    assert gated(lib, group=64) == ERR_UNSUPPORTED
+    assert gated(lib, ydt=3) == ERR_UNSUPPORTED
+    assert gated(lib, N=520) == ERR_SHAPE           # N % 16
+    assert gated(lib, K=100) == ERR_SHAPE
+    assert gated(lib, M=1 << 18, N=1 << 12) == ERR_SHAPE  # 2 M N >= 2^31
+    assert gated(lib, qu=NUL) == ERR_NULL
+    assert gated(lib, zg=NUL) == ERR_NULL
+    assert gated(lib, su=MIS) == ERR_ALIGN
+    need = w4.w4a16_workspace_bytes(w4.OP_LINEAR_GATED, 300, 512, 512)
+    assert need >= 2 * 300 * 512 * 4  # both projections' fp32 outputs
+    assert gated(lib, M=300, ws=NUL) == ERR_WORKSPACE
+    assert gated(lib, M=300, wsb=need - 1) == ERR_WORKSPACE
+    assert gated(lib, M=0) == 0 and gated(lib, N=0) == 0
+    assert w4.w4a16_workspace_bytes(w4.OP_LINEAR_GATED, 4, 520, 512) == 0  # N % 16
+
+
 def test_linear_empty_is_a_noop(lib):
     assert linear(lib, M=0, X=NUL, Y=NUL, ws=NUL, wsb=0) == OK
     assert linear(lib, N=0, qw=NUL, s=NUL, qz=NUL, Y=NUL, ws=NUL, wsb=0) == OK

@@ -1,0 +1,128 @@
+"""GPU parity of w4a16_linear_gated (Y = silu(X Wg^T) * (X Wu^T)) with the fp64 oracle.
+
+Tolerance: the linear's contract applied to the gated output, |dY| <= 1e-2 *
+rms(Y_oracle) on fp32 output (+ half a bf16 ulp of Y_oracle on bf16 output).  Both
+projections are accumulated in fp32 as in w4a16_linear (errors of about 1e-5 of that
+bound), and silu and the product add a few fp32 roundings.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import check, dev_inputs
+
+torch = pytest.importorskip("torch")
+w4 = pytest.importorskip("int4_weight_only_02_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    w4.lib()
+    return torch.device("cuda:0")
+
+
+def _grid(d, dev):
+    t = dev_inputs(d, dev)
+    qw, qz = w4.w4a16_pack(t["codes"], t["zeros"])
+    oqw, oqz = oracle.pack(d["codes"], d["zeros"])
+    return t, (qw, t["scales"], qz), (oqw, d["scales"], oqz)
+
+
+def _pair(seed, M, N, K, dev):
+    dg = synth.linear_inputs(seed, M, N, K)
+    du = synth.linear_inputs(seed + 1, M, N, K)
+    tg, gate, ogate = _grid(dg, dev)
+    _, up, oup = _grid(du, dev)
+    return dg["X"], tg["X"], gate, up, ogate, oup
+
+
+@pytest.mark.parametrize("ydt", ["f32", "bf16"])
+@pytest.mark.parametrize("workload,jg,ju", [("verify_block_m16", 4, 5), ("decode_gemv_m1", 0, 0)])
+def test_gated_full_size(dev, workload, jg, ju, ydt):
+    # the draft block's gate and up projections (M = 16, K 2560 -> N 9728) sharing the
+    # gate's activations; at M = 1 the decode gate/up shape with two seeded grids
+    label, M, K, N = synth.WORKLOADS[workload][jg]
+    print("gated full", workload, M, N, K, ydt, flush=True)
+    dg = synth.workload_inputs(workload, jg)
+    du = synth.workload_inputs(workload, ju) if ju != jg else synth.linear_inputs(synth.seed_for(workload, jg) + 5,
+                                                                                   M, N, K)
+    tg, gate, ogate = _grid(dg, dev)
+    _, up, oup = _grid(du, dev)
+    Y = w4.w4a16_linear_gated(tg["X"], gate, up, out_dtype=torch.float32 if ydt == "f32" else torch.bfloat16)
+    torch.cuda.synchronize()
+    Yo = oracle.gated(dg["X"], ogate, oup)
+    r = check(Y, Yo, "gated %s %s" % (workload, ydt))
+    print("  max|dY|/tol %.2e" % r)
+
+
+SHAPES = [(1, 16, 128), (2, 48, 640), (3, 528, 1280), (4, 2064, 2560), (5, 1040, 384), (8, 336, 9728),
+          (16, 4112, 2560), (16, 2560, 9728), (17, 528, 1280), (40, 1040, 640), (64, 272, 4096),
+          (65, 528, 1280), (130, 1040, 640)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gated_small(dev, M, N, K):
+    # ragged tile counts, every small-M plan (private, DMA, shared, chunked, direct) and
+    # the large-M path (M > 64: two tiled projections and the activation kernel)
+    print("gated", M, N, K, flush=True)
+    Xh, X, gate, up, ogate, oup = _pair(300 + M + N + K, M, N, K, dev)
+    Y = w4.w4a16_linear_gated(X, gate, up, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check(Y, oracle.gated(Xh, ogate, oup), "gated %d %d %d" % (M, N, K))
+
+
+def test_gated_prefill_sampled(dev):
+    # prefill of the MLP's first half (M = 8192, K 2560 -> N 9728), sampled outputs
+    # against the oracle evaluated one by one
+    M, N, K = 8192, 9728, 2560
+    print("gated prefill", M, N, K, flush=True)
+    Xh, X, gate, up, ogate, oup = _pair(77, M, N, K, dev)
+    Y = w4.w4a16_linear_gated(X, gate, up, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.concatenate([rng.integers(0, M, 600), [0, M - 1, M - 1]]).astype(np.int32)
+    cols = np.concatenate([rng.integers(0, N, 600), [0, N - 1, 0]]).astype(np.int32)
+    g = oracle.linear_at(Xh, *ogate, rows, cols)
+    u = oracle.linear_at(Xh, *oup, rows, cols)
+    yo = oracle.silu_mul(g, u)
+    y = Y.cpu().numpy()[rows, cols].astype(np.float64)
+    # the scale of the whole output, from the sample (the sample's rms stands in for it)
+    tol = 1e-2 * float(np.sqrt(np.mean(yo * yo)))
+    assert np.abs(y - yo).max() <= tol, (float(np.abs(y - yo).max()), tol)
+
+
+def test_gated_matches_the_linear_calls_and_is_deterministic(dev):
+    # the fused call against silu(gate) * up formed from w4a16_linear's own fp32 outputs
+    # (the two plans sum K in different orders: agreement to fp32 rounding, not bits),
+    # and bit-exact repeats
+    for M, N, K in [(16, 2560, 9728), (1, 9728, 2560), (3, 528, 1280), (130, 1040, 640)]:
+        Xh, X, gate, up, _, _ = _pair(93 + M, M, N, K, dev)
+        Y1 = w4.w4a16_linear_gated(X, gate, up, out_dtype=torch.float32)
+        Y2 = w4.w4a16_linear_gated(X, gate, up, out_dtype=torch.float32)
+        G = w4.w4a16_linear(X, *gate, out_dtype=torch.float32)
+        U = w4.w4a16_linear(X, *up, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(Y1, Y2), (M, N, K)
+        g, u = G.double().cpu().numpy(), U.double().cpu().numpy()
+        ref = g / (1.0 + np.exp(-g)) * u
+        err = np.abs(Y1.double().cpu().numpy() - ref).max()
+        assert err <= 1e-4 * float(np.sqrt(np.mean(ref * ref))), (M, N, K, float(err))
+
+
+def test_gated_errors(dev):
+    Xh, X, gate, up, _, _ = _pair(95, 4, 48, 256, dev)
+    with pytest.raises(w4.W4A16Error) as e:  # N % 16 != 0
+        qg, sg, zg = gate
+        qu, su, zu = up
+        w4.w4a16_linear_gated(X, (qg[:40], sg[:40], zg[:5]), (qu[:40], su[:40], zu[:5]))
+    assert e.value.status == 2
+    Xh, X, gate, up, _, _ = _pair(96, 65, 48, 256, dev)
+    Y = torch.empty((65, 48), dtype=torch.float32, device=dev)
+    st = w4.lib().w4a16_linear_gated(w4._ptr(X), w4._ptr(gate[0]), w4._ptr(gate[1]), w4._ptr(gate[2]),
+                                     w4._ptr(up[0]), w4._ptr(up[1]), w4._ptr(up[2]), 65, 48, 256, 128,
+                                     w4._ptr(Y), 1, None, 0, w4._stream(None))
+    assert st == 5  # M > 64 needs the workspace for both projections' outputs
