@@ -16,8 +16,11 @@ one step = both projections.  Prints ONE JSON line with:
   cpu_baseline   the fp64 CPU oracle timed on this host on a bounded sample
   workloads      the same measurements for the other shapes: a single 512x512
                  linear, one decoder layer's seven projections at M = 16 (a draft
-                 block), the fused lm_head verify over a 151936 vocabulary, and
-                 prefill at M = 8192 (TFLOP/s against the bf16 MFMA peak)
+                 block), the fused lm_head verify over a 151936 vocabulary,
+                 prefill at M = 8192 (TFLOP/s against the bf16 MFMA peak), and the
+                 further calls: the layer in four batched launches, re-quantization,
+                 an act-order projection, sliding-window attention and the gated
+                 gate/up pair (silu(gate) * up in one launch)
 Options: --only WORKLOAD times one workload (for profiling runs), --calib runs a
 plain copy of known size (HBM counter calibration), --pmc-summary writes the
 traffic summary from the counter CSVs of those runs (no GPU needed).
@@ -461,6 +464,85 @@ def measure_actorder(dev, steps, warmup, M=16, N=9728, K=2560):
             "GBps_actorder": round(nbytes / t_act / 1e3, 1), "sampled_max_err_over_rms": err}
 
 
+def measure_gated(dev, steps, warmup, N=9728, K=2560):
+    """The MLP's gate and up projections (K 2560 -> N 9728 each) on the same rows, at
+    M = 16 (a draft block) and M = 1: w4a16_linear_gated (both projections and
+    silu(gate) * up in one launch, one bf16 output) next to w4a16_linear_batch of the
+    two projections (one launch, two outputs, no activation).  Graph replay over
+    rotating weight copies.  Algorithmic bytes: both packed grids, X once, Y once."""
+    import torch
+    import int4_weight_only_02_amd as w4
+    import oracle
+    G = K // 128
+    out = {"N": N, "K": K}
+    for M in (16, 1):
+        dg = synth.linear_inputs(5151 + M, M, N, K)
+        du = synth.linear_inputs(5152 + M, M, N, K)
+        X = torch.from_numpy(dg["X"].view(np.int16)).to(dev).view(torch.bfloat16)
+
+        def grid(d):
+            qw, qz = w4.w4a16_pack(torch.from_numpy(d["codes"]).to(dev), torch.from_numpy(d["zeros"]).to(dev))
+            return qw, torch.from_numpy(d["scales"].view(np.int16)).to(dev).view(torch.float16), qz
+
+        gate, up = grid(dg), grid(du)
+        nbytes = 2 * (N * K // 2 + 2 * N * G + N * G // 2) + 2 * M * K + 2 * M * N
+        R = int(max(1, min(32, -(-CACHE_ROTATE_BYTES // nbytes))))
+        copies = [(gate, up)] + [(tuple(t.clone() for t in gate), tuple(t.clone() for t in up))
+                                 for _ in range(R - 1)]
+        ws = w4.Workspace(dev)
+        ws.get(max(w4.w4a16_workspace_bytes(w4.OP_LINEAR_GATED, M, N, K),
+                   2 * w4.w4a16_workspace_bytes(w4.OP_LINEAR, M, N, K), 1 << 20))
+        # check: sampled outputs against the oracle (both projections one by one)
+        Yf = w4.w4a16_linear_gated(X, gate, up, out_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(M)
+        rows = rng.integers(0, M, 256).astype(np.int32)
+        cols = rng.integers(0, N, 256).astype(np.int32)
+        og = oracle.pack(dg["codes"], dg["zeros"])
+        ou = oracle.pack(du["codes"], du["zeros"])
+        yo = oracle.silu_mul(oracle.linear_at(dg["X"], og[0], dg["scales"], og[1], rows, cols),
+                             oracle.linear_at(dg["X"], ou[0], du["scales"], ou[1], rows, cols))
+        err = float(np.abs(Yf.cpu().numpy()[rows, cols] - yo).max() / np.sqrt((yo ** 2).mean()))
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        Yg = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        Yu = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+        def timed(fn):
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(s):
+                fn(0)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=s):
+                    for r in range(R):
+                        fn(r)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            for _ in range(max(1, warmup // R)):
+                g.replay()
+            torch.cuda.synchronize()
+            reps = max(1, steps // R)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / (reps * R)
+
+        t_gated = timed(lambda r: w4.w4a16_linear_gated(X, *copies[r], out=Y, workspace=ws))
+        t_batch = timed(lambda r: w4.w4a16_linear_batch([(X,) + copies[r][0], (X,) + copies[r][1]],
+                                                        outs=[Yg, Yu], workspace=ws))
+        out["m%d" % M] = {"copies": R, "bytes_per_call": nbytes, "us_per_call_gated": round(t_gated, 3),
+                          "GBps_gated": round(nbytes / t_gated / 1e3, 1),
+                          "hbm_frac_gated": round(nbytes / t_gated / 1e3 / HBM_PEAK_GBS, 4),
+                          "us_per_call_batch_two_outputs": round(t_batch, 3),
+                          "sampled_max_err_over_rms": err}
+    return out
+
+
 def measure_swa(dev, steps, warmup, M=16, T=8192, Hq=32, Hkv=8, window=1024):
     """The drafter's sliding-window attention for one verify block: M = 16 queries at
     the end of an 8192-token context, 32 query heads over 8 key/value heads of 128,
@@ -606,14 +688,15 @@ def main():
         return
 
     names = [HEADLINE, "single_512", "verify_block_m16", "lmhead_verify_m16", "prefill_m8192",
-             "verify_block_m16+batch", "requantize_9728x2560", "actorder_gate_m16", "swa_verify_m16_t8192"]
+             "verify_block_m16+batch", "requantize_9728x2560", "actorder_gate_m16", "swa_verify_m16_t8192",
+             "mlp_gate_up_gated"]
     if args.only:
         names = [args.only]
     results = {}
     for key in names:
-        if key in ("requantize_9728x2560", "actorder_gate_m16", "swa_verify_m16_t8192"):
+        if key in ("requantize_9728x2560", "actorder_gate_m16", "swa_verify_m16_t8192", "mlp_gate_up_gated"):
             fn = {"requantize_9728x2560": measure_requant, "actorder_gate_m16": measure_actorder,
-                  "swa_verify_m16_t8192": measure_swa}[key]
+                  "swa_verify_m16_t8192": measure_swa, "mlp_gate_up_gated": measure_gated}[key]
             results[key] = fn(dev, max(64, min(args.steps, 1000)), 32)
             print("[bench] %s: %s" % (key, json.dumps(results[key])), file=sys.stderr, flush=True)
             continue

@@ -150,3 +150,14 @@ def test_quantize_graph_replays(dev):
     ws = _workspace(dev, 1 << 24)
     out = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
     _check_replays(dev, ws, lambda: w4.w4a16_quantize(Wt, S, qz, out=out), [out])
+
+
+@pytest.mark.parametrize("M,K", [(16, 2560), (16, 9728), (130, 640)])
+def test_gated_graph_replays(dev, M, K):
+    N = 2560
+    print("graph gated", M, N, K, flush=True)
+    X, qg, sg, zg = _packed(71 + K, M, N, K, dev)
+    _, qu, su, zu = _packed(72 + K, M, N, K, dev)
+    ws = _workspace(dev, max(w4.w4a16_workspace_bytes(w4.OP_LINEAR_GATED, M, N, K), 1 << 24))
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    _check_replays(dev, ws, lambda: w4.w4a16_linear_gated(X, (qg, sg, zg), (qu, su, zu), out=Y, workspace=ws), [Y])
