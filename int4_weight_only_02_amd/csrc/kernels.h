@@ -136,11 +136,15 @@ hipError_t launch_skinny_multi(SkinnyMulti &mp, int M, size_t ws_bytes, hipStrea
 struct TiledPlan {
     int G;
     int tiles_m, tiles_n;
+    int stream;       // 1: one balanced segment of tile-groups per CU (at least one tile per CU)
+    int grid;         // workgroups
+    int dp_rounds;    // stream: rounds of whole tiles before the segments
     int ksplit;       // K slices per tile (1: the tile kernel stores Y itself)
     int gper;         // groups per K slice
     size_t off_xh;    // X as fp16, each row scaled by a power of two, [M][K]
     size_t off_rs;    // the per-row scales (fp32, M)
-    size_t off_part;  // ksplit > 1: fp32 partial sums [ksplit][M][N]
+    size_t off_part;  // ksplit > 1: fp32 partial sums [ksplit][M][N]; stream: one pair of
+                      // fp32 tile regions per inner segment boundary
     size_t ws_bytes;
 };
 

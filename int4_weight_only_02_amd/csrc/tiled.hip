@@ -44,6 +44,7 @@ constexpr int kLdsBytes = 2 * kBufBytes; // 163840
 constexpr uint32_t kOob = 0xFFFFFF00u;   // an offset past the end of every tensor
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr uint32_t kF16Bias = 0x64006400u; // fp16 1024 in both halves
+constexpr int kSc1 = 16;                   // buffer cache-policy bit sc1
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
@@ -125,9 +126,25 @@ __device__ __forceinline__ f16x8_t dequant_word(uint32_t w, uint32_t mask, uint3
     return f16x8_t{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
 }
 
+// The work of a workgroup is a run of consecutive tile-groups u = t * G + g (tile t,
+// group g; tiles n-fastest), computed through one software pipeline that also runs
+// across tile boundaries (the next tile's first group is fetched while the current
+// tile's last group computes).
+//   split plan  (stream == 0): one tile, one K slice [ks * gper, ...) per workgroup;
+//               with ksplit > 1 the slice's fp32 partial sums go to the workspace and
+//               reduce_kernel finishes Y;
+//   stream plan (stream == 1, at least one tile per CU): workgroup b first takes whole
+//               tiles, one per round (all rounds but the last one or two), then owns
+//               segment s of the remaining tiles' tile-groups; segments differ by at
+//               most one tile-group and hold at least G, so a tile is either whole in
+//               one segment or split in two parts at one segment boundary.  Both parts store their fp32 sums in
+//               the workspace and take a ticket; the second to arrive adds the other
+//               part (a + b = b + a in fp32, so the result does not depend on the
+//               arrival order), scales and stores Y, and returns the ticket to zero.
+template <bool STREAM>
 __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan p)
 {
-    extern __shared__ __align__(16) unsigned char smem[];
+    extern __shared__ __align__(16) unsigned char smem[]; // all of the 160 KB: no static LDS
 
     const int M = a.M, N = a.N, K = a.K, G = a.G;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -135,19 +152,48 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
     const int wm = wave >> 2, wn = wave & 3; // 2 x 4 waves of 128 x 64
     const int h = lane >> 4, col = lane & 15;
 
-    // tiles are dealt out so that each XCD (blocks b, b + 8, ...) takes a contiguous
-    // run of tiles in n-fastest order: its CUs share X rows in their L2
-    // (K slices are the outermost index: unit u = slice * ntiles + tile)
+    // runs are dealt out so that each XCD (blocks b, b + 8, ...) takes a contiguous
+    // stretch of tiles in n-fastest order: its CUs share X rows in their L2
     const int ntiles = p.tiles_m * p.tiles_n;
-    const int nunits = ntiles * p.ksplit;
     const int b = blockIdx.x;
-    int u = (b & 7) * (nunits / 8) + (b >> 3);
-    if ((nunits & 7) != 0)
-        u = b; // uneven split: plain order
-    const int ks = u / ntiles, t = u - ks * ntiles;
-    const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
-    const int g0 = ks * p.gper, g1 = G < g0 + p.gper ? G : g0 + p.gper;
-    const int m0 = tm * BM, n0 = tn * BN;
+    // lo, hi: this workgroup's range of K-split or stream-segment tile-groups; dpr: the
+    // whole tiles it takes first (stream plan), tile k * grid + pos in round k
+    int lo, hi, seg, dpr = 0;
+    if constexpr (STREAM) {
+        seg = (p.grid & 7) == 0 ? (b & 7) * (p.grid >> 3) + (b >> 3) : b;
+        dpr = p.dp_rounds;
+        const long long U = (long long)(ntiles - dpr * p.grid) * G;
+        lo = (int)(U * seg / p.grid);
+        hi = (int)(U * (seg + 1) / p.grid);
+    } else {
+        // K slices are the outermost index: unit u = slice * ntiles + tile
+        const int nunits = ntiles * p.ksplit;
+        int u = (b & 7) * (nunits / 8) + (b >> 3);
+        if ((nunits & 7) != 0)
+            u = b; // uneven split: plain order
+        const int ks = u / ntiles, t = u - ks * ntiles;
+        const int g0 = ks * p.gper, g1 = G < g0 + p.gper ? G : g0 + p.gper;
+        lo = t * G + g0;
+        hi = t * G + g1;
+        seg = ks;
+    }
+    const int total = dpr * G + (hi - lo);
+    const int sk0 = dpr * p.grid * G; // first tile-group of the stream segments
+    // the i-th tile-group of this workgroup: tile t, group g
+    auto unit = [&](int i, int &t, int &g) {
+        if constexpr (!STREAM) {
+            t = lo / G; // one tile
+            g = lo - t * G + i;
+        } else if (i < dpr * G) {
+            const int k = i / G;
+            t = k * p.grid + seg;
+            g = i - k * G;
+        } else {
+            const int u = sk0 + lo + (i - dpr * G);
+            t = u / G;
+            g = u - t * G;
+        }
+    };
 
     const uint16_t *xh = (const uint16_t *)(a.ws + p.off_xh);
     const float *rowscale = (const float *)(a.ws + p.off_rs);
@@ -156,24 +202,35 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales, (uint32_t)((size_t)N * G * 2));
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.qz, (uint32_t)((size_t)(N / 8) * G * 4));
 
-    // DMA of group g into buffer bi: X 8 x 1 KB per wave, words 2 x 1 KB per wave.  The
-    // per-lane offsets of group 0 are computed once; group g adds g * 256 bytes (X) or
-    // g * 64 bytes (words) as the scalar offset.  Rows past M and columns past N start
-    // at kOob: with the scalar offset added the address may wrap to somewhere inside
-    // the tensor, which is harmless (those rows and columns are never stored).
-    uint32_t xoff[8], woff[2];
+    // Per-lane offsets of group 0 of the tile being fetched; group g adds g * 256 bytes
+    // (X), g * 64 (words), 2g (scales), 4g (zero words) as the scalar offset.  Rows past
+    // M and columns past N start at kOob: with the scalar offset added the address may
+    // wrap to somewhere inside the tensor, which is harmless (those rows and columns
+    // are never stored).
+    uint32_t xoff[8], woff[2], soff[4], zoff[4];
+    auto set_tile = [&](int t) {
+        const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
+        const int m0 = tm * BM, n0 = tn * BN;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int s = (wave * 8 + i) * 64 + lane; // X slot: row s/16, swizzled chunk s%16
-        const int row = s >> 4, c = (s & 15) ^ xswz(row);
-        xoff[i] = m0 + row < M ? ((uint32_t)(m0 + row) * (uint32_t)K + (uint32_t)(c * 8)) * 2u : kOob;
-    }
+        for (int i = 0; i < 8; ++i) {
+            const int s = (wave * 8 + i) * 64 + lane; // X slot: row s/16, swizzled chunk s%16
+            const int row = s >> 4, c = (s & 15) ^ xswz(row);
+            xoff[i] = m0 + row < M ? ((uint32_t)(m0 + row) * (uint32_t)K + (uint32_t)(c * 8)) * 2u : kOob;
+        }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int s = (wave * 2 + i) * 64 + lane; // word slot: column s/4, swizzled quarter s%4
-        const int cl = s >> 2, q = (s & 3) ^ ((cl >> 2) & 3);
-        woff[i] = n0 + cl < N ? (uint32_t)(n0 + cl) * (uint32_t)(K / 2) + (uint32_t)(q * 16) : kOob;
-    }
+        for (int i = 0; i < 2; ++i) {
+            const int s = (wave * 2 + i) * 64 + lane; // word slot: column s/4, swizzled quarter s%4
+            const int cl = s >> 2, q = (s & 3) ^ ((cl >> 2) & 3);
+            woff[i] = n0 + cl < N ? (uint32_t)(n0 + cl) * (uint32_t)(K / 2) + (uint32_t)(q * 16) : kOob;
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int n = n0 + wn * 64 + nt * 16 + col;
+            soff[nt] = n < N ? (uint32_t)(n * G) * 2u : kOob;
+            zoff[nt] = n < N ? (uint32_t)((n >> 3) * G) * 4u : kOob;
+        }
+    };
+    // DMA of group g into buffer bi: X 8 x 1 KB per wave, words 2 x 1 KB per wave
     auto issue = [&](int g, int bi) {
         unsigned char *base = smem + bi * kBufBytes;
 #pragma unroll
@@ -183,16 +240,7 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
         for (int i = 0; i < 2; ++i)
             dma16(rw, base + kXBytes + (wave * 2 + i) * 1024, woff[i], (uint32_t)g * 64u);
     };
-
-    // per-lane scale and zero word of the wave's 4 column tiles for group g (offsets of
-    // group 0 once, + 2g / 4g bytes as the scalar offset)
-    uint32_t soff[4], zoff[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int n = n0 + wn * 64 + nt * 16 + col;
-        soff[nt] = n < N ? (uint32_t)(n * G) * 2u : kOob;
-        zoff[nt] = n < N ? (uint32_t)((n >> 3) * G) * 4u : kOob;
-    }
+    // per-lane scale and zero word of the wave's 4 column tiles for group g
     uint32_t sc_raw[4], zw_raw[4];
     auto load_params = [&](int g) {
 #pragma unroll
@@ -214,13 +262,132 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
         for (int j = 0; j < 4; ++j)
             acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    issue(g0, 0);
-    load_params(g0);
+    // Y of the rows and columns of this lane: 2^e_m * (acc + the other part's sums, when
+    // add), stored as bf16 (RNE) or fp32.  rp/other: the other part's region (see finish)
+    auto store_y = [&](int m0, int n0, bool add, __amdgpu_buffer_rsrc_t rp, uint32_t other) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            float rsc[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + wm * 128 + mt * 16 + 4 * h + r;
+                rsc[r] = row < M ? rowscale[row] : 0.f;
+            }
+            // 16 values at a time, so the loads do not all take registers at once
+            float o[4][4];
+            __builtin_amdgcn_sched_barrier(0);
+            if (add) {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        o[nt][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                            rp, other + (uint32_t)(((mt * 4 + nt) * 4 + r) * kThreads * 4), 0, kSc1));
+            } else {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        o[nt][r] = 0.f;
+            }
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int cn = n0 + wn * 64 + nt * 16 + col;
+                if (cn >= N)
+                    continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = m0 + wm * 128 + mt * 16 + 4 * h + r;
+                    if (row < M) {
+                        const size_t off = (size_t)row * N + cn;
+                        const float y = (acc[mt][nt][r] + o[nt][r]) * rsc[r];
+                        if (a.y_f32)
+                            ((float *)a.Y)[off] = y;
+                        else
+                            ((uint16_t *)a.Y)[off] = f32_to_bf16_rne(y);
+                    }
+                }
+            }
+        }
+    };
+
+    // The end of a run of tile t (groups gs .. ge-1), origin (m0, n0), whose last group
+    // computed from LDS buffer bi.  Every thread of the workgroup calls it (the barriers
+    // inside are uniform).
+    auto finish = [&](int m0, int n0, int gs, int ge, int bi) {
+        if (!STREAM && p.ksplit > 1) {
+            // fp32 partial sums of this K slice; reduce_kernel finishes the rows
+            float *part = (float *)(a.ws + p.off_part) + (size_t)seg * M * N;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    const int cn = n0 + wn * 64 + nt * 16 + col;
+                    if (cn >= N)
+                        continue;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = m0 + wm * 128 + mt * 16 + 4 * h + r;
+                        if (row < M)
+                            part[(size_t)row * N + cn] = acc[mt][nt][r];
+                    }
+                }
+            return;
+        }
+        const __amdgpu_buffer_rsrc_t rp =
+            make_rsrc(a.ws + p.off_part, (uint32_t)((size_t)(p.grid - 1) * 2 * BM * BN * sizeof(float)));
+        // A tile split at a segment boundary: the boundary's pair of regions, one per
+        // part ([part][element][thread], so each store instruction covers 256
+        // consecutive bytes), stored and loaded with the sc1 cache policy (the
+        // instructions of relaxed device-scope atomics: coherent across the XCDs' L2s).
+        // (One call site of store_y: a second inlined copy makes the register
+        // allocator spill.)
+        const bool split = STREAM && !(gs == 0 && ge == G); // only stream segments split tiles
+        const int slot = gs == 0 ? seg : seg - 1; // boundary seg + 1 or seg, minus one
+        const int mine = gs == 0 ? 0 : 1;
+        const uint32_t other = ((uint32_t)(slot * 2 + 1 - mine) * (BM * BN) + (uint32_t)tid) * 4u;
+        uint32_t *tk = (uint32_t *)(a.ws + kOffCounters) + slot;
+        if constexpr (STREAM) {
+          if (split) {
+            const uint32_t own = ((uint32_t)(slot * 2 + mine) * (BM * BN) + (uint32_t)tid) * 4u;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            __float_as_uint(acc[mt][nt][r]), rp,
+                            own + (uint32_t)(((mt * 4 + nt) * 4 + r) * kThreads * 4), 0, kSc1);
+            wait_vmem(); // the stores (and anything in flight) have completed
+            __syncthreads();
+            // the arrival order passes through the first word of buffer bi: every wave is
+            // done reading it, and the next DMA into it follows the loop's barrier
+            int *flag = (int *)(smem + bi * kBufBytes);
+            if (tid == 0)
+                *flag = (int)__hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (*flag == 0)
+                return; // the other part finishes the tile (uniform over the workgroup)
+          }
+        }
+        store_y(m0, n0, split, rp, other);
+        if (split && tid == 0)
+            __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+
+    int t, g;
+    unit(0, t, g);
+    int gs = g;
+    set_tile(t);
+    int m0 = (t / p.tiles_n) * BM, n0 = (t % p.tiles_n) * BN;
+    issue(g, 0);
+    load_params(g);
     wait_vmem();
     __syncthreads();
 
-    for (int g = g0; g < g1; ++g) {
-        const int bi = (g - g0) & 1;
+    for (int i = 0; i < total; ++i) {
+        const int bi = i & 1;
         const unsigned char *base = smem + bi * kBufBytes;
         f16x2_t s2[4], zn[4];
 #pragma unroll
@@ -229,9 +396,14 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
             s2[nt] = as_h2((sc_raw[nt] & 0xFFFFu) * 0x00010001u);
             zn[nt] = as_h2((0xE400u | ((zw_raw[nt] >> zsh) & 15u)) * 0x00010001u); // -(1024 + z)
         }
-        if (g + 1 < g1) {
-            issue(g + 1, bi ^ 1);
-            load_params(g + 1);
+        // the next tile-group, possibly of another tile: fetched while this one computes
+        int tn = t, gn = g;
+        if (i + 1 < total) {
+            unit(i + 1, tn, gn);
+            if (tn != t)
+                set_tile(tn);
+            issue(gn, bi ^ 1);
+            load_params(gn);
         }
 
         // the 4 words (k-steps 0..3) of each of the lane's 4 columns
@@ -274,56 +446,26 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
             }
         }
 
+        if (STREAM && (i + 1 == total || tn != t)) {
+            finish(m0, n0, gs, g + 1, bi);
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y)
+                    acc[x][y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
         wait_vmem(); // the next group's DMA and parameters have landed
         __syncthreads();
-    }
-
-    if (p.ksplit > 1) {
-        // fp32 partial sums of this K slice; reduce_kernel finishes the rows
-        float *part = (float *)(a.ws + p.off_part) + (size_t)ks * M * N;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int cn = n0 + wn * 64 + nt * 16 + col;
-                if (cn >= N)
-                    continue;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = m0 + wm * 128 + mt * 16 + 4 * h + r;
-                    if (row < M)
-                        part[(size_t)row * N + cn] = acc[mt][nt][r];
-                }
-            }
-        return;
-    }
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-        float rsc[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = m0 + wm * 128 + mt * 16 + 4 * h + r;
-            rsc[r] = row < M ? rowscale[row] : 0.f;
+        if (tn != t) {
+            t = tn;
+            gs = gn;
+            m0 = (t / p.tiles_n) * BM;
+            n0 = (t % p.tiles_n) * BN;
         }
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const int cn = n0 + wn * 64 + nt * 16 + col;
-            if (cn >= N)
-                continue;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm * 128 + mt * 16 + 4 * h + r;
-                if (row < M) {
-                    const size_t o = (size_t)row * N + cn;
-                    const float y = acc[mt][nt][r] * rsc[r];
-                    if (a.y_f32)
-                        ((float *)a.Y)[o] = y;
-                    else
-                        ((uint16_t *)a.Y)[o] = f32_to_bf16_rne(y);
-                }
-            }
-        }
+        g = gn;
     }
+    if constexpr (!STREAM)
+        finish(m0, n0, gs, gs + total, 0); // the one tile (or K slice) of this workgroup
 }
 
 // Y[m, 4c .. 4c+3] = 2^e_m * sum over slices s (in order) of part[s][m][4c ..]; N % 8 == 0
@@ -365,11 +507,18 @@ TiledPlan plan_tiled(int M, int N, int K)
     p.G = K / kGroup;
     p.tiles_m = (M + BM - 1) / BM;
     p.tiles_n = (N + BN - 1) / BN;
-    // K slices: estimated time = rounds * groups per round (one tile-group ~ 3.5 us on a
-    // CU) plus the traffic of the partial sums (~5 TB/s) for ksplit > 1
     const long long ntiles = (long long)p.tiles_m * p.tiles_n;
     const int kCUs = 256;
+    p.off_xh = kZeroRegion;
+    p.off_rs = round_up(p.off_xh + (size_t)M * K * 2, 256);
+    p.off_part = round_up(p.off_rs + (size_t)M * sizeof(float), 256);
+    // Estimated time of each plan: rounds * groups per round (one tile-group ~ 3.5 us on
+    // a CU), plus the traffic of the partial sums (~5 TB/s) for K slices; the stream
+    // plan (at least one tile per CU) spreads the tile-groups evenly over the CUs at
+    // about 10% more per tile-group (split tiles meet in memory; measured on MI355X)
     double best = 1e30;
+    p.stream = 0;
+    p.dp_rounds = 0;
     p.ksplit = 1;
     for (int ks = 1; ks <= 4 && ks <= p.G; ++ks) {
         const int gper = (p.G + ks - 1) / ks;
@@ -382,11 +531,23 @@ TiledPlan plan_tiled(int M, int N, int K)
             p.ksplit = ks;
         }
     }
+    if (ntiles >= kCUs && (double)ntiles * p.G / kCUs * 3.5e-6 * 1.1 < best) {
+        // one segment of tile-groups per CU, balanced to one tile-group, after whole
+        // tiles in all rounds but the last two (tile k * grid + pos, so that the tiles in
+        // flight at a time are neighbours that share X rows in L2); the segments (at
+        // least G each) split at most one tile at each inner boundary: a pair of fp32
+        // regions and an arrival counter per boundary
+        p.stream = 1;
+        p.grid = kCUs;
+        p.dp_rounds = (int)(ntiles / kCUs) - 1;
+        p.ksplit = 1;
+        p.gper = p.G;
+        p.ws_bytes = p.off_part + (size_t)(p.grid - 1) * 2 * BM * BN * sizeof(float);
+        return p;
+    }
     p.gper = (p.G + p.ksplit - 1) / p.ksplit;
     p.ksplit = (p.G + p.gper - 1) / p.gper; // no empty slices
-    p.off_xh = kZeroRegion;
-    p.off_rs = round_up(p.off_xh + (size_t)M * K * 2, 256);
-    p.off_part = round_up(p.off_rs + (size_t)M * sizeof(float), 256);
+    p.grid = (int)(ntiles * p.ksplit);
     p.ws_bytes = p.off_part + (p.ksplit > 1 ? (size_t)p.ksplit * M * N * sizeof(float) : 0);
     return p;
 }
@@ -395,8 +556,11 @@ hipError_t launch_tiled(const TiledArgs &a, const TiledPlan &p, hipStream_t stre
 {
     static bool lds_set = false;
     if (!lds_set) {
-        const hipError_t e = hipFuncSetAttribute((const void *)tiled_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 kLdsBytes);
+        hipError_t e = hipFuncSetAttribute((const void *)tiled_kernel<false>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void *)tiled_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    kLdsBytes);
         if (e != hipSuccess)
             return e;
         lds_set = true;
@@ -406,7 +570,10 @@ hipError_t launch_tiled(const TiledArgs &a, const TiledPlan &p, hipStream_t stre
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(tiled_kernel, dim3(p.tiles_m * p.tiles_n * p.ksplit), dim3(kThreads), kLdsBytes, stream, a, p);
+    if (p.stream)
+        hipLaunchKernelGGL(tiled_kernel<true>, dim3(p.grid), dim3(kThreads), kLdsBytes, stream, a, p);
+    else
+        hipLaunchKernelGGL(tiled_kernel<false>, dim3(p.grid), dim3(kThreads), kLdsBytes, stream, a, p);
     e = hipGetLastError();
     if (e != hipSuccess || p.ksplit == 1)
         return e;

@@ -105,7 +105,11 @@ def _dyadic(seed, M, N, K):
 
 DYADIC = [(1, 9728, 2560), (1, 2560, 9728), (16, 4096, 2560), (16, 2560, 9728), (16, 1000, 640),
           (16, 264, 9728), (7, 520, 5248), (37, 520, 1280), (300, 1032, 2560), (8192, 9728, 2560),
-          (8192, 2560, 9728)]
+          (8192, 2560, 9728),
+          # at least one tile per CU (balanced segments of tile-groups): tiles split at
+          # segment boundaries, ragged last row and column tiles, 3 and 10 groups per tile;
+          # 540 tiles: a round of whole tiles before the segments
+          (4300, 4104, 384), (4352, 4096, 1280), (5100, 6664, 384)]
 
 
 @pytest.mark.parametrize("M,N,K", DYADIC)
@@ -222,7 +226,8 @@ def test_lmhead_ties_pick_lowest_column(dev):
 
 # ------------------------------------------------------------------ determinism, reuse, edges
 
-@pytest.mark.parametrize("M,N,K", [(1, 2560, 9728), (16, 2560, 9728), (16, 1024, 2560), (300, 520, 1280)])
+@pytest.mark.parametrize("M,N,K", [(1, 2560, 9728), (16, 2560, 9728), (16, 1024, 2560), (300, 520, 1280),
+                                   (4300, 4104, 384)])
 def test_deterministic_and_workspace_reuse(dev, M, N, K):
     d = synth.linear_inputs(99, M, N, K)
     t, qw, qz, _, _ = _prep(d, dev)
