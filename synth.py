@@ -99,3 +99,61 @@ def force_prefix(draft, L0, target_ids, rng, N):
         while d[L0] == target_ids[L0]:
             d[L0] = int(rng.integers(0, N))
     return d
+
+
+# ---------------------------------------------------------------- closed forms
+# Inputs at the size limits (about 2^31 elements) are too large to draw on the host.
+# They follow closed forms of their indices instead, evaluated on the device for the
+# whole tensor and on the host for the rows or columns a test samples; every value
+# is dyadic (integer activations, power-of-two scales), so any summation order of
+# the layer gives the exact result.
+
+def cf_x(rows, K):
+    """bf16 bits of X[m, k] = ((7m + 13k + (m k mod 11)) mod 17) - 8 for m in rows."""
+    m = np.asarray(rows, np.int64)[:, None]
+    k = np.arange(K, dtype=np.int64)[None, :]
+    v = (m * 7 + k * 13 + (m * k) % 11) % 17 - 8
+    return f32_to_bf16_bits(v.astype(np.float32))
+
+
+def cf_codes(cols, K):
+    """codes[n, k] = (5n + 3k + (n k mod 7)) mod 16 for n in cols (uint8)."""
+    n = np.asarray(cols, np.int64)[:, None]
+    k = np.arange(K, dtype=np.int64)[None, :]
+    return ((n * 5 + k * 3 + (n * k) % 7) % 16).astype(np.uint8)
+
+
+def cf_zeros(cols, G):
+    """zeros[n, g] = (3n + 5g) mod 16 (uint8)."""
+    n = np.asarray(cols, np.int64)[:, None]
+    g = np.arange(G, dtype=np.int64)[None, :]
+    return ((n * 3 + g * 5) % 16).astype(np.uint8)
+
+
+def cf_scales(cols, G):
+    """fp16 bits of scales[n, g] = 2^-(6 + (n + g) mod 4)."""
+    n = np.asarray(cols, np.int64)[:, None]
+    g = np.arange(G, dtype=np.int64)[None, :]
+    return f32_to_f16_bits(np.ldexp(1.0, -(6 + (n + g) % 4)).astype(np.float32))
+
+
+def cf_x_torch(M, K, device, chunk=1 << 16):
+    """cf_x for rows 0..M-1 on a torch device, as a bf16 tensor [M, K]."""
+    import torch
+    out = torch.empty((M, K), dtype=torch.bfloat16, device=device)
+    k = torch.arange(K, dtype=torch.int64, device=device)[None, :]
+    for r0 in range(0, M, chunk):
+        m = torch.arange(r0, min(M, r0 + chunk), dtype=torch.int64, device=device)[:, None]
+        out[r0:r0 + m.shape[0]] = ((m * 7 + k * 13 + (m * k) % 11) % 17 - 8).to(torch.bfloat16)
+    return out
+
+
+def cf_codes_torch(N, K, device, chunk=1 << 16):
+    """cf_codes for columns 0..N-1 on a torch device, as uint8 [N, K]."""
+    import torch
+    out = torch.empty((N, K), dtype=torch.uint8, device=device)
+    k = torch.arange(K, dtype=torch.int64, device=device)[None, :]
+    for r0 in range(0, N, chunk):
+        n = torch.arange(r0, min(N, r0 + chunk), dtype=torch.int64, device=device)[:, None]
+        out[r0:r0 + n.shape[0]] = ((n * 5 + k * 3 + (n * k) % 7) % 16).to(torch.uint8)
+    return out

@@ -77,7 +77,10 @@ def _check_replays(dev, ws, run, outs):
 
 
 @pytest.mark.parametrize("M,N,K,f32", [(16, 2560, 9728, True), (1, 9728, 2560, False), (5, 2560, 9728, True),
-                                       (300, 520, 1280, True)])
+                                       (300, 520, 1280, True),
+                                       # the prefill stream plan: tiles split at segment boundaries
+                                       # meet through arrival counters that each call returns to zero
+                                       (4300, 4104, 384, True)])
 def test_linear_graph_replays(dev, M, N, K, f32):
     print("graph linear", M, N, K, flush=True)
     X, qw, S, qz = _packed(11 + M, M, N, K, dev)
