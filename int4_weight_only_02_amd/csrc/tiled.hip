@@ -126,21 +126,21 @@ __device__ __forceinline__ f16x8_t dequant_word(uint32_t w, uint32_t mask, uint3
     return f16x8_t{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
 }
 
-// The work of a workgroup is a run of consecutive tile-groups u = t * G + g (tile t,
-// group g; tiles n-fastest), computed through one software pipeline that also runs
-// across tile boundaries (the next tile's first group is fetched while the current
-// tile's last group computes).
-//   split plan  (stream == 0): one tile, one K slice [ks * gper, ...) per workgroup;
+// A workgroup computes a sequence of tile-groups (tile t, group g; tiles n-fastest)
+// through one software pipeline that also runs across tile boundaries (the next
+// tile's first group is fetched while the current tile's last group computes).
+//   split plan  (STREAM false): one tile, one K slice [ks * gper, ...) per workgroup;
 //               with ksplit > 1 the slice's fp32 partial sums go to the workspace and
 //               reduce_kernel finishes Y;
-//   stream plan (stream == 1, at least one tile per CU): workgroup b first takes whole
+//   stream plan (STREAM true, at least one tile per CU): workgroup b first takes whole
 //               tiles, one per round (all rounds but the last one or two), then owns
 //               segment s of the remaining tiles' tile-groups; segments differ by at
 //               most one tile-group and hold at least G, so a tile is either whole in
-//               one segment or split in two parts at one segment boundary.  Both parts store their fp32 sums in
-//               the workspace and take a ticket; the second to arrive adds the other
-//               part (a + b = b + a in fp32, so the result does not depend on the
-//               arrival order), scales and stores Y, and returns the ticket to zero.
+//               one segment or split in two parts at one segment boundary.  Both parts
+//               store their fp32 sums in the workspace and take a ticket; the second
+//               to arrive adds the other part (a + b = b + a in fp32, so the result
+//               does not depend on the arrival order), scales and stores Y, and
+//               returns the ticket to zero.
 template <bool STREAM>
 __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan p)
 {
