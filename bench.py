@@ -665,6 +665,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--only", default=None, help="time one workload only (profiling runs)")
+    ap.add_argument("--proj", default=None, help="with --only: keep only the projection of this label "
+                    "(e.g. gate_up or down of prefill_m8192), for per-shape counter runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib", action="store_true")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV", "CALIB_WRITE_CSV"),
@@ -687,6 +689,13 @@ def main():
         calib_copy(dev)
         return
 
+    if args.proj:
+        if not args.only or args.only not in synth.WORKLOADS:
+            raise SystemExit("--proj needs --only with a linear workload")
+        keep = [p for p in synth.WORKLOADS[args.only] if p[0] == args.proj]
+        if not keep:
+            raise SystemExit("no projection %r in %s" % (args.proj, args.only))
+        synth.WORKLOADS[args.only] = keep
     names = [HEADLINE, "single_512", "verify_block_m16", "lmhead_verify_m16", "prefill_m8192",
              "verify_block_m16+batch", "requantize_9728x2560", "actorder_gate_m16", "swa_verify_m16_t8192",
              "mlp_gate_up_gated"]
