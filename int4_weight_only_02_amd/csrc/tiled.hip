@@ -515,7 +515,7 @@ TiledPlan plan_tiled(int M, int N, int K)
     // Estimated time of each plan: rounds * groups per round (one tile-group ~ 3.5 us on
     // a CU), plus the traffic of the partial sums (~5 TB/s) for K slices; the stream
     // plan (at least one tile per CU) spreads the tile-groups evenly over the CUs at
-    // about 3% more per tile-group (split tiles meet in memory; measured on MI355X)
+    // about 10% more per tile-group (split tiles meet in memory; measured on MI355X)
     double best = 1e30;
     p.stream = 0;
     p.dp_rounds = 0;
@@ -531,7 +531,7 @@ TiledPlan plan_tiled(int M, int N, int K)
             p.ksplit = ks;
         }
     }
-    if (ntiles >= kCUs && (double)ntiles * p.G / kCUs * 3.5e-6 * 1.03 < best) {
+    if (ntiles >= kCUs && (double)ntiles * p.G / kCUs * 3.5e-6 * 1.1 < best) {
         // one segment of tile-groups per CU, balanced to one tile-group, after whole
         // tiles in all rounds but the last two (tile k * grid + pos, so that the tiles in
         // flight at a time are neighbours that share X rows in L2); the segments (at
