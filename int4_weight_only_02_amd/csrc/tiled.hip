@@ -67,7 +67,28 @@ __device__ __forceinline__ int xswz(int r) { return ((r & 7) << 1) | ((r >> 3) &
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); } // vmcnt(0)
 
 // One row per workgroup: X[m] * 2^-e as fp16 (chunks permuted to the fragment order),
-// and 2^e into rowscale[m].
+// and 2^e into rowscale[m].  A row of up to kPrepHeld * 256 chunks of 8 (K <= 16384) is
+// read once, into registers, all loads in flight together; longer rows are read twice.
+constexpr int kPrepHeld = 8;
+
+__device__ __forceinline__ float absmax8(const u32x4_t &v)
+{
+    return fmaxf(fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))), fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))),
+                 fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))), fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
+}
+
+// eight activations times 2^-e, as fp16 in the fragment order k0 k4 k1 k5 k2 k6 k3 k7
+__device__ __forceinline__ u32x4_t scale8(const u32x4_t &v, float down)
+{
+    const float f0 = bf16_lo(v.x) * down, f1 = bf16_hi(v.x) * down;
+    const float f2 = bf16_lo(v.y) * down, f3 = bf16_hi(v.y) * down;
+    const float f4 = bf16_lo(v.z) * down, f5 = bf16_hi(v.z) * down;
+    const float f6 = bf16_lo(v.w) * down, f7 = bf16_hi(v.w) * down;
+    const f16x8_t o = {(_Float16)f0, (_Float16)f4, (_Float16)f1, (_Float16)f5,
+                       (_Float16)f2, (_Float16)f6, (_Float16)f3, (_Float16)f7};
+    return __builtin_bit_cast(u32x4_t, o);
+}
+
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t *X, int K, uint16_t *Xh, float *rowscale)
 {
     __shared__ float wmax[4];
@@ -75,12 +96,20 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t *X, int K, uin
     const u32x4_t *xr = (const u32x4_t *)(X + (size_t)m * K);
     u32x4_t *hr = (u32x4_t *)(Xh + (size_t)m * K);
     const int nc = K / 8;
+    const bool held = nc <= kPrepHeld * 256; // uniform
 
+    u32x4_t v[kPrepHeld];
     float mx = 0.f;
-    for (int c = tid; c < nc; c += 256) {
-        const u32x4_t v = xr[c];
-        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))), fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))));
-        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))), fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
+    if (held) {
+#pragma unroll
+        for (int i = 0; i < kPrepHeld; ++i)
+            v[i] = tid + i * 256 < nc ? xr[tid + i * 256] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < kPrepHeld; ++i)
+            mx = fmaxf(mx, absmax8(v[i]));
+    } else {
+        for (int c = tid; c < nc; c += 256)
+            mx = fmaxf(mx, absmax8(xr[c]));
     }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1)
@@ -99,16 +128,14 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t *X, int K, uin
     if (tid == 0)
         rowscale[m] = __uint_as_float((uint32_t)(127 + e) << 23); // 2^e
 
-    for (int c = tid; c < nc; c += 256) {
-        const u32x4_t v = xr[c];
-        const float f0 = bf16_lo(v.x) * down, f1 = bf16_hi(v.x) * down;
-        const float f2 = bf16_lo(v.y) * down, f3 = bf16_hi(v.y) * down;
-        const float f4 = bf16_lo(v.z) * down, f5 = bf16_hi(v.z) * down;
-        const float f6 = bf16_lo(v.w) * down, f7 = bf16_hi(v.w) * down;
-        // fragment order k0 k4 k1 k5 k2 k6 k3 k7
-        const f16x8_t o = {(_Float16)f0, (_Float16)f4, (_Float16)f1, (_Float16)f5,
-                           (_Float16)f2, (_Float16)f6, (_Float16)f3, (_Float16)f7};
-        hr[c] = __builtin_bit_cast(u32x4_t, o);
+    if (held) {
+#pragma unroll
+        for (int i = 0; i < kPrepHeld; ++i)
+            if (tid + i * 256 < nc)
+                hr[tid + i * 256] = scale8(v[i], down);
+    } else {
+        for (int c = tid; c < nc; c += 256)
+            hr[c] = scale8(xr[c], down);
     }
 }
 
