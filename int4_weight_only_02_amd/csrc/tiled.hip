@@ -290,16 +290,19 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
             acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // Y of the rows and columns of this lane: 2^e_m * (acc + the other part's sums, when
-    // add), stored as bf16 (RNE) or fp32.  rp/other: the other part's region (see finish)
+    // add), stored as bf16 (RNE, the hardware conversion) or fp32.  The row scales of
+    // all the lane's rows (four consecutive rows per 16-byte load) are requested before
+    // the first store, so waiting for them waits for no store (the memory counter the
+    // wait uses also counts stores).  rp/other: the other part's region (see finish).
     auto store_y = [&](int m0, int n0, bool add, __amdgpu_buffer_rsrc_t rp, uint32_t other) {
+        const __amdgpu_buffer_rsrc_t rr = make_rsrc(rowscale, (uint32_t)((size_t)M * sizeof(float)));
+        f32x4_t rsc[8]; // rows past M read 0 (never stored)
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            rsc[mt] = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rr, (uint32_t)(m0 + wm * 128 + mt * 16 + 4 * h) * 4u, 0, 0));
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-            float rsc[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm * 128 + mt * 16 + 4 * h + r;
-                rsc[r] = row < M ? rowscale[row] : 0.f;
-            }
             // 16 values at a time, so the loads do not all take registers at once
             float o[4][4];
             __builtin_amdgcn_sched_barrier(0);
@@ -327,11 +330,11 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
                     const int row = m0 + wm * 128 + mt * 16 + 4 * h + r;
                     if (row < M) {
                         const size_t off = (size_t)row * N + cn;
-                        const float y = (acc[mt][nt][r] + o[nt][r]) * rsc[r];
+                        const float y = (acc[mt][nt][r] + o[nt][r]) * rsc[mt][r];
                         if (a.y_f32)
                             ((float *)a.Y)[off] = y;
                         else
-                            ((uint16_t *)a.Y)[off] = f32_to_bf16_rne(y);
+                            ((__bf16 *)a.Y)[off] = (__bf16)y;
                     }
                 }
             }
@@ -398,6 +401,7 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
                 return; // the other part finishes the tile (uniform over the workgroup)
           }
         }
+        (void)bi;
         store_y(m0, n0, split, rp, other);
         if (split && tid == 0)
             __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -109,7 +109,9 @@ DYADIC = [(1, 9728, 2560), (1, 2560, 9728), (16, 4096, 2560), (16, 2560, 9728), 
           # at least one tile per CU (balanced segments of tile-groups): tiles split at
           # segment boundaries, ragged last row and column tiles, 3 and 10 groups per tile;
           # 540 tiles: a round of whole tiles before the segments
-          (4300, 4104, 384), (4352, 4096, 1280), (5100, 6664, 384)]
+          (4300, 4104, 384), (4352, 4096, 1280), (5100, 6664, 384),
+          # 510 tiles, one per workgroup: the LDS-staged epilogue at ragged row and column edges
+          (4300, 7624, 384)]
 
 
 @pytest.mark.parametrize("M,N,K", DYADIC)
