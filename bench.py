@@ -48,7 +48,12 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
 def algo_bytes(M, N, K, out_bytes=2, lmhead=False):
+    """Bytes a call must move: the packed grid, X, and Y (out_bytes per output).  The
+    lm_head call as timed here writes no logits, only the argmax ids and the accepted
+    length (and reads the draft ids)."""
     G = K // 128
+    if lmhead:
+        out_bytes = 0
     b = N * K // 2 + 2 * N * G + N * G // 2 + 2 * M * K + out_bytes * M * N
     if lmhead:
         b += 4 * M + 4 * M + 4  # draft ids in, argmax ids + accept length out
