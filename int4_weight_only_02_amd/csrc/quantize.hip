@@ -61,24 +61,27 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t *W, const 
                                                        const uint32_t *qzeros, int N, int K, int G,
                                                        uint32_t *qweight)
 {
-    const long long KW = K / 8;
-    const long long words = (long long)N * KW;
-    const long long step = (long long)gridDim.x * 256;
-    for (long long i0 = (long long)blockIdx.x * 256 + threadIdx.x; i0 < words; i0 += step * kWordsPerThread) {
+    // word i = n * KW + w (row n, word w of the row); N * K <= 2^31 - 256, so i fits in
+    // 32 bits: one 32-bit division per word gives the row, a shift the group
+    const uint32_t KW = (uint32_t)(K / 8);
+    const uint32_t words = (uint32_t)N * KW;
+    const uint32_t step = gridDim.x * 256u;
+    for (uint32_t i0 = blockIdx.x * 256u + threadIdx.x; i0 < words; i0 += step * kWordsPerThread) {
         u32x4_t v[kWordsPerThread];
         float sc[kWordsPerThread], zf[kWordsPerThread];
 #pragma unroll
         for (int u = 0; u < kWordsPerThread; ++u) {
-            const long long i = i0 + u * step < words ? i0 + u * step : words - 1;
-            const int n = (int)(i / KW);
-            const int g = (int)((i - (long long)n * KW) / (kGroup / 8));
+            const uint32_t iu = i0 + u * step;
+            const uint32_t i = iu < words ? iu : words - 1;
+            const uint32_t n = i / KW;
+            const uint32_t g = (i - n * KW) >> 4; // 16 words per group of 128
             v[u] = ((const u32x4_t *)W)[i];
             sc[u] = f16_bits_to_f32(scales[(size_t)n * G + g]);
             zf[u] = (float)((qzeros[(size_t)(n >> 3) * G + g] >> (4 * (n & 7))) & 15u);
         }
 #pragma unroll
         for (int u = 0; u < kWordsPerThread; ++u) {
-            const long long i = i0 + u * step;
+            const uint32_t i = i0 + u * step;
             if (i < words)
                 qweight[i] = quantize_word(v[u], sc[u], zf[u]);
         }
