@@ -22,11 +22,12 @@ namespace {
 template <typename T>
 __global__ __launch_bounds__(256) void gather_k_kernel(const T *src, const int32_t *perm, int rows, int K, T *dst)
 {
-    const int KB = K / 8;
-    const long long blocks = (long long)rows * KB;
-    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < blocks; i += (long long)gridDim.x * 256) {
+    // rows * K <= 2^31 - 256: block indices fit in 32 bits (a 32-bit division per block)
+    const uint32_t KB = (uint32_t)(K / 8);
+    const uint32_t blocks = (uint32_t)rows * KB;
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < blocks; i += gridDim.x * 256u) {
         const int r = (int)(i / KB);
-        const int j0 = (int)(i - (long long)r * KB) * 8;
+        const int j0 = (int)(i - (uint32_t)r * KB) * 8;
         const u32x4_t p0 = *(const u32x4_t *)(perm + j0);
         const u32x4_t p1 = *(const u32x4_t *)(perm + j0 + 4);
         const T *row = src + (size_t)r * K;
@@ -45,12 +46,12 @@ __global__ __launch_bounds__(256) void gather_k_kernel(const T *src, const int32
 __global__ __launch_bounds__(256) void pack_codes_perm_kernel(const uint8_t *codes, const int32_t *perm, int N,
                                                               int K, uint32_t *qweight)
 {
-    const int KW = K / 8;
-    const long long words = (long long)N * KW;
+    const uint32_t KW = (uint32_t)(K / 8);
+    const uint32_t words = (uint32_t)N * KW; // N * K <= 2^31 - 256
     const uint32_t last = (uint32_t)K - 1u;
-    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < words; i += (long long)gridDim.x * 256) {
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < words; i += gridDim.x * 256u) {
         const int n = (int)(i / KW);
-        const int j0 = (int)(i - (long long)n * KW) * 8;
+        const int j0 = (int)(i - (uint32_t)n * KW) * 8;
         const u32x4_t p0 = *(const u32x4_t *)(perm + j0);
         const u32x4_t p1 = *(const u32x4_t *)(perm + j0 + 4);
         const uint8_t *row = codes + (size_t)n * K;
