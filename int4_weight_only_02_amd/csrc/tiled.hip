@@ -99,14 +99,17 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t *X, int K, uin
     const bool held = nc <= kPrepHeld * 256; // uniform
 
     u32x4_t v[kPrepHeld];
+    const int rounds = (nc + 255) / 256; // uniform: rounds past it are skipped
     float mx = 0.f;
     if (held) {
 #pragma unroll
         for (int i = 0; i < kPrepHeld; ++i)
-            v[i] = tid + i * 256 < nc ? xr[tid + i * 256] : u32x4_t{0u, 0u, 0u, 0u};
+            if (i < rounds)
+                v[i] = tid + i * 256 < nc ? xr[tid + i * 256] : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < kPrepHeld; ++i)
-            mx = fmaxf(mx, absmax8(v[i]));
+            if (i < rounds)
+                mx = fmaxf(mx, absmax8(v[i]));
     } else {
         for (int c = tid; c < nc; c += 256)
             mx = fmaxf(mx, absmax8(xr[c]));
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t *X, int K, uin
     if (held) {
 #pragma unroll
         for (int i = 0; i < kPrepHeld; ++i)
-            if (tid + i * 256 < nc)
+            if (i < rounds && tid + i * 256 < nc)
                 hr[tid + i * 256] = scale8(v[i], down);
     } else {
         for (int c = tid; c < nc; c += 256)
