@@ -381,30 +381,31 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
         const uint32_t other = ((uint32_t)(slot * 2 + 1 - mine) * (BM * BN) + (uint32_t)tid) * 4u;
         uint32_t *tk = (uint32_t *)(a.ws + kOffCounters) + slot;
         if constexpr (STREAM) {
-          if (split) {
-            const uint32_t own = ((uint32_t)(slot * 2 + mine) * (BM * BN) + (uint32_t)tid) * 4u;
+            if (split) {
+                const uint32_t own = ((uint32_t)(slot * 2 + mine) * (BM * BN) + (uint32_t)tid) * 4u;
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
+                for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
+                    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        __builtin_amdgcn_raw_buffer_store_b32(
-                            __float_as_uint(acc[mt][nt][r]), rp,
-                            own + (uint32_t)(((mt * 4 + nt) * 4 + r) * kThreads * 4), 0, kSc1);
-            wait_vmem(); // the stores (and anything in flight) have completed
-            __syncthreads();
-            // the arrival order passes through the first word of buffer bi: every wave is
-            // done reading it, and the next DMA into it follows the loop's barrier
-            int *flag = (int *)(smem + bi * kBufBytes);
-            if (tid == 0)
-                *flag = (int)__hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
-            if (*flag == 0)
-                return; // the other part finishes the tile (uniform over the workgroup)
-          }
+                        for (int r = 0; r < 4; ++r)
+                            __builtin_amdgcn_raw_buffer_store_b32(
+                                __float_as_uint(acc[mt][nt][r]), rp,
+                                own + (uint32_t)(((mt * 4 + nt) * 4 + r) * kThreads * 4), 0, kSc1);
+                wait_vmem(); // the stores (and anything in flight) have completed
+                __syncthreads();
+                // the arrival order passes through the first word of buffer bi: every wave
+                // is done reading it, and the next DMA into it follows the loop's barrier
+                int *flag = (int *)(smem + bi * kBufBytes);
+                if (tid == 0)
+                    *flag = (int)__hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __syncthreads();
+                if (*flag == 0)
+                    return; // the other part finishes the tile (uniform over the workgroup)
+            }
+        } else {
+            (void)bi; // the split plan finishes after its loop, with no buffer in use
         }
-        (void)bi;
         store_y(m0, n0, split, rp, other);
         if (split && tid == 0)
             __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
