@@ -548,6 +548,43 @@ def measure_gated(dev, steps, warmup, N=9728, K=2560):
     return out
 
 
+def measure_gemm_ceiling(dev, steps, warmup):
+    """Context for the prefill figure, not part of the layer: a plain dense bf16 GEMM of
+    the prefill shapes through the vendor library (torch.mm -> hipBLASLt), fp32
+    accumulation, no quantization -- what a tuned library reaches on these shapes with
+    no dequantization work at all.  Back-to-back eager calls over two weight copies,
+    HIP events on the current stream (each call runs hundreds of microseconds)."""
+    import torch
+    out = {}
+    M = 8192
+    for label, K, N in (("gate_up", 2560, 9728), ("down", 9728, 2560)):
+        g = torch.Generator(device=dev)
+        g.manual_seed(1000 + K)
+        X = torch.randn((M, K), device=dev, generator=g).to(torch.bfloat16)
+        Ws = [(torch.randn((N, K), device=dev, generator=g) * 0.02).to(torch.bfloat16).t().contiguous()
+              for _ in range(2)]  # [K, N], contiguous (no transposed views)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        for r in range(4):
+            torch.mm(X, Ws[r % 2], out=Y)
+        torch.cuda.synchronize()
+        reps = max(4, min(steps, 40))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps):
+            torch.mm(X, Ws[r % 2], out=Y)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / reps
+        tf = 2.0 * M * N * K / t / 1e12
+        out[label] = {"M": M, "K": K, "N": N, "us_per_call": round(t * 1e6, 2), "TFLOPs": round(tf, 1),
+                      "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+        del X, Ws, Y
+        torch.cuda.empty_cache()
+    out["note"] = "dense bf16 torch.mm (hipBLASLt), unquantized weights: an achievable-ceiling reference only"
+    return out
+
+
 def measure_swa(dev, steps, warmup, M=16, T=8192, Hq=32, Hkv=8, window=1024):
     """The drafter's sliding-window attention for one verify block: M = 16 queries at
     the end of an 8192-token context, 32 query heads over 8 key/value heads of 128,
@@ -703,14 +740,16 @@ def main():
         synth.WORKLOADS[args.only] = keep
     names = [HEADLINE, "single_512", "verify_block_m16", "lmhead_verify_m16", "prefill_m8192",
              "verify_block_m16+batch", "requantize_9728x2560", "actorder_gate_m16", "swa_verify_m16_t8192",
-             "mlp_gate_up_gated"]
+             "mlp_gate_up_gated", "prefill_bf16_gemm_library"]
     if args.only:
         names = [args.only]
     results = {}
     for key in names:
-        if key in ("requantize_9728x2560", "actorder_gate_m16", "swa_verify_m16_t8192", "mlp_gate_up_gated"):
+        if key in ("requantize_9728x2560", "actorder_gate_m16", "swa_verify_m16_t8192", "mlp_gate_up_gated",
+                   "prefill_bf16_gemm_library"):
             fn = {"requantize_9728x2560": measure_requant, "actorder_gate_m16": measure_actorder,
-                  "swa_verify_m16_t8192": measure_swa, "mlp_gate_up_gated": measure_gated}[key]
+                  "swa_verify_m16_t8192": measure_swa, "mlp_gate_up_gated": measure_gated,
+                  "prefill_bf16_gemm_library": measure_gemm_ceiling}[key]
             results[key] = fn(dev, max(64, min(args.steps, 1000)), 32)
             print("[bench] %s: %s" % (key, json.dumps(results[key])), file=sys.stderr, flush=True)
             continue
