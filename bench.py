@@ -20,7 +20,8 @@ one step = both projections.  Prints ONE JSON line with:
                  prefill at M = 8192 (TFLOP/s against the bf16 MFMA peak), and the
                  further calls: the layer in four batched launches, re-quantization,
                  an act-order projection, sliding-window attention and the gated
-                 gate/up pair (silu(gate) * up in one launch)
+                 gate/up pair (silu(gate) * up in one launch); and, as context only, a
+                 dense bf16 library GEMM (hipBLASLt) of the prefill shapes
 Options: --only WORKLOAD times one workload (for profiling runs), --calib runs a
 plain copy of known size (HBM counter calibration), --pmc-summary writes the
 traffic summary from the counter CSVs of those runs (no GPU needed).
