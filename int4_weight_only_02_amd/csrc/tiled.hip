@@ -292,12 +292,12 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
         for (int j = 0; j < 4; ++j)
             acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Y of the rows and columns of this lane: 2^e_m * (acc + the other part's sums, when
-    // add), stored as bf16 (RNE, the hardware conversion) or fp32.  The row scales of
-    // all the lane's rows (four consecutive rows per 16-byte load) are requested before
-    // the first store, so waiting for them waits for no store (the memory counter the
-    // wait uses also counts stores).  rp/other: the other part's region (see finish).
-    auto store_y = [&](int m0, int n0, bool add, __amdgpu_buffer_rsrc_t rp, uint32_t other) {
+    // Y of the rows and columns of this lane: 2^e_m * acc, stored as bf16 (RNE, the
+    // hardware conversion) or fp32.  The row scales of all the lane's rows (four
+    // consecutive rows per 16-byte load) are requested before the first store, so
+    // waiting for them waits for no store (the memory counter the wait uses also counts
+    // stores).
+    auto store_y = [&](int m0, int n0) {
         const __amdgpu_buffer_rsrc_t rr = make_rsrc(rowscale, (uint32_t)((size_t)M * sizeof(float)));
         f32x4_t rsc[8]; // rows past M read 0 (never stored)
 #pragma unroll
@@ -306,23 +306,6 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
                 f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rr, (uint32_t)(m0 + wm * 128 + mt * 16 + 4 * h) * 4u, 0, 0));
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-            // 16 values at a time, so the loads do not all take registers at once
-            float o[4][4];
-            __builtin_amdgcn_sched_barrier(0);
-            if (add) {
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        o[nt][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                            rp, other + (uint32_t)(((mt * 4 + nt) * 4 + r) * kThreads * 4), 0, kSc1));
-            } else {
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        o[nt][r] = 0.f;
-            }
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 const int cn = n0 + wn * 64 + nt * 16 + col;
@@ -333,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
                     const int row = m0 + wm * 128 + mt * 16 + 4 * h + r;
                     if (row < M) {
                         const size_t off = (size_t)row * N + cn;
-                        const float y = (acc[mt][nt][r] + o[nt][r]) * rsc[mt][r];
+                        const float y = acc[mt][nt][r] * rsc[mt][r];
                         if (a.y_f32)
                             ((float *)a.Y)[off] = y;
                         else
@@ -370,28 +353,25 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
         const __amdgpu_buffer_rsrc_t rp =
             make_rsrc(a.ws + p.off_part, (uint32_t)((size_t)(p.grid - 1) * 2 * BM * BN * sizeof(float)));
         // A tile split at a segment boundary: the boundary's pair of regions, one per
-        // part ([part][element][thread], so each store instruction covers 256
-        // consecutive bytes), stored and loaded with the sc1 cache policy (the
+        // part ([part][row tile, column tile][thread][4 rows], so each store instruction
+        // covers 1 KB), stored and loaded with the sc1 cache policy (the
         // instructions of relaxed device-scope atomics: coherent across the XCDs' L2s).
         // (One call site of store_y: a second inlined copy makes the register
         // allocator spill.)
         const bool split = STREAM && !(gs == 0 && ge == G); // only stream segments split tiles
         const int slot = gs == 0 ? seg : seg - 1; // boundary seg + 1 or seg, minus one
         const int mine = gs == 0 ? 0 : 1;
-        const uint32_t other = ((uint32_t)(slot * 2 + 1 - mine) * (BM * BN) + (uint32_t)tid) * 4u;
+        const uint32_t other = ((uint32_t)(slot * 2 + 1 - mine) * (BM * BN) + (uint32_t)tid * 4u) * 4u;
         uint32_t *tk = (uint32_t *)(a.ws + kOffCounters) + slot;
         if constexpr (STREAM) {
             if (split) {
-                const uint32_t own = ((uint32_t)(slot * 2 + mine) * (BM * BN) + (uint32_t)tid) * 4u;
+                const uint32_t own = ((uint32_t)(slot * 2 + mine) * (BM * BN) + (uint32_t)tid * 4u) * 4u;
 #pragma unroll
                 for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            __builtin_amdgcn_raw_buffer_store_b32(
-                                __float_as_uint(acc[mt][nt][r]), rp,
-                                own + (uint32_t)(((mt * 4 + nt) * 4 + r) * kThreads * 4), 0, kSc1);
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[mt][nt]), rp,
+                                                               own + (uint32_t)((mt * 4 + nt) * kThreads * 16), 0, kSc1);
                 wait_vmem(); // the stores (and anything in flight) have completed
                 __syncthreads();
                 // the arrival order passes through the first word of buffer bi: every wave
@@ -402,11 +382,30 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
                 __syncthreads();
                 if (*flag == 0)
                     return; // the other part finishes the tile (uniform over the workgroup)
+                // the other part's sums into acc, 16 bytes per column tile, the next row
+                // tile's loads in flight while one adds: all before the first store, so
+                // no wait for them waits for a store
+                f32x4_t ob[2][4];
+                auto load_other = [&](int mt, f32x4_t (&o)[4]) {
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt)
+                        o[nt] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                rp, other + (uint32_t)((mt * 4 + nt) * kThreads * 16), 0, kSc1));
+                };
+                load_other(0, ob[0]);
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt) {
+                    if (mt + 1 < 8)
+                        load_other(mt + 1, ob[(mt + 1) & 1]);
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt)
+                        acc[mt][nt] += ob[mt & 1][nt];
+                }
             }
         } else {
             (void)bi; // the split plan finishes after its loop, with no buffer in use
         }
-        store_y(m0, n0, split, rp, other);
+        store_y(m0, n0);
         if (split && tid == 0)
             __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
