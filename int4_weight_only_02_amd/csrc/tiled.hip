@@ -292,35 +292,44 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
         for (int j = 0; j < 4; ++j)
             acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Y of the rows and columns of this lane: 2^e_m * acc, stored as bf16 (RNE, the
-    // hardware conversion) or fp32.  The row scales of all the lane's rows (four
-    // consecutive rows per 16-byte load) are requested before the first store, so
-    // waiting for them waits for no store (the memory counter the wait uses also counts
-    // stores).
+    // Y of the tile: 2^e_m * acc, stored as bf16 (RNE, the hardware conversion) or fp32.
+    // A lane holds 4 rows of one column per 16 x 16 tile; a 4 x 4 transpose within each
+    // quad of lanes (two exchanges with lanes j ^ 1 and j ^ 2) leaves lane j with row
+    // 4h + j of 4 consecutive columns, stored as one 8-byte (bf16) or 16-byte (fp32)
+    // run: a quarter of the store instructions.  The row scales are requested before
+    // the first store, so waiting for them waits for no store (the memory counter the
+    // wait uses also counts stores).
     auto store_y = [&](int m0, int n0) {
+        const int j = col & 3, cq = col & ~3; // lane in its quad, the quad's first column
+        const bool odd = (j & 1) != 0, hi2 = (j & 2) != 0;
         const __amdgpu_buffer_rsrc_t rr = make_rsrc(rowscale, (uint32_t)((size_t)M * sizeof(float)));
-        f32x4_t rsc[8]; // rows past M read 0 (never stored)
+        float rsj[8]; // the scale of row 4h + j of each row tile (rows past M read 0)
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
-            rsc[mt] = __builtin_bit_cast(
-                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rr, (uint32_t)(m0 + wm * 128 + mt * 16 + 4 * h) * 4u, 0, 0));
+            rsj[mt] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(m0 + wm * 128 + mt * 16 + 4 * h + j) * 4u, 0, 0));
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
+            const int row = m0 + wm * 128 + mt * 16 + 4 * h + j;
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                const int cn = n0 + wn * 64 + nt * 16 + col;
-                if (cn >= N)
-                    continue;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = m0 + wm * 128 + mt * 16 + 4 * h + r;
-                    if (row < M) {
-                        const size_t off = (size_t)row * N + cn;
-                        const float y = acc[mt][nt][r] * rsc[mt][r];
-                        if (a.y_f32)
-                            ((float *)a.Y)[off] = y;
-                        else
-                            ((__bf16 *)a.Y)[off] = (__bf16)y;
+                const f32x4_t v = acc[mt][nt];
+                // exchange with lane j ^ 1: the elements whose bit 0 differs from j's
+                const float r0 = __shfl_xor(odd ? v[0] : v[1], 1), r1 = __shfl_xor(odd ? v[2] : v[3], 1);
+                const f32x4_t t = odd ? f32x4_t{r0, v[1], r1, v[3]} : f32x4_t{v[0], r0, v[2], r1};
+                // exchange with lane j ^ 2: the elements whose bit 1 differs from j's
+                const float q0 = __shfl_xor(hi2 ? t[0] : t[2], 2), q1 = __shfl_xor(hi2 ? t[1] : t[3], 2);
+                const f32x4_t w = hi2 ? f32x4_t{q0, q1, t[2], t[3]} : f32x4_t{t[0], t[1], q0, q1};
+                const int cn = n0 + wn * 64 + nt * 16 + cq; // N % 8 == 0: 4 columns all in or all out
+                if (row < M && cn < N) {
+                    const size_t off = (size_t)row * N + cn;
+                    const float sc = rsj[mt];
+                    if (a.y_f32) {
+                        *(f32x4_t *)((float *)a.Y + off) = f32x4_t{w[0] * sc, w[1] * sc, w[2] * sc, w[3] * sc};
+                    } else {
+                        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+                        *(bf16x4_t *)((__bf16 *)a.Y + off) =
+                            bf16x4_t{(__bf16)(w[0] * sc), (__bf16)(w[1] * sc), (__bf16)(w[2] * sc), (__bf16)(w[3] * sc)};
                     }
                 }
             }
