@@ -115,31 +115,48 @@ class Workspace:
     """A zero-filled device scratch buffer reused across calls (grown on demand).
 
     The library leaves the counters it uses at zero after every call, so the
-    buffer only has to be zero when first allocated."""
+    buffer only has to be zero when first allocated.  Calls that share a workspace
+    must be ordered: use one Workspace per stream (the default workspaces are kept
+    per device and stream), or synchronize the streams between calls."""
 
     def __init__(self, device="cuda"):
         self.device = device
         self.buf = None
 
-    def get(self, nbytes):
+    def get(self, nbytes, stream=None):
+        """The buffer, at least nbytes long.  A new buffer is allocated and zero-filled
+        on `stream` (default: the current stream), the stream the call runs on, so the
+        call is ordered after the fill and the old buffer is released in that
+        stream's order."""
         import torch
         if nbytes == 0:
             return None
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+            if stream is None:
+                self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+            else:
+                with torch.cuda.stream(stream):
+                    self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
         return self.buf
 
 
 _default_ws = {}
 
 
-def _workspace(ws, device):
+def _workspace(ws, device, stream=None):
+    """The caller's workspace, or the default one of (device, stream)."""
+    import torch
     if ws is not None:
         return ws
-    key = str(device)
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    key = (str(device), int(s.cuda_stream))
     if key not in _default_ws:
         _default_ws[key] = Workspace(device)
     return _default_ws[key]
+
+
+def _scratch(ws, device, nbytes, stream):
+    return _workspace(ws, device, stream).get(nbytes, stream)
 
 
 def w4a16_pack(codes, zeros, group=GROUP, stream=None):
@@ -193,7 +210,7 @@ def w4a16_linear_actorder(X, perm, qweight, scales, qzeros, out_dtype=None, grou
     assert X.dtype == torch.bfloat16 and X.is_contiguous() and perm.dtype == torch.int32
     Y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=X.device)
     nbytes = w4a16_workspace_bytes(OP_LINEAR_ACTORDER, M, N, K, group)
-    ws = _workspace(workspace, X.device).get(nbytes)
+    ws = _scratch(workspace, X.device, nbytes, stream)
     st = lib().w4a16_linear_actorder(_ptr(X), _ptr(perm), _ptr(qweight), _ptr(scales), _ptr(qzeros), M, N, K,
                                      group, _ptr(Y), ydt, _ptr(ws), nbytes, _stream(stream))
     _check(st, "w4a16_linear_actorder")
@@ -214,7 +231,7 @@ def w4a16_swa_attention(Q, K, Vt, T, window, out_dtype=None, out=None, workspace
     odt = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
     O = out if out is not None else torch.empty((M, Hq, D), dtype=out_dtype, device=Q.device)
     nbytes = lib().w4a16_swa_workspace_bytes(M, T, Hq, Hkv, window)
-    ws = _workspace(workspace, Q.device).get(nbytes)
+    ws = _scratch(workspace, Q.device, nbytes, stream)
     st = lib().w4a16_swa_attention(_ptr(Q), _ptr(K), _ptr(Vt), M, T, Hq, Hkv, D, window, t_stride, _ptr(O), odt,
                                    _ptr(ws), nbytes, _stream(stream))
     _check(st, "w4a16_swa_attention")
@@ -248,7 +265,7 @@ def w4a16_linear(X, qweight, scales, qzeros, out_dtype=None, group=GROUP, out=No
     Y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=X.device)
     assert Y.shape == (M, N) and Y.dtype == out_dtype and Y.is_contiguous()
     nbytes = w4a16_workspace_bytes(OP_LINEAR, M, N, K, group)
-    ws = _workspace(workspace, X.device).get(nbytes)
+    ws = _scratch(workspace, X.device, nbytes, stream)
     st = lib().w4a16_linear(_ptr(X), _ptr(qweight), _ptr(scales), _ptr(qzeros), M, N, K, group,
                             _ptr(Y), ydt, _ptr(ws), nbytes, _stream(stream))
     _check(st, "w4a16_linear")
@@ -271,7 +288,7 @@ def w4a16_linear_gated(X, gate, up, out_dtype=None, group=GROUP, out=None, works
     Y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=X.device)
     assert Y.shape == (M, N) and Y.dtype == out_dtype and Y.is_contiguous()
     nbytes = w4a16_workspace_bytes(OP_LINEAR_GATED, M, N, K, group)
-    ws = _workspace(workspace, X.device).get(nbytes)
+    ws = _scratch(workspace, X.device, nbytes, stream)
     st = lib().w4a16_linear_gated(_ptr(X), _ptr(qg), _ptr(sg), _ptr(zg), _ptr(qu), _ptr(su), _ptr(zu), M, N, K,
                                   group, _ptr(Y), ydt, _ptr(ws), nbytes, _stream(stream))
     _check(st, "w4a16_linear_gated")
@@ -300,7 +317,7 @@ def w4a16_linear_batch(problems, out_dtype=None, group=GROUP, outs=None, workspa
         arr[q] = Problem(X.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(), Y.data_ptr(), N, K)
         need += w4a16_workspace_bytes(OP_LINEAR, M, N, K, group)
         ys.append(Y)
-    ws = _workspace(workspace, problems[0][0].device).get(need)
+    ws = _scratch(workspace, problems[0][0].device, need, stream)
     st = lib().w4a16_linear_batch(ctypes.cast(arr, ctypes.c_void_p), len(problems), M, group, ydt, _ptr(ws), need,
                                   _stream(stream))
     _check(st, "w4a16_linear_batch")
@@ -327,7 +344,7 @@ def w4a16_lmhead_verify(X, qweight, scales, qzeros, draft_ids, return_logits=Fal
         ydt = OUT_F32 if ldt == torch.float32 else OUT_BF16
         Y = torch.empty((M, N), dtype=ldt, device=X.device)
     nbytes = w4a16_workspace_bytes(OP_LMHEAD, M, N, K, group)
-    ws = _workspace(workspace, X.device).get(nbytes)
+    ws = _scratch(workspace, X.device, nbytes, stream)
     st = lib().w4a16_lmhead_verify(_ptr(X), _ptr(qweight), _ptr(scales), _ptr(qzeros), M, N, K, group,
                                    _ptr(draft_ids), _ptr(Y), ydt, _ptr(argmax), _ptr(accept),
                                    _ptr(ws), nbytes, _stream(stream))

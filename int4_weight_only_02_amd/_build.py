@@ -26,19 +26,35 @@ def stale():
 
 
 def build(force=True, verbose=False):
-    """Compile every HIP source into one shared library (always, unless force=False and fresh)."""
+    """Compile every HIP source into one shared library (always, unless force=False and
+    fresh).  The sources compile to objects in parallel under _build/, then link."""
     if not force and not stale():
         return LIB
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        cmd = [HIPCC] + compile_flags + ["-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for src, obj, pr in procs:
+        out, _ = pr.communicate()
+        out = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
+        if pr.returncode != 0:
+            failed.append(out)
+        elif verbose and out.strip():
+            print(out, flush=True)
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + SOURCES + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + [o for _, o, _ in procs] + ["-o", tmp]
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
-    if verbose and out.strip():
-        print(out, flush=True)
+        raise RuntimeError("link failed:\n" + res.stdout)
     os.replace(tmp, LIB)
     return LIB
 

@@ -256,8 +256,10 @@ SwaPlan plan_swa(int M, int T, int Hq, int Hkv, int window)
     // a lane reads is 8-byte aligned (the extra keys are masked)
     p.j_lo = T - M - window + 1 > 0 ? (T - M - window + 1) / 8 * 8 : 0;
     p.chunks = (T - p.j_lo + kChunk - 1) / kChunk;
-    p.ml_off = 0;
-    p.part_off = (size_t)p.chunks * Hq * 16 * 2 * sizeof(float);
+    // the scratch starts past the zero region (argmax keys, tickets, arrival counters),
+    // so an attention call never disturbs the counters the other calls expect at zero
+    p.ml_off = kZeroRegion;
+    p.part_off = p.ml_off + (size_t)p.chunks * Hq * 16 * 2 * sizeof(float);
     p.part_off = (p.part_off + 255) / 256 * 256;
     p.ws_bytes = p.part_off + (size_t)p.chunks * Hq * 16 * kD * sizeof(float);
     (void)Hkv;

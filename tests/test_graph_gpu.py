@@ -40,14 +40,36 @@ def _workspace(dev, nbytes):
     return ws
 
 
-def _disturb(dev, ws):
-    # eager calls of other shapes and paths through the same workspace: a chunked
-    # projection (arrival tickets, partial sums) and a small lm_head (argmax keys)
+_disturb_ref = {}
+
+
+def _disturb_calls(dev, ws):
+    # eager calls of other shapes and paths through one workspace: attention (its
+    # per-chunk scratch), a chunked projection (arrival tickets, partial sums) and a
+    # small lm_head (argmax keys, ticket)
+    rng = np.random.default_rng(7)
+    b = lambda shape: torch.from_numpy(synth.f32_to_bf16_bits(rng.normal(0, 1, shape).astype(np.float32))
+                                       .view(np.int16)).to(dev).view(torch.bfloat16)
+    Q, Kc, Vt = b((16, 8, 128)), b((3000, 2, 128)), b((2, 128, 3000))
+    O = w4.w4a16_swa_attention(Q, Kc, Vt, 3000, 2048, out_dtype=torch.float32, workspace=ws)
     X, qw, S, qz = _packed(5, 16, 1024, 9728, dev)
-    w4.w4a16_linear(X, qw, S, qz, out_dtype=torch.float32, workspace=ws)
+    Y = w4.w4a16_linear(X, qw, S, qz, out_dtype=torch.float32, workspace=ws)
     X, qw, S, qz = _packed(6, 3, 520, 640, dev)
-    w4.w4a16_lmhead_verify(X, qw, S, qz, torch.zeros(3, dtype=torch.int32, device=dev), workspace=ws)
+    draft = torch.tensor([1, 2, 3], dtype=torch.int32, device=dev)
+    am, acc, _ = w4.w4a16_lmhead_verify(X, qw, S, qz, draft, workspace=ws)
     torch.cuda.synchronize()
+    return [O, Y, am, acc]
+
+
+def _disturb(dev, ws):
+    """The eager calls between replays; each result must equal the same call on a
+    fresh zero-filled workspace (nothing any call leaves behind may change another)."""
+    if "ref" not in _disturb_ref:
+        fresh = w4.Workspace(dev)
+        fresh.get(1 << 24)
+        _disturb_ref["ref"] = [t.clone() for t in _disturb_calls(dev, fresh)]
+    for got, want in zip(_disturb_calls(dev, ws), _disturb_ref["ref"]):
+        assert torch.equal(got, want), "a call through the shared workspace differs from a fresh one"
 
 
 def _check_replays(dev, ws, run, outs):
@@ -164,3 +186,40 @@ def test_gated_graph_replays(dev, M, K):
     ws = _workspace(dev, max(w4.w4a16_workspace_bytes(w4.OP_LINEAR_GATED, M, N, K), 1 << 24))
     Y = torch.empty((M, N), dtype=torch.float32, device=dev)
     _check_replays(dev, ws, lambda: w4.w4a16_linear_gated(X, (qg, sg, zg), (qu, su, zu), out=Y, workspace=ws), [Y])
+
+
+def test_workspace_shared_across_paths(dev):
+    """Attention, then lm_head verify, then a K-chunked M = 16 projection through one
+    workspace: argmax, accept_len and Y equal the same calls on fresh workspaces."""
+    print("shared workspace", flush=True)
+    M, N, K = 16, 4096, 2560
+    X, qw, S, qz = _packed(81, M, N, K, dev)
+    draft = torch.from_numpy(np.random.default_rng(8).integers(0, N, M).astype(np.int32)).to(dev)
+    Xc, qwc, Sc, qzc = _packed(82, 16, 2560, 9728, dev)
+
+    def lm(ws):
+        am, acc, _ = w4.w4a16_lmhead_verify(X, qw, S, qz, draft, workspace=ws)
+        return am, acc
+
+    def lin(ws):
+        return w4.w4a16_linear(Xc, qwc, Sc, qzc, out_dtype=torch.float32, workspace=ws)
+
+    def fresh():
+        ws = w4.Workspace(dev)
+        ws.get(1 << 24)
+        return ws
+
+    am0, acc0 = lm(fresh())
+    y0 = lin(fresh())
+    torch.cuda.synchronize()
+    shared = fresh()
+    rng = np.random.default_rng(9)
+    b = lambda shape: torch.from_numpy(synth.f32_to_bf16_bits(rng.normal(0, 1, shape).astype(np.float32))
+                                       .view(np.int16)).to(dev).view(torch.bfloat16)
+    Q, Kc, Vt = b((16, 32, 128)), b((8192, 8, 128)), b((8, 128, 8192))
+    w4.w4a16_swa_attention(Q, Kc, Vt, 8192, 2048, workspace=shared)
+    am1, acc1 = lm(shared)
+    y1 = lin(shared)
+    torch.cuda.synchronize()
+    assert torch.equal(am1, am0) and torch.equal(acc1, acc0)
+    assert torch.equal(y1, y0)
