@@ -262,7 +262,20 @@ int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, con
         return W4A16_ERR_WORKSPACE;
 
     hipError_t e;
-    if (M <= kSkinnyMaxM) {
+    const GemvPlan gp = M == 1 ? plan_gemv(N, K) : GemvPlan{};
+    if (gp.ok) {
+        GemvArgs a{};
+        a.X = (const uint16_t *)X;
+        a.qw = qweight;
+        a.scales = (const uint16_t *)scales;
+        a.qz = qzeros;
+        a.N = N;
+        a.K = K;
+        a.G = K / kGroup;
+        a.Y = Y;
+        a.y_f32 = y_dtype == W4A16_OUT_F32;
+        e = launch_gemv(a, gp, (hipStream_t)stream);
+    } else if (M <= kSkinnyMaxM) {
         const SkinnyPlan p = plan_skinny(M, N, K, 0);
         SkinnyArgs a{};
         a.X = (const uint16_t *)X;

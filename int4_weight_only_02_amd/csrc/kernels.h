@@ -132,6 +132,32 @@ size_t skinny_chunk_ws_bound(int M, int N, int K);
 size_t skinny_multi_scratch(SkinnyMulti &mp, int M);
 hipError_t launch_skinny_multi(SkinnyMulti &mp, int M, size_t ws_bytes, hipStream_t stream);
 
+// ---------------------------------------------------------------- gemv (M = 1)
+// grid = wpc workgroups per CU; workgroup b owns columns [b N / grid, (b + 1) N / grid)
+// and all of K, cut into ns group sets of sw (4, 8 or 16) groups; wave w takes set
+// w / wps and up to cpw of the columns (slots = wps * cpw >= columns per workgroup).
+struct GemvPlan {
+    int ns, sw, wps, cpw, slots, waves, grid;
+    int xl;                                        // X staged in LDS by the workgroup (else per wave from L2)
+    int sc_off, z_off, t_off, s_off, p_off, x_off; // LDS byte offsets: scales, zero words, P, S, set partials, X
+    size_t lds_bytes;
+    bool ok;                                       // false: the shape needs another path
+};
+struct GemvArgs {
+    const uint16_t *X;
+    const uint32_t *qw;
+    const uint16_t *scales;
+    const uint32_t *qz;
+    int N, K, G;
+    void *Y;
+    int y_f32;
+    // copied from the plan by launch_gemv
+    int ns, wps, slots, sc_off, z_off, t_off, s_off, p_off, x_off;
+};
+GemvPlan plan_gemv(int N, int K);
+GemvPlan plan_gemv_with(int N, int K, int wpc, int cpw, int sw, int xl);
+hipError_t launch_gemv(const GemvArgs &a, const GemvPlan &p, hipStream_t stream);
+
 // ---------------------------------------------------------------- tiled (large M)
 struct TiledPlan {
     int G;

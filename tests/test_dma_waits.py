@@ -1,5 +1,5 @@
 """The LDS-DMA waits of the small-M kernels (CPU: reads the gfx950 assembly of our
-own skinny.hip).
+own skinny.hip and gemv.hip).
 
 A wave that pulls X into LDS with buffer_load ... lds then issues its first weight
 batches and waits with s_waitcnt vmcnt(n), n being the number of loads issued after
@@ -18,20 +18,23 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-@pytest.fixture(scope="module")
-def skinny_asm(tmp_path_factory):
+def _asm(tmp_path_factory, name):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "skinny.s"
+    out = tmp_path_factory.mktemp("asm") / (name + ".s")
     csrc = os.path.join(ROOT, "int4_weight_only_02_amd", "csrc")
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
            "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", csrc, "--cuda-device-only", "-S",
-           os.path.join(csrc, "skinny.hip"), "-o", str(out)]
+           os.path.join(csrc, name), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     return out.read_text().splitlines()
 
 
-def test_every_dma_wait_covers_the_dma(skinny_asm):
+# source, the fewest DMA waits it must contain: the chunked and the DMA private modes
+# in the single and the batched skinny kernels; the X-in-LDS instances of the M = 1 kernel
+@pytest.mark.parametrize("name,least", [("skinny.hip", 24), ("gemv.hip", 9)])
+def test_every_dma_wait_covers_the_dma(tmp_path_factory, name, least):
+    skinny_asm = _asm(tmp_path_factory, name)
     kern, last_dma, after = None, None, 0
     checked = []
     for line in skinny_asm:
@@ -48,7 +51,6 @@ def test_every_dma_wait_covers_the_dma(skinny_asm):
             n = int(re.search(r"vmcnt\((\d+)\)", t).group(1))
             checked.append((kern, n, after))
             last_dma = None
-    # the chunked and the DMA private modes, in the single and the batched kernel
-    assert len(checked) >= 24, checked
+    assert len(checked) >= least, checked
     bad = [c for c in checked if c[1] > c[2]]
     assert not bad, "waits that let the X DMA still be in flight: %s" % bad[:4]

@@ -59,7 +59,12 @@ SMALL = [(1, 8, 128), (1, 512, 512), (2, 136, 384), (3, 1032, 1280), (5, 264, 25
          (128, 256, 256), (200, 392, 1280), (257, 1032, 640),
          # K chunked across workgroups: 41 groups (not a multiple of 4) for 7 rows in one
          # chunk; 45 groups in two chunks; three chunks over 161 tiles (ragged last tile)
-         (7, 520, 5248), (16, 264, 5760), (12, 2568, 9728)]
+         (7, 520, 5248), (16, 264, 5760), (12, 2568, 9728),
+         # one row (the M = 1 kernel): sets of 4, 8 (X in LDS) and 16 groups, ragged last
+         # sets, column counts below and above one column per CU and not a multiple of 16,
+         # and a K too long for it (the general small-M path takes over)
+         (1, 264, 1408), (1, 136, 1536), (1, 40, 5888), (1, 2568, 6144), (1, 1032, 16384),
+         (1, 9736, 2560), (1, 3000, 640), (1, 16, 36864)]
 
 
 @pytest.mark.parametrize("M,N,K", SMALL)
@@ -103,7 +108,7 @@ def _dyadic(seed, M, N, K):
     return {"codes": codes, "zeros": zeros, "scales": scales, "X": X}
 
 
-DYADIC = [(1, 9728, 2560), (1, 2560, 9728), (16, 4096, 2560), (16, 2560, 9728), (16, 1000, 640),
+DYADIC = [(1, 9728, 2560), (1, 2560, 9728), (1, 1032, 1536), (1, 520, 640), (1, 264, 7808), (16, 4096, 2560), (16, 2560, 9728), (16, 1000, 640),
           (16, 264, 9728), (7, 520, 5248), (37, 520, 1280), (300, 1032, 2560), (8192, 9728, 2560),
           (8192, 2560, 9728),
           # at least one tile per CU (balanced segments of tile-groups): tiles split at
