@@ -195,6 +195,30 @@ int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, con
                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * w4a16_linear_static_ws -- w4a16_linear for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The same kernels and result bits as w4a16_linear with a fresh
+ * zero-filled workspace; the scratch memory is instead a per-device array inside
+ * the library of W4A16_STATIC_WS_BYTES, held by every GPU the library runs on
+ * until the process ends.  The caller passes inputs and outputs only.
+ *   X, qweight, scales, qzeros, Y, y_dtype, stream   as w4a16_linear
+ * The array belongs to the device current on the calling thread.  Its first call
+ * there obtains the array's address and clears its counter region with a kernel
+ * enqueued on `stream`; every call returns that region to zero.  All calls on one
+ * GPU share the array, which keeps the last call's contents: calls that overlap on
+ * one GPU (unordered streams, or threads) race and must be serialized by the caller.
+ * Nothing is allocated or freed, here or in any call below it.
+ * Errors: those of w4a16_linear; W4A16_ERR_WORKSPACE when the shape needs more
+ * scratch than the array holds, i.e. when
+ * w4a16_workspace_bytes(W4A16_OP_LINEAR, M, N, K, group) > W4A16_STATIC_WS_BYTES
+ * (the M > 64 path needs 2 M K bytes and more); W4A16_ERR_HIP when the array's
+ * address cannot be obtained or a launch fails.
+ */
+#define W4A16_STATIC_WS_BYTES (8u << 20)
+int w4a16_linear_static_ws(const void *X, const uint32_t *qweight, const void *scales, const uint32_t *qzeros,
+                           int M, int N, int K, int group, void *Y, int y_dtype, void *stream);
+
+/*
  * w4a16_linear_gated -- the gate and up projections of a gated MLP and its
  * activation in one call: Y = silu(X * Wg^T) * (X * Wu^T), elementwise, with
  * silu(g) = g / (1 + exp(-g)).  The pages serve a Qwen3.5-4B target (Pith review,

@@ -11,6 +11,8 @@ Calls (same names as the C ABI):
   w4a16_linear(X bf16[M,K], qweight, scales f16[N,G], qzeros, out_dtype) -> Y[M,N]
   w4a16_lmhead_verify(X, qweight, scales, qzeros, draft i32[M], return_logits) ->
         (argmax i32[M], accept_len i32[1], logits or None)
+  w4a16_linear_static_ws(X, qweight, scales, qzeros, out_dtype) -> Y[M,N]
+        (w4a16_linear with the library's own scratch array: no workspace argument)
   w4a16_linear_batch([(X, qweight, scales, qzeros), ...], out_dtype) -> [Y, ...]
         (up to 8 projections with the same M in one launch)
   w4a16_workspace_bytes(op, M, N, K)
@@ -27,7 +29,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libw4a16.so")
 _lib = None
 
-EXPORTED = ("w4a16_pack", "w4a16_quantize", "w4a16_linear", "w4a16_linear_gated", "w4a16_linear_batch",
+EXPORTED = ("w4a16_pack", "w4a16_quantize", "w4a16_linear", "w4a16_linear_static_ws", "w4a16_linear_gated",
+            "w4a16_linear_batch",
             "w4a16_lmhead_verify",
             "w4a16_actorder_perm", "w4a16_pack_actorder", "w4a16_linear_actorder",
             "w4a16_swa_attention", "w4a16_swa_workspace_bytes",
@@ -73,6 +76,8 @@ def lib():
     L.w4a16_linear_actorder.restype = I
     L.w4a16_linear.argtypes = [P, P, P, P, I, I, I, I, P, I, P, S, P]
     L.w4a16_linear.restype = I
+    L.w4a16_linear_static_ws.argtypes = [P, P, P, P, I, I, I, I, P, I, P]
+    L.w4a16_linear_static_ws.restype = I
     L.w4a16_linear_gated.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, I, P, S, P]
     L.w4a16_linear_gated.restype = I
     L.w4a16_linear_batch.argtypes = [P, I, I, I, I, P, S, P]
@@ -269,6 +274,25 @@ def w4a16_linear(X, qweight, scales, qzeros, out_dtype=None, group=GROUP, out=No
     st = lib().w4a16_linear(_ptr(X), _ptr(qweight), _ptr(scales), _ptr(qzeros), M, N, K, group,
                             _ptr(Y), ydt, _ptr(ws), nbytes, _stream(stream))
     _check(st, "w4a16_linear")
+    return Y
+
+
+def w4a16_linear_static_ws(X, qweight, scales, qzeros, out_dtype=None, group=GROUP, out=None, stream=None):
+    """w4a16_linear with the library's own per-device scratch array (no workspace
+    argument); pass `out` to make the call allocate nothing at all."""
+    import torch
+    M, K = X.shape
+    N = qweight.shape[0]
+    assert X.dtype == torch.bfloat16 and scales.dtype == torch.float16
+    assert X.is_contiguous() and qweight.is_contiguous() and scales.is_contiguous() and qzeros.is_contiguous()
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    ydt = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    Y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=X.device)
+    assert Y.shape == (M, N) and Y.dtype == out_dtype and Y.is_contiguous()
+    st = lib().w4a16_linear_static_ws(_ptr(X), _ptr(qweight), _ptr(scales), _ptr(qzeros), M, N, K, group,
+                                      _ptr(Y), ydt, _stream(stream))
+    _check(st, "w4a16_linear_static_ws")
     return Y
 
 

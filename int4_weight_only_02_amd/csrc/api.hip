@@ -3,6 +3,8 @@
 // runs before the first launch, so a rejected call leaves the stream untouched.
 #include "w4a16.h"
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -56,6 +58,45 @@ size_t gated_ws(int M, int N, int K)
     if (M <= kSkinnyMaxM)
         return plan_skinny_pair(M, N, K).ws_bytes;
     return gated_gu_offset(M, N, K) + 2 * (size_t)M * N * 4;
+}
+
+// ---------------------------------------------------------------- static scratch
+// The scratch of w4a16_linear_static_ws: one array per device (each GPU the library
+// runs on holds its own copy at its own address).  In host code `scratch` names a
+// host-side stand-in, not the device memory: only the address obtained from
+// hipGetSymbolAddress (kept per device below) is ever passed to a kernel.
+constexpr size_t kStaticWsBytes = W4A16_STATIC_WS_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kStaticWsBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+__global__ void zero_words_kernel(uint32_t *p, int n)
+{
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+// the current device's scratch address; on its first use on a device, the address is
+// looked up and the counter region cleared by a kernel on `stream`
+int static_scratch(void **out, hipStream_t stream)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return W4A16_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return W4A16_ERR_HIP;
+        hipLaunchKernelGGL(zero_words_kernel, dim3(8), dim3(256), 0, stream, (uint32_t *)p, (int)(kZeroRegion / 4));
+        if (hipGetLastError() != hipSuccess)
+            return W4A16_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return W4A16_OK;
 }
 
 } // namespace
@@ -308,6 +349,29 @@ int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, con
         e = launch_tiled(a, p, (hipStream_t)stream);
     }
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+int w4a16_linear_static_ws(const void *X, const uint32_t *qweight, const void *scales, const uint32_t *qzeros,
+                           int M, int N, int K, int group, void *Y, int y_dtype, void *stream)
+{
+    if (group != kGroup || (y_dtype != W4A16_OUT_BF16 && y_dtype != W4A16_OUT_F32))
+        return W4A16_ERR_UNSUPPORTED;
+    const int st = check_dims(M, N, K);
+    if (st != W4A16_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return W4A16_OK;
+    if (!X || !qweight || !scales || !qzeros || !Y)
+        return W4A16_ERR_NULL;
+    if (misaligned(X) || misaligned(qweight) || misaligned(scales) || misaligned(qzeros) || misaligned(Y))
+        return W4A16_ERR_ALIGN;
+    if (linear_ws(M, N, K) > kStaticWsBytes)
+        return W4A16_ERR_WORKSPACE;
+    void *ws = nullptr;
+    const int sst = static_scratch(&ws, (hipStream_t)stream);
+    if (sst != W4A16_OK)
+        return sst;
+    return w4a16_linear(X, qweight, scales, qzeros, M, N, K, group, Y, y_dtype, ws, kStaticWsBytes, stream);
 }
 
 int w4a16_linear_gated(const void *X, const uint32_t *qweight_gate, const void *scales_gate,

@@ -112,6 +112,23 @@ def gated(lib, X=A, qg=A, sg=A, zg=A, qu=A, su=A, zu=A, M=1, N=512, K=512, group
     return lib.w4a16_linear_gated(X, qg, sg, zg, qu, su, zu, M, N, K, group, Y, ydt, ws, wsb, None)
 
 
+def test_static_ws_rejections(lib):
+    def call(X=A, qw=A, s=A, qz=A, M=16, N=2560, K=9728, group=128, Y=A2, ydt=0):
+        return lib.w4a16_linear_static_ws(X, qw, s, qz, M, N, K, group, Y, ydt, None)
+    assert call(group=64) == ERR_UNSUPPORTED
+    assert call(ydt=5) == ERR_UNSUPPORTED
+    assert call(N=12) == ERR_SHAPE
+    assert call(K=100) == ERR_SHAPE
+    assert call(M=-1) == ERR_SHAPE
+    assert call(M=0) == OK and call(N=0) == OK
+    assert call(X=NUL) == ERR_NULL
+    assert call(Y=NUL) == ERR_NULL
+    assert call(qz=MIS) == ERR_ALIGN
+    # more scratch than the library's array (8 MiB) holds: refused on the host
+    assert call(M=8192) == ERR_WORKSPACE
+    assert call(M=4096, N=9728, K=2560) == ERR_WORKSPACE
+
+
 def test_gated_rejections(lib):
     assert gated(lib, group=64) == ERR_UNSUPPORTED
     assert gated(lib, ydt=3) == ERR_UNSUPPORTED
