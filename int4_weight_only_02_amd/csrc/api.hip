@@ -32,7 +32,9 @@ size_t linear_ws(int M, int N, int K)
 {
     if (M <= kSkinnyMaxM) {
         const size_t a = plan_skinny(M, N, K, 0).ws_bytes, b = skinny_chunk_ws_bound(M, N, K);
-        return a > b ? a : b;
+        const size_t c = (M >= 2 && M <= 16) ? block_linear_ws(M, N, K) : 0;
+        const size_t ab = a > b ? a : b;
+        return ab > c ? ab : c;
     }
     return plan_tiled(M, N, K).ws_bytes;
 }
@@ -304,6 +306,7 @@ int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, con
 
     hipError_t e;
     const GemvPlan gp = M == 1 ? plan_gemv(N, K) : GemvPlan{};
+    BlockPlan bp{};
     if (gp.ok) {
         GemvArgs a{};
         a.X = (const uint16_t *)X;
@@ -316,6 +319,20 @@ int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, con
         a.Y = Y;
         a.y_f32 = y_dtype == W4A16_OUT_F32;
         e = launch_gemv(a, gp, (hipStream_t)stream);
+    } else if (M >= 2 && M <= 16 && (bp = plan_block(&N, &K, 1, M)).ok && bp.ws_bytes <= workspace_bytes &&
+               (bp.ws_bytes == 0 || workspace)) {
+        BlockArgs a{};
+        a.ws = (unsigned char *)workspace;
+        a.pr[0].X = (const uint16_t *)X;
+        a.pr[0].qw = qweight;
+        a.pr[0].scales = (const uint16_t *)scales;
+        a.pr[0].qz = qzeros;
+        a.pr[0].Y = Y;
+        a.pr[0].N = N;
+        a.pr[0].K = K;
+        a.M = M;
+        a.y_f32 = y_dtype == W4A16_OUT_F32;
+        e = launch_block(a, bp, (hipStream_t)stream);
     } else if (M <= kSkinnyMaxM) {
         const SkinnyPlan p = plan_skinny(M, N, K, 0);
         SkinnyArgs a{};
@@ -481,6 +498,35 @@ int w4a16_linear_batch(const w4a16_problem *problems, int count, int M, int grou
                 return st;
         }
         return W4A16_OK;
+    }
+    if (M >= 2 && M <= 16) {
+        // one draft block: the block kernel, every projection's tiles in one launch
+        int bn[W4A16_MAX_BATCH], bk[W4A16_MAX_BATCH], nb = 0;
+        BlockArgs a{};
+        for (int q = 0; q < count; ++q) {
+            const w4a16_problem &pr = problems[q];
+            if (pr.N == 0)
+                continue;
+            a.pr[nb].X = (const uint16_t *)pr.X;
+            a.pr[nb].qw = pr.qweight;
+            a.pr[nb].scales = (const uint16_t *)pr.scales;
+            a.pr[nb].qz = pr.qzeros;
+            a.pr[nb].Y = pr.Y;
+            a.pr[nb].N = pr.N;
+            a.pr[nb].K = pr.K;
+            bn[nb] = pr.N;
+            bk[nb] = pr.K;
+            ++nb;
+        }
+        if (nb == 0)
+            return W4A16_OK;
+        const BlockPlan bp = plan_block(bn, bk, nb, M);
+        if (bp.ok && bp.ws_bytes <= workspace_bytes && (bp.ws_bytes == 0 || workspace)) {
+            a.ws = (unsigned char *)workspace;
+            a.M = M;
+            a.y_f32 = y_dtype == W4A16_OUT_F32;
+            return launch_block(a, bp, (hipStream_t)stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+        }
     }
     SkinnyMulti mp{};
     int bn[W4A16_MAX_BATCH], bk[W4A16_MAX_BATCH], btw[W4A16_MAX_BATCH], nb = 0;

@@ -1,0 +1,459 @@
+// block.hip -- W4A16 linear for one draft block (2 <= M <= 16 rows) on gfx950, one or
+// several projections per launch.
+//
+// The pages' verifier runs the target over a block of 16 draft tokens at every
+// speculative step (Pith review, Assumptions & free parameters: block size 16;
+// mlsanity index page, Abstract), so every projection of a decoder layer runs at
+// M = 16.  There the layer streams its packed weights once and each CU must also
+// read all of X (16 rows x K bf16: 82 KB at K = 2560, 311 KB at K = 9728, as much
+// as or more than the CU's share of the weights).  The kernel is shaped for that:
+//
+//   * One workgroup per CU (or a few), each owning a balanced run of 16-column
+//     tiles and ALL of K, so no partial sum ever crosses a workgroup (a
+//     cross-workgroup hand-off costs several round trips through the memory side).
+//   * K is split over the workgroup's waves; each wave loads its K slice of X once,
+//     straight into registers as MFMA A fragments (lane (r, h): row r, k-block h),
+//     and keeps it for every tile of the workgroup.  X is therefore read once per
+//     CU, with no LDS staging and no barrier in front of it.
+//   * The codes of every (tile, group) of the wave's slice are requested up front:
+//     lane (c, h) loads bytes 16h .. 16h+15 of column c's group, the B operand of
+//     four v_mfma_f32_16x16x32_bf16 on the exact biased codes 128 + q (every product
+//     exact in fp32), P = sum x * (128 + q); the bias and the zero-point come out in
+//     fp32 with the row sums S of X over the group: acc += s * (P - (128 + z) * S).
+//   * The scales and zero words of the workgroup's columns (contiguous runs) come in
+//     by LDS DMA; the waves' K-slice accumulators are added through LDS in slice
+//     order.  All sums run in a fixed order: results are deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace w4a16 {
+
+namespace {
+
+constexpr uint32_t kOobB = 0xFFFFFF00u; // an offset past the end of every tensor
+constexpr int kRsrcWord3B = 0x00020000; // raw (untyped) buffer loads on gfx9-class GPUs
+constexpr int kBlockCUs = 256;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_b(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcWord3B);
+}
+
+__device__ __forceinline__ u32x4_t ld16_b(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void dma4_b(__amdgpu_buffer_rsrc_t r, unsigned char *dst, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 4, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t frag_b(uint32_t w, uint32_t mask, uint32_t bias)
+{
+    u32x4_t r;
+    r.x = (w & mask) | bias;
+    r.y = ((w >> 4) & mask) | bias;
+    r.z = ((w >> 8) & mask) | bias;
+    r.w = ((w >> 12) & mask) | bias;
+    return __builtin_bit_cast(bf16x8_t, r);
+}
+
+// rows 4 (l / 16) .. + 3 of column 16 t + l % 16 of Y (those inside M x N)
+__device__ __forceinline__ void store_rows(const BlockProb &pr, const BlockArgs &a, const f32x4_t &y, int t, int l,
+                                           int M, int N)
+{
+    const int n = t * 16 + (l & 15);
+    const int r0 = 4 * (l >> 4);
+    if (n >= N)
+        return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i;
+        if (r < M) {
+            if (a.y_f32)
+                ((float *)pr.Y)[(size_t)r * N + n] = y[i];
+            else
+                ((uint16_t *)pr.Y)[(size_t)r * N + n] = f32_to_bf16_rne(y[i]);
+        }
+    }
+}
+
+// 4 x 4 transpose across the four 16-lane rows of a wave: afterwards register j of
+// row h holds what register h of row j held.  Two swap stages (rows {0,1} <-> {2,3}
+// between registers j and j + 2, then rows {0,2} <-> {1,3} between j and j + 1).
+__device__ __forceinline__ void transpose_rows4(u32x4_t (&v)[4])
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const auto r = __builtin_amdgcn_permlane32_swap(v[j][e], v[j + 2][e], false, false);
+            v[j][e] = r[0];
+            v[j + 2][e] = r[1];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+            const auto r = __builtin_amdgcn_permlane16_swap(v[j][e], v[j + 1][e], false, false);
+            v[j][e] = r[0];
+            v[j + 1][e] = r[1];
+        }
+    }
+}
+
+// GPW: the most groups a wave's K slice holds; TMAX: the most tiles a workgroup owns
+template <int GPW, int TMAX>
+__global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
+{
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int W = blockDim.x >> 6;
+    // the workgroup's projection, its tile group [t0, t1) (balanced over the projection's
+    // ntg tile groups) and its part of K (parts of a tile group are adjacent workgroups)
+    int q = 0;
+    while (q + 1 < a.count && (int)blockIdx.x >= a.pr[q + 1].wg0)
+        ++q;
+    const BlockProb &pr = a.pr[q];
+    const int P = pr.parts;
+    const int b = blockIdx.x - pr.wg0;
+    const int tg = b / P, part = b - tg * P;
+    const int t0 = (int)((long long)tg * pr.nt / pr.ntg);
+    const int t1 = (int)((long long)(tg + 1) * pr.nt / pr.ntg);
+    const int T = t1 - t0;
+    const int G = pr.K / kGroup, N = pr.N, M = a.M;
+    const int Gp = (G + P - 1) / P;
+    const int ga = part * Gp, gnp = min(Gp, G - ga); // the part's groups [ga, ga + gnp)
+    const int gpw = (gnp + W - 1) / W;
+    // the wave's K slice, rotated by the workgroup index so that the CUs, which all
+    // read the same X, do not walk its lines in step
+    const int slice = (w + (int)blockIdx.x) % W;
+    const int g0 = ga + slice * gpw;
+    const int gn = min(gpw, ga + gnp - g0); // this wave's groups (may be <= 0)
+    const int c = lane & 15, h = lane >> 4;
+    const uint32_t rowb = (uint32_t)(pr.K / 2);
+
+    const __amdgpu_buffer_rsrc_t rw = rsrc_b(pr.qw, (uint32_t)N * rowb);
+    const __amdgpu_buffer_rsrc_t rs = rsrc_b(pr.scales, (uint32_t)N * (uint32_t)G * 2u);
+    const __amdgpu_buffer_rsrc_t rz = rsrc_b(pr.qz, (uint32_t)(N / 8) * (uint32_t)G * 4u);
+    const __amdgpu_buffer_rsrc_t rx = rsrc_b(pr.X, (uint32_t)M * (uint32_t)pr.K * 2u);
+
+    // 1. the scales and zero words of the part's groups for the workgroup's columns
+    //    (16 t0 .. 16 t1 - 1, zero rows 2 t0 .. 2 t1 - 1), by DMA of 4-byte words: each
+    //    column's run of gnp halves sits in the wpr words from the one that holds its
+    //    first half ([row][wpr] words); the zero words as [zero row][gnp]
+    unsigned char *sc_lds = lds;
+    unsigned char *z_lds = lds + a.z_off;
+    const int wpr = gnp / 2 + 1;
+    const int sc_units = 16 * T * wpr;
+    const int z_units = 2 * T * gnp;
+    for (int u0 = w * 64; u0 < sc_units; u0 += W * 64) {
+        const int u = u0 + lane;
+        const int row = u / wpr, wi = u - row * wpr;
+        const uint32_t first = ((uint32_t)(t0 * 16 + row) * (uint32_t)G + (uint32_t)ga) >> 1;
+        dma4_b(rs, sc_lds + u0 * 4, u < sc_units ? (first + (uint32_t)wi) * 4u : kOobB);
+    }
+    for (int u0 = w * 64; u0 < z_units; u0 += W * 64) {
+        const int u = u0 + lane;
+        const int row = u / gnp, gi = u - row * gnp;
+        dma4_b(rz, z_lds + u0 * 4,
+               u < z_units ? ((uint32_t)(t0 * 2 + row) * (uint32_t)G + (uint32_t)(ga + gi)) * 4u : kOobB);
+    }
+    asm volatile("" ::: "memory");
+
+    // 2. the wave's K slice of X (rows past M read as 0).  The MFMAs need lane (r, h) to
+    //    hold X[r][(g0 + i) * 128 + 32h + 8j .. + 8] for j = 0..3 (the 64 bytes at 64h of
+    //    the group's row); load j instead brings the 16 bytes at 64j + 16h, so that the
+    //    four lanes of a row read 64 contiguous bytes per instruction, and a 4 x 4
+    //    transpose across the lane rows (below) puts each chunk in place
+    u32x4_t xf[GPW][4];
+#pragma unroll
+    for (int i = 0; i < GPW; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            xf[i][j] = ld16_b(rx, (c < M && i < gn) ? (uint32_t)c * (uint32_t)pr.K * 2u +
+                                                          (uint32_t)(g0 + i) * 256u + 64u * j + 16u * h
+                                                    : kOobB);
+
+    // 3. the codes of every (tile, group) of the slice
+    u32x4_t wv[TMAX][GPW];
+#pragma unroll
+    for (int tl = 0; tl < TMAX; ++tl)
+#pragma unroll
+        for (int i = 0; i < GPW; ++i) {
+            const int n = (t0 + tl) * 16 + c;
+            wv[tl][i] = ld16_b(rw, (tl < T && i < gn && n < N)
+                                       ? (uint32_t)n * rowb + (uint32_t)(g0 + i) * 64u + 16u * h
+                                       : kOobB);
+        }
+    asm volatile("" ::: "memory");
+    // the DMA of this wave was issued before its 4 GPW + TMAX GPW register loads:
+    // vmcnt(that many) means it has landed; the barrier makes every wave's part visible
+    constexpr int kAfter = 4 * GPW + TMAX * GPW;
+    static_assert(kAfter < 64, "vmcnt is a 6-bit counter");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (kAfter & 15) | ((kAfter >> 4) << 14));
+    __syncthreads();
+
+    // X in place, and S[r][g] = sum of row r of X over group g (the lane's 32 values,
+    // then across its row's four lanes, in a fixed order) through this wave's LDS
+    // region: lane (c, h) keeps S of rows 4h .. 4h+3, the rows its accumulators hold
+    float *sS = (float *)(lds + a.s_off) + w * GPW * 16;
+    f32x4_t Sv[GPW];
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        transpose_rows4(xf[i]);
+        float ps = (sum8_bf16(xf[i][0]) + sum8_bf16(xf[i][1])) + (sum8_bf16(xf[i][2]) + sum8_bf16(xf[i][3]));
+        ps += __int_as_float(__shfl_xor(__float_as_int(ps), 16));
+        ps += __int_as_float(__shfl_xor(__float_as_int(ps), 32));
+        if (h == 0)
+            sS[i * 16 + c] = ps;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            xf[i][j] = x_permute8(xf[i][j]);
+    }
+#pragma unroll
+    for (int i = 0; i < GPW; ++i)
+        Sv[i] = *(const f32x4_t *)(sS + i * 16 + 4 * h);
+
+    // 4. per (tile, group): four MFMAs on the biased codes (P = sum x * (128 + q)), then
+    //    acc += s * (P - (128 + z) * S) in fp32
+    uint32_t mask = 0x000F000Fu, bias = kBiasBits;
+    asm volatile("" : "+v"(mask));
+    asm volatile("" : "+v"(bias));
+    const int zsh = (c & 7) * 4;
+    f32x4_t acc[TMAX];
+#pragma unroll
+    for (int tl = 0; tl < TMAX; ++tl) {
+        acc[tl] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (tl < T) {
+            const int srow = tl * 16 + c;
+            const uint16_t *scl = (const uint16_t *)sc_lds + srow * wpr * 2 +
+                                  (((t0 * 16 + srow) * G + ga) & 1) - ga;
+            const uint32_t *zl = (const uint32_t *)z_lds + (tl * 2 + (c >> 3)) * gnp - ga;
+#pragma unroll
+            for (int i = 0; i < GPW; ++i) {
+                if (i < gn) {
+                    const int g = g0 + i;
+                    f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+                    d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][0]), frag_b(wv[tl][i].x, mask, bias), d);
+                    d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][1]), frag_b(wv[tl][i].y, mask, bias), d);
+                    d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][2]), frag_b(wv[tl][i].z, mask, bias), d);
+                    d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][3]), frag_b(wv[tl][i].w, mask, bias), d);
+                    const float zb = -(float)(kCodeBias + ((zl[g] >> zsh) & 15u));
+                    const float s = f16_bits_to_f32(scl[g]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[tl][e] = fmaf(s, fmaf(zb, Sv[i][e], d[e]), acc[tl][e]);
+                }
+            }
+        }
+    }
+
+    // 5. the K slices of each tile added in slice order; lane (c, h) holds rows 4h .. 4h+3
+    //    of column c
+    f32x4_t *red = (f32x4_t *)(lds + a.r_off); // [W][TMAX][64]
+#pragma unroll
+    for (int tl = 0; tl < TMAX; ++tl)
+        if (tl < T)
+            red[(slice * TMAX + tl) * 64 + lane] = acc[tl];
+    __syncthreads();
+    __shared__ int s_last;
+    float *pb = (float *)(a.ws + pr.part_off) + (size_t)tg * P * pr.tmx * 256; // [part][tmx * 64][4]
+    uint32_t *ctr = (uint32_t *)(a.ws + kOffCounters) + pr.tkt + tg;
+    for (int e = threadIdx.x; e < T * 64; e += W * 64) {
+        const int tl = e >> 6, l = e & 63;
+        f32x4_t y = red[tl * 64 + l];
+        for (int v = 1; v < W; ++v) {
+            const f32x4_t o = red[(v * TMAX + tl) * 64 + l];
+            y[0] += o[0];
+            y[1] += o[1];
+            y[2] += o[2];
+            y[3] += o[3];
+        }
+        if (P == 1) {
+            store_rows(pr, a, y, t0 + tl, l, M, N);
+        } else {
+            // the part's partial sums, device-coherent, for the tile group's last arriver
+            float *dst = pb + ((size_t)part * pr.tmx * 64 + e) * 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __hip_atomic_store(dst + i, y[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (P > 1) {
+        // parts of K meet in the workspace: each part stores its partial sums, then takes
+        // an arrival ticket; the last to arrive adds the P parts in part order and stores
+        // Y, so the result does not depend on the arrival order
+        __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): this thread's stores have completed
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(P - 1);
+        __syncthreads();
+        if (s_last) {
+            for (int e = threadIdx.x; e < T * 64; e += W * 64) {
+                f32x4_t y;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    y[i] = __hip_atomic_load(pb + (size_t)e * 4 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int pp = 1; pp < P; ++pp) {
+                    const float *src = pb + ((size_t)pp * pr.tmx * 64 + e) * 4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        y[i] += __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                store_rows(pr, a, y, t0 + (e >> 6), e & 63, M, N);
+            }
+            if (threadIdx.x == 0)
+                __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+} // namespace
+
+static size_t block_ws_bytes(int N, int T, int P)
+{
+    if (P <= 1)
+        return 0;
+    const int nt = (N + 15) / 16;
+    const int ntg = (nt + T - 1) / T;
+    const int tmx = (nt + ntg - 1) / ntg;
+    return (size_t)ntg * P * tmx * 1024;
+}
+
+// Measured on MI355X at M = 16 (graph replays, K = 2560 .. 9728, N = 1024 .. 19456): K
+// stays whole up to 47 groups (every CU reads all of X, and the hand-off of partial
+// sums between parts costs more than the X it saves); longer K is cut into parts of
+// about 13 groups, so each CU reads a part of X.  The tile groups then spread the
+// (tile group, part) workgroups of the whole launch about once over the CUs, at most
+// 5 tiles each.
+static int block_parts(int K)
+{
+    const int G = K / kGroup;
+    return G < 48 ? 1 : (G + 12) / 13;
+}
+
+// Per projection the tile-group size T and the parts of K P (block_choose, or the
+// hints); one wave count for the launch: enough that each wave's share of a part
+// holds about two groups.
+BlockPlan plan_block(const int *N, const int *K, int count, int M, int tmax_hint, int waves_hint, int parts_hint)
+{
+    BlockPlan p{};
+    p.count = count;
+    if (M < 2 || M > 16 || count < 1 || count > kMaxProblemsBlock)
+        return p;
+    int tmax = 1, gpmax = 1, tkt = 0;
+    size_t off = kZeroRegion;
+    int wg = 0;
+    long long units = 0; // (tile, part) pairs of the launch
+    for (int q = 0; q < count; ++q)
+        units += (long long)((N[q] + 15) / 16) * block_parts(K[q]);
+    int Tl = (int)((units + kBlockCUs - 1) / kBlockCUs);
+    Tl = Tl < 1 ? 1 : Tl > 5 ? 5 : Tl;
+    for (int q = 0; q < count; ++q) {
+        int T = Tl, P = block_parts(K[q]);
+        if (tmax_hint > 0)
+            T = tmax_hint;
+        if (parts_hint > 0)
+            P = parts_hint;
+        const int G = K[q] / kGroup;
+        P = P > G ? G : P;
+        const int nt = (N[q] + 15) / 16;
+        const int ntg = (nt + T - 1) / T;
+        const int tmx = (nt + ntg - 1) / ntg;
+        p.parts[q] = P;
+        p.ntg[q] = ntg;
+        p.tmx[q] = tmx;
+        p.wg0[q] = wg;
+        wg += ntg * P;
+        tmax = tmx > tmax ? tmx : tmax;
+        const int Gp = (G + P - 1) / P;
+        gpmax = Gp > gpmax ? Gp : gpmax;
+        p.tkt[q] = tkt;
+        p.part_off[q] = off;
+        if (P > 1) {
+            tkt += ntg;
+            off += block_ws_bytes(N[q], T, P);
+        }
+    }
+    if (tkt > (int)((kZeroRegion - kOffCounters) / 4))
+        return p;
+    p.ws_bytes = off == kZeroRegion ? 0 : off;
+    p.grid = wg;
+    int W = (gpmax + 1) / 2;
+    if (waves_hint > 0)
+        W = waves_hint;
+    W = W < 1 ? 1 : W > 16 ? 16 : W;
+    int gpw = (gpmax + W - 1) / W;
+    p.tmax = tmax <= 1 ? 1 : tmax <= 2 ? 2 : tmax <= 5 ? 5 : 0;
+    // register budget: three groups per wave at most with up to two tiles, else two
+    const int gcap = p.tmax <= 2 ? 3 : 2;
+    while (gpw > gcap && W < 16) {
+        ++W;
+        gpw = (gpmax + W - 1) / W;
+    }
+    p.gpw = gpw <= 1 ? 1 : gpw <= 2 ? 2 : gpw <= gcap ? 3 : 0;
+    if (p.gpw == 0 || p.tmax == 0)
+        return p;
+    p.waves = W;
+    // LDS: scales ([16 tmax][gpmax / 2 + 1] words) and zero words ([2 tmax][gpmax]), rounded up
+    // to whole DMA rounds; per-wave row sums; the slice accumulators [W][TMAX][64] of 16 B
+    const size_t sc = (size_t)((16 * p.tmax * (gpmax / 2 + 1) + 63) / 64 * 64) * 4;
+    const size_t zw = (size_t)((2 * p.tmax * gpmax + 63) / 64 * 64) * 4;
+    p.z_off = (int)((sc + 15) / 16 * 16);
+    p.s_off = (int)((p.z_off + zw + 15) / 16 * 16);
+    p.r_off = p.s_off + W * p.gpw * 16 * 4;
+    p.lds_bytes = (size_t)p.r_off + (size_t)W * p.tmax * 64 * 16;
+    p.ok = p.lds_bytes <= 160 * 1024;
+    return p;
+}
+
+hipError_t launch_block(const BlockArgs &args, const BlockPlan &p, hipStream_t stream)
+{
+    if (!p.ok)
+        return hipErrorInvalidValue;
+    BlockArgs a = args;
+    a.count = p.count;
+    a.z_off = p.z_off;
+    a.s_off = p.s_off;
+    a.r_off = p.r_off;
+    for (int q = 0; q < p.count; ++q) {
+        a.pr[q].wg0 = p.wg0[q];
+        a.pr[q].nt = (a.pr[q].N + 15) / 16;
+        a.pr[q].ntg = p.ntg[q];
+        a.pr[q].parts = p.parts[q];
+        a.pr[q].tmx = p.tmx[q];
+        a.pr[q].tkt = p.tkt[q];
+        a.pr[q].part_off = p.part_off[q];
+    }
+    const dim3 grid(p.grid), block(64 * p.waves);
+    switch (p.gpw * 10 + p.tmax) {
+#define W4A16_BLOCK_CASE(GP, TM)                                                                               \
+    case GP * 10 + TM:                                                                                         \
+        if (p.lds_bytes > 64 * 1024)                                                                           \
+            (void)hipFuncSetAttribute((const void *)block_kernel<GP, TM>,                                      \
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);         \
+        hipLaunchKernelGGL((block_kernel<GP, TM>), grid, block, p.lds_bytes, stream, a);                       \
+        break;
+        W4A16_BLOCK_CASE(1, 1)
+        W4A16_BLOCK_CASE(1, 2)
+        W4A16_BLOCK_CASE(1, 5)
+        W4A16_BLOCK_CASE(2, 1)
+        W4A16_BLOCK_CASE(2, 2)
+        W4A16_BLOCK_CASE(2, 5)
+        W4A16_BLOCK_CASE(3, 1)
+        W4A16_BLOCK_CASE(3, 2)
+#undef W4A16_BLOCK_CASE
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+size_t block_linear_ws(int M, int N, int K)
+{
+    const BlockPlan p = plan_block(&N, &K, 1, M);
+    return p.ok ? p.ws_bytes : 0;
+}
+
+} // namespace w4a16

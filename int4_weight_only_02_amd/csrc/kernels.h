@@ -8,6 +8,8 @@
 
 namespace w4a16 {
 
+constexpr int kMaxProblemsBlock = 8; // projections per block launch
+
 // Workspace layout shared by every call.  The first kZeroRegion bytes hold
 // counters that must read zero when a call starts (the caller zero-fills the
 // workspace once; every call returns them to zero before it completes); scratch
@@ -157,6 +159,43 @@ struct GemvArgs {
 GemvPlan plan_gemv(int N, int K);
 GemvPlan plan_gemv_with(int N, int K, int wpc, int cpw, int sw, int xl);
 hipError_t launch_gemv(const GemvArgs &a, const GemvPlan &p, hipStream_t stream);
+
+// ---------------------------------------------------------------- block (2 <= M <= 16)
+// One or several projections with the same M.  Projection q is cut into ntg tile
+// groups (balanced runs of at most tmx 16-column tiles) and `parts` parts of K; its
+// workgroups (from wg0) take (tile group, part) in that order.  Parts of one tile group
+// meet in the workspace (partial sums at part_off, an arrival counter at tkt).
+struct BlockProb {
+    const uint16_t *X;
+    const uint32_t *qw;
+    const uint16_t *scales;
+    const uint32_t *qz;
+    void *Y;
+    int N, K;
+    // filled by launch_block
+    int nt, wg0, ntg, parts, tmx, tkt;
+    size_t part_off;
+};
+struct BlockArgs {
+    BlockProb pr[kMaxProblemsBlock];
+    int count, M, y_f32;
+    unsigned char *ws;       // workspace base (partial sums, arrival counters)
+    int z_off, s_off, r_off; // filled by launch_block
+};
+struct BlockPlan {
+    int count, gpw, tmax, waves, grid;
+    int wg0[kMaxProblemsBlock], ntg[kMaxProblemsBlock], parts[kMaxProblemsBlock], tmx[kMaxProblemsBlock];
+    int tkt[kMaxProblemsBlock];
+    size_t part_off[kMaxProblemsBlock];
+    int z_off, s_off, r_off;
+    size_t lds_bytes, ws_bytes; // ws_bytes: 0 when no projection splits K
+    bool ok;
+};
+BlockPlan plan_block(const int *N, const int *K, int count, int M, int tmax_hint = 0, int waves_hint = 0,
+                     int parts_hint = 0);
+hipError_t launch_block(const BlockArgs &a, const BlockPlan &p, hipStream_t stream);
+// workspace of a single projection's block plan (the zero region included when K is split)
+size_t block_linear_ws(int M, int N, int K);
 
 // ---------------------------------------------------------------- tiled (large M)
 struct TiledPlan {
