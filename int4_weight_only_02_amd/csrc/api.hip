@@ -68,7 +68,6 @@ size_t gated_ws(int M, int N, int K)
 // host-side stand-in, not the device memory: only the address obtained from
 // hipGetSymbolAddress (kept per device below) is ever passed to a kernel.
 constexpr size_t kStaticWsBytes = W4A16_STATIC_WS_BYTES;
-constexpr int kMaxDevices = 64;
 __device__ __align__(256) unsigned char scratch[kStaticWsBytes];
 
 std::mutex g_scratch_mu;
@@ -85,7 +84,7 @@ __global__ void zero_words_kernel(uint32_t *p, int n)
 int static_scratch(void **out, hipStream_t stream)
 {
     int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    if (current_device(&dev) != hipSuccess)
         return W4A16_ERR_HIP;
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_ptr[dev]) {

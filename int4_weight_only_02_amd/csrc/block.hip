@@ -33,6 +33,7 @@ namespace {
 constexpr uint32_t kOobB = 0xFFFFFF00u; // an offset past the end of every tensor
 constexpr int kRsrcWord3B = 0x00020000; // raw (untyped) buffer loads on gfx9-class GPUs
 constexpr int kBlockCUs = 256;
+constexpr int kBlockLds = 160 * 1024 - 256; // the rest holds the kernel's static LDS
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_b(const void *p, uint32_t bytes)
 {
@@ -404,8 +405,24 @@ BlockPlan plan_block(const int *N, const int *K, int count, int M, int tmax_hint
     p.s_off = (int)((p.z_off + zw + 15) / 16 * 16);
     p.r_off = p.s_off + W * p.gpw * 16 * 4;
     p.lds_bytes = (size_t)p.r_off + (size_t)W * p.tmax * 64 * 16;
-    p.ok = p.lds_bytes <= 160 * 1024;
+    p.ok = p.lds_bytes <= (size_t)kBlockLds;
     return p;
+}
+
+// every block kernel may use up to kBlockLds bytes of dynamic LDS (beyond the 64 KB
+// default); raised once per device
+static hipError_t allow_block_lds(int)
+{
+    const void *fns[] = {(const void *)block_kernel<1, 1>, (const void *)block_kernel<1, 2>,
+                         (const void *)block_kernel<1, 5>, (const void *)block_kernel<2, 1>,
+                         (const void *)block_kernel<2, 2>, (const void *)block_kernel<2, 5>,
+                         (const void *)block_kernel<3, 1>, (const void *)block_kernel<3, 2>};
+    for (const void *f : fns) {
+        const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kBlockLds);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_block(const BlockArgs &args, const BlockPlan &p, hipStream_t stream)
@@ -426,13 +443,13 @@ hipError_t launch_block(const BlockArgs &args, const BlockPlan &p, hipStream_t s
         a.pr[q].tkt = p.tkt[q];
         a.pr[q].part_off = p.part_off[q];
     }
+    const hipError_t e = once_per_device(kOnceBlock, allow_block_lds);
+    if (e != hipSuccess)
+        return e;
     const dim3 grid(p.grid), block(64 * p.waves);
     switch (p.gpw * 10 + p.tmax) {
 #define W4A16_BLOCK_CASE(GP, TM)                                                                               \
     case GP * 10 + TM:                                                                                         \
-        if (p.lds_bytes > 64 * 1024)                                                                           \
-            (void)hipFuncSetAttribute((const void *)block_kernel<GP, TM>,                                      \
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);         \
         hipLaunchKernelGGL((block_kernel<GP, TM>), grid, block, p.lds_bytes, stream, a);                       \
         break;
         W4A16_BLOCK_CASE(1, 1)

@@ -8,6 +8,14 @@
 
 namespace w4a16 {
 
+// ---------------------------------------------------------------- host set-up (host.hip)
+constexpr int kMaxDevices = 64;
+enum { kOnceSkinny = 0, kOnceTiled = 1, kOnceBlock = 2, kOnceSlots = 3 };
+// the device current on the calling thread (below kMaxDevices)
+hipError_t current_device(int *dev);
+// init(dev) runs at most once per (slot, device), under a lock; every caller gets its status
+hipError_t once_per_device(int slot, hipError_t (*init)(int dev));
+
 constexpr int kMaxProblemsBlock = 8; // projections per block launch
 
 // Workspace layout shared by every call.  The first kZeroRegion bytes hold

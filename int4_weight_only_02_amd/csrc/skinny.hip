@@ -1003,39 +1003,7 @@ size_t lds_for(const SkinnyPlan &p, int M)
     return (p.xlds == 2 ? xs * p.waves : xs) + red;
 }
 
-// Tuning override for the split-mode shape, read once from W4A16_SKINNY_SPLIT="tw,sk"
-// (tiles per workgroup, K slices per tile; tw * sk <= 8).  Unset: the heuristic.
-bool split_override(int *tw, int *sk)
-{
-    static int state = -1, otw = 0, osk = 0;
-    if (state < 0) {
-        state = 0;
-        const char *e = getenv("W4A16_SKINNY_SPLIT");
-        if (e && sscanf(e, "%d,%d", &otw, &osk) == 2 && otw >= 1 && osk >= 1 && otw * osk <= kMaxWaves)
-            state = 1;
-    }
-    *tw = otw;
-    *sk = osk;
-    return state == 1;
-}
-
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
-
-// Tuning override for the chunked mode, read once from W4A16_SKINNY_CHUNK="tw,cg"
-// (tiles per workgroup, groups per K chunk; cg 0 = all of K).  Unset: the heuristic.
-bool chunk_override(int *tw, int *cg)
-{
-    static int state = -1, otw = 0, ocg = 0;
-    if (state < 0) {
-        state = 0;
-        const char *e = getenv("W4A16_SKINNY_CHUNK");
-        if (e && sscanf(e, "%d,%d", &otw, &ocg) == 2 && otw >= 1 && otw <= kMaxWaves && ocg >= 0)
-            state = 1;
-    }
-    *tw = otw;
-    *cg = ocg;
-    return state == 1;
-}
 
 // Chunked split mode: tw tiles per workgroup share X, whose K range is cut into C
 // chunks of cg groups (one workgroup per tile group and chunk).  Fills p.tw, sk, per,
@@ -1089,14 +1057,8 @@ bool plan_chunk(SkinnyPlan &p, int M, size_t lds_limit, int tw, int cg, bool fix
 // more tiles than CUs the workgroup-shared staging of the other split modes wins.
 bool choose_chunk(SkinnyPlan &p, int M, size_t lds_limit, bool fixed, int tw_hint)
 {
-    int tw = 0, cg = 0;
+    int tw = 0;
     SkinnyPlan c = p;
-    if (chunk_override(&tw, &cg) && !(p.pair && (tw & 1))) {
-        if (!plan_chunk(c, M, lds_limit, tw, cg, fixed))
-            return false;
-        p = c;
-        return true;
-    }
     if (p.mblocks != 1 || M <= 4 || (tw_hint <= 0 && p.nt > kCUs))
         return false;
     tw = tw_hint > 0 ? tw_hint : 1;
@@ -1150,11 +1112,6 @@ SkinnyPlan plan_skinny(int M, int N, int K, int lmhead, size_t lds_limit)
         int sk = kMaxWaves / tw;
         sk = sk > batches ? batches : sk;
         sk = sk < 1 ? 1 : sk;
-        int otw = 0, osk = 0;
-        if (split_override(&otw, &osk)) {
-            tw = otw;
-            sk = osk;
-        }
         const size_t red = sk > 1 ? (size_t)tw * sk * 1024 : 0;
         // whole batches per slice; drop the slices that rounding left empty
         p.per = round_up((p.G + sk - 1) / sk, kB);
@@ -1284,43 +1241,54 @@ void allow_lds_multi(size_t bytes)
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-// LDS per workgroup: whatever the device allows, up to the budget the plans assume
+// LDS per workgroup: whatever the device allows, up to the budget the plans assume;
+// looked up, and the kernels' limits raised to it, once per device
+size_t g_lds_limit[kMaxDevices];
+
+hipError_t init_lds_limit(int dev)
+{
+    int v = 0;
+    const hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess)
+        return e;
+    const size_t lim = (size_t)v > 4096 ? (size_t)v - 4096 : 0; // room for the static LDS
+    const size_t lds_limit = lim < kLdsBudget ? lim : kLdsBudget;
+    if (lds_limit > 64 * 1024) {
+        allow_lds<kSplitLds, false>(lds_limit);
+        allow_lds<kSplitLds, true>(lds_limit);
+        allow_lds<kStream, false>(lds_limit);
+        allow_lds<kStream, true>(lds_limit);
+        allow_lds<kSplitPriv, false>(lds_limit);
+        allow_lds<kSplitPriv, true>(lds_limit);
+        allow_lds<kSplitPrivDma, false>(lds_limit);
+        allow_lds<kSplitPrivDma, true>(lds_limit);
+        allow_lds<kSplitChunk, false>(lds_limit);
+        allow_lds<kSplitChunk, true>(lds_limit);
+        allow_lds<kSplitLds, false, true>(lds_limit);
+        allow_lds<kSplitLds, true, true>(lds_limit);
+        allow_lds<kSplitPriv, false, true>(lds_limit);
+        allow_lds<kSplitPriv, true, true>(lds_limit);
+        allow_lds<kSplitPrivDma, false, true>(lds_limit);
+        allow_lds<kSplitPrivDma, true, true>(lds_limit);
+        allow_lds<kSplitChunk, false, true>(lds_limit);
+        allow_lds<kSplitChunk, true, true>(lds_limit);
+        allow_lds_multi<false>(lds_limit);
+        allow_lds_multi<true>(lds_limit);
+    }
+    g_lds_limit[dev] = lds_limit;
+    return hipSuccess;
+}
+
 hipError_t device_lds_limit(size_t *limit)
 {
-    static size_t lds_limit = 0;
-    if (lds_limit == 0) {
-        int dev = 0, v = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess)
-            e = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
-        if (e != hipSuccess)
-            return e;
-        const size_t lim = (size_t)v > 4096 ? (size_t)v - 4096 : 0; // room for the static LDS
-        lds_limit = lim < kLdsBudget ? lim : kLdsBudget;
-        if (lds_limit > 64 * 1024) {
-            allow_lds<kSplitLds, false>(lds_limit);
-            allow_lds<kSplitLds, true>(lds_limit);
-            allow_lds<kStream, false>(lds_limit);
-            allow_lds<kStream, true>(lds_limit);
-            allow_lds<kSplitPriv, false>(lds_limit);
-            allow_lds<kSplitPriv, true>(lds_limit);
-            allow_lds<kSplitPrivDma, false>(lds_limit);
-            allow_lds<kSplitPrivDma, true>(lds_limit);
-            allow_lds<kSplitChunk, false>(lds_limit);
-            allow_lds<kSplitChunk, true>(lds_limit);
-            allow_lds<kSplitLds, false, true>(lds_limit);
-            allow_lds<kSplitLds, true, true>(lds_limit);
-            allow_lds<kSplitPriv, false, true>(lds_limit);
-            allow_lds<kSplitPriv, true, true>(lds_limit);
-            allow_lds<kSplitPrivDma, false, true>(lds_limit);
-            allow_lds<kSplitPrivDma, true, true>(lds_limit);
-            allow_lds<kSplitChunk, false, true>(lds_limit);
-            allow_lds<kSplitChunk, true, true>(lds_limit);
-            allow_lds_multi<false>(lds_limit);
-            allow_lds_multi<true>(lds_limit);
-        }
-    }
-    *limit = lds_limit;
+    const hipError_t e = once_per_device(kOnceSkinny, init_lds_limit);
+    if (e != hipSuccess)
+        return e;
+    int dev = 0;
+    const hipError_t d = current_device(&dev);
+    if (d != hipSuccess)
+        return d;
+    *limit = g_lds_limit[dev];
     return hipSuccess;
 }
 

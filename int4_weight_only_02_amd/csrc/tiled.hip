@@ -597,20 +597,20 @@ TiledPlan plan_tiled(int M, int N, int K)
 
 hipError_t launch_tiled(const TiledArgs &a, const TiledPlan &p, hipStream_t stream)
 {
-    static bool lds_set = false;
-    if (!lds_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)tiled_kernel<false>,
+    // every tile kernel uses all 160 KB of LDS: allowed once per device
+    hipError_t e = once_per_device(kOnceTiled, [](int) -> hipError_t {
+        hipError_t r = hipFuncSetAttribute((const void *)tiled_kernel<false>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute((const void *)tiled_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        if (r == hipSuccess)
+            r = hipFuncSetAttribute((const void *)tiled_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                     kLdsBytes);
-        if (e != hipSuccess)
-            return e;
-        lds_set = true;
-    }
+        return r;
+    });
+    if (e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(prep_kernel, dim3(a.M), dim3(256), 0, stream, a.X, a.K, (uint16_t *)(a.ws + p.off_xh),
                        (float *)(a.ws + p.off_rs));
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     if (p.stream)

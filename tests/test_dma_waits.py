@@ -32,7 +32,7 @@ def _asm(tmp_path_factory, name):
 
 # source, the fewest DMA waits it must contain: the chunked and the DMA private modes
 # in the single and the batched skinny kernels; the X-in-LDS instances of the M = 1 kernel
-@pytest.mark.parametrize("name,least", [("skinny.hip", 24), ("gemv.hip", 9), ("block.hip", 9)])
+@pytest.mark.parametrize("name,least", [("skinny.hip", 24), ("gemv.hip", 9), ("block.hip", 8)])
 def test_every_dma_wait_covers_the_dma(tmp_path_factory, name, least):
     skinny_asm = _asm(tmp_path_factory, name)
     kern, last_dma, after = None, None, 0

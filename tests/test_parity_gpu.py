@@ -169,7 +169,7 @@ def _verify_rules(am_gpu, L_gpu, am_o, gap, tol, draft, Yo):
     assert L_gpu == expect_L
 
 
-def _lmhead_case(dev, d, L0=None, seed=0, return_logits=True):
+def _lmhead_case(dev, d, L0=None, seed=0, return_logits=True, logits_dtype=None):
     M = d["X"].shape[0]
     N = d["codes"].shape[0]
     t, qw, qz, oqw, oqz = _prep(d, dev)
@@ -181,7 +181,7 @@ def _lmhead_case(dev, d, L0=None, seed=0, return_logits=True):
     draft = synth.force_prefix(draft, L0, am_o, rng, N)
     assert oracle.argmax_accept(Yo, draft)[2] == L0
     am, acc, Y = w4.w4a16_lmhead_verify(t["X"], qw, t["scales"], qz, torch.from_numpy(draft).to(dev),
-                                        return_logits=return_logits)
+                                        return_logits=return_logits, logits_dtype=logits_dtype)
     torch.cuda.synchronize()
     am = am.cpu().numpy()
     L = int(acc.cpu()[0])
@@ -189,6 +189,7 @@ def _lmhead_case(dev, d, L0=None, seed=0, return_logits=True):
     if (gap[: min(L0 + 1, M)] > tol).all():
         assert L == L0
     if return_logits:
+        assert Y.dtype == (torch.float32 if logits_dtype is None else logits_dtype)
         check(Y, Yo, "lm_head logits")
     return am, L
 
@@ -210,6 +211,19 @@ def test_lmhead_small(dev, M, N, K):
     d = synth.linear_inputs(M * 3 + N + K, M, N, K)
     for L0 in (0, M // 2, M):
         _lmhead_case(dev, d, L0, seed=L0)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 151936, 2560), (16, 1000, 2560), (3, 264, 640)])
+def test_lmhead_bf16_logits(dev, M, N, K):
+    # bf16 logits beside the argmax (the full vocabulary runs the persistent stream
+    # plan): every logit within the bf16 bound, argmax and accept length by the rules
+    print("lm_head bf16 logits", M, N, K, flush=True)
+    if N == 151936:
+        d = synth.workload_inputs("lmhead_verify_m16", 0)
+    else:
+        d = synth.linear_inputs(M * 5 + N + K, M, N, K)
+    for L0 in (0, M // 2):
+        _lmhead_case(dev, d, L0, seed=L0 + 3, return_logits=True, logits_dtype=torch.bfloat16)
 
 
 def test_lmhead_ties_pick_lowest_column(dev):

@@ -32,6 +32,11 @@ def _case(seed, M, N, K, dev):
     return d, t, qw, qz, oqw, oqz
 
 
+def _allocations(dev):
+    """Device allocations torch's allocator has made so far (a running count)."""
+    return torch.cuda.memory_stats(dev).get("allocation.all.allocated", 0)
+
+
 # each uses the scratch: K chunked across workgroups (partial sums and arrival
 # counters), the same with fewer rows, columns and chunks, and the large-M path
 # (X staged as fp16); then a call that needs none
@@ -46,10 +51,10 @@ def test_static_ws_matches_linear_on_consecutive_calls(dev):
         ref = w4.w4a16_linear(t["X"], qw, t["scales"], qz, out_dtype=dt)
         Y = torch.empty((M, N), dtype=dt, device=dev)
         torch.cuda.synchronize()
-        before = torch.cuda.memory_allocated(dev)
+        before = _allocations(dev)
         w4.w4a16_linear_static_ws(t["X"], qw, t["scales"], qz, out=Y)
         torch.cuda.synchronize()
-        assert torch.cuda.memory_allocated(dev) == before
+        assert _allocations(dev) == before, "the call allocated device memory"
         assert torch.equal(Y, ref), "static-scratch call differs from w4a16_linear"
         check(Y, oracle.linear(d["X"], oqw, d["scales"], oqz), "static ws M=%d N=%d K=%d" % (M, N, K))
         # a second call into the dirty array gives the same bits
