@@ -7,10 +7,10 @@ one step = both projections.  Prints ONE JSON line with:
   value          algorithmic HBM GB/s of the whole step (inputs resident in HBM,
                  weight copies rotated over > 768 MB so the 256 MB Infinity Cache
                  cannot serve them), steps replayed from a HIP graph
-  roofline       the dominant kernel (skinny_kernel) against 8 TB/s: algorithmic
+  roofline       the dominant kernel (gemv_kernel) against 8 TB/s: algorithmic
                  bytes per launch / average launch time, from HIP events recorded on
                  the launch stream around the timed region (every launch in it is a
-                 skinny_kernel); traffic = HBM bytes per launch from the committed
+                 gemv_kernel); traffic = HBM bytes per launch from the committed
                  rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain
                  copy of known size), or null if the kernel sources changed since
   cpu_baseline   the fp64 CPU oracle timed on this host on a bounded sample
@@ -61,16 +61,24 @@ def algo_bytes(M, N, K, out_bytes=2, lmhead=False):
     return b
 
 
-SKINNY_SOURCES = ("common.h", "kernels.h", "skinny.hip", "api.hip")
+# the kernel each small-M workload's launches run, and the sources that decide what it
+# reads and writes (their hash stamps a counter summary)
+KERNEL_OF = {"decode_gemv_m1": "gemv_kernel", "single_512": "gemv_kernel", "verify_block_m16": "block_kernel",
+             "verify_block_m16+batch": "block_kernel", "lmhead_verify_m16": "skinny_kernel",
+             "prefill_m8192": "tiled_kernel"}
+KERNEL_SOURCES = {"gemv_kernel": ("common.h", "kernels.h", "gemv.hip", "api.hip"),
+                  "block_kernel": ("common.h", "kernels.h", "block.hip", "api.hip"),
+                  "skinny_kernel": ("common.h", "kernels.h", "skinny.hip", "api.hip"),
+                  "tiled_kernel": ("common.h", "kernels.h", "tiled.hip", "api.hip")}
 CALIB_BYTES = 1 << 30
 
 
-def kernel_source_sha():
-    """Hash of the code (comments and blank lines removed) of the sources that
-    decide what skinny_kernel reads and writes."""
+def kernel_source_sha(kernel="gemv_kernel"):
+    """Hash of the code (comments and blank lines removed) of the sources that decide
+    what the kernel reads and writes."""
     import re
     h = hashlib.sha256()
-    for f in SKINNY_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "int4_weight_only_02_amd", "csrc", f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -79,9 +87,13 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload, launches_per_step):
+def pmc_path(workload):
+    return os.path.join(PROFILE_DIR, "%s__%s__pmc.txt" % (KERNEL_OF[workload], workload.replace("+", "_")))
+
+
+def load_traffic(workload):
     """HBM bytes per launch from the committed counter summary, if it matches the current kernels."""
-    path = os.path.join(PROFILE_DIR, "skinny_kernel__%s__pmc.txt" % workload)
+    path = pmc_path(workload)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -89,12 +101,70 @@ def load_traffic(workload, launches_per_step):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha") != kernel_source_sha():
+    if kv.get("kernel_source_sha") != kernel_source_sha(KERNEL_OF[workload]):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+class ReadProbe:
+    """A plain streaming read (libw4a16_bench.so) of a launch's byte count, over
+    rotating slices of a 1 GiB buffer: the ceiling of a kernel that only reads them."""
+
+    def __init__(self, dev):
+        import ctypes
+        import torch
+        self.lib = ctypes.CDLL(os.path.join(ROOT, "int4_weight_only_02_amd", "libw4a16_bench.so"))
+        self.lib.w4a16_bench_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.w4a16_bench_read.restype = ctypes.c_int
+        self.buf = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        self.sink = torch.zeros(4, dtype=torch.uint8, device=dev)
+
+    def us(self, nbytes, reps=200):
+        import ctypes
+        import torch
+        nb = (nbytes + 255) // 256 * 256
+        R = max(2, min(256, (1 << 30) // nb))
+        base = self.buf.data_ptr()
+
+        def one(r, s):
+            st = self.lib.w4a16_bench_read(ctypes.c_void_p(base + r * nb), nb, ctypes.c_void_p(self.sink.data_ptr()),
+                                           ctypes.c_void_p(s.cuda_stream))
+            assert st == 0
+
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            one(0, s)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                for r in range(R):
+                    one(r, s)
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()
+        torch.cuda.synchronize()
+        n = max(1, reps // R)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (n * R)
 
 
 # Projections of one step that read the same activations, so that nothing in the
@@ -135,7 +205,17 @@ class Workload:
             Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             p = {"label": label, "M": M, "K": K, "N": N, "copies": copies, "Y": Y, "host": d}
             if lmhead:
+                # the draft block: seeded ids, the first L0 forced to the oracle's greedy
+                # choice (the pages' verifier accepts exactly that prefix); the oracle's
+                # logits are kept for the check of the benchmarked call
+                import oracle
                 draft, L0, rng = synth.draft_block(synth.seed_for(name, j), M, N)
+                oqw, oqz = oracle.pack(d["codes"], d["zeros"])
+                p["Yo"] = oracle.linear_matmul(d["X"], oqw, d["scales"], oqz)
+                del oqw, oqz
+                am_o = oracle.argmax_accept(p["Yo"], np.zeros(M, np.int32))[0]
+                draft = synth.force_prefix(draft, L0, am_o, rng, N)
+                p["L0"] = L0
                 p["draft"] = torch.from_numpy(draft).to(dev)
                 p["argmax"] = torch.empty((M,), dtype=torch.int32, device=dev)
                 p["accept"] = torch.empty((1,), dtype=torch.int32, device=dev)
@@ -183,10 +263,13 @@ class Workload:
 
     def check(self):
         """Sanity check of one step against the oracle on sampled outputs: f32 Y, so the
-        figure is the arithmetic error alone (no bf16 output rounding)."""
+        figure is the arithmetic error alone (no bf16 output rounding).  The lm_head
+        call is checked by its own rules instead (check_lmhead)."""
         import torch
         import oracle
         import int4_weight_only_02_amd as w4
+        if self.lmhead:
+            return None
         worst = 0.0
         ys = None
         if self.batched:
@@ -197,8 +280,6 @@ class Workload:
                 for q, y in zip(g, out):
                     ys[q] = y
         for q, p in enumerate(self.projs):
-            if self.lmhead:
-                continue
             X, qw, S, qz = p["copies"][0]
             Y = ys[q] if ys is not None else w4.w4a16_linear(X, qw, S, qz, out_dtype=torch.float32,
                                                               workspace=self.ws)
@@ -214,6 +295,36 @@ class Workload:
             worst = max(worst, float(np.abs(got - ref).max()) / rms)
             del Y
         return worst
+
+    def check_lmhead(self):
+        """The benchmarked lm_head call against the oracle's logits on the same inputs:
+        argmax equal wherever the oracle's top-2 gap exceeds 1e-2 * rms(logits), the
+        chosen logit within that tolerance of the maximum elsewhere, the accepted length
+        equal to the first mismatch of the GPU's argmax with the draft, and equal to the
+        forced prefix L0 when the rows up to it are clear."""
+        import torch
+        import oracle
+        import int4_weight_only_02_amd as w4
+        p = self.projs[0]
+        X, qw, S, qz = p["copies"][0]
+        w4.w4a16_lmhead_verify(X, qw, S, qz, p["draft"], workspace=self.ws, argmax_out=p["argmax"],
+                               accept_out=p["accept"])
+        torch.cuda.synchronize()
+        am = p["argmax"].cpu().numpy()
+        L = int(p["accept"].cpu()[0])
+        Yo = p["Yo"]
+        tol = 1e-2 * float(np.sqrt(np.mean(Yo * Yo)))
+        am_o, gap, _ = oracle.argmax_accept(Yo, np.zeros(p["M"], np.int32))
+        draft = p["draft"].cpu().numpy()
+        clear = gap > tol
+        agree = bool((am[clear] == am_o[clear]).all())
+        near = bool(all(Yo[i, am[i]] >= Yo[i].max() - tol for i in np.nonzero(~clear)[0]))
+        expect_L = next((i for i in range(p["M"]) if am[i] != draft[i]), p["M"])
+        L0 = p["L0"]
+        l0_ok = L == L0 if bool(clear[: min(L0 + 1, p["M"])].all()) else None
+        return {"rows": int(p["M"]), "clear_rows": int(clear.sum()), "argmax_agree_on_clear_rows": agree,
+                "ambiguous_rows_within_tol": near, "accept_len": L, "accept_len_matches_argmax": L == expect_L,
+                "forced_prefix_L0": int(L0), "accept_len_equals_L0": l0_ok}
 
 
 def time_events(wl, reps):
@@ -311,26 +422,98 @@ def cpu_baseline(name, budget_s=10.0):
             break
     dt = (time.perf_counter() - t0) / n
     gbs = sum(b for *_, b in data) / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": oracle.num_threads(), "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": "%d full decode steps (M=1, K2560xN9728 and K9728xN2560), fp64 naive loops, %.1f s"
                       % (n, dt * n),
             "ms_per_step": round(dt * 1e3, 3)}
 
 
+def _graph_of(fn, count):
+    """A HIP graph of fn(0) .. fn(count - 1) captured on a side stream."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        fn(0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for r in range(count):
+                fn(r)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_median_steps(wl, calls=200):
+    """Median over `calls` back-to-back steps, each step one graph replay (a graph per
+    weight copy, in rotation) bracketed by its own HIP events: the median of >= 200
+    calls, queued behind a GPU-side wait so that the host's launch rate does not enter
+    the figure.  Returns microseconds."""
+    import torch
+    graphs = [_graph_of(lambda i, r=r: wl.step(r), 1) for r in range(wl.R)]
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    # hold the GPU (about 20 ms) while the host queues every call, so that the calls
+    # then run back to back and each pair of events brackets GPU time only
+    torch.cuda._sleep(50_000_000)
+    evs = []
+    for i in range(calls):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graphs[i % wl.R].replay()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+
+
+def time_launch_graph(wl, p, calls=200):
+    """One projection alone: graph replays of the rotating copies back to back; the
+    median of five runs of about `calls` launches each.  Microseconds per launch."""
+    import torch
+    g = _graph_of(lambda r: wl.launch(p, r % wl.R), wl.R)
+    g.replay()
+    torch.cuda.synchronize()
+    n = max(1, calls // wl.R)
+    runs = []
+    for _ in range(5):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        runs.append(e0.elapsed_time(e1) * 1e3 / (n * wl.R))
+    return float(np.median(runs))
+
+
+READ_PROBE = None
+
+
 def measure(name, dev, steps, warmup, lmhead=False, ev_reps=200, batched=False):
     wl = Workload(name, dev, lmhead=lmhead, batched=batched)
     err = wl.check()
+    lm = wl.check_lmhead() if lmhead else None
     ev = time_events(wl, ev_reps)
     wall, gpu = time_steps(wl, steps, warmup)
+    med = time_median_steps(wl)
     res = {"copies": wl.R, "bytes_per_step": wl.bytes_per_step, "flops_per_step": wl.flops_per_step,
            "us_per_step": round(wall * 1e6, 3), "us_per_step_gpu_events": round(gpu * 1e6, 3),
+           "us_per_step_median200": round(med, 3),
            "GBps": round(wl.bytes_per_step / wall / 1e9, 2),
            "hbm_frac": round(wl.bytes_per_step / wall / 1e9 / HBM_PEAK_GBS, 4),
            "TFLOPs": round(wl.flops_per_step / wall / 1e12, 3),
            "launches_per_step": len(wl.groups) if batched else len(wl.projs),
-           "batched": batched,
+           "batched": batched, "kernel": KERNEL_OF.get(name + ("+batch" if batched else "")),
            "kernel_us_eager_median": {k: round(v, 3) for k, v in ev.items()},
            "sampled_max_err_over_rms": err}
+    if lm is not None:
+        res["lmhead_check"] = lm
     per = {}
     for p in wl.projs:
         if batched:
@@ -338,9 +521,18 @@ def measure(name, dev, steps, warmup, lmhead=False, ev_reps=200, batched=False):
         t = ev[p["label"]] * 1e-6
         b = algo_bytes(p["M"], p["N"], p["K"], lmhead=lmhead)
         f = 2 * p["M"] * p["N"] * p["K"]
-        per[p["label"]] = {"M": p["M"], "K": p["K"], "N": p["N"], "eager_us": round(t * 1e6, 3),
-                           "GBps": round(b / t / 1e9, 1), "hbm_frac": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
-                           "TFLOPs": round(f / t / 1e12, 2), "mfma_frac": round(f / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        entry = {"M": p["M"], "K": p["K"], "N": p["N"], "eager_us": round(t * 1e6, 3),
+                 "GBps": round(b / t / 1e9, 1), "hbm_frac": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+                 "TFLOPs": round(f / t / 1e12, 2), "mfma_frac": round(f / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        if p["M"] <= 64:
+            tg = time_launch_graph(wl, p)
+            entry.update({"graph_us": round(tg, 3), "graph_GBps": round(b / tg / 1e3, 1),
+                          "graph_hbm_frac": round(b / tg / 1e3 / HBM_PEAK_GBS, 4)})
+            if READ_PROBE is not None:
+                tr = READ_PROBE.us(b)
+                entry.update({"plain_read_us": round(tr, 3), "plain_read_GBps": round(b / tr / 1e3, 1),
+                              "kernel_over_plain_read": round(tg / tr, 3)})
+        per[p["label"]] = entry
     res["per_launch"] = per
     del wl
     import torch
@@ -671,19 +863,28 @@ def _pmc_mean(path, counter, name_filter):
 
 
 def pmc_summary(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, commands):
-    """HBM traffic of skinny_kernel per launch: FETCH_SIZE and WRITE_SIZE (KiB per
+    """HBM traffic per launch of the workload's kernel: FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch) scaled by what the same counters read for a plain copy of CALIB_BYTES."""
-    fk, fn = _pmc_mean(fetch_csv, "FETCH_SIZE", "skinny_kernel")
-    wk, wn = _pmc_mean(write_csv, "WRITE_SIZE", "skinny_kernel")
+    kernel = KERNEL_OF[workload]
+    fk, fn = _pmc_mean(fetch_csv, "FETCH_SIZE", kernel)
+    wk, wn = _pmc_mean(write_csv, "WRITE_SIZE", kernel)
     cf, _ = _pmc_mean(calib_fetch_csv, "FETCH_SIZE", "copy")
     cw, _ = _pmc_mean(calib_write_csv, "WRITE_SIZE", "copy")
     f_scale = CALIB_BYTES / (cf * 1024.0)
     w_scale = CALIB_BYTES / (cw * 1024.0)
     fetch_b = fk * 1024.0 * f_scale
     write_b = wk * 1024.0 * w_scale
-    launches = synth.WORKLOADS[workload]
-    algo = float(np.mean([algo_bytes(M, N, K) for _, M, K, N in launches]))
-    lines = ["# skinny_kernel HBM traffic per launch, workload %s" % workload,
+    base = workload.split("+")[0]
+    launches = synth.WORKLOADS[base]
+    lm = base == "lmhead_verify_m16"
+    if workload.endswith("+batch"):
+        groups = BATCH_GROUPS[base]
+        idx = {l[0]: l for l in launches}
+        per = [sum(algo_bytes(idx[x][1], idx[x][3], idx[x][2]) for x in g) for g in groups]
+        algo = float(np.mean(per))
+    else:
+        algo = float(np.mean([algo_bytes(M, N, K, lmhead=lm) for _, M, K, N in launches]))
+    lines = ["# %s HBM traffic per launch, workload %s" % (kernel, workload),
              "# shapes (label, M, K, N): %s" % (launches,),
              "# commands (each counter in its own run):"] + ["#   %s" % c for c in commands] + [
              "# calibration: a plain device copy of %d bytes (torch copy_) reads FETCH_SIZE %.1f KiB and"
@@ -694,9 +895,9 @@ def pmc_summary(workload, fetch_csv, write_csv, calib_fetch_csv, calib_write_csv
              "hbm_bytes_per_launch: %.0f" % (fetch_b + write_b),
              "algorithmic_bytes_per_launch: %.0f" % algo,
              "traffic_over_algorithmic: %.4f" % ((fetch_b + write_b) / algo),
-             "kernel_source_sha: %s" % kernel_source_sha()]
+             "kernel_source_sha: %s" % kernel_source_sha(kernel)]
     os.makedirs(PROFILE_DIR, exist_ok=True)
-    out = os.path.join(PROFILE_DIR, "skinny_kernel__%s__pmc.txt" % workload)
+    out = pmc_path(workload)
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -711,6 +912,7 @@ def main():
     ap.add_argument("--proj", default=None, help="with --only: keep only the projection of this label "
                     "(e.g. gate_up or down of prefill_m8192), for per-shape counter runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-probe", action="store_true", help="skip the plain-read ceiling beside each launch")
     ap.add_argument("--calib", action="store_true")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV", "CALIB_WRITE_CSV"),
                     help="write the traffic summary of --only WORKLOAD (default the headline) from counter CSVs")
@@ -731,6 +933,9 @@ def main():
     if args.calib:
         calib_copy(dev)
         return
+    global READ_PROBE
+    if not args.no_read_probe:
+        READ_PROBE = ReadProbe(dev)
 
     if args.proj:
         if not args.only or args.only not in synth.WORKLOADS:
@@ -768,14 +973,15 @@ def main():
         return
     head_name = HEADLINE if HEADLINE in results else names[0]
     per = head["per_launch"]
-    # every launch in the timed region is a skinny_kernel (one per projection)
+    kernel = KERNEL_OF.get(head_name, "gemv_kernel")
+    # every launch in the timed region is one `kernel` launch (one per projection)
     b_launch = head["bytes_per_step"] / head["launches_per_step"]
     t_launch = head["us_per_step_gpu_events"] * 1e-6 / head["launches_per_step"]
     achieved = b_launch / t_launch / 1e9
-    traffic = load_traffic(head_name, len(per))
+    traffic = load_traffic(head_name)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "skinny_kernel", "algorithmic_bytes_per_launch": int(b_launch),
+            "kernel": kernel, "algorithmic_bytes_per_launch": int(b_launch),
             "avg_launch_us": round(t_launch * 1e6, 3),
             "timing": "HIP events on the launch stream around the timed graph replays / launches"}
     cpu = None

@@ -9,6 +9,9 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libw4a16.so")
 SOURCES = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 HEADERS = sorted(glob.glob(os.path.join(PKG, "csrc", "*.h"))) + [os.path.join(ROOT, "include", "w4a16.h")]
+# measurement aid for bench.py (a plain read of a launch's bytes), a library of its own
+BENCH_LIB = os.path.join(PKG, "libw4a16_bench.so")
+BENCH_SOURCES = sorted(glob.glob(os.path.join(PKG, "bench", "*.hip")))
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.
@@ -56,6 +59,12 @@ def build(force=True, verbose=False):
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stdout)
     os.replace(tmp, LIB)
+    tmpb = BENCH_LIB + ".tmp%d" % os.getpid()
+    res = subprocess.run([HIPCC] + FLAGS + BENCH_SOURCES + ["-o", tmpb], stdout=subprocess.PIPE,
+                         stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed (bench aid):\n" + res.stdout)
+    os.replace(tmpb, BENCH_LIB)
     return LIB
 
 

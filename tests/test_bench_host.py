@@ -69,17 +69,17 @@ def test_pmc_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     # two dispatches per counter whose scaled mean is 1.1x the algorithmic fetch, and
     # the output's bytes written
     f_kib = 1.1 * algo / 2 / 1024
-    _counter_csv(tmp_path / "f.csv", [("skinny_kernel<1>", "FETCH_SIZE", f_kib * 0.9),
-                                      ("skinny_kernel<1>", "FETCH_SIZE", f_kib * 1.1),
+    _counter_csv(tmp_path / "f.csv", [("gemv_kernel<8, 8, true>", "FETCH_SIZE", f_kib * 0.9),
+                                      ("gemv_kernel<8, 8, true>", "FETCH_SIZE", f_kib * 1.1),
                                       ("prep_kernel", "FETCH_SIZE", 1e9)])
-    _counter_csv(tmp_path / "w.csv", [("skinny_kernel<1>", "WRITE_SIZE", 0.0),
-                                      ("skinny_kernel<1>", "WRITE_SIZE", 0.0)])
+    _counter_csv(tmp_path / "w.csv", [("gemv_kernel<8, 8, true>", "WRITE_SIZE", 0.0),
+                                      ("gemv_kernel<8, 8, true>", "WRITE_SIZE", 0.0)])
     bench.pmc_summary("decode_gemv_m1", str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
                       str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), commands=["cmd"])
-    text = open(tmp_path / "out" / "skinny_kernel__decode_gemv_m1__pmc.txt").read()
+    text = open(tmp_path / "out" / "gemv_kernel__decode_gemv_m1__pmc.txt").read()
     fields = dict(l.split(": ", 1) for l in text.splitlines() if not l.startswith("#"))
     assert int(fields["fetch_dispatches"]) == 2
     assert float(fields["hbm_fetch_bytes_per_launch"]) == pytest.approx(1.1 * algo, rel=1e-6)
     assert float(fields["algorithmic_bytes_per_launch"]) == algo
     assert float(fields["traffic_over_algorithmic"]) == pytest.approx(1.1, abs=1e-4)
-    assert fields["kernel_source_sha"] == bench.kernel_source_sha()
+    assert fields["kernel_source_sha"] == bench.kernel_source_sha("gemv_kernel")
