@@ -57,6 +57,7 @@ def _bind(path):
     lib.oracle_quantize.argtypes = [P, P, P, I, I, I, P]
     lib.oracle_linear_gidx.argtypes = [P, P, P, P, P, I, I, I, I, P]
     lib.oracle_swa.argtypes = [P, P, P, I, I, I, I, I, I, P]
+    lib.oracle_swa_block.argtypes = [P, P, P, I, I, I, I, I, I, P]
     lib.oracle_silu_mul.argtypes = [P, P, ctypes.c_longlong, P]
     lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_f64.restype = ctypes.c_double
@@ -220,6 +221,20 @@ def swa(Q, K, Vt, window):
     assert D2 == D and Vt.shape == (Hkv, D, T) and Hq % Hkv == 0 and M <= T and window >= 1
     O = np.zeros((M, Hq, D), np.float64)
     _load().oracle_swa(pq, pk, pv, M, T, Hq, Hkv, D, window, O.ctypes.data_as(ctypes.c_void_p))
+    return O
+
+
+def swa_block(Q, K, Vt, window):
+    """Attention of the last M tokens, bidirectional within that block, the window over
+    the context (oracle_swa_block)."""
+    Q, pq = _c(Q, np.uint16)
+    K, pk = _c(K, np.uint16)
+    Vt, pv = _c(Vt, np.uint16)
+    M, Hq, D = Q.shape
+    T, Hkv, D2 = K.shape
+    assert D2 == D and Vt.shape == (Hkv, D, T) and Hq % Hkv == 0 and M <= T and window >= 1
+    O = np.zeros((M, Hq, D), np.float64)
+    _load().oracle_swa_block(pq, pk, pv, M, T, Hq, Hkv, D, window, O.ctypes.data_as(ctypes.c_void_p))
     return O
 
 

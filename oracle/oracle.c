@@ -359,6 +359,54 @@ void oracle_swa(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt, int M,
         }
 }
 
+/* The drafter proposes a whole block of tokens at once (mlsanity index page, Builds
+ * on: block diffusion for speculative decoding; Pith review, What carries the
+ * argument), so its queries may also attend within the block in both directions.
+ * Reading of that mode: query i of the block (position p_i = T - M + i) sees every
+ * key of the block, T - M <= j < T, and the context keys inside its window,
+ * p_i - window < j < T - M (and j >= 0); the rest as oracle_swa. */
+void oracle_swa_block(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt, int M, int T, int Hq, int Hkv,
+                      int D, int window, double *O)
+{
+    int grp = Hq / Hkv;
+    double scale = 1.0 / sqrt((double)D);
+    int b0 = T - M; /* first key of the block */
+#pragma omp parallel for schedule(static) collapse(2)
+    for (int i = 0; i < M; ++i)
+        for (int h = 0; h < Hq; ++h) {
+            int kv = h / grp;
+            int p = b0 + i;
+            int c0 = p - window + 1 > 0 ? p - window + 1 : 0; /* first context key in the window */
+            if (c0 > b0)
+                c0 = b0;
+            int j1 = T;      /* one past the last key seen: the whole block */
+            int n = j1 - c0; /* the keys c0 .. j1 - 1: the context part, then the block */
+            double *sc = (double *)malloc(sizeof(double) * (size_t)n);
+            double mx = -INFINITY;
+            for (int j = c0; j < j1; ++j) {
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d)
+                    dot += oracle_bf16_to_f64(Q[((size_t)i * Hq + h) * D + d]) *
+                           oracle_bf16_to_f64(K[((size_t)j * Hkv + kv) * D + d]);
+                sc[j - c0] = dot * scale;
+                if (sc[j - c0] > mx)
+                    mx = sc[j - c0];
+            }
+            double sum = 0.0;
+            for (int t = 0; t < n; ++t) {
+                sc[t] = exp(sc[t] - mx);
+                sum += sc[t];
+            }
+            for (int d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (int j = c0; j < j1; ++j)
+                    acc += sc[j - c0] * oracle_bf16_to_f64(Vt[((size_t)kv * D + d) * T + j]);
+                O[((size_t)i * Hq + h) * D + d] = acc / sum;
+            }
+            free(sc);
+        }
+}
+
 /* ---- gated MLP activation -------------------------------------------------- */
 
 /* The pages serve a Qwen3.5-4B target (Pith review, Referee Report: Summary) and do

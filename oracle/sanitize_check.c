@@ -26,6 +26,8 @@ void oracle_quantize(const uint16_t *W, const uint16_t *scales, const uint8_t *z
                      uint8_t *codes);
 void oracle_swa(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt, int M, int T, int Hq, int Hkv, int D,
                 int window, double *O);
+void oracle_swa_block(const uint16_t *Q, const uint16_t *K, const uint16_t *Vt, int M, int T, int Hq, int Hkv,
+                      int D, int window, double *O);
 void oracle_silu_mul(const double *G, const double *U, long long n, double *Y);
 
 static uint32_t rng_state = 12345u;
@@ -104,6 +106,10 @@ int main(void)
         oracle_swa(Q, Kc, Vt, Ms, T, Hq, Hkv, D, window, O);
         for (int i = 0; i < Ms * Hq * D; ++i)
             CHECK(isfinite(O[i]));
+        oracle_swa_block(Q, Kc, Vt, Ms, T, Hq, Hkv, D, window, O);
+        for (int i = 0; i < Ms * Hq * D; ++i)
+            CHECK(isfinite(O[i]));
+        oracle_swa_block(Q, Kc, Vt, Ms, T, Hq, Hkv, D, 1, O);
         free(Q);
         free(Kc);
         free(Vt);

@@ -552,6 +552,67 @@ def test_swa_matches_masked_softmax_formulation(W):
         assert np.abs(O[:, h, :] - want).max() < 1e-12
 
 
+# ---- attention bidirectional within the block (oracle_swa_block) -----------------
+
+def test_swa_block_single_query_is_causal():
+    # a block of one token has no later key: the bidirectional mode is the causal one
+    rng = np.random.default_rng(11)
+    M, T, Hq, Hkv, D = 1, 60, 4, 2, 16
+    Q, K, Vt = _swa_inputs(rng, M, T, Hq, Hkv, D)
+    for W in (1, 7, 100):
+        assert np.array_equal(oracle.swa_block(Q, K, Vt, W), oracle.swa(Q, K, Vt, W))
+
+
+def test_swa_block_equal_keys_give_the_mean_over_context_window_and_block():
+    # every key the same: uniform weights over the context keys in the window and all
+    # M keys of the block
+    rng = np.random.default_rng(12)
+    M, T, Hq, Hkv, D, W = 4, 50, 2, 1, 8, 7
+    Q, K, Vt = _swa_inputs(rng, M, T, Hq, Hkv, D)
+    K[:] = K[0]
+    O = oracle.swa_block(Q, K, Vt, W)
+    V = _bits_to_f64(Vt)
+    for i in range(M):
+        p = T - M + i
+        lo = max(0, p - W + 1)
+        want = V[0, :, lo:T].mean(axis=1)
+        assert np.abs(O[i, 0] - want).max() < 1e-12
+
+
+def test_swa_block_is_invariant_to_permuting_the_block():
+    # every query sees every key of the block, so reordering the block's keys and values
+    # together changes no output (the causal mode would)
+    rng = np.random.default_rng(13)
+    M, T, Hq, Hkv, D, W = 6, 40, 4, 2, 16, 9
+    Q, K, Vt = _swa_inputs(rng, M, T, Hq, Hkv, D)
+    perm = np.arange(T)
+    perm[T - M:] = T - M + rng.permutation(M)
+    O1 = oracle.swa_block(Q, K, Vt, W)
+    O2 = oracle.swa_block(Q, K[perm], Vt[:, :, perm], W)
+    assert np.abs(O1 - O2).max() < 1e-12
+    assert np.abs(oracle.swa(Q, K, Vt, W) - oracle.swa(Q, K[perm], Vt[:, :, perm], W)).max() > 1e-6
+
+
+@pytest.mark.parametrize("W", [1, 3, 64, 1000])
+def test_swa_block_matches_masked_softmax_formulation(W):
+    rng = np.random.default_rng(20 + W)
+    M, T, Hq, Hkv, D = 5, 70, 6, 2, 32
+    Q, K, Vt = _swa_inputs(rng, M, T, Hq, Hkv, D)
+    O = oracle.swa_block(Q, K, Vt, W)
+    q, k, v = _bits_to_f64(Q), _bits_to_f64(K), _bits_to_f64(Vt)
+    pos = np.arange(T - M, T)
+    j = np.arange(T)
+    in_block = j[None, :] >= T - M
+    mask = in_block | (j[None, :] > pos[:, None] - W)  # [M, T]
+    for h in range(Hq):
+        kv = h // (Hq // Hkv)
+        s = q[:, h, :] @ k[:, kv, :].T / np.sqrt(D)
+        s = np.where(mask, s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        assert np.abs(O[:, h, :] - p @ v[kv].T).max() < 1e-12
+
+
 # ---- gated MLP activation (oracle_silu_mul, gated) ----------------------------
 
 def test_silu_closed_forms():

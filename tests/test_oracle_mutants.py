@@ -42,6 +42,10 @@ MUTANTS = [
     ("swa_unscaled", "double scale = 1.0 / sqrt((double)D);", "double scale = 1.0;"),
     ("swa_window_off_by_one", "int j0 = p - window + 1 > 0 ? p - window + 1 : 0;", "int j0 = p - window > 0 ? p - window : 0;"),
     ("swa_kv_head_modulo", "int kv = h / grp;", "int kv = h % Hkv;"),
+    ("swa_block_causal_in_block", "int j1 = T;      /* one past the last key seen: the whole block */",
+     "int j1 = p + 1;"),
+    ("swa_block_window_from_block_start", "int c0 = p - window + 1 > 0 ? p - window + 1 : 0; /* first context key in the window */",
+     "int c0 = b0 - window + 1 > 0 ? b0 - window + 1 : 0;"),
     ("swa_v_untransposed", "acc += sc[j - j0] * oracle_bf16_to_f64(Vt[((size_t)kv * D + d) * T + j]);",
      "acc += sc[j - j0] * oracle_bf16_to_f64(Vt[((size_t)j * Hkv + kv) * D + d]);"),
     ("quantize_ties_away", "if (d > 0.0 || (d == 0.0 && fmod(r, 2.0) != 0.0))", "if (d >= 0.0)"),
@@ -71,6 +75,10 @@ PIN_TESTS = [
     lambda: pins.test_swa_window_of_one_returns_own_value(),
     lambda: pins.test_swa_equal_keys_give_the_window_mean(),
     lambda: pins.test_swa_matches_masked_softmax_formulation(5),
+    lambda: pins.test_swa_block_single_query_is_causal(),
+    lambda: pins.test_swa_block_equal_keys_give_the_mean_over_context_window_and_block(),
+    lambda: pins.test_swa_block_is_invariant_to_permuting_the_block(),
+    lambda: pins.test_swa_block_matches_masked_softmax_formulation(3),
     lambda: pins.test_quantize_worked_by_hand(),
     lambda: pins.test_quantize_returns_on_grid_weights_to_their_codes(0),
     lambda: pins.test_quantize_matches_exact_rational_rounding(),
