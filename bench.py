@@ -781,7 +781,8 @@ def measure_gemm_ceiling(dev, steps, warmup):
 def measure_swa(dev, steps, warmup, M=16, T=8192, Hq=32, Hkv=8, window=1024):
     """The drafter's sliding-window attention for one verify block: M = 16 queries at
     the end of an 8192-token context, 32 query heads over 8 key/value heads of 128,
-    window 1024 (the pages' leaderboard setting) and 2048.  Algorithmic bytes: the keys
+    window 1024 (the pages' leaderboard setting) and 2048; causal, and bidirectional
+    within the block (block_window_*).  Algorithmic bytes: the keys
     and values of the union of the windows, Q and O (bf16)."""
     import torch
     import int4_weight_only_02_amd as w4
@@ -794,7 +795,7 @@ def measure_swa(dev, steps, warmup, M=16, T=8192, Hq=32, Hkv=8, window=1024):
     Vt = bits(rng.normal(0, 1, (Hkv, D, T)))
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
     out = {}
-    for W in (window, 2 * window):
+    for block, W in ((False, window), (False, 2 * window), (True, window), (True, 2 * window)):
         nkeys = min(T, W + M - 1)
         nbytes = 2 * nkeys * Hkv * D * 2 + 2 * M * Hq * D * 2
         R = int(max(1, min(32, -(-CACHE_ROTATE_BYTES // (2 * T * Hkv * D * 2)))))
@@ -802,19 +803,19 @@ def measure_swa(dev, steps, warmup, M=16, T=8192, Hq=32, Hkv=8, window=1024):
         Qd = t(Q)
         O = torch.empty((M, Hq, D), dtype=torch.bfloat16, device=dev)
         ws = w4.Workspace(dev)
-        Of = w4.w4a16_swa_attention(Qd, *caches[0], T, W, out_dtype=torch.float32, workspace=ws)
+        Of = w4.w4a16_swa_attention(Qd, *caches[0], T, W, out_dtype=torch.float32, workspace=ws, block=block)
         torch.cuda.synchronize()
-        Oo = oracle.swa(Q, K, Vt, W)
+        Oo = (oracle.swa_block if block else oracle.swa)(Q, K, Vt, W)
         err = float(np.abs(Of.cpu().numpy() - Oo).max() / np.sqrt((Oo ** 2).mean()))
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(s):
-            w4.w4a16_swa_attention(Qd, *caches[0], T, W, out=O, workspace=ws)
+            w4.w4a16_swa_attention(Qd, *caches[0], T, W, out=O, workspace=ws, block=block)
             torch.cuda.synchronize()
             with torch.cuda.graph(g, stream=s):
                 for r in range(R):
-                    w4.w4a16_swa_attention(Qd, *caches[r], T, W, out=O, workspace=ws)
+                    w4.w4a16_swa_attention(Qd, *caches[r], T, W, out=O, workspace=ws, block=block)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         for _ in range(max(1, warmup // R)):
@@ -829,7 +830,7 @@ def measure_swa(dev, steps, warmup, M=16, T=8192, Hq=32, Hkv=8, window=1024):
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / (reps * R)
-        out["window_%d" % W] = {"us_per_call": round(us, 3), "bytes_per_call": nbytes,
+        out[("block_window_%d" if block else "window_%d") % W] = {"us_per_call": round(us, 3), "bytes_per_call": nbytes,
                                 "GBps": round(nbytes / us / 1e3, 1), "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
                                 "max_err_over_rms": err, "copies": R}
     out.update({"M": M, "T": T, "Hq": Hq, "Hkv": Hkv, "D": D})

@@ -133,7 +133,8 @@ int w4a16_linear_actorder(const void *X, const int32_t *perm, const uint32_t *qw
  *   query i (0 <= i < M) sits at position p_i = T - M + i; head h reads key/value
  *   head h / (Hq / Hkv); it attends to keys p_i - window < j <= p_i (j >= 0):
  *   O[i,h,:] = sum_j softmax_j(Q[i,h,:] . K[j,kv,:] / sqrt(D)) V[j,kv,:]
- * fp32 scores and sums; the softmax weights enter the value product as bf16.
+ * fp32 scores and sums; the softmax weights enter the value product as a pair of
+ * bf16 values (hi + lo, relative error about 2^-17).
  *   Q   [M][Hq][D]         bf16 (device)
  *   K   [T][Hkv][D]        bf16 key cache, token-major (device)
  *   Vt  [Hkv][D][t_stride] bf16 value cache, transposed: row (kv, d) holds the values
@@ -149,6 +150,19 @@ int w4a16_swa_attention(const void *Q, const void *K, const void *Vt, int M, int
                         int window, int t_stride, void *O, int o_dtype, void *workspace, size_t workspace_bytes,
                         void *stream);
 size_t w4a16_swa_workspace_bytes(int M, int T, int Hq, int Hkv, int window);
+
+/*
+ * w4a16_swa_attention_block -- as w4a16_swa_attention, bidirectional within the block:
+ * the drafter proposes a whole block of tokens at once (mlsanity index page, Builds
+ * on: block diffusion for speculative decoding; Pith review, What carries the
+ * argument), so each query attends to every key of the block and to the context
+ * keys inside its window.  Reading: query i (position p_i = T - M + i) sees keys
+ * T - M <= j < T and p_i - window < j < T - M (j >= 0).  Arguments, layouts,
+ * workspace (w4a16_swa_workspace_bytes), shapes and errors as w4a16_swa_attention.
+ */
+int w4a16_swa_attention_block(const void *Q, const void *K, const void *Vt, int M, int T, int Hq, int Hkv, int D,
+                              int window, int t_stride, void *O, int o_dtype, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /*
  * w4a16_quantize -- round a weight matrix back onto the grid, keeping the grid's

@@ -33,7 +33,7 @@ EXPORTED = ("w4a16_pack", "w4a16_quantize", "w4a16_linear", "w4a16_linear_static
             "w4a16_linear_batch",
             "w4a16_lmhead_verify",
             "w4a16_actorder_perm", "w4a16_pack_actorder", "w4a16_linear_actorder",
-            "w4a16_swa_attention", "w4a16_swa_workspace_bytes",
+            "w4a16_swa_attention", "w4a16_swa_attention_block", "w4a16_swa_workspace_bytes",
             "w4a16_workspace_bytes", "w4a16_status_string", "w4a16_abi_version")
 MAX_BATCH = 8
 
@@ -66,6 +66,8 @@ def lib():
     L.w4a16_quantize.restype = I
     L.w4a16_swa_attention.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, P, S, P]
     L.w4a16_swa_attention.restype = I
+    L.w4a16_swa_attention_block.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, P, S, P]
+    L.w4a16_swa_attention_block.restype = I
     L.w4a16_swa_workspace_bytes.argtypes = [I, I, I, I, I]
     L.w4a16_swa_workspace_bytes.restype = S
     L.w4a16_actorder_perm.argtypes = [P, I, I, P]
@@ -222,9 +224,11 @@ def w4a16_linear_actorder(X, perm, qweight, scales, qzeros, out_dtype=None, grou
     return Y
 
 
-def w4a16_swa_attention(Q, K, Vt, T, window, out_dtype=None, out=None, workspace=None, stream=None):
+def w4a16_swa_attention(Q, K, Vt, T, window, out_dtype=None, out=None, workspace=None, stream=None, block=False):
     """Causal sliding-window attention of Q [M,Hq,128] over K [T_alloc,Hkv,128] and the
-    transposed values Vt [Hkv,128,t_stride] (the first T tokens are the context)."""
+    transposed values Vt [Hkv,128,t_stride] (the first T tokens are the context).
+    block=True: bidirectional within the block of the last M tokens
+    (w4a16_swa_attention_block)."""
     import torch
     M, Hq, D = Q.shape
     Hkv = K.shape[1]
@@ -237,9 +241,10 @@ def w4a16_swa_attention(Q, K, Vt, T, window, out_dtype=None, out=None, workspace
     O = out if out is not None else torch.empty((M, Hq, D), dtype=out_dtype, device=Q.device)
     nbytes = lib().w4a16_swa_workspace_bytes(M, T, Hq, Hkv, window)
     ws = _scratch(workspace, Q.device, nbytes, stream)
-    st = lib().w4a16_swa_attention(_ptr(Q), _ptr(K), _ptr(Vt), M, T, Hq, Hkv, D, window, t_stride, _ptr(O), odt,
-                                   _ptr(ws), nbytes, _stream(stream))
-    _check(st, "w4a16_swa_attention")
+    fn = lib().w4a16_swa_attention_block if block else lib().w4a16_swa_attention
+    st = fn(_ptr(Q), _ptr(K), _ptr(Vt), M, T, Hq, Hkv, D, window, t_stride, _ptr(O), odt, _ptr(ws), nbytes,
+            _stream(stream))
+    _check(st, "w4a16_swa_attention_block" if block else "w4a16_swa_attention")
     return O
 
 

@@ -231,9 +231,8 @@ size_t w4a16_swa_workspace_bytes(int M, int T, int Hq, int Hkv, int window)
     return plan_swa(M, T, Hq, Hkv, window).ws_bytes;
 }
 
-int w4a16_swa_attention(const void *Q, const void *K, const void *Vt, int M, int T, int Hq, int Hkv, int D,
-                        int window, int t_stride, void *O, int o_dtype, void *workspace, size_t workspace_bytes,
-                        void *stream)
+static int swa_call(const void *Q, const void *K, const void *Vt, int M, int T, int Hq, int Hkv, int D, int window,
+                    int t_stride, void *O, int o_dtype, void *workspace, size_t workspace_bytes, void *stream, int block)
 {
     if (o_dtype != W4A16_OUT_BF16 && o_dtype != W4A16_OUT_F32)
         return W4A16_ERR_UNSUPPORTED;
@@ -256,12 +255,27 @@ int w4a16_swa_attention(const void *Q, const void *K, const void *Vt, int M, int
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.window = window;
+    a.block = block;
     a.t_stride = t_stride;
     a.scale = 0.08838834764831845f; // 1 / sqrt(128)
     a.O = O;
     a.o_f32 = o_dtype == W4A16_OUT_F32;
     const hipError_t e = launch_swa(a, p, (unsigned char *)workspace, (hipStream_t)stream);
     return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+int w4a16_swa_attention(const void *Q, const void *K, const void *Vt, int M, int T, int Hq, int Hkv, int D,
+                        int window, int t_stride, void *O, int o_dtype, void *workspace, size_t workspace_bytes,
+                        void *stream)
+{
+    return swa_call(Q, K, Vt, M, T, Hq, Hkv, D, window, t_stride, O, o_dtype, workspace, workspace_bytes, stream, 0);
+}
+
+int w4a16_swa_attention_block(const void *Q, const void *K, const void *Vt, int M, int T, int Hq, int Hkv, int D,
+                              int window, int t_stride, void *O, int o_dtype, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    return swa_call(Q, K, Vt, M, T, Hq, Hkv, D, window, t_stride, O, o_dtype, workspace, workspace_bytes, stream, 1);
 }
 
 int w4a16_quantize(const void *W, const void *scales, const uint32_t *qzeros, int N, int K, int group,

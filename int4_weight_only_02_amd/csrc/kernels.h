@@ -47,6 +47,7 @@ hipError_t launch_gather_k(const void *src, const int32_t *perm, int rows, int K
 struct SwaArgs {
     const uint16_t *Q, *K, *Vt; // bf16: [M][Hq][128], [T][Hkv][128], [Hkv][128][t_stride]
     int M, T, Hq, Hkv, window;
+    int block;                  // 1: every key of the block is seen (bidirectional within it)
     int t_stride;               // row length of V^T (>= T, a multiple of 8)
     float scale;                // 1 / sqrt(128)
     void *O;                    // [M][Hq][128], bf16 or fp32

@@ -4,8 +4,10 @@
 //
 // Reading (the pages give no kernel or formula): scaled-dot-product attention of the
 // last M tokens of a context of T, query i at position p_i = T - M + i, over the keys
-// p_i - window < j <= p_i, with grouped key/value heads (head h reads head
-// h / (Hq / Hkv)).  K is token-major [T][Hkv][D]; V is kept transposed [Hkv][D][T], so
+// p_i - window < j <= p_i (causal), or, in the block mode, over every key of the block
+// (T - M <= j < T) and the context keys p_i - window < j < T - M (the drafter proposes
+// a whole block at once: mlsanity index page, Builds on, block diffusion), with
+// grouped key/value heads (head h reads head h / (Hq / Hkv)).  K is token-major [T][Hkv][D]; V is kept transposed [Hkv][D][T], so
 // that both matrix products read 8 or 16 contiguous bytes per lane.
 //
 // Split over keys (flash-decoding): workgroup (chunk, kv head) has one wave per query
@@ -14,7 +16,9 @@
 //   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16: keys are the rows, so each lane ends up
 //                  with 4 keys of one query -- exactly what the second product needs)
 //   m = row max, P = exp(S - m) (masked keys 0), l = row sum
-//   O~ = P V      (P from registers as bf16, V^T rows as the B operand)
+//   O~ = P V      (P from registers as a pair of bf16 values hi + lo, P - hi rounded
+//                  again, in two MFMAs: P enters to about 2^-17; V^T rows as the B
+//                  operand)
 // and writes (m, l, O~) of its chunk; swa_combine_kernel adds the chunks in order:
 //   O = sum_c e^(m_c - m) O~_c / sum_c e^(m_c - m) l_c,  m = max_c m_c.
 #include "common.h"
@@ -124,7 +128,8 @@ __global__ __launch_bounds__(1024) void swa_partial_kernel(SwaArgs a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int j = j0 + 16 * t + 4 * h4 + r;
-            const bool ok = j <= p && j > p - a.window && j < a.T;
+            const bool ok = j < a.T && (a.block ? (j >= a.T - a.M || j > p - a.window)
+                                                : (j <= p && j > p - a.window));
             st[t][r] = ok ? st[t][r] * sc : -INFINITY;
             mx = fmaxf(mx, st[t][r]);
         }
@@ -150,9 +155,16 @@ __global__ __launch_bounds__(1024) void swa_partial_kernel(SwaArgs a)
         o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < kTiles / 2; ++u) {
-        const u32x4_t pf = {pack_bf16x2(st[2 * u][0], st[2 * u][1]), pack_bf16x2(st[2 * u][2], st[2 * u][3]),
-                            pack_bf16x2(st[2 * u + 1][0], st[2 * u + 1][1]),
-                            pack_bf16x2(st[2 * u + 1][2], st[2 * u + 1][3])};
+        // P = hi + lo: hi = bf16(P), lo = bf16(P - hi) (P - hi is exact in fp32)
+        u32x4_t ph, pl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const f32x4_t &src = st[2 * u + (e >> 1)];
+            const float x0 = src[2 * (e & 1)], x1 = src[2 * (e & 1) + 1];
+            const uint32_t h2 = pack_bf16x2(x0, x1);
+            ph[e] = h2;
+            pl[e] = pack_bf16x2(x0 - __uint_as_float(h2 << 16), x1 - __uint_as_float(h2 & 0xFFFF0000u));
+        }
         const int ja = j0 + 32 * u + 4 * h4, jb = ja + 16;
         // V of keys at or past T (row padding, whatever it holds) is replaced by 0: their
         // weights are 0, and 0 * NaN would not be
@@ -171,7 +183,9 @@ __global__ __launch_bounds__(1024) void swa_partial_kernel(SwaArgs a)
             typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
             const u32x2_t va = *(const u32x2_t *)(Vl + (d * 16 + (ua ^ (d & 15))) * 16 + half);
             const u32x2_t vb = *(const u32x2_t *)(Vl + (d * 16 + (ub ^ (d & 15))) * 16 + half);
-            o[dt] = mfma(pf, u32x4_t{va.x & keep[0], va.y & keep[1], vb.x & keep[2], vb.y & keep[3]}, o[dt]);
+            const u32x4_t vf = {va.x & keep[0], va.y & keep[1], vb.x & keep[2], vb.y & keep[3]};
+            o[dt] = mfma(ph, vf, o[dt]);
+            o[dt] = mfma(pl, vf, o[dt]);
         }
     }
 
