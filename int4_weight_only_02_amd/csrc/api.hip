@@ -206,6 +206,38 @@ int w4a16_linear_actorder(const void *X, const int32_t *perm, const uint32_t *qw
         return W4A16_ERR_NULL;
     if (misaligned(qweight) || misaligned(scales) || misaligned(qzeros) || misaligned(Y))
         return W4A16_ERR_ALIGN;
+    // M = 1 up to 40 groups, and 2 <= M <= 16 while the X rows fit in LDS: the gather
+    // runs inside the kernel's X staging
+    const GemvPlan gp = (M == 1 && K / kGroup <= 40) ? plan_gemv(N, K, 1) : GemvPlan{};
+    const BlockPlan bp = (M >= 2 && M <= 16) ? plan_block_ao(N, K, M) : BlockPlan{};
+    if (bp.ok) {
+        BlockArgs a{};
+        a.perm = perm;
+        a.pr[0].X = (const uint16_t *)X;
+        a.pr[0].qw = qweight;
+        a.pr[0].scales = (const uint16_t *)scales;
+        a.pr[0].qz = qzeros;
+        a.pr[0].Y = Y;
+        a.pr[0].N = N;
+        a.pr[0].K = K;
+        a.M = M;
+        a.y_f32 = y_dtype == W4A16_OUT_F32;
+        return launch_block(a, bp, (hipStream_t)stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+    }
+    if (gp.ok) {
+        GemvArgs a{};
+        a.X = (const uint16_t *)X;
+        a.perm = perm;
+        a.qw = qweight;
+        a.scales = (const uint16_t *)scales;
+        a.qz = qzeros;
+        a.N = N;
+        a.K = K;
+        a.G = K / kGroup;
+        a.Y = Y;
+        a.y_f32 = y_dtype == W4A16_OUT_F32;
+        return launch_gemv(a, gp, (hipStream_t)stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+    }
     void *xg = (unsigned char *)workspace + off;
     if (launch_gather_k(X, perm, M, K, 2, xg, (hipStream_t)stream) != hipSuccess)
         return W4A16_ERR_HIP;
@@ -318,7 +350,7 @@ int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, con
         return W4A16_ERR_WORKSPACE;
 
     hipError_t e;
-    const GemvPlan gp = M == 1 ? plan_gemv(N, K) : GemvPlan{};
+    const GemvPlan gp = M == 1 ? plan_gemv(N, K, 0) : GemvPlan{};
     BlockPlan bp{};
     if (gp.ok) {
         GemvArgs a{};

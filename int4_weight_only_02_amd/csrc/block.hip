@@ -23,6 +23,13 @@
 //   * The scales and zero words of the workgroup's columns (contiguous runs) come in
 //     by LDS DMA; the waves' K-slice accumulators are added through LDS in slice
 //     order.  All sums run in a fixed order: results are deterministic.
+//   * Act-order (GPTQ g_idx, codes stored in the permuted order; Pith review,
+//     Assumptions & free parameters): the contraction needs X'[r][k] = X[r][perm[k]].
+//     For a projection whose X rows fit in LDS, the workgroup brings the rows and perm
+//     in by DMA and each lane gathers its fragments from there, so the permuted copy
+//     of X is never written to HBM and no extra launch runs.  The rows sit in 16-byte
+//     units with the unit index XOR-ed by the row, so that the 16 rows a lane row
+//     reads at one k fall on 16 different banks.
 #include "common.h"
 #include "kernels.h"
 
@@ -102,8 +109,15 @@ __device__ __forceinline__ void transpose_rows4(u32x4_t (&v)[4])
     }
 }
 
-// GPW: the most groups a wave's K slice holds; TMAX: the most tiles a workgroup owns
-template <int GPW, int TMAX>
+// LDS DMA: 16 bytes per lane from offset voff of r into LDS at dst + 16 * lane
+__device__ __forceinline__ void dma16_b(__amdgpu_buffer_rsrc_t r, unsigned char *dst, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, 0, 0, 0);
+}
+
+// GPW: the most groups a wave's K slice holds; TMAX: the most tiles a workgroup owns;
+// AO: act-order (X gathered through perm in LDS; one projection, K whole)
+template <int GPW, int TMAX, bool AO>
 __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
 {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -166,15 +180,34 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     //    hold X[r][(g0 + i) * 128 + 32h + 8j .. + 8] for j = 0..3 (the 64 bytes at 64h of
     //    the group's row); load j instead brings the 16 bytes at 64j + 16h, so that the
     //    four lanes of a row read 64 contiguous bytes per instruction, and a 4 x 4
-    //    transpose across the lane rows (below) puts each chunk in place
+    //    transpose across the lane rows (below) puts each chunk in place.
+    //    Act-order: the M rows of X (LDS unit r U + (j ^ (r % 16)) holds unit j of row
+    //    r, U = K / 8 units per row) and perm come in by DMA instead
     u32x4_t xf[GPW][4];
+    const int U = pr.K / 8;
+    if constexpr (AO) {
+        const __amdgpu_buffer_rsrc_t rp = rsrc_b(a.perm, (uint32_t)pr.K * 4u);
+        unsigned char *xa = lds + a.x_off;
+        unsigned char *pa = lds + a.p_off;
+        const int xunits = M * U, punits = pr.K / 4;
+        for (int u0 = w * 64; u0 < xunits; u0 += W * 64) {
+            const int u = u0 + lane;
+            const int r = u / U, j = (u - r * U) ^ (r & 15);
+            dma16_b(rx, xa + u0 * 16, u < xunits ? (uint32_t)r * (uint32_t)pr.K * 2u + 16u * (uint32_t)j : kOobB);
+        }
+        for (int u0 = w * 64; u0 < punits; u0 += W * 64) {
+            const int u = u0 + lane;
+            dma16_b(rp, pa + u0 * 16, u < punits ? 16u * (uint32_t)u : kOobB);
+        }
+    } else {
 #pragma unroll
-    for (int i = 0; i < GPW; ++i)
+        for (int i = 0; i < GPW; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            xf[i][j] = ld16_b(rx, (c < M && i < gn) ? (uint32_t)c * (uint32_t)pr.K * 2u +
-                                                          (uint32_t)(g0 + i) * 256u + 64u * j + 16u * h
-                                                    : kOobB);
+            for (int j = 0; j < 4; ++j)
+                xf[i][j] = ld16_b(rx, (c < M && i < gn) ? (uint32_t)c * (uint32_t)pr.K * 2u +
+                                                              (uint32_t)(g0 + i) * 256u + 64u * j + 16u * h
+                                                        : kOobB);
+    }
 
     // 3. the codes of every (tile, group) of the slice
     u32x4_t wv[TMAX][GPW];
@@ -188,12 +221,40 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
                                        : kOobB);
         }
     asm volatile("" ::: "memory");
-    // the DMA of this wave was issued before its 4 GPW + TMAX GPW register loads:
+    // the DMA of this wave was issued before its (4 GPW +) TMAX GPW register loads:
     // vmcnt(that many) means it has landed; the barrier makes every wave's part visible
-    constexpr int kAfter = 4 * GPW + TMAX * GPW;
+    constexpr int kAfter = (AO ? 0 : 4 * GPW) + TMAX * GPW;
     static_assert(kAfter < 64, "vmcnt is a 6-bit counter");
     __builtin_amdgcn_s_waitcnt(0x0F70 | (kAfter & 15) | ((kAfter >> 4) << 14));
     __syncthreads();
+
+    if constexpr (AO) {
+        // lane (c, h), fragment (i, j): X'[c][k .. k + 8), k = (g0 + i) 128 + 32h + 8j,
+        // gathered through perm (an entry past the row reads the row's last element);
+        // then a barrier, as the slice accumulators below reuse this LDS
+        const uint32_t *pa = (const uint32_t *)(lds + a.p_off);
+        const unsigned char *xa = lds + a.x_off + (size_t)c * U * 16;
+        const uint32_t last = (uint32_t)pr.K - 1u;
+#pragma unroll
+        for (int i = 0; i < GPW; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                xf[i][j] = u32x4_t{0u, 0u, 0u, 0u};
+                if (c < M && i < gn) {
+                    const int k = (g0 + i) * kGroup + 32 * h + 8 * j;
+                    const u32x4_t p0 = *(const u32x4_t *)(pa + k), p1 = *(const u32x4_t *)(pa + k + 4);
+                    uint32_t v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t kk = min(e < 4 ? p0[e] : p1[e - 4], last);
+                        v[e] = *(const uint16_t *)(xa + (((kk >> 3) ^ (uint32_t)c) << 4) + ((kk & 7u) << 1));
+                    }
+                    xf[i][j] = u32x4_t{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                                       v[6] | (v[7] << 16)};
+                }
+            }
+        __syncthreads();
+    }
 
     // X in place, and S[r][g] = sum of row r of X over group g (the lane's 32 values,
     // then across its row's four lanes, in a fixed order) through this wave's LDS
@@ -202,7 +263,8 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     f32x4_t Sv[GPW];
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
-        transpose_rows4(xf[i]);
+        if constexpr (!AO)
+            transpose_rows4(xf[i]);
         float ps = (sum8_bf16(xf[i][0]) + sum8_bf16(xf[i][1])) + (sum8_bf16(xf[i][2]) + sum8_bf16(xf[i][3]));
         ps += __int_as_float(__shfl_xor(__float_as_int(ps), 16));
         ps += __int_as_float(__shfl_xor(__float_as_int(ps), 32));
@@ -409,14 +471,35 @@ BlockPlan plan_block(const int *N, const int *K, int count, int M, int tmax_hint
     return p;
 }
 
+// The plain plan of one projection, with the X rows (M K bf16) and perm (K int32) laid
+// over the slice accumulators (the kernel separates the two uses by a barrier).  K
+// stays whole, so the split-K cases (48 groups and more) take the separate gather.
+BlockPlan plan_block_ao(int N, int K, int M)
+{
+    BlockPlan p = plan_block(&N, &K, 1, M);
+    if (!p.ok || p.parts[0] != 1 || p.gpw > 2)
+        return BlockPlan{};
+    // both regions in whole DMA rounds (64 units of 16 bytes)
+    p.ao = 1;
+    p.x_off = p.r_off;
+    p.p_off = p.x_off + (M * (K / 8) + 63) / 64 * 64 * 16;
+    const size_t need = (size_t)p.p_off + (size_t)(K / 4 + 63) / 64 * 64 * 16;
+    p.lds_bytes = need > p.lds_bytes ? need : p.lds_bytes;
+    p.ok = p.lds_bytes <= (size_t)kBlockLds;
+    return p;
+}
+
 // every block kernel may use up to kBlockLds bytes of dynamic LDS (beyond the 64 KB
 // default); raised once per device
 static hipError_t allow_block_lds(int)
 {
-    const void *fns[] = {(const void *)block_kernel<1, 1>, (const void *)block_kernel<1, 2>,
-                         (const void *)block_kernel<1, 5>, (const void *)block_kernel<2, 1>,
-                         (const void *)block_kernel<2, 2>, (const void *)block_kernel<2, 5>,
-                         (const void *)block_kernel<3, 1>, (const void *)block_kernel<3, 2>};
+    const void *fns[] = {(const void *)block_kernel<1, 1, false>, (const void *)block_kernel<1, 2, false>,
+                         (const void *)block_kernel<1, 5, false>, (const void *)block_kernel<2, 1, false>,
+                         (const void *)block_kernel<2, 2, false>, (const void *)block_kernel<2, 5, false>,
+                         (const void *)block_kernel<3, 1, false>, (const void *)block_kernel<3, 2, false>,
+                         (const void *)block_kernel<1, 1, true>,  (const void *)block_kernel<1, 2, true>,
+                         (const void *)block_kernel<1, 5, true>,  (const void *)block_kernel<2, 1, true>,
+                         (const void *)block_kernel<2, 2, true>,  (const void *)block_kernel<2, 5, true>};
     for (const void *f : fns) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kBlockLds);
         if (e != hipSuccess)
@@ -434,6 +517,10 @@ hipError_t launch_block(const BlockArgs &args, const BlockPlan &p, hipStream_t s
     a.z_off = p.z_off;
     a.s_off = p.s_off;
     a.r_off = p.r_off;
+    a.x_off = p.x_off;
+    a.p_off = p.p_off;
+    if (p.ao && (p.count != 1 || !a.perm))
+        return hipErrorInvalidValue;
     for (int q = 0; q < p.count; ++q) {
         a.pr[q].wg0 = p.wg0[q];
         a.pr[q].nt = (a.pr[q].N + 15) / 16;
@@ -447,19 +534,25 @@ hipError_t launch_block(const BlockArgs &args, const BlockPlan &p, hipStream_t s
     if (e != hipSuccess)
         return e;
     const dim3 grid(p.grid), block(64 * p.waves);
-    switch (p.gpw * 10 + p.tmax) {
-#define W4A16_BLOCK_CASE(GP, TM)                                                                               \
-    case GP * 10 + TM:                                                                                         \
-        hipLaunchKernelGGL((block_kernel<GP, TM>), grid, block, p.lds_bytes, stream, a);                       \
+    switch (p.gpw * 100 + p.tmax * 10 + (p.ao ? 1 : 0)) {
+#define W4A16_BLOCK_CASE(GP, TM, AO)                                                                           \
+    case GP * 100 + TM * 10 + AO:                                                                              \
+        hipLaunchKernelGGL((block_kernel<GP, TM, AO != 0>), grid, block, p.lds_bytes, stream, a);              \
         break;
-        W4A16_BLOCK_CASE(1, 1)
-        W4A16_BLOCK_CASE(1, 2)
-        W4A16_BLOCK_CASE(1, 5)
-        W4A16_BLOCK_CASE(2, 1)
-        W4A16_BLOCK_CASE(2, 2)
-        W4A16_BLOCK_CASE(2, 5)
-        W4A16_BLOCK_CASE(3, 1)
-        W4A16_BLOCK_CASE(3, 2)
+        W4A16_BLOCK_CASE(1, 1, 0)
+        W4A16_BLOCK_CASE(1, 2, 0)
+        W4A16_BLOCK_CASE(1, 5, 0)
+        W4A16_BLOCK_CASE(2, 1, 0)
+        W4A16_BLOCK_CASE(2, 2, 0)
+        W4A16_BLOCK_CASE(2, 5, 0)
+        W4A16_BLOCK_CASE(3, 1, 0)
+        W4A16_BLOCK_CASE(3, 2, 0)
+        W4A16_BLOCK_CASE(1, 1, 1)
+        W4A16_BLOCK_CASE(1, 2, 1)
+        W4A16_BLOCK_CASE(1, 5, 1)
+        W4A16_BLOCK_CASE(2, 1, 1)
+        W4A16_BLOCK_CASE(2, 2, 1)
+        W4A16_BLOCK_CASE(2, 5, 1)
 #undef W4A16_BLOCK_CASE
     default:
         return hipErrorInvalidValue;

@@ -1,41 +1,39 @@
 // gemv.hip -- W4A16 linear for a single activation row (M = 1, decode) on gfx950.
 //
 // The layer at M = 1 streams every packed byte once and uses it for one
-// multiply-add, so the kernel is shaped around the HBM stream alone:
+// multiply-add, so the kernel is shaped around getting the whole stream in flight
+// with as few load instructions as possible:
 //
-//   * Group sets on the diagonal of one MFMA.  One v_mfma_f32_16x16x32_bf16
-//     takes sixteen A rows and sixteen B columns.  Here A row r holds X of group
-//     g0 + r and B column r holds the codes of the same group g0 + r of ONE
-//     output column, so D[r][r] is that group's dot product sum x * (128 + q)
-//     (the off-diagonal products are discarded; the matrix cores have ample
-//     headroom at this intensity).  Lane (r, h) of a B fragment therefore loads
-//     bytes 16h .. 16h+15 of group g0 + r of the column: one 128-bit load per lane
-//     and one contiguous run of up to 16 x 64 B = 1 KB per wave instruction.
-//   * X stays in registers.  Lane (r, h) needs X[(g0 + r) * 128 + 32h .. + 32]
-//     (64 bytes) for every column of the set, so each wave loads the X of its
-//     group set once and reuses it for all the columns it serves: no LDS staging,
-//     no LDS reads in the contraction.
-//   * The scale/zero fold runs once per (column, group) in the epilogue:
-//       y = sum_g s[g] * (P[g] - (128 + z[g]) * S[g]),  S[g] = sum of X over g,
-//     with P[g] = D[r][r] handed over through LDS, and the scales and zero words
-//     of the workgroup's columns brought into LDS by DMA (contiguous runs, in
-//     flight with the codes).
-//
-// The grid is a whole number of workgroups per CU (256 CUs), and workgroup b owns
-// the columns [b N / grid, (b + 1) N / grid) and all of K, so every CU streams the
-// same number of bytes (within one column): with the workgroups all resident at
-// once, the CU with the most bytes would set the end of the kernel.  K is cut into
-// ns group sets of at most 16 groups; the workgroup runs ns * wps waves, wave w
-// taking set w / wps and up to CPW of the workgroup's columns.  Every wave issues
-// all of its loads (params by DMA, X, then the codes of its columns) before it
-// waits for any, so the whole workgroup's bytes are in flight at once.  All sums
-// run in a fixed order: results are deterministic.
+//   * A workgroup owns TC = 16 / PL adjacent columns and all of K.  Its W waves
+//     split K: wave w takes the NG = GPW * PL groups from w * NG.  The grid is
+//     N / TC small workgroups, so every CU holds many waves and all of its bytes
+//     are requested at once; each lane issues GPW 128-bit code loads plus the
+//     scale and zero word of each of its (column, group) pairs.
+//   * Groups on the diagonal of one MFMA.  One v_mfma_f32_16x16x32_bf16 takes
+//     sixteen A rows and sixteen B columns.  B column c + TC p holds the codes of
+//     column c in group part p (lane (c + TC p, h) loads bytes 16h .. 16h+15 of
+//     that group), and A row r holds X of group part r % PL, so D[4h + p][c + TC p]
+//     is the dot product sum x * (128 + q) of column c over group part p (the other
+//     products are discarded; the matrix cores have ample headroom here).
+//   * X costs one load per lane per four groups: the wave loads its NG * 128
+//     values as 8-value slots (slot s: group s / 16 of the wave), adds each group's
+//     S = sum of X across the 16 lanes of a row, and parks the slots, permuted into
+//     the fragment order, in its own LDS region; the MFMA A operands are read from
+//     there.  No barrier precedes the contraction.
+//   * The scale/zero fold runs per (column, group) in fp32:
+//       y = sum_g s[g] * (P[g] - (128 + z[g]) * S[g]),
+//     and the waves' partial sums meet in LDS, added in wave order.
+//   * Act-order (GPTQ g_idx, stored permuted): the contraction needs X'[k] =
+//     X[perm[k]].  The workgroup brings all of X into LDS by DMA, and each lane
+//     gathers its slots from there through perm (one read per value); the rest is
+//     unchanged, so the permuted copy of X never goes through HBM.
+// All sums run in a fixed order: results are deterministic.
 //
 // The grid follows the pages' statement of the layer: packed uint4 codes with a
 // per-group fp16 scale and a uint4 zero-point, group 128 (Pith review, Assumptions &
-// free parameters: the drafter's GPTQ group size; Referee Report, Summary: the
-// target's AWQ grid), and decode runs it at one row per step (mlsanity index page,
-// Abstract: the drafter runs at every speculative decoding step).
+// free parameters: the drafter's GPTQ group size, act-order; Referee Report,
+// Summary: the target's AWQ grid), and decode runs it at one row per step (mlsanity
+// index page, Abstract: the drafter runs at every speculative decoding step).
 #include "common.h"
 #include "kernels.h"
 
@@ -46,7 +44,8 @@ namespace {
 constexpr uint32_t kOobG = 0xFFFFFF00u; // an offset past the end of every tensor
 constexpr int kRsrcWord3G = 0x00020000; // raw (untyped) buffer loads on gfx9-class GPUs
 constexpr int kGemvMaxWaves = 16;
-constexpr int kGemvCUs = 256;          // MI355X compute units
+constexpr int kGemvMaxGroups = 12;      // groups per wave (NG)
+constexpr int kGemvMaxLds = 64 * 1024;  // dynamic LDS without a per-kernel attribute
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_g(const void *p, uint32_t bytes)
 {
@@ -58,21 +57,22 @@ __device__ __forceinline__ u32x4_t ld16_g(__amdgpu_buffer_rsrc_t r, uint32_t off
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// LDS DMA: 16 (or 4) bytes per lane from offset voff of r into LDS at dst + 16 * lane
-// (or 4 * lane; dst the same for the whole wave); no registers involved
+// LDS DMA: 16 bytes per lane from offset voff of r into LDS at dst + 16 * lane (dst
+// the same for the whole wave); no registers involved
 __device__ __forceinline__ void dma16_g(__amdgpu_buffer_rsrc_t r, unsigned char *dst, uint32_t voff)
 {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, 0, 0, 0);
 }
 
-__device__ __forceinline__ void dma4_g(__amdgpu_buffer_rsrc_t r, unsigned char *dst, uint32_t voff)
+// sum over the 16 lanes of each lane row (quad swaps, then half-row and row mirrors);
+// every lane of the row receives it
+__device__ __forceinline__ float row_sum16(float v)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 4, voff, 0, 0, 0);
-}
-
-__device__ __forceinline__ float shfl_xor_f(float v, int m)
-{
-    return __int_as_float(__shfl_xor(__float_as_int(v), m));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
 }
 
 // 8 codes -> MFMA fragment (bf16 128 + q), mask and bias held in registers
@@ -86,252 +86,208 @@ __device__ __forceinline__ bf16x8_t frag_r(uint32_t w, uint32_t mask, uint32_t b
     return __builtin_bit_cast(bf16x8_t, r);
 }
 
-template <int CPW, int SW, bool XL>
+// element p of v (p < PL)
+template <int PL>
+__device__ __forceinline__ float pick(f32x4_t v, int p)
+{
+    if constexpr (PL == 1)
+        return v[0];
+    else if constexpr (PL == 2)
+        return p ? v[1] : v[0];
+    else
+        return (p & 2) ? ((p & 1) ? v[3] : v[2]) : ((p & 1) ? v[1] : v[0]);
+}
+
+// LDS layout (bytes): X slots [W][NG * 16] x 16, S [W][16] floats, wave partials
+// [W][16] floats, then (act-order) X of the row, K bf16
+__host__ __device__ constexpr int gemv_s_off(int W, int NG) { return W * NG * 256; }
+__host__ __device__ constexpr int gemv_r_off(int W, int NG) { return W * NG * 256 + W * 64; }
+__host__ __device__ constexpr int gemv_x_off(int W, int NG) { return W * NG * 256 + W * 128; }
+
+template <int GPW, int PL, bool AO>
 __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
 {
-    constexpr int CPI = 16 / SW;  // columns per load instruction (slots p: column p / SW, group p % SW)
-    constexpr int NI = CPW / CPI; // load instructions per wave
-    static_assert(NI >= 1 && NI * CPI == CPW, "CPW must be a multiple of 16 / SW");
+    constexpr int TC = 16 / PL;             // columns per workgroup
+    constexpr int NG = GPW * PL;            // groups per wave
+    constexpr int XR = NG / 4;              // X slots per lane
+    static_assert(NG <= kGemvMaxGroups && NG % 4 == 0, "a lane row's slots hold one group");
     extern __shared__ __align__(16) unsigned char lds[];
+    const int W = a.waves;
+    const int G = a.G, K = a.K;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int W = a.ns * a.wps;
-    const int G = a.G;
-    const int set = w / a.wps, part = w - set * a.wps;
-    const int g0 = set * SW;
-    const int gn = min(SW, G - g0);
-    const int p = lane & 15, h = lane >> 4;
-    const int pg = p % SW, pc = p / SW; // the lane's group in the set, column within an instruction
-    // the workgroup's columns [cb, ce); the wave's slots part * CPW .. + CPW - 1
-    const int cb = (int)((long long)blockIdx.x * a.N / gridDim.x);
-    const int ce = (int)((long long)(blockIdx.x + 1) * a.N / gridDim.x);
-    const int cnt = ce - cb;
-    const int slot0 = part * CPW;
-    const int ncw = min(CPW, cnt - slot0); // this wave's live columns (wave-uniform; may be <= 0)
-    const uint32_t rowb = (uint32_t)(a.K / 2);
+    const int nid = lane & 15, h = lane >> 4;
+    const int c = nid % TC, p = nid / TC;
+    const int n = blockIdx.x * TC + c;
+    const int g0 = w * NG;
+    const uint32_t rowb = (uint32_t)(K / 2);
+    u32x4_t *xs = (u32x4_t *)lds + w * NG * 16;             // this wave's X slots, fragment order
+    float *Ss = (float *)(lds + gemv_s_off(W, NG)) + w * 16; // S of the wave's groups
+    float *red = (float *)(lds + gemv_r_off(W, NG));         // [W][16] lane partials
 
     const __amdgpu_buffer_rsrc_t rw = rsrc_g(a.qw, (uint32_t)a.N * rowb);
     const __amdgpu_buffer_rsrc_t rs = rsrc_g(a.scales, (uint32_t)a.N * (uint32_t)G * 2u);
     const __amdgpu_buffer_rsrc_t rz = rsrc_g(a.qz, (uint32_t)(a.N / 8) * (uint32_t)G * 4u);
-    const __amdgpu_buffer_rsrc_t rx = rsrc_g(a.X, (uint32_t)a.K * 2u);
+    const __amdgpu_buffer_rsrc_t rx = rsrc_g(a.X, (uint32_t)K * 2u);
 
-    unsigned char *sc_lds = lds + a.sc_off;
-    unsigned char *z_lds = lds + a.z_off;
-    float *sT = (float *)(lds + a.t_off); // [slot][G]: P of (column, group)
-    float *sS = (float *)(lds + a.s_off); // [G]: S of each group
-    float *sP = (float *)(lds + a.p_off); // [ns][slot]: the set partials
-
-    // 1. the workgroup's scales (one contiguous run from the 16-byte boundary at or
-    //    below row cb; N % 8 == 0 keeps the tensor's end on a 16-byte boundary) and
-    //    zero words (rows cb / 8 .. (ce - 1) / 8), by DMA
-    const uint32_t sb = ((uint32_t)cb * (uint32_t)G * 2u) & ~15u;
-    const int sc_units = (int)(((uint32_t)ce * (uint32_t)G * 2u - sb + 15u) / 16u);
-    const int zr0 = cb / 8;
-    const int z_units = ((ce - 1) / 8 + 1 - zr0) * G;
-    for (int u0 = w * 64; u0 < sc_units; u0 += W * 64) {
-        const int u = u0 + lane;
-        dma16_g(rs, sc_lds + u0 * 16, u < sc_units ? sb + 16u * u : kOobG);
-    }
-    for (int u0 = w * 64; u0 < z_units; u0 += W * 64) {
-        const int u = u0 + lane;
-        dma4_g(rz, z_lds + u0 * 4, u < z_units ? ((uint32_t)zr0 * (uint32_t)G + u) * 4u : kOobG);
-    }
-    asm volatile("" ::: "memory");
-
-    // 2. X of the lane's group: lane (p, h) needs X[(g0 + p % SW) * 128 + 32h + 8j .. + 8],
-    //    j = 0..3.  XL: the workgroup brings all of X into LDS by DMA, each group's 16
-    //    16-byte units rotated by the group index so that the sixteen groups a wave reads
-    //    at once fall on different banks; else each wave loads its own from L2
-    const bool glive = pg < gn;
-    unsigned char *sX = lds + a.x_off;
-    if constexpr (XL) {
-        const int xu = a.K / 8;
-        for (int q0 = w * 64; q0 < xu; q0 += W * 64) {
-            const int q = q0 + lane;
-            const int g = q >> 4, u = ((q & 15) - g) & 15;
-            dma16_g(rx, sX + q0 * 16, q < xu ? (uint32_t)g * 256u + 16u * u : kOobG);
+    // 1. X: slot s = r * 64 + lane holds X'[(g0 + s / 16) * 128 + 8 (s % 16) .. + 8].
+    //    Plain: one 16-byte load per slot.  Act-order: the row by DMA into LDS (every
+    //    wave a share of it) and the slot's 8 entries of perm
+    u32x4_t xv[XR];
+    u32x4_t pv[AO ? XR : 1][2];
+    unsigned char *xrow = lds + gemv_x_off(W, NG);
+    if constexpr (AO) {
+        const __amdgpu_buffer_rsrc_t rp = rsrc_g(a.perm, (uint32_t)K * 4u);
+        const int xu = K / 8;
+        for (int u0 = w * 64; u0 < xu; u0 += W * 64) {
+            const int u = u0 + lane;
+            dma16_g(rx, xrow + u0 * 16, u < xu ? 16u * (uint32_t)u : kOobG);
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < XR; ++r) {
+            const int slot = r * 64 + lane;
+            const bool live = g0 * kGroup + slot * 8 < K;
+            const uint32_t off = (uint32_t)(g0 * kGroup + slot * 8) * 4u;
+            pv[r][0] = ld16_g(rp, live ? off : kOobG);
+            pv[r][1] = ld16_g(rp, live ? off + 16u : kOobG);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < XR; ++r) {
+            const int slot = r * 64 + lane;
+            xv[r] = ld16_g(rx, g0 * kGroup + slot * 8 < K ? (uint32_t)(g0 * kGroup + slot * 8) * 2u : kOobG);
         }
     }
-    u32x4_t xr[4];
-    if constexpr (!XL) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            xr[j] = ld16_g(rx, (glive && ncw > 0) ? (uint32_t)((g0 + pg) * kGroup + 32 * h + 8 * j) * 2u : kOobG);
-    }
+    asm volatile("" ::: "memory");
 
-    // 3. the codes: instruction i, lane (p, h) loads bytes 16h .. of group g0 + p % SW of
-    //    column slot0 + i * CPI + p / SW
-    u32x4_t wv[NI];
+    // 2. the codes: instruction i, lane (c + TC p, h) loads bytes 16h .. of group
+    //    g0 + i PL + p of column n; then that pair's scale and zero word
+    u32x4_t wv[GPW];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int c = i * CPI + pc;
-        wv[i] = ld16_g(rw, (glive && c < ncw) ? (uint32_t)(cb + slot0 + c) * rowb + (uint32_t)(g0 + pg) * 64u + 16u * h
-                                               : kOobG);
+    for (int i = 0; i < GPW; ++i) {
+        const int g = g0 + i * PL + p;
+        wv[i] = ld16_g(rw, g < G ? (uint32_t)n * rowb + (uint32_t)g * 64u + 16u * h : kOobG);
+    }
+    uint32_t sv[GPW], zv[GPW];
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        const int g = g0 + i * PL + p;
+        sv[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, g < G ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobG, 0, 0);
+        zv[i] = __builtin_amdgcn_raw_buffer_load_b32(rz, g < G ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobG,
+                                                     0, 0);
     }
     asm volatile("" ::: "memory");
-    if constexpr (XL) {
-        // every DMA of this wave was issued before its NI code loads: vmcnt(NI) means
-        // they have landed; the barrier makes all waves' parts visible
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (NI & 15) | ((NI >> 4) << 14));
+
+    if constexpr (AO) {
+        // the DMA and the perm loads were issued before the 3 GPW loads above:
+        // vmcnt(3 GPW) means they have landed; the barrier makes every wave's part of
+        // the row visible.  Then each slot gathers its 8 values (an entry of perm past
+        // the row reads the row's last element)
+        constexpr int kAfter = 3 * GPW;
+        static_assert(kAfter < 16, "vmcnt field");
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kAfter);
         __syncthreads();
-        const int g = g0 + (glive ? pg : 0);
+        const uint16_t *xr16 = (const uint16_t *)xrow;
+        const uint32_t last = (uint32_t)K - 1u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            xr[j] = *(const u32x4_t *)(sX + (g * 16 + ((4 * h + j + g) & 15)) * 16);
-        if (!glive) {
+        for (int r = 0; r < XR; ++r) {
+            uint32_t v[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                xr[j] = u32x4_t{0u, 0u, 0u, 0u};
+            for (int e = 0; e < 4; ++e) {
+                v[e] = xr16[min(pv[r][0][e], last)];
+                v[4 + e] = xr16[min(pv[r][1][e], last)];
+            }
+            const int slot = r * 64 + lane;
+            const bool live = g0 * kGroup + slot * 8 < K;
+            xv[r] = live ? u32x4_t{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)}
+                         : u32x4_t{0u, 0u, 0u, 0u};
         }
     }
 
-    // 4. S of the set's groups (fixed order: the lane's 32 values, then across h)
-    float ps = (sum8_bf16(xr[0]) + sum8_bf16(xr[1])) + (sum8_bf16(xr[2]) + sum8_bf16(xr[3]));
-    ps += shfl_xor_f(ps, 16);
-    ps += shfl_xor_f(ps, 32);
-    if (h == 0 && p < SW && glive && part == 0)
-        sS[g0 + p] = ps;
-    bf16x8_t xa[4];
+    // 3. S of each group (the slot's 8 values, then across the 16 slots of the group,
+    //    in a fixed order) and the slots in fragment order, into the wave's LDS region
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        xa[j] = __builtin_bit_cast(bf16x8_t, x_permute8(xr[j]));
+    for (int r = 0; r < XR; ++r) {
+        const float ps = row_sum16(sum8_bf16(xv[r]));
+        if (nid == 0)
+            Ss[r * 4 + h] = ps;
+        xs[r * 64 + lane] = x_permute8(xv[r]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): the wave's LDS writes are done
+    asm volatile("" ::: "memory");
 
-    // 5. per instruction, four MFMAs; lane (p, p / 4) holds D[p][p] in element p % 4.
-    //    Instructions go in batches of NB whose MFMA chains interleave
+    // 4. per instruction, four MFMAs (A row r: X of group part r % PL), then the fold
+    //    s * (P - (128 + z) * S) of the lane's (column, group) pair
     uint32_t mask = 0x000F000Fu, bias = kBiasBits;
     asm volatile("" : "+v"(mask));
     asm volatile("" : "+v"(bias));
-    const bool diag = glive && h == (p >> 2);
-    constexpr int NB = NI < 4 ? NI : 4;
+    const int zsh = (n & 7) * 4;
+    const int m = nid % PL;
+    float acc = 0.f;
 #pragma unroll
-    for (int i0 = 0; i0 < NI; i0 += NB) {
-        if (i0 * CPI < ncw) {
-            f32x4_t d[NB];
+    for (int i = 0; i < GPW; ++i) {
+        if (g0 + i * PL < G) {
+            f32x4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-                d[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    d[b] = mfma16x16x32(xa[j], frag_r(wv[i0 + b][j], mask, bias), d[b]);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const float v = (p & 2) ? ((p & 1) ? d[b][3] : d[b][2]) : ((p & 1) ? d[b][1] : d[b][0]);
-                const int c = (i0 + b) * CPI + pc;
-                if (diag && c < ncw)
-                    sT[(slot0 + c) * G + g0 + pg] = v;
+            for (int j = 0; j < 4; ++j) {
+                const u32x4_t xf = xs[(i * PL + m) * 16 + 4 * h + j];
+                const uint32_t wj = j == 0 ? wv[i].x : j == 1 ? wv[i].y : j == 2 ? wv[i].z : wv[i].w;
+                d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf), frag_r(wj, mask, bias), d);
             }
+            const bool live = g0 + i * PL + p < G;
+            const float s = live ? f16_bits_to_f32((uint16_t)sv[i]) : 0.f;
+            const float zb = -(float)(kCodeBias + ((zv[i] >> zsh) & 15u));
+            acc = fmaf(s, fmaf(zb, Ss[i * PL + p], pick<PL>(d, p)), acc);
         }
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): this wave's DMA has landed
-    __syncthreads();
 
-    // 6. the fold, per wave over its set: lane (j, c) = (lane / CPW, lane % CPW) takes
-    //    column slot part * CPW + c and the set's groups g0 + j, g0 + j + 64 / CPW, ...;
-    //    s * (P - (128 + z) * S) is summed in that order, then over j by a fixed
-    //    butterfly; the ns set partials of a column are added in set order below
-    {
-        constexpr int J = 64 / CPW;
-        const int c = lane % CPW, j = lane / CPW;
-        const int sl = slot0 + c;
-        const int col = cb + sl;
-        const uint16_t *scl = (const uint16_t *)(sc_lds + ((uint32_t)col * (uint32_t)G * 2u - sb));
-        const uint32_t *zl = (const uint32_t *)z_lds + (col / 8 - zr0) * G;
-        const int zsh = (col & 7) * 4;
-        float acc = 0.f;
-        if (c < ncw) {
-#pragma unroll
-            for (int it = 0; it < (SW + J - 1) / J; ++it) {
-                const int gi = j + it * J;
-                if (gi < gn) {
-                    const int g = g0 + gi;
-                    const float sc = f16_bits_to_f32(scl[g]);
-                    const uint32_t z = (zl[g] >> zsh) & 15u;
-                    acc = fmaf(sc, fmaf(-(float)(kCodeBias + z), sS[g], sT[sl * G + g]), acc);
-                }
-            }
-        }
-#pragma unroll
-        for (int m = CPW; m < 64; m <<= 1)
-            acc += shfl_xor_f(acc, m);
-        if (j == 0 && c < ncw)
-            sP[set * a.slots + sl] = acc;
-    }
+    // 5. lane (c + TC p, 0) holds column c's sum over the wave's groups of part p; the
+    //    partials are added in wave order, then part order
+    if (lane < 16)
+        red[w * 16 + lane] = acc;
     __syncthreads();
-    for (int sl = threadIdx.x; sl < cnt; sl += W * 64) {
-        float y = sP[sl];
-        for (int q = 1; q < a.ns; ++q)
-            y += sP[q * a.slots + sl];
+    if (w == 0 && lane < TC) {
+        float y = 0.f;
+        for (int v = 0; v < W; ++v)
+#pragma unroll
+            for (int q = 0; q < PL; ++q)
+                y += red[v * 16 + lane + TC * q];
+        const int col = blockIdx.x * TC + lane;
         if (a.y_f32)
-            ((float *)a.Y)[cb + sl] = y;
+            ((float *)a.Y)[col] = y;
         else
-            ((uint16_t *)a.Y)[cb + sl] = f32_to_bf16_rne(y);
+            ((uint16_t *)a.Y)[col] = f32_to_bf16_rne(y);
     }
 }
-
-int round_up_g(int v, int m) { return (v + m - 1) / m * m; }
 
 } // namespace
 
-GemvPlan plan_gemv_with(int N, int K, int wpc, int cpw, int sw, int xl)
+GemvPlan plan_gemv_with(int N, int K, int gpw, int pl, int ao)
 {
     GemvPlan p{};
-    p.xl = xl;
     const int G = K / kGroup;
-    p.sw = sw;
-    p.ns = (G + sw - 1) / sw;
-    p.cpw = cpw;
-    // wpc > 0: that many workgroups per CU; wpc < 0: -wpc columns per workgroup
-    p.grid = wpc > 0 ? kGemvCUs * wpc : (N + (-wpc) - 1) / (-wpc);
-    p.grid = p.grid < N ? p.grid : N;
-    const int cmax = (N + p.grid - 1) / p.grid;
-    p.wps = (cmax + cpw - 1) / cpw;
-    p.slots = p.wps * cpw;
-    p.waves = p.ns * p.wps;
-    // LDS: scales (a run of cmax rows from a 16-byte boundary), zero words (rows of up
-    // to cmax / 8 + 2 octets), P per (slot, group), S per group, set partials
-    const int sc_units = (cmax * G * 2 + 15) / 16 + 1;
-    const int z_units = (cmax / 8 + 2) * G;
-    size_t off = 0;
-    p.sc_off = (int)off;
-    off += (size_t)round_up_g(sc_units, 64) * 16;
-    p.z_off = (int)off;
-    off += (size_t)round_up_g(z_units, 64) * 4;
-    p.t_off = (int)off;
-    off += (size_t)p.slots * G * 4;
-    off = (off + 15) / 16 * 16;
-    p.s_off = (int)off;
-    off += (size_t)G * 4;
-    off = (off + 15) / 16 * 16;
-    p.p_off = (int)off;
-    off += (size_t)p.ns * p.slots * 4;
-    off = (off + 15) / 16 * 16;
-    p.x_off = (int)off;
-    if (p.xl)
-        off += (size_t)round_up_g(K / 8, 64) * 16;
-    p.lds_bytes = (off + 15) / 16 * 16;
-    p.ok = N >= 1 && (cpw == 4 || cpw == 8 || cpw == 16) && (sw == 4 || sw == 8 || sw == 16) &&
-           cpw * sw >= 16 && p.waves >= 1 && p.waves <= kGemvMaxWaves && p.lds_bytes <= 64 * 1024;
+    const int tc = pl > 0 ? 16 / pl : 0;
+    const int ng = gpw * pl;
+    p.gpw = gpw;
+    p.pl = pl;
+    p.ao = ao;
+    p.waves = ng > 0 ? (G + ng - 1) / ng : 0;
+    p.grid = tc > 0 ? N / tc : 0;
+    p.lds_bytes = (size_t)gemv_x_off(p.waves, ng) + (ao ? (size_t)K * 2 : 0);
+    p.ok = N >= 1 && K >= kGroup && ((pl == 2 && gpw == 2) || (pl == 4 && gpw == 3)) && N % tc == 0 &&
+           p.waves >= 1 && p.waves <= kGemvMaxWaves && p.lds_bytes <= (size_t)kGemvMaxLds;
     return p;
 }
 
-GemvPlan plan_gemv(int N, int K)
+GemvPlan plan_gemv(int N, int K, int ao)
 {
-    // measured on MI355X at M = 1 over 512 .. 9728 columns and K = 512 .. 9728 (graph
-    // replays over rotating weights): sets of 16 groups for long K, 8 for mid K (with X
-    // staged in LDS), 4 for short K; columns per wave from the columns per workgroup
+    // measured on MI355X at M = 1 (graph replays over rotating weights): two groups of
+    // 8 columns per instruction and 4 groups per wave up to 40 groups (5 waves of 8
+    // columns at K = 2560), three instructions of 4 columns x 4 groups beyond (7 waves
+    // of 4 columns at K = 9728)
     const int G = K / kGroup;
-    const int sw = G >= 48 ? 16 : G >= 12 ? 8 : 4;
-    const int xl = sw == 8 ? 1 : 0;
-    GemvPlan p{};
-    for (int wpc = 1; wpc <= 4 && !p.ok; wpc *= 2) {
-        const int grid = kGemvCUs * wpc < N ? kGemvCUs * wpc : N;
-        const int cmax = (N + grid - 1) / grid;
-        const int cpw = sw == 16 ? 4 : cmax > 16 ? 8 : cmax > 8 ? 16 : cmax > 4 ? 8 : 4;
-        p = plan_gemv_with(N, K, wpc, cpw, sw, xl);
-    }
-    return p;
+    return G <= 40 ? plan_gemv_with(N, K, 2, 2, ao) : plan_gemv_with(N, K, 3, 4, ao);
 }
 
 hipError_t launch_gemv(const GemvArgs &args, const GemvPlan &p, hipStream_t stream)
@@ -339,33 +295,18 @@ hipError_t launch_gemv(const GemvArgs &args, const GemvPlan &p, hipStream_t stre
     if (!p.ok)
         return hipErrorInvalidValue;
     GemvArgs a = args;
-    a.ns = p.ns;
-    a.wps = p.wps;
-    a.slots = p.slots;
-    a.sc_off = p.sc_off;
-    a.z_off = p.z_off;
-    a.t_off = p.t_off;
-    a.s_off = p.s_off;
-    a.p_off = p.p_off;
-    a.x_off = p.x_off;
+    a.waves = p.waves;
     const dim3 grid(p.grid), block(64 * p.waves);
-    const int v = p.cpw * 1000 + p.sw * 10 + (p.xl ? 1 : 0);
+    const int v = p.gpw * 100 + p.pl * 10 + (p.ao ? 1 : 0);
     switch (v) {
-#define W4A16_GEMV_CASE(C, S, X)                                                                               \
-    case C * 1000 + S * 10 + X:                                                                                \
-        hipLaunchKernelGGL((gemv_kernel<C, S, X != 0>), grid, block, p.lds_bytes, stream, a);                  \
+#define W4A16_GEMV_CASE(GPW, PL, AO)                                                                           \
+    case GPW * 100 + PL * 10 + AO:                                                                             \
+        hipLaunchKernelGGL((gemv_kernel<GPW, PL, AO != 0>), grid, block, p.lds_bytes, stream, a);              \
         break;
-#define W4A16_GEMV_CASES(C, S) W4A16_GEMV_CASE(C, S, 0) W4A16_GEMV_CASE(C, S, 1)
-        W4A16_GEMV_CASES(4, 4)
-        W4A16_GEMV_CASES(4, 8)
-        W4A16_GEMV_CASES(4, 16)
-        W4A16_GEMV_CASES(8, 4)
-        W4A16_GEMV_CASES(8, 8)
-        W4A16_GEMV_CASES(8, 16)
-        W4A16_GEMV_CASES(16, 4)
-        W4A16_GEMV_CASES(16, 8)
-        W4A16_GEMV_CASES(16, 16)
-#undef W4A16_GEMV_CASES
+        W4A16_GEMV_CASE(2, 2, 0)
+        W4A16_GEMV_CASE(2, 2, 1)
+        W4A16_GEMV_CASE(3, 4, 0)
+        W4A16_GEMV_CASE(3, 4, 1)
 #undef W4A16_GEMV_CASE
     default:
         return hipErrorInvalidValue;

@@ -148,25 +148,24 @@ hipError_t launch_skinny_multi(SkinnyMulti &mp, int M, size_t ws_bytes, hipStrea
 // and all of K, cut into ns group sets of sw (4, 8 or 16) groups; wave w takes set
 // w / wps and up to cpw of the columns (slots = wps * cpw >= columns per workgroup).
 struct GemvPlan {
-    int ns, sw, wps, cpw, slots, waves, grid;
-    int xl;                                        // X staged in LDS by the workgroup (else per wave from L2)
-    int sc_off, z_off, t_off, s_off, p_off, x_off; // LDS byte offsets: scales, zero words, P, S, set partials, X
+    int gpw, pl, ao;  // code loads per lane, group parts per instruction, act-order
+    int waves, grid;  // waves per workgroup (each NG = gpw * pl groups), N / (16 / pl)
     size_t lds_bytes;
-    bool ok;                                       // false: the shape needs another path
+    bool ok;          // false: the shape needs another path
 };
 struct GemvArgs {
     const uint16_t *X;
+    const int32_t *perm; // act-order only: X'[k] = X[perm[k]]
     const uint32_t *qw;
     const uint16_t *scales;
     const uint32_t *qz;
     int N, K, G;
     void *Y;
     int y_f32;
-    // copied from the plan by launch_gemv
-    int ns, wps, slots, sc_off, z_off, t_off, s_off, p_off, x_off;
+    int waves; // copied from the plan by launch_gemv
 };
-GemvPlan plan_gemv(int N, int K);
-GemvPlan plan_gemv_with(int N, int K, int wpc, int cpw, int sw, int xl);
+GemvPlan plan_gemv(int N, int K, int ao);
+GemvPlan plan_gemv_with(int N, int K, int gpw, int pl, int ao);
 hipError_t launch_gemv(const GemvArgs &a, const GemvPlan &p, hipStream_t stream);
 
 // ---------------------------------------------------------------- block (2 <= M <= 16)
@@ -189,10 +188,13 @@ struct BlockArgs {
     BlockProb pr[kMaxProblemsBlock];
     int count, M, y_f32;
     unsigned char *ws;       // workspace base (partial sums, arrival counters)
+    const int32_t *perm;     // act-order plans (one projection, K whole): X'[k] = X[perm[k]]
     int z_off, s_off, r_off; // filled by launch_block
+    int x_off, p_off;        // act-order: LDS of the X rows and of perm
 };
 struct BlockPlan {
     int count, gpw, tmax, waves, grid;
+    int ao, x_off, p_off; // act-order plan: X rows and perm in LDS (over the slice accumulators)
     int wg0[kMaxProblemsBlock], ntg[kMaxProblemsBlock], parts[kMaxProblemsBlock], tmx[kMaxProblemsBlock];
     int tkt[kMaxProblemsBlock];
     size_t part_off[kMaxProblemsBlock];
@@ -202,6 +204,9 @@ struct BlockPlan {
 };
 BlockPlan plan_block(const int *N, const int *K, int count, int M, int tmax_hint = 0, int waves_hint = 0,
                      int parts_hint = 0);
+// one act-order projection with the gather of X folded into the kernel (K whole, the X
+// rows and perm in LDS); !ok when they do not fit
+BlockPlan plan_block_ao(int N, int K, int M);
 hipError_t launch_block(const BlockArgs &a, const BlockPlan &p, hipStream_t stream);
 // workspace of a single projection's block plan (the zero region included when K is split)
 size_t block_linear_ws(int M, int N, int K);

@@ -542,8 +542,12 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
     };
 
     if constexpr (STREAM) {
-        // ---- stream mode: X of the m-block is staged once (all of K); each wave walks
-        // tile groups blockIdx.x, +grid, ... and takes tile tg * nwaves + wave of each.
+        // ---- stream mode: X of the m-block is staged once (all of K); workgroup b owns
+        // the tiles [b nt / grid, (b + 1) nt / grid) (every CU the same bytes, within a
+        // tile), and wave w walks tiles t0 + w, t0 + w + nwaves, ... of that run.
+        const int t0 = (int)((long long)first * p.nt / stride);
+        const int t1 = (int)((long long)(first + 1) * p.nt / stride);
+        const int jn = (t1 - t0 + nwaves - 1) / nwaves; // tile rounds of the workgroup
         for (int mb = 0; mb < p.mblocks; ++mb) {
             const int m0 = mb * 16;
             const int Mb = M - m0 < 16 ? M - m0 : 16;
@@ -554,9 +558,9 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
                 flush_best(cur_mb);
             cur_mb = mb;
 
-            int tgA = first, gA = 0;
-            int tileA = tgA * nwaves + wave;
-            bool liveA = tgA < p.ntg && tileA * 16 < N;
+            int tgA = 0, gA = 0;
+            int tileA = t0 + tgA * nwaves + wave;
+            bool liveA = tgA < jn && tileA < t1;
             LaneGrid LA = lane_grid(tileA, col, h, N, K, G, liveA);
             // X first, then the first weight batch: both in flight together
             const XStage st = x_stage(m0, Mb);
@@ -576,11 +580,11 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
                 // phase A: prefetch the batch after A into bB, compute A
                 int tgB = tgA, gB = gA + kB;
                 if (gB >= G) {
-                    tgB += stride;
+                    tgB += 1;
                     gB = 0;
                 }
-                const int tileB = tgB * nwaves + wave;
-                const bool liveB = tgB < p.ntg && tileB * 16 < N;
+                const int tileB = t0 + tgB * nwaves + wave;
+                const bool liveB = tgB < jn && tileB < t1;
                 const LaneGrid LB = lane_grid(tileB, col, h, N, K, G, liveB);
                 load_batch<ALIGNED>(bB, rw, rs, rz, LB, gB, G);
                 __builtin_amdgcn_sched_barrier(0);
@@ -591,16 +595,16 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
                         finish_tile(acc, m0, Mb, tileA * 16 + col);
                     acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 }
-                if (tgB >= p.ntg)
+                if (tgB >= jn)
                     break;
                 // phase B: prefetch the batch after B into bA, compute B
                 int tgC = tgB, gC = gB + kB;
                 if (gC >= G) {
-                    tgC += stride;
+                    tgC += 1;
                     gC = 0;
                 }
-                const int tileC = tgC * nwaves + wave;
-                const bool liveC = tgC < p.ntg && tileC * 16 < N;
+                const int tileC = t0 + tgC * nwaves + wave;
+                const bool liveC = tgC < jn && tileC < t1;
                 const LaneGrid LC = lane_grid(tileC, col, h, N, K, G, liveC);
                 load_batch<ALIGNED>(bA, rw, rs, rz, LC, gC, G);
                 __builtin_amdgcn_sched_barrier(0);
@@ -611,7 +615,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
                         finish_tile(acc, m0, Mb, tileB * 16 + col);
                     acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 }
-                if (tgC >= p.ntg)
+                if (tgC >= jn)
                     break;
                 tgA = tgC;
                 gA = gC;

@@ -1,5 +1,5 @@
 """The LDS-DMA waits of the small-M kernels (CPU: reads the gfx950 assembly of our
-own skinny.hip and gemv.hip).
+own skinny.hip, gemv.hip and block.hip).
 
 A wave that pulls X into LDS with buffer_load ... lds then issues its first weight
 batches and waits with s_waitcnt vmcnt(n), n being the number of loads issued after
@@ -31,8 +31,9 @@ def _asm(tmp_path_factory, name):
 
 
 # source, the fewest DMA waits it must contain: the chunked and the DMA private modes
-# in the single and the batched skinny kernels; the X-in-LDS instances of the M = 1 kernel
-@pytest.mark.parametrize("name,least", [("skinny.hip", 24), ("gemv.hip", 9), ("block.hip", 8)])
+# in the single and the batched skinny kernels; the act-order instances of the M = 1
+# kernel (X of the row by DMA, perm and the codes after it); every block instance
+@pytest.mark.parametrize("name,least", [("skinny.hip", 24), ("gemv.hip", 2), ("block.hip", 8)])
 def test_every_dma_wait_covers_the_dma(tmp_path_factory, name, least):
     skinny_asm = _asm(tmp_path_factory, name)
     kern, last_dma, after = None, None, 0
