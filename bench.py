@@ -666,14 +666,16 @@ def measure_gated(dev, steps, warmup, N=9728, K=2560):
     """The MLP's gate and up projections (K 2560 -> N 9728 each) on the same rows, at
     M = 16 (a draft block) and M = 1: w4a16_linear_gated (both projections and
     silu(gate) * up in one launch, one bf16 output) next to w4a16_linear_batch of the
-    two projections (one launch, two outputs, no activation).  Graph replay over
-    rotating weight copies.  Algorithmic bytes: both packed grids, X once, Y once."""
+    two projections (one launch, two outputs, no activation); at M = 8192 (prefill) the
+    gated tile kernel next to the two w4a16_linear calls alone (two bf16 outputs, no
+    activation).  Graph replay over rotating weight copies.  Algorithmic bytes: both
+    packed grids, X once, Y once; flops 2 * 2MNK."""
     import torch
     import int4_weight_only_02_amd as w4
     import oracle
     G = K // 128
     out = {"N": N, "K": K}
-    for M in (16, 1):
+    for M in (16, 1, 8192):
         dg = synth.linear_inputs(5151 + M, M, N, K)
         du = synth.linear_inputs(5152 + M, M, N, K)
         X = torch.from_numpy(dg["X"].view(np.int16)).to(dev).view(torch.bfloat16)
@@ -698,9 +700,15 @@ def measure_gated(dev, steps, warmup, N=9728, K=2560):
         cols = rng.integers(0, N, 256).astype(np.int32)
         og = oracle.pack(dg["codes"], dg["zeros"])
         ou = oracle.pack(du["codes"], du["zeros"])
-        yo = oracle.silu_mul(oracle.linear_at(dg["X"], og[0], dg["scales"], og[1], rows, cols),
-                             oracle.linear_at(dg["X"], ou[0], du["scales"], ou[1], rows, cols))
-        err = float(np.abs(Yf.cpu().numpy()[rows, cols] - yo).max() / np.sqrt((yo ** 2).mean()))
+        go = oracle.linear_at(dg["X"], og[0], dg["scales"], og[1], rows, cols)
+        uo = oracle.linear_at(dg["X"], ou[0], du["scales"], ou[1], rows, cols)
+        yo = oracle.silu_mul(go, uo)
+        dy = np.abs(Yf.cpu().numpy()[rows, cols] - yo)
+        err = float(dy.max() / np.sqrt((yo ** 2).mean()))
+        # the gated bound: each projection's 1e-2 rms carried through silu(g) * u
+        eg, eu = 1e-2 * np.sqrt((go ** 2).mean()), 1e-2 * np.sqrt((uo ** 2).mean())
+        bound = 1.1 * np.abs(uo) * eg + np.abs(go / (1.0 + np.exp(-go))) * eu + 1.1 * eg * eu
+        err_b = float((dy / bound).max())
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         Yg = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         Yu = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -731,13 +739,23 @@ def measure_gated(dev, steps, warmup, N=9728, K=2560):
             return e0.elapsed_time(e1) * 1e3 / (reps * R)
 
         t_gated = timed(lambda r: w4.w4a16_linear_gated(X, *copies[r], out=Y, workspace=ws))
-        t_batch = timed(lambda r: w4.w4a16_linear_batch([(X,) + copies[r][0], (X,) + copies[r][1]],
-                                                        outs=[Yg, Yu], workspace=ws))
-        out["m%d" % M] = {"copies": R, "bytes_per_call": nbytes, "us_per_call_gated": round(t_gated, 3),
-                          "GBps_gated": round(nbytes / t_gated / 1e3, 1),
-                          "hbm_frac_gated": round(nbytes / t_gated / 1e3 / HBM_PEAK_GBS, 4),
-                          "us_per_call_batch_two_outputs": round(t_batch, 3),
-                          "sampled_max_err_over_rms": err}
+        if M <= 16:
+            t_batch = timed(lambda r: w4.w4a16_linear_batch([(X,) + copies[r][0], (X,) + copies[r][1]],
+                                                            outs=[Yg, Yu], workspace=ws))
+            out["m%d" % M] = {"copies": R, "bytes_per_call": nbytes, "us_per_call_gated": round(t_gated, 3),
+                              "GBps_gated": round(nbytes / t_gated / 1e3, 1),
+                              "hbm_frac_gated": round(nbytes / t_gated / 1e3 / HBM_PEAK_GBS, 4),
+                              "us_per_call_batch_two_outputs": round(t_batch, 3),
+                              "sampled_max_err_over_rms": err, "sampled_max_err_over_bound": err_b}
+        else:
+            t_two = timed(lambda r: (w4.w4a16_linear(X, *copies[r][0], out=Yg, workspace=ws),
+                                     w4.w4a16_linear(X, *copies[r][1], out=Yu, workspace=ws)))
+            flops = 2 * 2 * M * N * K
+            out["m%d" % M] = {"copies": R, "flops_per_call": flops, "us_per_call_gated": round(t_gated, 3),
+                              "TFLOPs_gated": round(flops / t_gated / 1e6, 1),
+                              "mfma_frac_gated": round(flops / t_gated / 1e6 / BF16_PEAK_TFLOPS, 4),
+                              "us_per_call_two_linear_calls": round(t_two, 3),
+                              "sampled_max_err_over_bound": err_b}
     return out
 
 

@@ -59,6 +59,9 @@ size_t gated_ws(int M, int N, int K)
 {
     if (M <= kSkinnyMaxM)
         return plan_skinny_pair(M, N, K).ws_bytes;
+    const TiledPlan tp = plan_tiled_gated(M, N, K);
+    if (tp.ok)
+        return tp.ws_bytes;
     return gated_gu_offset(M, N, K) + 2 * (size_t)M * N * 4;
 }
 
@@ -482,9 +485,27 @@ int w4a16_linear_gated(const void *X, const uint32_t *qweight_gate, const void *
         a.ws = (unsigned char *)workspace;
         a.lmhead = 0;
         e = launch_skinny(a, p, (hipStream_t)stream);
+    } else if (const TiledPlan tp = plan_tiled_gated(M, N, K); tp.ok) {
+        // large M: one tile kernel, each wave holding gate and up tiles of the same columns
+        TiledArgs a{};
+        a.X = (const uint16_t *)X;
+        a.qw = qweight_gate;
+        a.scales = (const uint16_t *)scales_gate;
+        a.qz = qzeros_gate;
+        a.qw2 = qweight_up;
+        a.scales2 = (const uint16_t *)scales_up;
+        a.qz2 = qzeros_up;
+        a.M = M;
+        a.N = N;
+        a.K = K;
+        a.G = K / kGroup;
+        a.Y = Y;
+        a.y_f32 = y_dtype == W4A16_OUT_F32;
+        a.ws = (unsigned char *)workspace;
+        e = launch_tiled(a, tp, (hipStream_t)stream);
     } else {
-        // large M: the two projections in turn (fp32, into the workspace), then the
-        // elementwise activation
+        // mid M (the tiles would not fill the CUs once): the two projections in turn
+        // (fp32, into the workspace, each with its own K split), then the activation
         unsigned char *ws = (unsigned char *)workspace;
         const size_t off = gated_gu_offset(M, N, K);
         float *G = (float *)(ws + off), *U = G + (size_t)M * N;

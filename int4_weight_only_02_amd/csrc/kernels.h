@@ -225,6 +225,8 @@ struct TiledPlan {
     size_t off_part;  // ksplit > 1: fp32 partial sums [ksplit][M][N]; stream: one pair of
                       // fp32 tile regions per inner segment boundary
     size_t ws_bytes;
+    int gated;        // the gated pair in one launch (whole tiles of 128 output columns)
+    bool ok;
 };
 
 struct TiledArgs {
@@ -232,6 +234,9 @@ struct TiledArgs {
     const uint32_t *qw;
     const uint16_t *scales;
     const uint32_t *qz;
+    const uint32_t *qw2; // gated plans: the up projection (qw etc.: gate)
+    const uint16_t *scales2;
+    const uint32_t *qz2;
     int M, N, K, G;
     void *Y;
     int y_f32;
@@ -239,6 +244,9 @@ struct TiledArgs {
 };
 
 TiledPlan plan_tiled(int M, int N, int K);
+// Y = silu(X Wg^T) * (X Wu^T) in one tile kernel (no fp32 intermediates); !ok when
+// the tiles would not fill one round of the CUs
+TiledPlan plan_tiled_gated(int M, int N, int K);
 hipError_t launch_tiled(const TiledArgs &a, const TiledPlan &p, hipStream_t stream);
 
 // path choice for w4a16_linear: small M streams the weights once per 16 rows

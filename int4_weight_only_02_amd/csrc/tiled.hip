@@ -23,7 +23,12 @@
 //   * the epilogue multiplies each row by 2^e and stores bf16 (RNE) or fp32.  When
 //     the tiles alone would leave most CUs idle in the last round, K is split into
 //     slices: each slice stores its fp32 partial sums and reduce_kernel adds them in
-//     slice order (deterministic), scales the row and stores Y.
+//     slice order (deterministic), scales the row and stores Y;
+//   * gated pair (the MLP's silu(X Wg^T) * (X Wu^T); Pith review, Referee Report,
+//     Summary: the target's MLP): a tile covers 128 output columns, and each wave's
+//     four column tiles are two of gate and the same two of up, so the epilogue forms
+//     silu(gate) * up from the wave's own accumulators and neither projection's
+//     output is ever stored.
 // With X ~ N(0, 1) the rounding of the weights contributes about 3e-4 * rms(Y) (rms),
 // a few percent of the 1e-2 * rms(Y) bound at the largest shapes.
 #include "common.h"
@@ -171,9 +176,11 @@ __device__ __forceinline__ f16x8_t dequant_word(uint32_t w, uint32_t mask, uint3
 //               to arrive adds the other part (a + b = b + a in fp32, so the result
 //               does not depend on the arrival order), scales and stores Y, and
 //               returns the ticket to zero.
-template <bool STREAM>
+template <bool STREAM, bool GATED>
 __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan p)
 {
+    static_assert(!(STREAM && GATED), "the gated pair runs whole tiles");
+    constexpr int BNO = GATED ? BN / 2 : BN; // output columns per tile
     extern __shared__ __align__(16) unsigned char smem[]; // all of the 160 KB: no static LDS
 
     const int M = a.M, N = a.N, K = a.K, G = a.G;
@@ -231,6 +238,17 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.qw, (uint32_t)((size_t)N * K / 2));
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales, (uint32_t)((size_t)N * G * 2));
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(a.qz, (uint32_t)((size_t)(N / 8) * G * 4));
+    // gated: the up projection's grid (column slots 32 .. 63 of each quarter of the tile)
+    const __amdgpu_buffer_rsrc_t rw2 = make_rsrc(GATED ? a.qw2 : a.qw, (uint32_t)((size_t)N * K / 2));
+    const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(GATED ? a.scales2 : a.scales, (uint32_t)((size_t)N * G * 2));
+    const __amdgpu_buffer_rsrc_t rz2 = make_rsrc(GATED ? a.qz2 : a.qz, (uint32_t)((size_t)(N / 8) * G * 4));
+    // the output column of column slot cl (0 .. 255) of a tile at n0, and of the lane's
+    // column tile nt; gated: quarter cl / 64 holds 32 columns of gate, then the same 32
+    // of up
+    auto slot_col = [&](int n0, int cl) { return GATED ? n0 + (cl >> 6) * 32 + (cl & 31) : n0 + cl; };
+    auto lane_col = [&](int n0, int nt) {
+        return GATED ? n0 + wn * 32 + (nt & 1) * 16 + col : n0 + wn * 64 + nt * 16 + col;
+    };
 
     // Per-lane offsets of group 0 of the tile being fetched; group g adds g * 256 bytes
     // (X), g * 64 (words), 2g (scales), 4g (zero words) as the scalar offset.  Rows past
@@ -240,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
     uint32_t xoff[8], woff[2], soff[4], zoff[4];
     auto set_tile = [&](int t) {
         const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
-        const int m0 = tm * BM, n0 = tn * BN;
+        const int m0 = tm * BM, n0 = tn * BNO;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int s = (wave * 8 + i) * 64 + lane; // X slot: row s/16, swizzled chunk s%16
@@ -251,11 +269,12 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
         for (int i = 0; i < 2; ++i) {
             const int s = (wave * 2 + i) * 64 + lane; // word slot: column s/4, swizzled quarter s%4
             const int cl = s >> 2, q = (s & 3) ^ ((cl >> 2) & 3);
-            woff[i] = n0 + cl < N ? (uint32_t)(n0 + cl) * (uint32_t)(K / 2) + (uint32_t)(q * 16) : kOob;
+            const int n = slot_col(n0, cl);
+            woff[i] = n < N ? (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(q * 16) : kOob;
         }
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            const int n = n0 + wn * 64 + nt * 16 + col;
+            const int n = lane_col(n0, nt);
             soff[nt] = n < N ? (uint32_t)(n * G) * 2u : kOob;
             zoff[nt] = n < N ? (uint32_t)((n >> 3) * G) * 4u : kOob;
         }
@@ -266,17 +285,20 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             dma16(rx, base + (wave * 8 + i) * 1024, xoff[i], (uint32_t)g * (kGroup * 2));
+        // a word instruction covers 16 column slots, all of one projection
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            dma16(rw, base + kXBytes + (wave * 2 + i) * 1024, woff[i], (uint32_t)g * 64u);
+            dma16(GATED && (((wave * 2 + i) >> 1) & 1) ? rw2 : rw, base + kXBytes + (wave * 2 + i) * 1024, woff[i],
+                  (uint32_t)g * 64u);
     };
     // per-lane scale and zero word of the wave's 4 column tiles for group g
     uint32_t sc_raw[4], zw_raw[4];
     auto load_params = [&](int g) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            sc_raw[nt] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[nt], (uint32_t)g * 2u, 0);
-            zw_raw[nt] = __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[nt], (uint32_t)g * 4u, 0);
+            const bool up = GATED && nt >= 2;
+            sc_raw[nt] = __builtin_amdgcn_raw_buffer_load_b16(up ? rs2 : rs, soff[nt], (uint32_t)g * 2u, 0);
+            zw_raw[nt] = __builtin_amdgcn_raw_buffer_load_b32(up ? rz2 : rz, zoff[nt], (uint32_t)g * 4u, 0);
         }
     };
 
@@ -308,28 +330,38 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
         for (int mt = 0; mt < 8; ++mt)
             rsj[mt] = __uint_as_float(
                 __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(m0 + wm * 128 + mt * 16 + 4 * h + j) * 4u, 0, 0));
+        auto quad_t = [&](const f32x4_t &v) {
+            // exchange with lane j ^ 1: the elements whose bit 0 differs from j's
+            const float r0 = __shfl_xor(odd ? v[0] : v[1], 1), r1 = __shfl_xor(odd ? v[2] : v[3], 1);
+            const f32x4_t t = odd ? f32x4_t{r0, v[1], r1, v[3]} : f32x4_t{v[0], r0, v[2], r1};
+            // exchange with lane j ^ 2: the elements whose bit 1 differs from j's
+            const float q0 = __shfl_xor(hi2 ? t[0] : t[2], 2), q1 = __shfl_xor(hi2 ? t[1] : t[3], 2);
+            return hi2 ? f32x4_t{q0, q1, t[2], t[3]} : f32x4_t{t[0], t[1], q0, q1};
+        };
+        // gated: column tiles 0, 1 (gate) pair with 2, 3 (up) of the same columns
+        constexpr int NT = GATED ? 2 : 4;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             const int row = m0 + wm * 128 + mt * 16 + 4 * h + j;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const f32x4_t v = acc[mt][nt];
-                // exchange with lane j ^ 1: the elements whose bit 0 differs from j's
-                const float r0 = __shfl_xor(odd ? v[0] : v[1], 1), r1 = __shfl_xor(odd ? v[2] : v[3], 1);
-                const f32x4_t t = odd ? f32x4_t{r0, v[1], r1, v[3]} : f32x4_t{v[0], r0, v[2], r1};
-                // exchange with lane j ^ 2: the elements whose bit 1 differs from j's
-                const float q0 = __shfl_xor(hi2 ? t[0] : t[2], 2), q1 = __shfl_xor(hi2 ? t[1] : t[3], 2);
-                const f32x4_t w = hi2 ? f32x4_t{q0, q1, t[2], t[3]} : f32x4_t{t[0], t[1], q0, q1};
-                const int cn = n0 + wn * 64 + nt * 16 + cq; // N % 8 == 0: 4 columns all in or all out
+            for (int nt = 0; nt < NT; ++nt) {
+                const float sc = rsj[mt];
+                const f32x4_t w = quad_t(acc[mt][nt]);
+                f32x4_t y = {w[0] * sc, w[1] * sc, w[2] * sc, w[3] * sc};
+                if constexpr (GATED) {
+                    const f32x4_t u = quad_t(acc[mt][nt + 2]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        y[r] = silu_f32(y[r]) * (u[r] * sc);
+                }
+                const int cn = lane_col(n0, nt) - col + cq; // N % 8 == 0: 4 columns all in or all out
                 if (row < M && cn < N) {
                     const size_t off = (size_t)row * N + cn;
-                    const float sc = rsj[mt];
                     if (a.y_f32) {
-                        *(f32x4_t *)((float *)a.Y + off) = f32x4_t{w[0] * sc, w[1] * sc, w[2] * sc, w[3] * sc};
+                        *(f32x4_t *)((float *)a.Y + off) = y;
                     } else {
                         typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-                        *(bf16x4_t *)((__bf16 *)a.Y + off) =
-                            bf16x4_t{(__bf16)(w[0] * sc), (__bf16)(w[1] * sc), (__bf16)(w[2] * sc), (__bf16)(w[3] * sc)};
+                        *(bf16x4_t *)((__bf16 *)a.Y + off) = bf16x4_t{(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
                     }
                 }
             }
@@ -340,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
     // computed from LDS buffer bi.  Every thread of the workgroup calls it (the barriers
     // inside are uniform).
     auto finish = [&](int m0, int n0, int gs, int ge, int bi) {
-        if (!STREAM && p.ksplit > 1) {
+        if (!STREAM && !GATED && p.ksplit > 1) {
             // fp32 partial sums of this K slice; reduce_kernel finishes the rows
             float *part = (float *)(a.ws + p.off_part) + (size_t)seg * M * N;
 #pragma unroll
@@ -423,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
     unit(0, t, g);
     int gs = g;
     set_tile(t);
-    int m0 = (t / p.tiles_n) * BM, n0 = (t % p.tiles_n) * BN;
+    int m0 = (t / p.tiles_n) * BM, n0 = (t % p.tiles_n) * BNO;
     issue(g, 0);
     load_params(g);
     wait_vmem();
@@ -435,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
         f16x2_t s2[4], zn[4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            const int zsh = ((n0 + wn * 64 + nt * 16 + col) & 7) * 4;
+            const int zsh = (lane_col(n0, nt) & 7) * 4;
             s2[nt] = as_h2((sc_raw[nt] & 0xFFFFu) * 0x00010001u);
             zn[nt] = as_h2((0xE400u | ((zw_raw[nt] >> zsh) & 15u)) * 0x00010001u); // -(1024 + z)
         }
@@ -503,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
             t = tn;
             gs = gn;
             m0 = (t / p.tiles_n) * BM;
-            n0 = (t % p.tiles_n) * BN;
+            n0 = (t % p.tiles_n) * BNO;
         }
         g = gn;
     }
@@ -586,25 +618,49 @@ TiledPlan plan_tiled(int M, int N, int K)
         p.ksplit = 1;
         p.gper = p.G;
         p.ws_bytes = p.off_part + (size_t)(p.grid - 1) * 2 * BM * BN * sizeof(float);
+        p.ok = true;
         return p;
     }
     p.gper = (p.G + p.ksplit - 1) / p.ksplit;
     p.ksplit = (p.G + p.gper - 1) / p.gper; // no empty slices
     p.grid = (int)(ntiles * p.ksplit);
     p.ws_bytes = p.off_part + (p.ksplit > 1 ? (size_t)p.ksplit * M * N * sizeof(float) : 0);
+    p.ok = true;
+    return p;
+}
+
+// The gated pair (gate and up of the same N x K shape): tiles of 256 rows x 128 output
+// columns, whole K, no split; ok when the tiles alone fill at least one round of the
+// CUs (otherwise the two projections run as separate calls).
+TiledPlan plan_tiled_gated(int M, int N, int K)
+{
+    TiledPlan p = plan_tiled(M, N, K);
+    p.tiles_n = (N + BN / 2 - 1) / (BN / 2);
+    p.stream = 0;
+    p.dp_rounds = 0;
+    p.ksplit = 1;
+    p.gper = p.G;
+    p.grid = p.tiles_m * p.tiles_n;
+    p.gated = 1;
+    p.ws_bytes = p.off_part;
+    p.ok = p.grid >= 256;
     return p;
 }
 
 hipError_t launch_tiled(const TiledArgs &a, const TiledPlan &p, hipStream_t stream)
 {
+    if (p.gated && (!a.qw2 || !a.scales2 || !a.qz2 || p.stream || p.ksplit != 1))
+        return hipErrorInvalidValue;
     // every tile kernel uses all 160 KB of LDS: allowed once per device
     hipError_t e = once_per_device(kOnceTiled, [](int) -> hipError_t {
-        hipError_t r = hipFuncSetAttribute((const void *)tiled_kernel<false>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-        if (r == hipSuccess)
-            r = hipFuncSetAttribute((const void *)tiled_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    kLdsBytes);
-        return r;
+        const void *fns[] = {(const void *)tiled_kernel<false, false>, (const void *)tiled_kernel<true, false>,
+                             (const void *)tiled_kernel<false, true>};
+        for (const void *f : fns) {
+            const hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+            if (r != hipSuccess)
+                return r;
+        }
+        return hipSuccess;
     });
     if (e != hipSuccess)
         return e;
@@ -613,10 +669,12 @@ hipError_t launch_tiled(const TiledArgs &a, const TiledPlan &p, hipStream_t stre
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    if (p.stream)
-        hipLaunchKernelGGL(tiled_kernel<true>, dim3(p.grid), dim3(kThreads), kLdsBytes, stream, a, p);
+    if (p.gated)
+        hipLaunchKernelGGL((tiled_kernel<false, true>), dim3(p.grid), dim3(kThreads), kLdsBytes, stream, a, p);
+    else if (p.stream)
+        hipLaunchKernelGGL((tiled_kernel<true, false>), dim3(p.grid), dim3(kThreads), kLdsBytes, stream, a, p);
     else
-        hipLaunchKernelGGL(tiled_kernel<false>, dim3(p.grid), dim3(kThreads), kLdsBytes, stream, a, p);
+        hipLaunchKernelGGL((tiled_kernel<false, false>), dim3(p.grid), dim3(kThreads), kLdsBytes, stream, a, p);
     e = hipGetLastError();
     if (e != hipSuccess || p.ksplit == 1)
         return e;

@@ -8,6 +8,11 @@ Contract (from the layer's accuracy requirement, fp32 accumulation):
   argmax:       equal to the oracle's wherever the oracle's top-2 gap exceeds
                 1e-2 * rms(Y_oracle); elsewhere the chosen logit is within that
                 tolerance of the maximum.
+  gated pair:   y = silu(g) * u of two projections, each held to the contract above
+                (|dg| <= eg = 1e-2 rms(G), |du| <= eu = 1e-2 rms(U)), carried through
+                to first order with |silu'| <= 1.1, plus the product term:
+                |dy| <= 1.1 |u| eg + |silu(g)| eu + 1.1 eg eu (+ half a bf16 ulp of y
+                on bf16 output).
 """
 import numpy as np
 
@@ -65,6 +70,32 @@ def check(Y, Yo, what=""):
         raise AssertionError("%s: %d outputs outside the bound, e.g. %s: got %s want %s (tol %g)" % (
             what, int(bad.sum()), idx.tolist(), y[tuple(idx[0])], Yo[tuple(idx[0])], tol))
     return float(err.max() / tol) if tol > 0 else 0.0
+
+
+def gated_bound(G, U):
+    """Elementwise bound of silu(G) * U given the contract on each projection."""
+    G = np.asarray(G, np.float64)
+    U = np.asarray(U, np.float64)
+    eg = TOL_REL * float(np.sqrt(np.mean(G * G))) if G.size else 0.0
+    eu = TOL_REL * float(np.sqrt(np.mean(U * U))) if U.size else 0.0
+    sg = G / (1.0 + np.exp(-G))
+    return 1.1 * np.abs(U) * eg + np.abs(sg) * eu + 1.1 * eg * eu
+
+
+def check_gated(Y, G, U, Yo, what=""):
+    """Assert the gated bound (Yo = silu(G) * U from the oracle); return max |dY| / bound."""
+    import torch
+    y = y_to_f64(Y)
+    bound = gated_bound(G, U)
+    if Y.dtype != torch.float32:
+        bound = bound + half_ulp_bf16(Yo)
+    err = np.abs(y - Yo)
+    bad = err > bound
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError("%s: %d outputs outside the bound, e.g. %s: got %s want %s (bound %g)" % (
+            what, int(bad.sum()), idx.tolist(), y[tuple(idx[0])], Yo[tuple(idx[0])], bound[tuple(idx[0])]))
+    return float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0
 
 
 def expected_bf16_bits(Yo_exact):

@@ -177,8 +177,9 @@ def test_quantize_graph_replays(dev):
     _check_replays(dev, ws, lambda: w4.w4a16_quantize(Wt, S, qz, out=out), [out])
 
 
-@pytest.mark.parametrize("M,K", [(16, 2560), (16, 9728), (130, 640)])
+@pytest.mark.parametrize("M,K", [(16, 2560), (16, 9728), (130, 640), (3100, 256)])
 def test_gated_graph_replays(dev, M, K):
+    # M = 3100: the gated tile kernel (13 x 20 tiles of 256 rows x 128 columns)
     N = 2560
     print("graph gated", M, N, K, flush=True)
     X, qg, sg, zg = _packed(71 + K, M, N, K, dev)
