@@ -226,6 +226,36 @@ def test_lmhead_bf16_logits(dev, M, N, K):
         _lmhead_case(dev, d, L0, seed=L0 + 3, return_logits=True, logits_dtype=torch.bfloat16)
 
 
+@pytest.mark.parametrize("M,N,K,logits", [(1, 65544, 2560, "f32"), (7, 70000, 1024, None),
+                                          (16, 131080, 2560, "bf16"), (12, 65536, 2048, "f32")])
+def test_lmhead_vocab_shapes(dev, M, N, K, logits):
+    # the stream plan (at least 4096 tiles): ragged last tiles (N % 16 = 8), fewer rows
+    # than a block, short and long K, tile runs that do not divide evenly over the CUs
+    print("lm_head vocab", M, N, K, logits, flush=True)
+    d = synth.linear_inputs(M * 7 + N + K, M, N, K)
+    ldt = {"f32": torch.float32, "bf16": torch.bfloat16, None: None}[logits]
+    for L0 in (0, M // 2, M):
+        _lmhead_case(dev, d, L0, seed=L0 + 11, return_logits=logits is not None, logits_dtype=ldt)
+
+
+def test_lmhead_vocab_ties_across_workgroups(dev):
+    # the stream plan with the maximal column repeated in the runs of different
+    # workgroups (and twice in one): the lowest column wins
+    M, N, K = 4, 65552, 1024
+    d = _dyadic(5, M, N, K)
+    d["codes"][:, :] = np.random.default_rng(2).integers(0, 4, size=(N, K))
+    for c in (40000, 777, 65551, 777 + 16, 30000):
+        d["codes"][c, :] = 15
+        d["zeros"][c, :] = 0
+        d["scales"][c, :] = 0x2400  # 2^-6
+    d["X"] = synth.f32_to_bf16_bits(np.ones((M, K), np.float32))
+    t, qw, qz, oqw, oqz = _prep(d, dev)
+    draft = np.full(M, 777, np.int32)
+    draft[2] = 778
+    am, acc, _ = w4.w4a16_lmhead_verify(t["X"], qw, t["scales"], qz, torch.from_numpy(draft).to(dev))
+    assert (am.cpu().numpy() == 777).all() and int(acc.cpu()[0]) == 2
+
+
 def test_lmhead_ties_pick_lowest_column(dev):
     # duplicate the same weight column at several places; make it the maximum of every row
     M, N, K = 8, 1024, 256
