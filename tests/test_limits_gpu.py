@@ -50,9 +50,13 @@ def test_large_m_at_the_mk_limit(dev):
     assert (got == Yo).all(), "max |dY| %g" % np.abs(got - Yo).max()
 
 
-def test_small_m_at_the_nk_limit(dev):
-    M, K = 16, 2560
-    N = (LIMIT // K) // 8 * 8  # 838856 columns: a 1 GiB packed grid, the streaming plan
+@pytest.mark.parametrize("M", [16, 1])
+def test_small_m_at_the_nk_limit(dev, M):
+    # 838856 columns: a 1 GiB packed grid; M = 16 runs the draft-block kernel (10486
+    # workgroups of 5 tiles), M = 1 the decode kernel (104857 workgroups of 8 columns);
+    # the lm_head call below runs the stream plan
+    K = 2560
+    N = (LIMIT // K) // 8 * 8
     print("limit N*K", M, N, K, flush=True)
     codes = synth.cf_codes_torch(N, K, dev)
     zeros = torch.from_numpy(synth.cf_zeros(np.arange(N), K // 128)).to(dev)
