@@ -259,15 +259,20 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
     auto set_tile = [&](int t) {
         const int tm = t / p.tiles_n, tn = t - tm * p.tiles_n;
         const int m0 = tm * BM, n0 = tn * BNO;
+        // the lane index through an opaque copy: the per-lane terms below are recomputed
+        // at each tile instead of being hoisted out of the loop and kept live throughout
+        // (which pushes the stream plan's instance past the register file)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int s = (wave * 8 + i) * 64 + lane; // X slot: row s/16, swizzled chunk s%16
+            const int s = (wave * 8 + i) * 64 + ln; // X slot: row s/16, swizzled chunk s%16
             const int row = s >> 4, c = (s & 15) ^ xswz(row);
             xoff[i] = m0 + row < M ? ((uint32_t)(m0 + row) * (uint32_t)K + (uint32_t)(c * 8)) * 2u : kOob;
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int s = (wave * 2 + i) * 64 + lane; // word slot: column s/4, swizzled quarter s%4
+            const int s = (wave * 2 + i) * 64 + ln; // word slot: column s/4, swizzled quarter s%4
             const int cl = s >> 2, q = (s & 3) ^ ((cl >> 2) & 3);
             const int n = slot_col(n0, cl);
             woff[i] = n < N ? (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(q * 16) : kOob;
