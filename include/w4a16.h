@@ -114,11 +114,15 @@ int w4a16_pack_actorder(const uint8_t *codes, const uint8_t *zeros, const int32_
 
 /*
  * w4a16_linear_actorder -- Y = X * W^T for an act-order grid packed by
- * w4a16_pack_actorder: X [M][K] bf16 in natural column order is gathered by perm
- * into the workspace, then the call proceeds as w4a16_linear (same kernels, same
- * accuracy bound).  workspace: at least
- * w4a16_workspace_bytes(W4A16_OP_LINEAR_ACTORDER, M, N, K, group).  Shapes and
- * errors as w4a16_linear; perm (device) must be 16-byte aligned.
+ * w4a16_pack_actorder: X [M][K] bf16 in natural column order enters the
+ * contraction as X'[m][k] = X[m][perm[k]].  Where X fits on chip (M = 1 up to 40
+ * groups; 2 <= M <= 16 with K whole) the gather runs inside the kernel's X staging;
+ * otherwise X' is written to the workspace first and the call proceeds as
+ * w4a16_linear (same kernels, same accuracy bound).  An entry of perm outside
+ * [0, K) reads X[m][K - 1].  workspace: at least
+ * w4a16_workspace_bytes(W4A16_OP_LINEAR_ACTORDER, M, N, K, group) (the size of the
+ * separate gather, whichever path runs).  Shapes and errors as w4a16_linear; perm
+ * (device) must be 16-byte aligned.
  */
 int w4a16_linear_actorder(const void *X, const int32_t *perm, const uint32_t *qweight, const void *scales,
                           const uint32_t *qzeros, int M, int N, int K, int group, void *Y, int y_dtype,
@@ -241,15 +245,17 @@ int w4a16_linear_static_ws(const void *X, const uint32_t *qweight, const void *s
  * (a reading).  Wg and Wu are two grids of the layouts of w4a16_linear over the
  * same N columns.  For M <= 64 one launch computes both projections (each
  * workgroup holds a gate tile and the up tile of the same columns) and applies the
- * activation in its epilogue, so neither projection's output reaches memory; for
- * M > 64 the two projections run in turn into the workspace (fp32) and a third
- * kernel applies the activation.
+ * activation in its epilogue, so neither projection's output reaches memory; so
+ * does the large-M tile kernel when its tiles of 256 rows x 128 columns fill the
+ * GPU's compute units at least once.  In between, the two projections run in turn
+ * into the workspace (fp32) and a third kernel applies the activation.
  *   X                                     [M][K] bf16, row-major
  *   qweight_gate, scales_gate, qzeros_gate   the gate grid (layouts of w4a16_linear)
  *   qweight_up, scales_up, qzeros_up         the up grid, same N and K
  *   Y                                     [M][N] row-major, bf16 or fp32
  *   workspace   at least w4a16_workspace_bytes(W4A16_OP_LINEAR_GATED, M, N, K, group)
- *               bytes (M > 64: the fp32 outputs of both projections); the
+ *               bytes (M > 64: X as scaled fp16, and in the in-between range the
+ *               fp32 outputs of both projections); the
  *               counter-region rule of w4a16_linear; may be NULL when that size is 0
  * Shapes: as w4a16_linear, and N % 16 == 0, 2 * M * N at most 2^31 - 256.
  * Errors: as w4a16_linear (W4A16_ERR_SHAPE also for N % 16 != 0).  Y must not
