@@ -144,9 +144,8 @@ size_t skinny_multi_scratch(SkinnyMulti &mp, int M);
 hipError_t launch_skinny_multi(SkinnyMulti &mp, int M, size_t ws_bytes, hipStream_t stream);
 
 // ---------------------------------------------------------------- gemv (M = 1)
-// grid = wpc workgroups per CU; workgroup b owns columns [b N / grid, (b + 1) N / grid)
-// and all of K, cut into ns group sets of sw (4, 8 or 16) groups; wave w takes set
-// w / wps and up to cpw of the columns (slots = wps * cpw >= columns per workgroup).
+// Workgroup b owns the TC = 16 / pl columns from b TC and all of K; its waves split K,
+// wave w taking the gpw * pl groups from w gpw pl.
 struct GemvPlan {
     int gpw, pl, ao;  // code loads per lane, group parts per instruction, act-order
     int waves, grid;  // waves per workgroup (each NG = gpw * pl groups), N / (16 / pl)
