@@ -109,6 +109,32 @@ __device__ __forceinline__ void transpose_rows4(u32x4_t (&v)[4])
     }
 }
 
+// Full-line loads.  An instruction whose lanes read 16 rows (or columns) x 64 bytes
+// touches 16 half-used cache lines; the load pipeline of a CU takes about the same time
+// per line touched whatever the bytes used, so reading X from L2 that way costs about
+// three times the bytes.  Two instructions that each read 8 rows x 128 bytes (full
+// lines) bring the same data; one exchange between the lane halves of each 16-lane row
+// (DPP row rotate by 8, applied to half of the lanes through the bank mask) then puts
+// every chunk where the 16 x 64-byte instructions would have put it:
+//   lo = A on lanes r < 8, B of lane r - 8 on lanes r >= 8
+//   hi = A of lane r + 8 on lanes r < 8, B on lanes r >= 8
+// with A from rows (or columns) r & 7 and B from 8 + (r & 7), lane r reading bytes
+// 64 (r >> 3) + 16 h of the 128-byte span.
+__device__ __forceinline__ u32x4_t half_swap(const u32x4_t &keep, const u32x4_t &from, int bank_mask)
+{
+    u32x4_t r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        r[e] = bank_mask == 0xC ? (uint32_t)__builtin_amdgcn_update_dpp((int)keep[e], (int)from[e], 0x128, 0xF, 0xC, false)
+                                : (uint32_t)__builtin_amdgcn_update_dpp((int)keep[e], (int)from[e], 0x128, 0xF, 0x3, false);
+    return r;
+}
+__device__ __forceinline__ void full_line_pair(const u32x4_t &A, const u32x4_t &B, u32x4_t &lo, u32x4_t &hi)
+{
+    lo = half_swap(A, B, 0xC);
+    hi = half_swap(B, A, 0x3);
+}
+
 // LDS DMA: 16 bytes per lane from offset voff of r into LDS at dst + 16 * lane
 __device__ __forceinline__ void dma16_b(__amdgpu_buffer_rsrc_t r, unsigned char *dst, uint32_t voff)
 {
@@ -116,8 +142,15 @@ __device__ __forceinline__ void dma16_b(__amdgpu_buffer_rsrc_t r, unsigned char 
 }
 
 // GPW: the most groups a wave's K slice holds; TMAX: the most tiles a workgroup owns;
-// AO: act-order (X gathered through perm in LDS; one projection, K whole)
-template <int GPW, int TMAX, bool AO>
+// AO: act-order (X gathered through perm in LDS; one projection, K whole); MULTI:
+// several projections in the launch.
+//
+// The arguments live in memory that every CU reads through its scalar cache, and each
+// read that depends on an earlier one costs a round trip to memory (about half a
+// microsecond on a cold cache).  So every argument is read at a fixed offset: one
+// projection reads pr[0] directly; several find their projection with one compare per
+// entry (all entries read at once), then read its fields, two round trips in all.
+template <int GPW, int TMAX, bool AO, bool MULTI>
 __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
 {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -127,14 +160,18 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     // the workgroup's projection, its tile group [t0, t1) (balanced over the projection's
     // ntg tile groups) and its part of K (parts of a tile group are adjacent workgroups)
     int q = 0;
-    while (q + 1 < a.count && (int)blockIdx.x >= a.pr[q + 1].wg0)
-        ++q;
-    const BlockProb &pr = a.pr[q];
+    if constexpr (MULTI) {
+#pragma unroll
+        for (int j = 1; j < kMaxProblemsBlock; ++j)
+            q += (j < a.count && (int)blockIdx.x >= a.pr[j].wg0) ? 1 : 0;
+    }
+    const BlockProb &pr = a.pr[MULTI ? q : 0];
     const int P = pr.parts;
     const int b = blockIdx.x - pr.wg0;
     const int tg = b / P, part = b - tg * P;
-    const int t0 = (int)((long long)tg * pr.nt / pr.ntg);
-    const int t1 = (int)((long long)(tg + 1) * pr.nt / pr.ntg);
+    // tg * nt < 2^31: at most 2^16 tiles of 16 columns
+    const int t0 = tg * pr.nt / pr.ntg;
+    const int t1 = (tg + 1) * pr.nt / pr.ntg;
     const int T = t1 - t0;
     const int G = pr.K / kGroup, N = pr.N, M = a.M;
     const int Gp = (G + P - 1) / P;
@@ -200,27 +237,48 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
             dma16_b(rp, pa + u0 * 16, u < punits ? 16u * (uint32_t)u : kOobB);
         }
     } else {
+        // per group, its two 128-byte halves q, each as rows 0..7 (A) and 8..15 (B) in
+        // full lines; combined into the j = 2q, 2q + 1 loads of the layout above after
+        // they land
+        const int ra = c & 7, rb = 8 + (c & 7);
 #pragma unroll
         for (int i = 0; i < GPW; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                xf[i][j] = ld16_b(rx, (c < M && i < gn) ? (uint32_t)c * (uint32_t)pr.K * 2u +
-                                                              (uint32_t)(g0 + i) * 256u + 64u * j + 16u * h
-                                                        : kOobB);
+            for (int q = 0; q < 2; ++q) {
+                const uint32_t off = (uint32_t)(g0 + i) * 256u + 128u * q + 64u * (c >> 3) + 16u * h;
+                xf[i][2 * q] = ld16_b(rx, (ra < M && i < gn) ? (uint32_t)ra * (uint32_t)pr.K * 2u + off : kOobB);
+                xf[i][2 * q + 1] = ld16_b(rx, (rb < M && i < gn) ? (uint32_t)rb * (uint32_t)pr.K * 2u + off : kOobB);
+            }
     }
 
-    // 3. the codes of every (tile, group) of the slice
+    // 3. the codes of every (tile, group) of the slice.  Groups i, i + 1 of a column are
+    //    128 adjacent bytes: columns 0..7 (A) and 8..15 (B) of the tile in full lines,
+    //    lane (c, h) reading bytes 16 h of group i + (c >> 3) of its column; a last odd
+    //    group of the slice alone (lane (c, h): bytes 16 h of column c)
     u32x4_t wv[TMAX][GPW];
 #pragma unroll
-    for (int tl = 0; tl < TMAX; ++tl)
+    for (int tl = 0; tl < TMAX; ++tl) {
 #pragma unroll
-        for (int i = 0; i < GPW; ++i) {
+        for (int i = 0; i + 1 < GPW; i += 2) {
+            const int gi = i + (c >> 3);
+            const int na = (t0 + tl) * 16 + (c & 7), nb = na + 8;
+            const uint32_t go = (uint32_t)(g0 + gi) * 64u + 16u * h;
+            wv[tl][i] = ld16_b(rw, (tl < T && gi < gn && na < N) ? (uint32_t)na * rowb + go : kOobB);
+            wv[tl][i + 1] = ld16_b(rw, (tl < T && gi < gn && nb < N) ? (uint32_t)nb * rowb + go : kOobB);
+        }
+        if constexpr (GPW % 2 == 1) {
+            constexpr int i = GPW - 1;
             const int n = (t0 + tl) * 16 + c;
             wv[tl][i] = ld16_b(rw, (tl < T && i < gn && n < N)
                                        ? (uint32_t)n * rowb + (uint32_t)(g0 + i) * 64u + 16u * h
                                        : kOobB);
         }
+    }
     asm volatile("" ::: "memory");
+    // every load of the wave is issued before any arithmetic on X: left to itself the
+    // compiler moves the arrangement of X (below) above the code loads and waits for X
+    // first, so the codes' HBM latency would start only after X had arrived
+    __builtin_amdgcn_sched_barrier(0);
     // the DMA of this wave was issued before its (4 GPW +) TMAX GPW register loads:
     // vmcnt(that many) means it has landed; the barrier makes every wave's part visible
     constexpr int kAfter = (AO ? 0 : 4 * GPW) + TMAX * GPW;
@@ -263,8 +321,14 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     f32x4_t Sv[GPW];
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
-        if constexpr (!AO)
+        if constexpr (!AO) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const u32x4_t A = xf[i][2 * q], B = xf[i][2 * q + 1];
+                full_line_pair(A, B, xf[i][2 * q], xf[i][2 * q + 1]);
+            }
             transpose_rows4(xf[i]);
+        }
         float ps = (sum8_bf16(xf[i][0]) + sum8_bf16(xf[i][1])) + (sum8_bf16(xf[i][2]) + sum8_bf16(xf[i][3]));
         ps += __int_as_float(__shfl_xor(__float_as_int(ps), 16));
         ps += __int_as_float(__shfl_xor(__float_as_int(ps), 32));
@@ -277,6 +341,14 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
 #pragma unroll
     for (int i = 0; i < GPW; ++i)
         Sv[i] = *(const f32x4_t *)(sS + i * 16 + 4 * h);
+
+#pragma unroll
+    for (int tl = 0; tl < TMAX; ++tl)
+#pragma unroll
+        for (int i = 0; i + 1 < GPW; i += 2) {
+            const u32x4_t A = wv[tl][i], B = wv[tl][i + 1];
+            full_line_pair(A, B, wv[tl][i], wv[tl][i + 1]);
+        }
 
     // 4. per (tile, group): four MFMAs on the biased codes (P = sum x * (128 + q)), then
     //    acc += s * (P - (128 + z) * S) in fp32
@@ -493,13 +565,18 @@ BlockPlan plan_block_ao(int N, int K, int M)
 // default); raised once per device
 static hipError_t allow_block_lds(int)
 {
-    const void *fns[] = {(const void *)block_kernel<1, 1, false>, (const void *)block_kernel<1, 2, false>,
-                         (const void *)block_kernel<1, 5, false>, (const void *)block_kernel<2, 1, false>,
-                         (const void *)block_kernel<2, 2, false>, (const void *)block_kernel<2, 5, false>,
-                         (const void *)block_kernel<3, 1, false>, (const void *)block_kernel<3, 2, false>,
-                         (const void *)block_kernel<1, 1, true>,  (const void *)block_kernel<1, 2, true>,
-                         (const void *)block_kernel<1, 5, true>,  (const void *)block_kernel<2, 1, true>,
-                         (const void *)block_kernel<2, 2, true>,  (const void *)block_kernel<2, 5, true>};
+    const void *fns[] = {
+        (const void *)block_kernel<1, 1, false, false>, (const void *)block_kernel<1, 2, false, false>,
+        (const void *)block_kernel<1, 5, false, false>, (const void *)block_kernel<2, 1, false, false>,
+        (const void *)block_kernel<2, 2, false, false>, (const void *)block_kernel<2, 5, false, false>,
+        (const void *)block_kernel<3, 1, false, false>, (const void *)block_kernel<3, 2, false, false>,
+        (const void *)block_kernel<1, 1, false, true>,  (const void *)block_kernel<1, 2, false, true>,
+        (const void *)block_kernel<1, 5, false, true>,  (const void *)block_kernel<2, 1, false, true>,
+        (const void *)block_kernel<2, 2, false, true>,  (const void *)block_kernel<2, 5, false, true>,
+        (const void *)block_kernel<3, 1, false, true>,  (const void *)block_kernel<3, 2, false, true>,
+        (const void *)block_kernel<1, 1, true, false>,  (const void *)block_kernel<1, 2, true, false>,
+        (const void *)block_kernel<1, 5, true, false>,  (const void *)block_kernel<2, 1, true, false>,
+        (const void *)block_kernel<2, 2, true, false>,  (const void *)block_kernel<2, 5, true, false>};
     for (const void *f : fns) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kBlockLds);
         if (e != hipSuccess)
@@ -534,25 +611,34 @@ hipError_t launch_block(const BlockArgs &args, const BlockPlan &p, hipStream_t s
     if (e != hipSuccess)
         return e;
     const dim3 grid(p.grid), block(64 * p.waves);
-    switch (p.gpw * 100 + p.tmax * 10 + (p.ao ? 1 : 0)) {
-#define W4A16_BLOCK_CASE(GP, TM, AO)                                                                           \
-    case GP * 100 + TM * 10 + AO:                                                                              \
-        hipLaunchKernelGGL((block_kernel<GP, TM, AO != 0>), grid, block, p.lds_bytes, stream, a);              \
+    const int multi = p.count > 1 ? 1 : 0;
+    switch (p.gpw * 1000 + p.tmax * 100 + (p.ao ? 10 : 0) + multi) {
+#define W4A16_BLOCK_CASE(GP, TM, AO, MU)                                                                       \
+    case GP * 1000 + TM * 100 + AO * 10 + MU:                                                                  \
+        hipLaunchKernelGGL((block_kernel<GP, TM, AO != 0, MU != 0>), grid, block, p.lds_bytes, stream, a);     \
         break;
-        W4A16_BLOCK_CASE(1, 1, 0)
-        W4A16_BLOCK_CASE(1, 2, 0)
-        W4A16_BLOCK_CASE(1, 5, 0)
-        W4A16_BLOCK_CASE(2, 1, 0)
-        W4A16_BLOCK_CASE(2, 2, 0)
-        W4A16_BLOCK_CASE(2, 5, 0)
-        W4A16_BLOCK_CASE(3, 1, 0)
-        W4A16_BLOCK_CASE(3, 2, 0)
-        W4A16_BLOCK_CASE(1, 1, 1)
-        W4A16_BLOCK_CASE(1, 2, 1)
-        W4A16_BLOCK_CASE(1, 5, 1)
-        W4A16_BLOCK_CASE(2, 1, 1)
-        W4A16_BLOCK_CASE(2, 2, 1)
-        W4A16_BLOCK_CASE(2, 5, 1)
+        W4A16_BLOCK_CASE(1, 1, 0, 0)
+        W4A16_BLOCK_CASE(1, 2, 0, 0)
+        W4A16_BLOCK_CASE(1, 5, 0, 0)
+        W4A16_BLOCK_CASE(2, 1, 0, 0)
+        W4A16_BLOCK_CASE(2, 2, 0, 0)
+        W4A16_BLOCK_CASE(2, 5, 0, 0)
+        W4A16_BLOCK_CASE(3, 1, 0, 0)
+        W4A16_BLOCK_CASE(3, 2, 0, 0)
+        W4A16_BLOCK_CASE(1, 1, 0, 1)
+        W4A16_BLOCK_CASE(1, 2, 0, 1)
+        W4A16_BLOCK_CASE(1, 5, 0, 1)
+        W4A16_BLOCK_CASE(2, 1, 0, 1)
+        W4A16_BLOCK_CASE(2, 2, 0, 1)
+        W4A16_BLOCK_CASE(2, 5, 0, 1)
+        W4A16_BLOCK_CASE(3, 1, 0, 1)
+        W4A16_BLOCK_CASE(3, 2, 0, 1)
+        W4A16_BLOCK_CASE(1, 1, 1, 0)
+        W4A16_BLOCK_CASE(1, 2, 1, 0)
+        W4A16_BLOCK_CASE(1, 5, 1, 0)
+        W4A16_BLOCK_CASE(2, 1, 1, 0)
+        W4A16_BLOCK_CASE(2, 2, 1, 0)
+        W4A16_BLOCK_CASE(2, 5, 1, 0)
 #undef W4A16_BLOCK_CASE
     default:
         return hipErrorInvalidValue;
