@@ -36,7 +36,7 @@
  *   - Pointers must be 16-byte aligned (they are read with 128-bit loads).
  *   - Empty problems (M == 0 or N == 0) return W4A16_OK and enqueue nothing.
  *   - Results are deterministic: the same inputs give bit-identical outputs.
- *   - Workspace: the first 8 KiB hold arrival counters and argmax keys that
+ *   - Workspace: the first 64 KiB hold arrival counters and argmax keys that
  *     must be zero when a call starts.  Zero-fill a workspace once when it is
  *     allocated; every call returns that region to zero before it completes,
  *     so one workspace serves calls of any shape in sequence.  Calls that

@@ -394,7 +394,7 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     __syncthreads();
     __shared__ int s_last;
     float *pb = (float *)(a.ws + pr.part_off) + (size_t)tg * P * pr.tmx * 256; // [part][tmx * 64][4]
-    uint32_t *ctr = (uint32_t *)(a.ws + kOffCounters) + pr.tkt + tg;
+    uint32_t *ctr = (uint32_t *)(a.ws + kOffCounters) + (size_t)(pr.tkt + tg) * kCounterStride;
     for (int e = threadIdx.x; e < T * 64; e += W * 64) {
         const int tl = e >> 6, l = e & 63;
         f32x4_t y = red[tl * 64 + l];
@@ -511,7 +511,7 @@ BlockPlan plan_block(const int *N, const int *K, int count, int M, int tmax_hint
             off += block_ws_bytes(N[q], T, P);
         }
     }
-    if (tkt > (int)((kZeroRegion - kOffCounters) / 4))
+    if (tkt > kMaxCounters)
         return p;
     p.ws_bytes = off == kZeroRegion ? 0 : off;
     p.grid = wg;

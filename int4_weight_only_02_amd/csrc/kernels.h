@@ -25,8 +25,13 @@ constexpr int kMaxProblemsBlock = 8; // projections per block launch
 // path can share one workspace.
 constexpr size_t kOffTicket = 0;          // u32: workgroups finished (lm_head)
 constexpr size_t kOffKeys = 256;          // u64[64]: per-row argmax keys (lm_head)
-constexpr size_t kOffCounters = 1024;     // u32[]: arrivals of K-chunked tile groups (small M)
-constexpr size_t kZeroRegion = 8192;
+constexpr size_t kOffCounters = 1024;     // arrival counters (small-M parts of K, prefill tile hand-offs)
+constexpr size_t kZeroRegion = 65536;
+// Every arrival counter sits alone in a 128-byte line: device-scope atomics on one line
+// complete one at a time (about 33 ns each on MI355X), so counters packed into a few
+// lines would queue every arrival of a launch behind each other.
+constexpr int kCounterStride = 32; // u32 per counter
+constexpr int kMaxCounters = (int)((kZeroRegion - kOffCounters) / (4 * kCounterStride));
 
 // ---------------------------------------------------------------- pack
 hipError_t launch_pack(const uint8_t *codes, const uint8_t *zeros, int N, int K, int G,

@@ -51,7 +51,7 @@ constexpr int kCUs = 256;
 constexpr size_t kLdsBudget = 160 * 1024 - 4096;
 constexpr uint32_t kOob = 0xFFFFFF00u; // an offset past the end of every tensor
 constexpr int kSplitDirect = 0, kSplitLds = 1, kStream = 2, kSplitPriv = 3, kSplitChunk = 4, kSplitPrivDma = 5;
-constexpr int kMaxTickets = (int)((kZeroRegion - kOffCounters) / 4); // arrival counters of chunked tiles
+constexpr int kMaxTickets = kMaxCounters; // arrival counters of chunked tiles
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m)
 {
@@ -861,7 +861,7 @@ __device__ __forceinline__ void skinny_body(const SkinnyArgs &a, const SkinnyPla
                 // does not depend on the arrival order
                 // (gated: over the 2N columns of the pair, gate and up tiles alternating)
                 float *pbuf = (float *)(a.ws + p.part_off);
-                uint32_t *tk = (uint32_t *)(a.ws + kOffCounters) + p.tkt + rest;
+                uint32_t *tk = (uint32_t *)(a.ws + kOffCounters) + (size_t)(p.tkt + rest) * kCounterStride;
                 const int Nv = GATED ? 2 * N : N;
                 const int n = tile * 16 + col;
                 if (ks == 0 && live && n < Nv) {

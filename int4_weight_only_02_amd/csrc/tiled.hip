@@ -408,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void tiled_kernel(TiledArgs a, TiledPlan 
         const int slot = gs == 0 ? seg : seg - 1; // boundary seg + 1 or seg, minus one
         const int mine = gs == 0 ? 0 : 1;
         const uint32_t other = ((uint32_t)(slot * 2 + 1 - mine) * (BM * BN) + (uint32_t)tid * 4u) * 4u;
-        uint32_t *tk = (uint32_t *)(a.ws + kOffCounters) + slot;
+        uint32_t *tk = (uint32_t *)(a.ws + kOffCounters) + (size_t)slot * kCounterStride;
         if constexpr (STREAM) {
             if (split) {
                 const uint32_t own = ((uint32_t)(slot * 2 + mine) * (BM * BN) + (uint32_t)tid * 4u) * 4u;
@@ -617,6 +617,7 @@ TiledPlan plan_tiled(int M, int N, int K)
         // flight at a time are neighbours that share X rows in L2); the segments (at
         // least G each) split at most one tile at each inner boundary: a pair of fp32
         // regions and an arrival counter per boundary
+        static_assert(kCUs - 1 <= kMaxCounters, "one arrival counter per inner boundary");
         p.stream = 1;
         p.grid = kCUs;
         p.dp_rounds = (int)(ntiles / kCUs) - 1;
