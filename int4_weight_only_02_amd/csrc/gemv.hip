@@ -161,14 +161,10 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
     }
     asm volatile("" ::: "memory");
 
-    // 2. the codes: instruction i, lane (c + TC p, h) loads bytes 16h .. of group
-    //    g0 + i PL + p of column n; then that pair's scale and zero word
-    u32x4_t wv[GPW];
-#pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-        const int g = g0 + i * PL + p;
-        wv[i] = ld16_g(rw, g < G ? (uint32_t)n * rowb + (uint32_t)g * 64u + 16u * h : kOobG);
-    }
+    // 2. the scale and zero word of each (column, group) pair of the lane, then the
+    //    codes: instruction i, lane (c + TC p, h) loads bytes 16h .. of group g0 + i PL + p
+    //    of column n.  The small parameter loads go first, so that they do not queue
+    //    behind the code loads
     uint32_t sv[GPW], zv[GPW];
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
@@ -176,6 +172,12 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
         sv[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, g < G ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobG, 0, 0);
         zv[i] = __builtin_amdgcn_raw_buffer_load_b32(rz, g < G ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobG,
                                                      0, 0);
+    }
+    u32x4_t wv[GPW];
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        const int g = g0 + i * PL + p;
+        wv[i] = ld16_g(rw, g < G ? (uint32_t)n * rowb + (uint32_t)g * 64u + 16u * h : kOobG);
     }
     asm volatile("" ::: "memory");
 
