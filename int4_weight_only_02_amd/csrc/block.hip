@@ -314,10 +314,15 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
         __syncthreads();
     }
 
-    // X in place, and S[r][g] = sum of row r of X over group g (the lane's 32 values,
-    // then across its row's four lanes, in a fixed order) through this wave's LDS
-    // region: lane (c, h) keeps S of rows 4h .. 4h+3, the rows its accumulators hold
-    float *sS = (float *)(lds + a.s_off) + w * GPW * 16;
+    // X in place (the fragment order of the codes), and S[r][g] = sum of row r of X over
+    // group g from the matrix cores: four MFMAs of the group's X fragments against a B of
+    // ones (bf16 1.0) give D[r][c] = S[r][g] for every column c, so lane (c, h) receives
+    // S of rows 4h .. 4h+3, the rows its accumulators hold (every product is exact; the
+    // sums run in the matrix cores' fixed order).  Per wave that is four MFMAs per group
+    // in place of some seventy VALU instructions and a round trip through LDS.
+    uint32_t one = 0x3F803F80u;
+    asm volatile("" : "+v"(one));
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{one, one, one, one});
     f32x4_t Sv[GPW];
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
@@ -329,18 +334,15 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
             }
             transpose_rows4(xf[i]);
         }
-        float ps = (sum8_bf16(xf[i][0]) + sum8_bf16(xf[i][1])) + (sum8_bf16(xf[i][2]) + sum8_bf16(xf[i][3]));
-        ps += __int_as_float(__shfl_xor(__float_as_int(ps), 16));
-        ps += __int_as_float(__shfl_xor(__float_as_int(ps), 32));
-        if (h == 0)
-            sS[i * 16 + c] = ps;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             xf[i][j] = x_permute8(xf[i][j]);
-    }
+        f32x4_t sv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < GPW; ++i)
-        Sv[i] = *(const f32x4_t *)(sS + i * 16 + 4 * h);
+        for (int j = 0; j < 4; ++j)
+            sv = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][j]), ones, sv);
+        Sv[i] = sv;
+    }
 
 #pragma unroll
     for (int tl = 0; tl < TMAX; ++tl)
@@ -532,12 +534,11 @@ BlockPlan plan_block(const int *N, const int *K, int count, int M, int tmax_hint
         return p;
     p.waves = W;
     // LDS: scales ([16 tmax][gpmax / 2 + 1] words) and zero words ([2 tmax][gpmax]), rounded up
-    // to whole DMA rounds; per-wave row sums; the slice accumulators [W][TMAX][64] of 16 B
+    // to whole DMA rounds; the slice accumulators [W][TMAX][64] of 16 B
     const size_t sc = (size_t)((16 * p.tmax * (gpmax / 2 + 1) + 63) / 64 * 64) * 4;
     const size_t zw = (size_t)((2 * p.tmax * gpmax + 63) / 64 * 64) * 4;
     p.z_off = (int)((sc + 15) / 16 * 16);
-    p.s_off = (int)((p.z_off + zw + 15) / 16 * 16);
-    p.r_off = p.s_off + W * p.gpw * 16 * 4;
+    p.r_off = (int)((p.z_off + zw + 15) / 16 * 16);
     p.lds_bytes = (size_t)p.r_off + (size_t)W * p.tmax * 64 * 16;
     p.ok = p.lds_bytes <= (size_t)kBlockLds;
     return p;
@@ -592,7 +593,6 @@ hipError_t launch_block(const BlockArgs &args, const BlockPlan &p, hipStream_t s
     BlockArgs a = args;
     a.count = p.count;
     a.z_off = p.z_off;
-    a.s_off = p.s_off;
     a.r_off = p.r_off;
     a.x_off = p.x_off;
     a.p_off = p.p_off;

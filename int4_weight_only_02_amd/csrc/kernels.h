@@ -193,7 +193,7 @@ struct BlockArgs {
     int count, M, y_f32;
     unsigned char *ws;       // workspace base (partial sums, arrival counters)
     const int32_t *perm;     // act-order plans (one projection, K whole): X'[k] = X[perm[k]]
-    int z_off, s_off, r_off; // filled by launch_block
+    int z_off, r_off;        // filled by launch_block
     int x_off, p_off;        // act-order: LDS of the X rows and of perm
 };
 struct BlockPlan {
@@ -202,7 +202,7 @@ struct BlockPlan {
     int wg0[kMaxProblemsBlock], ntg[kMaxProblemsBlock], parts[kMaxProblemsBlock], tmx[kMaxProblemsBlock];
     int tkt[kMaxProblemsBlock];
     size_t part_off[kMaxProblemsBlock];
-    int z_off, s_off, r_off;
+    int z_off, r_off;
     size_t lds_bytes, ws_bytes; // ws_bytes: 0 when no projection splits K
     bool ok;
 };
