@@ -109,32 +109,6 @@ __device__ __forceinline__ void transpose_rows4(u32x4_t (&v)[4])
     }
 }
 
-// Full-line loads.  An instruction whose lanes read 16 rows (or columns) x 64 bytes
-// touches 16 half-used cache lines; the load pipeline of a CU takes about the same time
-// per line touched whatever the bytes used, so reading X from L2 that way costs about
-// three times the bytes.  Two instructions that each read 8 rows x 128 bytes (full
-// lines) bring the same data; one exchange between the lane halves of each 16-lane row
-// (DPP row rotate by 8, applied to half of the lanes through the bank mask) then puts
-// every chunk where the 16 x 64-byte instructions would have put it:
-//   lo = A on lanes r < 8, B of lane r - 8 on lanes r >= 8
-//   hi = A of lane r + 8 on lanes r < 8, B on lanes r >= 8
-// with A from rows (or columns) r & 7 and B from 8 + (r & 7), lane r reading bytes
-// 64 (r >> 3) + 16 h of the 128-byte span.
-__device__ __forceinline__ u32x4_t half_swap(const u32x4_t &keep, const u32x4_t &from, int bank_mask)
-{
-    u32x4_t r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        r[e] = bank_mask == 0xC ? (uint32_t)__builtin_amdgcn_update_dpp((int)keep[e], (int)from[e], 0x128, 0xF, 0xC, false)
-                                : (uint32_t)__builtin_amdgcn_update_dpp((int)keep[e], (int)from[e], 0x128, 0xF, 0x3, false);
-    return r;
-}
-__device__ __forceinline__ void full_line_pair(const u32x4_t &A, const u32x4_t &B, u32x4_t &lo, u32x4_t &hi)
-{
-    lo = half_swap(A, B, 0xC);
-    hi = half_swap(B, A, 0x3);
-}
-
 // LDS DMA: 16 bytes per lane from offset voff of r into LDS at dst + 16 * lane
 __device__ __forceinline__ void dma16_b(__amdgpu_buffer_rsrc_t r, unsigned char *dst, uint32_t voff)
 {
@@ -237,43 +211,26 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
             dma16_b(rp, pa + u0 * 16, u < punits ? 16u * (uint32_t)u : kOobB);
         }
     } else {
-        // per group, its two 128-byte halves q, each as rows 0..7 (A) and 8..15 (B) in
-        // full lines; combined into the j = 2q, 2q + 1 loads of the layout above after
-        // they land
-        const int ra = c & 7, rb = 8 + (c & 7);
 #pragma unroll
         for (int i = 0; i < GPW; ++i)
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const uint32_t off = (uint32_t)(g0 + i) * 256u + 128u * q + 64u * (c >> 3) + 16u * h;
-                xf[i][2 * q] = ld16_b(rx, (ra < M && i < gn) ? (uint32_t)ra * (uint32_t)pr.K * 2u + off : kOobB);
-                xf[i][2 * q + 1] = ld16_b(rx, (rb < M && i < gn) ? (uint32_t)rb * (uint32_t)pr.K * 2u + off : kOobB);
-            }
+            for (int j = 0; j < 4; ++j)
+                xf[i][j] = ld16_b(rx, (c < M && i < gn) ? (uint32_t)c * (uint32_t)pr.K * 2u +
+                                                              (uint32_t)(g0 + i) * 256u + 64u * j + 16u * h
+                                                        : kOobB);
     }
 
-    // 3. the codes of every (tile, group) of the slice.  Groups i, i + 1 of a column are
-    //    128 adjacent bytes: columns 0..7 (A) and 8..15 (B) of the tile in full lines,
-    //    lane (c, h) reading bytes 16 h of group i + (c >> 3) of its column; a last odd
-    //    group of the slice alone (lane (c, h): bytes 16 h of column c)
+    // 3. the codes of every (tile, group) of the slice
     u32x4_t wv[TMAX][GPW];
 #pragma unroll
-    for (int tl = 0; tl < TMAX; ++tl) {
+    for (int tl = 0; tl < TMAX; ++tl)
 #pragma unroll
-        for (int i = 0; i + 1 < GPW; i += 2) {
-            const int gi = i + (c >> 3);
-            const int na = (t0 + tl) * 16 + (c & 7), nb = na + 8;
-            const uint32_t go = (uint32_t)(g0 + gi) * 64u + 16u * h;
-            wv[tl][i] = ld16_b(rw, (tl < T && gi < gn && na < N) ? (uint32_t)na * rowb + go : kOobB);
-            wv[tl][i + 1] = ld16_b(rw, (tl < T && gi < gn && nb < N) ? (uint32_t)nb * rowb + go : kOobB);
-        }
-        if constexpr (GPW % 2 == 1) {
-            constexpr int i = GPW - 1;
+        for (int i = 0; i < GPW; ++i) {
             const int n = (t0 + tl) * 16 + c;
             wv[tl][i] = ld16_b(rw, (tl < T && i < gn && n < N)
                                        ? (uint32_t)n * rowb + (uint32_t)(g0 + i) * 64u + 16u * h
                                        : kOobB);
         }
-    }
     asm volatile("" ::: "memory");
     // every load of the wave is issued before any arithmetic on X: left to itself the
     // compiler moves the arrangement of X (below) above the code loads and waits for X
@@ -326,14 +283,8 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     f32x4_t Sv[GPW];
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
-        if constexpr (!AO) {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const u32x4_t A = xf[i][2 * q], B = xf[i][2 * q + 1];
-                full_line_pair(A, B, xf[i][2 * q], xf[i][2 * q + 1]);
-            }
+        if constexpr (!AO)
             transpose_rows4(xf[i]);
-        }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             xf[i][j] = x_permute8(xf[i][j]);
@@ -343,14 +294,6 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
             sv = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][j]), ones, sv);
         Sv[i] = sv;
     }
-
-#pragma unroll
-    for (int tl = 0; tl < TMAX; ++tl)
-#pragma unroll
-        for (int i = 0; i + 1 < GPW; i += 2) {
-            const u32x4_t A = wv[tl][i], B = wv[tl][i + 1];
-            full_line_pair(A, B, wv[tl][i], wv[tl][i + 1]);
-        }
 
     // 4. per (tile, group): four MFMAs on the biased codes (P = sum x * (128 + q)), then
     //    acc += s * (P - (128 + z) * S) in fp32
