@@ -164,28 +164,33 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     const __amdgpu_buffer_rsrc_t rz = rsrc_b(pr.qz, (uint32_t)(N / 8) * (uint32_t)G * 4u);
     const __amdgpu_buffer_rsrc_t rx = rsrc_b(pr.X, (uint32_t)M * (uint32_t)pr.K * 2u);
 
-    // 1. the scales and zero words of the part's groups for the workgroup's columns
-    //    (16 t0 .. 16 t1 - 1, zero rows 2 t0 .. 2 t1 - 1), by DMA of 4-byte words: each
-    //    column's run of gnp halves sits in the wpr words from the one that holds its
-    //    first half ([row][wpr] words); the zero words as [zero row][gnp]
+    // 1. act-order: the scales and zero words of the part's groups for the workgroup's
+    //    columns (16 t0 .. 16 t1 - 1, zero rows 2 t0 .. 2 t1 - 1), by DMA of 4-byte
+    //    words, behind the barrier that the gathered X needs anyway: each column's run of
+    //    gnp halves sits in the wpr words from the one that holds its first half
+    //    ([row][wpr] words); the zero words as [zero row][gnp].  (The plain path loads
+    //    each lane's own scale and zero words below instead, and has no barrier before
+    //    its contraction.)
     unsigned char *sc_lds = lds;
     unsigned char *z_lds = lds + a.z_off;
     const int wpr = gnp / 2 + 1;
-    const int sc_units = 16 * T * wpr;
-    const int z_units = 2 * T * gnp;
-    for (int u0 = w * 64; u0 < sc_units; u0 += W * 64) {
-        const int u = u0 + lane;
-        const int row = u / wpr, wi = u - row * wpr;
-        const uint32_t first = ((uint32_t)(t0 * 16 + row) * (uint32_t)G + (uint32_t)ga) >> 1;
-        dma4_b(rs, sc_lds + u0 * 4, u < sc_units ? (first + (uint32_t)wi) * 4u : kOobB);
+    if constexpr (AO) {
+        const int sc_units = 16 * T * wpr;
+        const int z_units = 2 * T * gnp;
+        for (int u0 = w * 64; u0 < sc_units; u0 += W * 64) {
+            const int u = u0 + lane;
+            const int row = u / wpr, wi = u - row * wpr;
+            const uint32_t first = ((uint32_t)(t0 * 16 + row) * (uint32_t)G + (uint32_t)ga) >> 1;
+            dma4_b(rs, sc_lds + u0 * 4, u < sc_units ? (first + (uint32_t)wi) * 4u : kOobB);
+        }
+        for (int u0 = w * 64; u0 < z_units; u0 += W * 64) {
+            const int u = u0 + lane;
+            const int row = u / gnp, gi = u - row * gnp;
+            dma4_b(rz, z_lds + u0 * 4,
+                   u < z_units ? ((uint32_t)(t0 * 2 + row) * (uint32_t)G + (uint32_t)(ga + gi)) * 4u : kOobB);
+        }
+        asm volatile("" ::: "memory");
     }
-    for (int u0 = w * 64; u0 < z_units; u0 += W * 64) {
-        const int u = u0 + lane;
-        const int row = u / gnp, gi = u - row * gnp;
-        dma4_b(rz, z_lds + u0 * 4,
-               u < z_units ? ((uint32_t)(t0 * 2 + row) * (uint32_t)G + (uint32_t)(ga + gi)) * 4u : kOobB);
-    }
-    asm volatile("" ::: "memory");
 
     // 2. the wave's K slice of X (rows past M read as 0).  The MFMAs need lane (r, h) to
     //    hold X[r][(g0 + i) * 128 + 32h + 8j .. + 8] for j = 0..3 (the 64 bytes at 64h of
@@ -220,7 +225,23 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
                                                         : kOobB);
     }
 
-    // 3. the codes of every (tile, group) of the slice
+    // 3. the plain path: the scale and zero word of each (tile, group) of the lane's
+    //    column; then the codes of every (tile, group) of the slice
+    uint32_t sv[AO ? 1 : TMAX][GPW], zv[AO ? 1 : TMAX][GPW];
+    if constexpr (!AO) {
+#pragma unroll
+        for (int tl = 0; tl < TMAX; ++tl)
+#pragma unroll
+            for (int i = 0; i < GPW; ++i) {
+                const int n = (t0 + tl) * 16 + c;
+                const bool live = tl < T && i < gn && n < N;
+                const uint32_t g = (uint32_t)(g0 + i);
+                sv[tl][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, live ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobB,
+                                                                 0, 0);
+                zv[tl][i] = __builtin_amdgcn_raw_buffer_load_b32(
+                    rz, live ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobB, 0, 0);
+            }
+    }
     u32x4_t wv[TMAX][GPW];
 #pragma unroll
     for (int tl = 0; tl < TMAX; ++tl)
@@ -236,12 +257,14 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     // compiler moves the arrangement of X (below) above the code loads and waits for X
     // first, so the codes' HBM latency would start only after X had arrived
     __builtin_amdgcn_sched_barrier(0);
-    // the DMA of this wave was issued before its (4 GPW +) TMAX GPW register loads:
-    // vmcnt(that many) means it has landed; the barrier makes every wave's part visible
-    constexpr int kAfter = (AO ? 0 : 4 * GPW) + TMAX * GPW;
-    static_assert(kAfter < 64, "vmcnt is a 6-bit counter");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (kAfter & 15) | ((kAfter >> 4) << 14));
-    __syncthreads();
+    if constexpr (AO) {
+        // the DMA of this wave was issued before its TMAX GPW register loads: vmcnt(that
+        // many) means it has landed; the barrier makes every wave's part visible
+        constexpr int kAfter = TMAX * GPW;
+        static_assert(kAfter < 64, "vmcnt is a 6-bit counter");
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (kAfter & 15) | ((kAfter >> 4) << 14));
+        __syncthreads();
+    }
 
     if constexpr (AO) {
         // lane (c, h), fragment (i, j): X'[c][k .. k + 8), k = (g0 + i) 128 + 32h + 8j,
@@ -319,8 +342,9 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
                     d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][1]), frag_b(wv[tl][i].y, mask, bias), d);
                     d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][2]), frag_b(wv[tl][i].z, mask, bias), d);
                     d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][3]), frag_b(wv[tl][i].w, mask, bias), d);
-                    const float zb = -(float)(kCodeBias + ((zl[g] >> zsh) & 15u));
-                    const float s = f16_bits_to_f32(scl[g]);
+                    const uint32_t zw = AO ? zl[g] : zv[AO ? 0 : tl][i];
+                    const float zb = -(float)(kCodeBias + ((zw >> zsh) & 15u));
+                    const float s = f16_bits_to_f32(AO ? scl[g] : (uint16_t)sv[AO ? 0 : tl][i]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         acc[tl][e] = fmaf(s, fmaf(zb, Sv[i][e], d[e]), acc[tl][e]);

@@ -32,8 +32,9 @@ def _asm(tmp_path_factory, name):
 
 # source, the fewest DMA waits it must contain: the chunked and the DMA private modes
 # in the single and the batched skinny kernels; the act-order instances of the M = 1
-# kernel (X of the row by DMA, perm and the codes after it); every block instance
-@pytest.mark.parametrize("name,least", [("skinny.hip", 24), ("gemv.hip", 2), ("block.hip", 8)])
+# kernel (X of the row by DMA, perm and the codes after it); the act-order instances of
+# the block kernel (X rows, perm, scales and zero words by DMA)
+@pytest.mark.parametrize("name,least", [("skinny.hip", 24), ("gemv.hip", 2), ("block.hip", 6)])
 def test_every_dma_wait_covers_the_dma(tmp_path_factory, name, least):
     skinny_asm = _asm(tmp_path_factory, name)
     kern, last_dma, after = None, None, 0
