@@ -67,7 +67,8 @@ __device__ __forceinline__ bf16x8_t frag_b(uint32_t w, uint32_t mask, uint32_t b
     return __builtin_bit_cast(bf16x8_t, r);
 }
 
-// rows 4 (l / 16) .. + 3 of column 16 t + l % 16 of Y (those inside M x N)
+// rows 4 (l / 16) .. + 3 of column 16 t + l % 16 of Y (those inside M x N), by buffer
+// stores at 32-bit offsets (Y is below 2^31 bytes)
 __device__ __forceinline__ void store_rows(const BlockProb &pr, const BlockArgs &a, const f32x4_t &y, int t, int l,
                                            int M, int N)
 {
@@ -75,14 +76,17 @@ __device__ __forceinline__ void store_rows(const BlockProb &pr, const BlockArgs 
     const int r0 = 4 * (l >> 4);
     if (n >= N)
         return;
+    const uint32_t esz = a.y_f32 ? 4u : 2u;
+    const __amdgpu_buffer_rsrc_t ry = rsrc_b(pr.Y, (uint32_t)M * (uint32_t)N * esz);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = r0 + i;
         if (r < M) {
+            const uint32_t off = ((uint32_t)r * (uint32_t)N + (uint32_t)n) * esz;
             if (a.y_f32)
-                ((float *)pr.Y)[(size_t)r * N + n] = y[i];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[i]), ry, off, 0, 0);
             else
-                ((uint16_t *)pr.Y)[(size_t)r * N + n] = f32_to_bf16_rne(y[i]);
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(y[i]), ry, off, 0, 0);
         }
     }
 }

@@ -43,13 +43,15 @@ __device__ __forceinline__ bf16x8_t codes_to_frag(uint32_t w)
 
 // 8 consecutive bf16 activations x0..x7 (4 dwords, little-endian pairs) ->
 // the same order as codes_to_frag: x0 x4 x1 x5 x2 x6 x3 x7
+// One byte permute per dword: v_perm_b32(hi, lo, sel) picks result byte i from the
+// eight bytes lo (selectors 0..3) and hi (4..7).
 __device__ __forceinline__ u32x4_t x_permute8(u32x4_t d)
 {
     u32x4_t r;
-    r.x = (d.x & 0xFFFFu) | (d.z << 16);
-    r.y = (d.x >> 16) | (d.z & 0xFFFF0000u);
-    r.z = (d.y & 0xFFFFu) | (d.w << 16);
-    r.w = (d.y >> 16) | (d.w & 0xFFFF0000u);
+    r.x = __builtin_amdgcn_perm(d.z, d.x, 0x05040100u); // x0 x4
+    r.y = __builtin_amdgcn_perm(d.z, d.x, 0x07060302u); // x1 x5
+    r.z = __builtin_amdgcn_perm(d.w, d.y, 0x05040100u); // x2 x6
+    r.w = __builtin_amdgcn_perm(d.w, d.y, 0x07060302u); // x3 x7
     return r;
 }
 
