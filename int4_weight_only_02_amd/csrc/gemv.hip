@@ -244,22 +244,33 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
         }
     }
 
-    // 5. lane (c + TC p, 0) holds column c's sum over the wave's groups of part p; the
-    //    partials are added in wave order, then part order
+    // 5. lane (c + TC p, 0) holds column c's sum over the wave's groups of part p.  Wave
+    //    0 adds the W waves' partials in a fixed tree: lane slot + 16 k adds those of
+    //    waves k, k + 4, ... (all its reads in flight together), the four lane rows are
+    //    added by two exchanges, then the parts p by log2(PL) more
     if (lane < 16)
         red[w * 16 + lane] = acc;
     __syncthreads();
-    if (w == 0 && lane < TC) {
+    if (w == 0) {
+        const int slot = lane & 15, k = lane >> 4;
         float y = 0.f;
-        for (int v = 0; v < W; ++v)
 #pragma unroll
-            for (int q = 0; q < PL; ++q)
-                y += red[v * 16 + lane + TC * q];
-        const int col = blockIdx.x * TC + lane;
-        if (a.y_f32)
-            ((float *)a.Y)[col] = y;
-        else
-            ((uint16_t *)a.Y)[col] = f32_to_bf16_rne(y);
+        for (int v4 = 0; v4 < kGemvMaxWaves; v4 += 4)
+            if (v4 < W)
+                y += v4 + k < W ? red[(v4 + k) * 16 + slot] : 0.f;
+        y += __shfl_xor(y, 16);
+        y += __shfl_xor(y, 32);
+        if constexpr (PL >= 2)
+            y += __shfl_xor(y, TC);
+        if constexpr (PL >= 4)
+            y += __shfl_xor(y, 2 * TC);
+        if (lane < TC) {
+            const int col = blockIdx.x * TC + lane;
+            if (a.y_f32)
+                ((float *)a.Y)[col] = y;
+            else
+                ((uint16_t *)a.Y)[col] = f32_to_bf16_rne(y);
+        }
     }
 }
 
