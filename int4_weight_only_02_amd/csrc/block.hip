@@ -20,9 +20,12 @@
 //     four v_mfma_f32_16x16x32_bf16 on the exact biased codes 128 + q (every product
 //     exact in fp32), P = sum x * (128 + q); the bias and the zero-point come out in
 //     fp32 with the row sums S of X over the group: acc += s * (P - (128 + z) * S).
-//   * The scales and zero words of the workgroup's columns (contiguous runs) come in
-//     by LDS DMA; the waves' K-slice accumulators are added through LDS in slice
-//     order.  All sums run in a fixed order: results are deterministic.
+//   * Each wave needs the scale and zero word of every (tile, group) pair of its slice,
+//     the same value on the four lane rows of a column.  So lane row h loads them for
+//     pair 4j + h (one instruction per four pairs, not one per pair), and two lane
+//     swaps hand each value to all four rows when its fold runs.  The waves' K-slice
+//     accumulators are added through LDS in slice order.  All sums run in a fixed
+//     order: results are deterministic.
 //   * Act-order (GPTQ g_idx, codes stored in the permuted order; Pith review,
 //     Assumptions & free parameters): the contraction needs X'[r][k] = X[r][perm[k]].
 //     For a projection whose X rows fit in LDS, the workgroup brings the rows and perm
@@ -111,6 +114,17 @@ __device__ __forceinline__ void transpose_rows4(u32x4_t (&v)[4])
             v[j + 1][e] = r[1];
         }
     }
+}
+
+// the value that lane row r (of four) holds in v, on every lane row (column by column):
+// swapping rows 0 <-> 1 and 2 <-> 3 gives [v0 v0 v2 v2] and [v1 v1 v3 v3], swapping the
+// halves of the one that holds row r gives row r on all four
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v, int r)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    const uint32_t x = (r & 1) ? p[1] : p[0];
+    const auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (r & 2) ? q[1] : q[0];
 }
 
 // LDS DMA: 16 bytes per lane from offset voff of r into LDS at dst + 16 * lane
@@ -229,22 +243,22 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
                                                         : kOobB);
     }
 
-    // 3. the plain path: the scale and zero word of each (tile, group) of the lane's
-    //    column; then the codes of every (tile, group) of the slice
-    uint32_t sv[AO ? 1 : TMAX][GPW], zv[AO ? 1 : TMAX][GPW];
+    // 3. the plain path: the scale and zero word of (tile, group) pair 4j + h (pairs
+    //    numbered tile-major) of the lane's column; then the codes of every (tile, group)
+    //    of the slice
+    constexpr int PB = (TMAX * GPW + 3) / 4;
+    uint32_t sv[AO ? 1 : PB], zv[AO ? 1 : PB];
     if constexpr (!AO) {
 #pragma unroll
-        for (int tl = 0; tl < TMAX; ++tl)
-#pragma unroll
-            for (int i = 0; i < GPW; ++i) {
-                const int n = (t0 + tl) * 16 + c;
-                const bool live = tl < T && i < gn && n < N;
-                const uint32_t g = (uint32_t)(g0 + i);
-                sv[tl][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, live ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobB,
-                                                                 0, 0);
-                zv[tl][i] = __builtin_amdgcn_raw_buffer_load_b32(
-                    rz, live ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobB, 0, 0);
-            }
+        for (int j = 0; j < PB; ++j) {
+            const int pp = 4 * j + h, tl = pp / GPW, i = pp - tl * GPW;
+            const int n = (t0 + tl) * 16 + c;
+            const bool live = tl < T && i < gn && n < N;
+            const uint32_t g = (uint32_t)(g0 + i);
+            sv[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, live ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobB, 0, 0);
+            zv[j] = __builtin_amdgcn_raw_buffer_load_b32(rz, live ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobB,
+                                                         0, 0);
+        }
     }
     u32x4_t wv[TMAX][GPW];
 #pragma unroll
@@ -346,9 +360,10 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
                     d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][1]), frag_b(wv[tl][i].y, mask, bias), d);
                     d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][2]), frag_b(wv[tl][i].z, mask, bias), d);
                     d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][3]), frag_b(wv[tl][i].w, mask, bias), d);
-                    const uint32_t zw = AO ? zl[g] : zv[AO ? 0 : tl][i];
+                    const int pp = tl * GPW + i;
+                    const uint32_t zw = AO ? zl[g] : row_bcast(zv[AO ? 0 : pp >> 2], pp & 3);
                     const float zb = -(float)(kCodeBias + ((zw >> zsh) & 15u));
-                    const float s = f16_bits_to_f32(AO ? scl[g] : (uint16_t)sv[AO ? 0 : tl][i]);
+                    const float s = f16_bits_to_f32(AO ? scl[g] : (uint16_t)row_bcast(sv[AO ? 0 : pp >> 2], pp & 3));
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         acc[tl][e] = fmaf(s, fmaf(zb, Sv[i][e], d[e]), acc[tl][e]);
