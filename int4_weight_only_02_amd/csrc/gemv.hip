@@ -75,6 +75,18 @@ __device__ __forceinline__ float row_sum16(float v)
     return v;
 }
 
+// lane row 0 receives what lane row r (0, 1 or 2) holds in v, column by column (the
+// other rows receive other rows' values): a swap of rows 0 <-> 1 and 2 <-> 3, or of the
+// wave halves
+__device__ __forceinline__ uint32_t to_row0(uint32_t v, int r)
+{
+    if (r == 1)
+        return __builtin_amdgcn_permlane16_swap(v, v, false, false)[1];
+    if (r == 2)
+        return __builtin_amdgcn_permlane32_swap(v, v, false, false)[1];
+    return v;
+}
+
 // 8 codes -> MFMA fragment (bf16 128 + q), mask and bias held in registers
 __device__ __forceinline__ bf16x8_t frag_r(uint32_t w, uint32_t mask, uint32_t bias)
 {
@@ -161,17 +173,18 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
     }
     asm volatile("" ::: "memory");
 
-    // 2. the scale and zero word of each (column, group) pair of the lane, then the
-    //    codes: instruction i, lane (c + TC p, h) loads bytes 16h .. of group g0 + i PL + p
-    //    of column n.  The small parameter loads go first, so that they do not queue
-    //    behind the code loads
-    uint32_t sv[GPW], zv[GPW];
-#pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-        const int g = g0 + i * PL + p;
-        sv[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, g < G ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobG, 0, 0);
-        zv[i] = __builtin_amdgcn_raw_buffer_load_b32(rz, g < G ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobG,
-                                                     0, 0);
+    // 2. the scale and zero word of the lane's column for instruction i = h (group
+    //    g0 + h PL + p: lane row h loads what row 0 folds at instruction h, one load for
+    //    all GPW instructions), then the codes: instruction i, lane (c + TC p, h) loads
+    //    bytes 16h .. of group g0 + i PL + p of column n.  The small parameter loads go
+    //    first, so that they do not queue behind the code loads
+    static_assert(GPW <= 3, "one lane row per instruction, delivered to row 0 by one swap");
+    uint32_t sv, zv;
+    {
+        const int g = g0 + h * PL + p;
+        const bool live = h < GPW && g < G;
+        sv = __builtin_amdgcn_raw_buffer_load_b16(rs, live ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobG, 0, 0);
+        zv = __builtin_amdgcn_raw_buffer_load_b32(rz, live ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobG, 0, 0);
     }
     u32x4_t wv[GPW];
 #pragma unroll
@@ -238,8 +251,8 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
                 d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf), frag_r(wj, mask, bias), d);
             }
             const bool live = g0 + i * PL + p < G;
-            const float s = live ? f16_bits_to_f32((uint16_t)sv[i]) : 0.f;
-            const float zb = -(float)(kCodeBias + ((zv[i] >> zsh) & 15u));
+            const float s = live ? f16_bits_to_f32((uint16_t)to_row0(sv, i)) : 0.f;
+            const float zb = -(float)(kCodeBias + ((to_row0(zv, i) >> zsh) & 15u));
             acc = fmaf(s, fmaf(zb, Ss[i * PL + p], pick<PL>(d, p)), acc);
         }
     }
