@@ -45,6 +45,13 @@ constexpr int kRsrcWord3B = 0x00020000; // raw (untyped) buffer loads on gfx9-cl
 constexpr int kBlockCUs = 256;
 constexpr int kBlockLds = 160 * 1024 - 256; // the rest holds the kernel's static LDS
 
+// bytes of LDS per K slice when X goes through LDS (up to two groups per wave): the
+// slice's X (4 KB per group), later its partial sums (1 KB per tile)
+__host__ __device__ constexpr int block_xl_stride(int gpw, int tmax)
+{
+    return gpw * 4096 > tmax * 1024 ? gpw * 4096 : tmax * 1024;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_b(const void *p, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcWord3B);
@@ -210,16 +217,39 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
         asm volatile("" ::: "memory");
     }
 
-    // 2. the wave's K slice of X (rows past M read as 0).  The MFMAs need lane (r, h) to
-    //    hold X[r][(g0 + i) * 128 + 32h + 8j .. + 8] for j = 0..3 (the 64 bytes at 64h of
-    //    the group's row); load j instead brings the 16 bytes at 64j + 16h, so that the
-    //    four lanes of a row read 64 contiguous bytes per instruction, and a 4 x 4
-    //    transpose across the lane rows (below) puts each chunk in place.
+    // 2. the wave's K slice of X.  The MFMAs need lane (r, h) to hold
+    //    X[r][(g0 + i) * 128 + 32h + 8j .. + 8] for j = 0..3 (the 64 bytes at 64h of the
+    //    group's row).
+    //    Up to two groups per wave (XL): the wave pulls its slice into its own LDS region
+    //    by DMA in whole 128-byte lines (the load pipeline pays per line touched, so
+    //    half-used lines would cost about half as much again): instruction u of group i
+    //    brings rows 4u .. 4u+3, lane (c, h) the 16-byte chunk c ^ r of row r = 4u + h
+    //    into slot c, so that the sixteen lanes of a lane row, which read one chunk of
+    //    rows 0..15 below, find it in sixteen different slots (no bank conflicts).  Rows
+    //    past M are not read (no output row depends on them).  Only this wave reads the
+    //    region, after its own wait: no barrier.
+    //    Three groups per wave: load j brings the 16 bytes at 64j + 16h into registers,
+    //    so that the four lanes of a row read 64 contiguous bytes per instruction, and a
+    //    4 x 4 transpose across the lane rows (below) puts each chunk in place (rows past
+    //    M read as 0).
     //    Act-order: the M rows of X (LDS unit r U + (j ^ (r % 16)) holds unit j of row
     //    r, U = K / 8 units per row) and perm come in by DMA instead
+    constexpr bool XL = !AO && GPW <= 2;
     u32x4_t xf[GPW][4];
     const int U = pr.K / 8;
-    if constexpr (AO) {
+    unsigned char *xsl = lds + slice * block_xl_stride(GPW, TMAX); // XL: the slice's region
+    if constexpr (XL) {
+#pragma unroll
+        for (int i = 0; i < GPW; ++i)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = 4 * u + h;
+                dma16_b(rx, xsl + i * 4096 + u * 1024,
+                        (r < M && i < gn) ? (uint32_t)r * (uint32_t)pr.K * 2u + (uint32_t)(g0 + i) * 256u +
+                                                16u * (uint32_t)(c ^ r)
+                                          : kOobB);
+            }
+    } else if constexpr (AO) {
         const __amdgpu_buffer_rsrc_t rp = rsrc_b(a.perm, (uint32_t)pr.K * 4u);
         unsigned char *xa = lds + a.x_off;
         unsigned char *pa = lds + a.p_off;
@@ -275,6 +305,19 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     // compiler moves the arrangement of X (below) above the code loads and waits for X
     // first, so the codes' HBM latency would start only after X had arrived
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (XL) {
+        // the DMA was issued before the parameter and code loads: vmcnt(that many) means
+        // it has landed; then chunk 4h + j of row c sits in slot (4h + j) ^ c
+        constexpr int kAfter = 2 * PB + TMAX * GPW;
+        static_assert(kAfter < 64, "vmcnt is a 6-bit counter");
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (kAfter & 15) | ((kAfter >> 4) << 14));
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < GPW; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                xf[i][j] = *(const u32x4_t *)(xsl + i * 4096 + c * 256 + 16 * ((4 * h + j) ^ c));
+    }
     if constexpr (AO) {
         // the DMA of this wave was issued before its TMAX GPW register loads: vmcnt(that
         // many) means it has landed; the barrier makes every wave's part visible
@@ -324,7 +367,7 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     f32x4_t Sv[GPW];
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
-        if constexpr (!AO)
+        if constexpr (!AO && !XL)
             transpose_rows4(xf[i]);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -373,21 +416,25 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     }
 
     // 5. the K slices of each tile added in slice order; lane (c, h) holds rows 4h .. 4h+3
-    //    of column c
-    f32x4_t *red = (f32x4_t *)(lds + a.r_off); // [W][TMAX][64]
+    //    of column c.  Slice v's partial sums of tile tl: XL, in the slice's own region
+    //    (its X is no longer read); else [W][TMAX][64] from r_off
+    auto slice_acc = [&](int v, int tl) -> f32x4_t * {
+        return XL ? (f32x4_t *)(lds + v * block_xl_stride(GPW, TMAX) + tl * 1024)
+                  : (f32x4_t *)(lds + a.r_off) + (v * TMAX + tl) * 64;
+    };
 #pragma unroll
     for (int tl = 0; tl < TMAX; ++tl)
         if (tl < T)
-            red[(slice * TMAX + tl) * 64 + lane] = acc[tl];
+            slice_acc(slice, tl)[lane] = acc[tl];
     __syncthreads();
     __shared__ int s_last;
     float *pb = (float *)(a.ws + pr.part_off) + (size_t)tg * P * pr.tmx * 256; // [part][tmx * 64][4]
     uint32_t *ctr = (uint32_t *)(a.ws + kOffCounters) + (size_t)(pr.tkt + tg) * kCounterStride;
     for (int e = threadIdx.x; e < T * 64; e += W * 64) {
         const int tl = e >> 6, l = e & 63;
-        f32x4_t y = red[tl * 64 + l];
+        f32x4_t y = slice_acc(0, tl)[l];
         for (int v = 1; v < W; ++v) {
-            const f32x4_t o = red[(v * TMAX + tl) * 64 + l];
+            const f32x4_t o = slice_acc(v, tl)[l];
             y[0] += o[0];
             y[1] += o[1];
             y[2] += o[2];
@@ -525,7 +572,10 @@ BlockPlan plan_block(const int *N, const int *K, int count, int M, int tmax_hint
     const size_t zw = (size_t)((2 * p.tmax * gpmax + 63) / 64 * 64) * 4;
     p.z_off = (int)((sc + 15) / 16 * 16);
     p.r_off = (int)((p.z_off + zw + 15) / 16 * 16);
-    p.lds_bytes = (size_t)p.r_off + (size_t)W * p.tmax * 64 * 16;
+    // up to two groups per wave, X goes through LDS (one region per K slice); else the
+    // slice accumulators sit from r_off (the act-order plan lays X and perm over them)
+    p.lds_bytes = p.gpw <= 2 ? (size_t)W * block_xl_stride(p.gpw, p.tmax)
+                             : (size_t)p.r_off + (size_t)W * p.tmax * 64 * 16;
     p.ok = p.lds_bytes <= (size_t)kBlockLds;
     return p;
 }
@@ -543,7 +593,8 @@ BlockPlan plan_block_ao(int N, int K, int M)
     p.x_off = p.r_off;
     p.p_off = p.x_off + (M * (K / 8) + 63) / 64 * 64 * 16;
     const size_t need = (size_t)p.p_off + (size_t)(K / 4 + 63) / 64 * 64 * 16;
-    p.lds_bytes = need > p.lds_bytes ? need : p.lds_bytes;
+    const size_t acc = (size_t)p.r_off + (size_t)p.waves * p.tmax * 64 * 16;
+    p.lds_bytes = need > acc ? need : acc;
     p.ok = p.lds_bytes <= (size_t)kBlockLds;
     return p;
 }
