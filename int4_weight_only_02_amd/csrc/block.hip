@@ -494,13 +494,14 @@ static size_t block_ws_bytes(int N, int T, int P)
 // Measured on MI355X at M = 16 (graph replays, K = 2560 .. 9728, N = 1024 .. 19456): K
 // stays whole up to 47 groups (every CU reads all of X, and the hand-off of partial
 // sums between parts costs more than the X it saves); longer K is cut into parts of
-// about 13 groups, so each CU reads a part of X.  The tile groups then spread the
-// (tile group, part) workgroups of the whole launch about once over the CUs, at most
-// 5 tiles each.
+// at most 16 groups, so each CU reads a part of X (at K = 9728: 5 parts of 8 waves,
+// 0.2 us faster than 4 or 6 parts, 3 us faster than 7 or 8).  The tile groups then
+// spread the (tile group, part) workgroups of the whole launch about once over the
+// CUs, at most 5 tiles each.
 static int block_parts(int K)
 {
     const int G = K / kGroup;
-    return G < 48 ? 1 : (G + 12) / 13;
+    return G < 48 ? 1 : (G + 15) / 16;
 }
 
 // Per projection the tile-group size T and the parts of K P (block_choose, or the
