@@ -4,8 +4,9 @@
 // multiply-add, so the kernel is shaped around getting the whole stream in flight
 // with as few load instructions as possible:
 //
-//   * A workgroup owns TC = 16 / PL adjacent columns and all of K.  Its W waves
-//     split K: wave w takes the NG = GPW * PL groups from w * NG.  The grid is
+//   * A workgroup owns TC = 16 / PL adjacent columns (or TC = 5 with PL = 3, the 16th
+//     lane column idle, where that makes the grid whole rounds of the CUs) and all of
+//     K.  Its W waves split K: wave w takes the NG = GPW * PL groups from w * NG.  The grid is
 //     N / TC small workgroups, so every CU holds many waves and all of its bytes
 //     are requested at once; each lane issues GPW 128-bit code loads plus the
 //     scale and zero word of each of its (column, group) pairs.
@@ -75,15 +76,19 @@ __device__ __forceinline__ float row_sum16(float v)
     return v;
 }
 
-// lane row 0 receives what lane row r (0, 1 or 2) holds in v, column by column (the
-// other rows receive other rows' values): a swap of rows 0 <-> 1 and 2 <-> 3, or of the
-// wave halves
+// lane row 0 receives what lane row r (0..3) holds in v, column by column (the other
+// rows receive other rows' values): a swap of rows 0 <-> 1 and 2 <-> 3, of the wave
+// halves, or both
 __device__ __forceinline__ uint32_t to_row0(uint32_t v, int r)
 {
     if (r == 1)
         return __builtin_amdgcn_permlane16_swap(v, v, false, false)[1];
     if (r == 2)
         return __builtin_amdgcn_permlane32_swap(v, v, false, false)[1];
+    if (r == 3) {
+        const uint32_t x = __builtin_amdgcn_permlane32_swap(v, v, false, false)[1];
+        return __builtin_amdgcn_permlane16_swap(x, x, false, false)[1];
+    }
     return v;
 }
 
@@ -119,7 +124,7 @@ __host__ __device__ constexpr int gemv_x_off(int W, int NG) { return W * NG * 25
 template <int GPW, int PL, bool AO>
 __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
 {
-    constexpr int TC = 16 / PL;             // columns per workgroup
+    constexpr int TC = PL == 3 ? 5 : 16 / PL; // columns per workgroup
     constexpr int NG = GPW * PL;            // groups per wave
     constexpr int XR = NG / 4;              // X slots per lane
     static_assert(NG <= kGemvMaxGroups && NG % 4 == 0, "a lane row's slots hold one group");
@@ -130,6 +135,7 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nid = lane & 15, h = lane >> 4;
     const int c = nid % TC, p = nid / TC;
+    const bool plive = p < PL; // PL = 3: lane column 15 idle
     const int n = blockIdx.x * TC + c;
     const int g0 = w * NG;
     const uint32_t rowb = (uint32_t)(K / 2);
@@ -178,11 +184,11 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
     //    all GPW instructions), then the codes: instruction i, lane (c + TC p, h) loads
     //    bytes 16h .. of group g0 + i PL + p of column n.  The small parameter loads go
     //    first, so that they do not queue behind the code loads
-    static_assert(GPW <= 3, "one lane row per instruction, delivered to row 0 by one swap");
+    static_assert(GPW <= 4, "one lane row per instruction");
     uint32_t sv, zv;
     {
         const int g = g0 + h * PL + p;
-        const bool live = h < GPW && g < G;
+        const bool live = h < GPW && g < G && plive;
         sv = __builtin_amdgcn_raw_buffer_load_b16(rs, live ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobG, 0, 0);
         zv = __builtin_amdgcn_raw_buffer_load_b32(rz, live ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobG, 0, 0);
     }
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
         const int g = g0 + i * PL + p;
-        wv[i] = ld16_g(rw, g < G ? (uint32_t)n * rowb + (uint32_t)g * 64u + 16u * h : kOobG);
+        wv[i] = ld16_g(rw, (g < G && plive) ? (uint32_t)n * rowb + (uint32_t)g * 64u + 16u * h : kOobG);
     }
     asm volatile("" ::: "memory");
 
@@ -250,7 +256,7 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
                 const uint32_t wj = j == 0 ? wv[i].x : j == 1 ? wv[i].y : j == 2 ? wv[i].z : wv[i].w;
                 d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf), frag_r(wj, mask, bias), d);
             }
-            const bool live = g0 + i * PL + p < G;
+            const bool live = g0 + i * PL + p < G && plive;
             const float s = live ? f16_bits_to_f32((uint16_t)to_row0(sv, i)) : 0.f;
             const float zb = -(float)(kCodeBias + ((to_row0(zv, i) >> zsh) & 15u));
             acc = fmaf(s, fmaf(zb, Ss[i * PL + p], pick<PL>(d, p)), acc);
@@ -260,7 +266,8 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
     // 5. lane (c + TC p, 0) holds column c's sum over the wave's groups of part p.  Wave
     //    0 adds the W waves' partials in a fixed tree: lane slot + 16 k adds those of
     //    waves k, k + 4, ... (all its reads in flight together), the four lane rows are
-    //    added by two exchanges, then the parts p by log2(PL) more
+    //    added by two exchanges, then the parts p by log2(PL) more (PL = 3: lane c adds
+    //    those of lanes c + 5 and c + 10)
     if (lane < 16)
         red[w * 16 + lane] = acc;
     __syncthreads();
@@ -273,10 +280,15 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
                 y += v4 + k < W ? red[(v4 + k) * 16 + slot] : 0.f;
         y += __shfl_xor(y, 16);
         y += __shfl_xor(y, 32);
-        if constexpr (PL >= 2)
-            y += __shfl_xor(y, TC);
-        if constexpr (PL >= 4)
-            y += __shfl_xor(y, 2 * TC);
+        if constexpr (PL == 3) {
+            const float y1 = __shfl(y, (lane + TC) & 63), y2 = __shfl(y, (lane + 2 * TC) & 63);
+            y = (y + y1) + y2;
+        } else {
+            if constexpr (PL >= 2)
+                y += __shfl_xor(y, TC);
+            if constexpr (PL >= 4)
+                y += __shfl_xor(y, 2 * TC);
+        }
         if (lane < TC) {
             const int col = blockIdx.x * TC + lane;
             if (a.y_f32)
@@ -293,7 +305,7 @@ GemvPlan plan_gemv_with(int N, int K, int gpw, int pl, int ao)
 {
     GemvPlan p{};
     const int G = K / kGroup;
-    const int tc = pl > 0 ? 16 / pl : 0;
+    const int tc = pl == 3 ? 5 : pl > 0 ? 16 / pl : 0;
     const int ng = gpw * pl;
     p.gpw = gpw;
     p.pl = pl;
@@ -301,7 +313,7 @@ GemvPlan plan_gemv_with(int N, int K, int gpw, int pl, int ao)
     p.waves = ng > 0 ? (G + ng - 1) / ng : 0;
     p.grid = tc > 0 ? N / tc : 0;
     p.lds_bytes = (size_t)gemv_x_off(p.waves, ng) + (ao ? (size_t)K * 2 : 0);
-    p.ok = N >= 1 && K >= kGroup && ((pl == 2 && gpw == 2) || (pl == 4 && gpw == 3)) && N % tc == 0 &&
+    p.ok = N >= 1 && K >= kGroup && ((pl == 2 && gpw == 2) || (pl == 4 && gpw == 3) || (pl == 3 && gpw == 4 && !ao)) && N % tc == 0 &&
            p.waves >= 1 && p.waves <= kGemvMaxWaves && p.lds_bytes <= (size_t)kGemvMaxLds;
     return p;
 }
@@ -311,9 +323,15 @@ GemvPlan plan_gemv(int N, int K, int ao)
     // measured on MI355X at M = 1 (graph replays over rotating weights): two groups of
     // 8 columns per instruction and 4 groups per wave up to 40 groups (5 waves of 8
     // columns at K = 2560), three instructions of 4 columns x 4 groups beyond (7 waves
-    // of 4 columns at K = 9728)
+    // of 4 columns at K = 9728), or four of 5 columns x 3 groups where N / 5 workgroups
+    // are whole rounds of the CUs (9728 -> 2560: 512 workgroups, two per CU, 6.15 us,
+    // against 640 as two or three per CU, 6.4 us)
     const int G = K / kGroup;
-    return G <= 40 ? plan_gemv_with(N, K, 2, 2, ao) : plan_gemv_with(N, K, 3, 4, ao);
+    if (G <= 40)
+        return plan_gemv_with(N, K, 2, 2, ao);
+    if (!ao && N % (5 * 256) == 0)
+        return plan_gemv_with(N, K, 4, 3, ao);
+    return plan_gemv_with(N, K, 3, 4, ao);
 }
 
 hipError_t launch_gemv(const GemvArgs &args, const GemvPlan &p, hipStream_t stream)
@@ -333,6 +351,7 @@ hipError_t launch_gemv(const GemvArgs &args, const GemvPlan &p, hipStream_t stre
         W4A16_GEMV_CASE(2, 2, 1)
         W4A16_GEMV_CASE(3, 4, 0)
         W4A16_GEMV_CASE(3, 4, 1)
+        W4A16_GEMV_CASE(4, 3, 0)
 #undef W4A16_GEMV_CASE
     default:
         return hipErrorInvalidValue;

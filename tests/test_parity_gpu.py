@@ -62,9 +62,11 @@ SMALL = [(1, 8, 128), (1, 512, 512), (2, 136, 384), (3, 1032, 1280), (5, 264, 25
          (7, 520, 5248), (16, 264, 5760), (12, 2568, 9728),
          # one row (the M = 1 kernel): sets of 4, 8 (X in LDS) and 16 groups, ragged last
          # sets, column counts below and above one column per CU and not a multiple of 16,
-         # and a K too long for it (the general small-M path takes over)
+         # and a K too long for it (the general small-M path takes over); workgroups of 5
+         # columns x 3 group parts (N a multiple of 1280, more than 40 groups) with a
+         # ragged last wave
          (1, 264, 1408), (1, 136, 1536), (1, 40, 5888), (1, 2568, 6144), (1, 1032, 16384),
-         (1, 9736, 2560), (1, 3000, 640), (1, 16, 36864)]
+         (1, 9736, 2560), (1, 3000, 640), (1, 16, 36864), (1, 1280, 5376), (1, 3840, 7808)]
 
 
 @pytest.mark.parametrize("M,N,K", SMALL)
