@@ -115,10 +115,9 @@ int w4a16_pack_actorder(const uint8_t *codes, const uint8_t *zeros, const int32_
 /*
  * w4a16_linear_actorder -- Y = X * W^T for an act-order grid packed by
  * w4a16_pack_actorder: X [M][K] bf16 in natural column order enters the
- * contraction as X'[m][k] = X[m][perm[k]].  Where X fits on chip (M = 1 up to 40
- * groups; 2 <= M <= 16 with K whole) the gather runs inside the kernel's X staging;
- * otherwise X' is written to the workspace first and the call proceeds as
- * w4a16_linear (same kernels, same accuracy bound).  An entry of perm outside
+ * contraction as X'[m][k] = X[m][perm[k]].  At M = 1 up to 40 groups the gather
+ * runs inside the kernel's X staging; otherwise X' is written to the workspace first
+ * and the call proceeds as w4a16_linear (same kernels, same accuracy bound).  An entry of perm outside
  * [0, K) reads X[m][K - 1].  workspace: at least
  * w4a16_workspace_bytes(W4A16_OP_LINEAR_ACTORDER, M, N, K, group) (the size of the
  * separate gather, whichever path runs).  Shapes and errors as w4a16_linear; perm

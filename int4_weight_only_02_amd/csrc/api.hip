@@ -209,24 +209,11 @@ int w4a16_linear_actorder(const void *X, const int32_t *perm, const uint32_t *qw
         return W4A16_ERR_NULL;
     if (misaligned(qweight) || misaligned(scales) || misaligned(qzeros) || misaligned(Y))
         return W4A16_ERR_ALIGN;
-    // M = 1 up to 40 groups, and 2 <= M <= 16 while the X rows fit in LDS: the gather
-    // runs inside the kernel's X staging
+    // M = 1 up to 40 groups: the gather runs inside the kernel's X staging (K values per
+    // workgroup).  Otherwise a gather launch writes the permuted X to the workspace and
+    // the plain linear reads it (for 2 <= M <= 16, a gather inside the draft-block
+    // kernel, from the X rows in LDS, measured 2 us slower at 16 x 2560 -> 9728)
     const GemvPlan gp = (M == 1 && K / kGroup <= 40) ? plan_gemv(N, K, 1) : GemvPlan{};
-    const BlockPlan bp = (M >= 2 && M <= 16) ? plan_block_ao(N, K, M) : BlockPlan{};
-    if (bp.ok) {
-        BlockArgs a{};
-        a.perm = perm;
-        a.pr[0].X = (const uint16_t *)X;
-        a.pr[0].qw = qweight;
-        a.pr[0].scales = (const uint16_t *)scales;
-        a.pr[0].qz = qzeros;
-        a.pr[0].Y = Y;
-        a.pr[0].N = N;
-        a.pr[0].K = K;
-        a.M = M;
-        a.y_f32 = y_dtype == W4A16_OUT_F32;
-        return launch_block(a, bp, (hipStream_t)stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
-    }
     if (gp.ok) {
         GemvArgs a{};
         a.X = (const uint16_t *)X;

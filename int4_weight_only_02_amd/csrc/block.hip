@@ -26,13 +26,9 @@
 //     swaps hand each value to all four rows when its fold runs.  The waves' K-slice
 //     accumulators are added through LDS in slice order.  All sums run in a fixed
 //     order: results are deterministic.
-//   * Act-order (GPTQ g_idx, codes stored in the permuted order; Pith review,
-//     Assumptions & free parameters): the contraction needs X'[r][k] = X[r][perm[k]].
-//     For a projection whose X rows fit in LDS, the workgroup brings the rows and perm
-//     in by DMA and each lane gathers its fragments from there, so the permuted copy
-//     of X is never written to HBM and no extra launch runs.  The rows sit in 16-byte
-//     units with the unit index XOR-ed by the row, so that the 16 rows a lane row
-//     reads at one k fall on 16 different banks.
+//   * Act-order (GPTQ g_idx) reaches this kernel with X already permuted by a gather
+//     launch: gathering inside it, from the X rows in LDS, measured 2 us slower (about
+//     40 thousand two-byte LDS reads per workgroup).
 #include "common.h"
 #include "kernels.h"
 
@@ -60,11 +56,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_b(const void *p, uint32_t
 __device__ __forceinline__ u32x4_t ld16_b(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
-__device__ __forceinline__ void dma4_b(__amdgpu_buffer_rsrc_t r, unsigned char *dst, uint32_t voff)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 4, voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8_t frag_b(uint32_t w, uint32_t mask, uint32_t bias)
@@ -141,15 +132,14 @@ __device__ __forceinline__ void dma16_b(__amdgpu_buffer_rsrc_t r, unsigned char 
 }
 
 // GPW: the most groups a wave's K slice holds; TMAX: the most tiles a workgroup owns;
-// AO: act-order (X gathered through perm in LDS; one projection, K whole); MULTI:
-// several projections in the launch.
+// MULTI: several projections in the launch.
 //
 // The arguments live in memory that every CU reads through its scalar cache, and each
 // read that depends on an earlier one costs a round trip to memory (about half a
 // microsecond on a cold cache).  So every argument is read at a fixed offset: one
 // projection reads pr[0] directly; several find their projection with one compare per
 // entry (all entries read at once), then read its fields, two round trips in all.
-template <int GPW, int TMAX, bool AO, bool MULTI>
+template <int GPW, int TMAX, bool MULTI>
 __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
 {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -189,35 +179,7 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     const __amdgpu_buffer_rsrc_t rz = rsrc_b(pr.qz, (uint32_t)(N / 8) * (uint32_t)G * 4u);
     const __amdgpu_buffer_rsrc_t rx = rsrc_b(pr.X, (uint32_t)M * (uint32_t)pr.K * 2u);
 
-    // 1. act-order: the scales and zero words of the part's groups for the workgroup's
-    //    columns (16 t0 .. 16 t1 - 1, zero rows 2 t0 .. 2 t1 - 1), by DMA of 4-byte
-    //    words, behind the barrier that the gathered X needs anyway: each column's run of
-    //    gnp halves sits in the wpr words from the one that holds its first half
-    //    ([row][wpr] words); the zero words as [zero row][gnp].  (The plain path loads
-    //    each lane's own scale and zero words below instead, and has no barrier before
-    //    its contraction.)
-    unsigned char *sc_lds = lds;
-    unsigned char *z_lds = lds + a.z_off;
-    const int wpr = gnp / 2 + 1;
-    if constexpr (AO) {
-        const int sc_units = 16 * T * wpr;
-        const int z_units = 2 * T * gnp;
-        for (int u0 = w * 64; u0 < sc_units; u0 += W * 64) {
-            const int u = u0 + lane;
-            const int row = u / wpr, wi = u - row * wpr;
-            const uint32_t first = ((uint32_t)(t0 * 16 + row) * (uint32_t)G + (uint32_t)ga) >> 1;
-            dma4_b(rs, sc_lds + u0 * 4, u < sc_units ? (first + (uint32_t)wi) * 4u : kOobB);
-        }
-        for (int u0 = w * 64; u0 < z_units; u0 += W * 64) {
-            const int u = u0 + lane;
-            const int row = u / gnp, gi = u - row * gnp;
-            dma4_b(rz, z_lds + u0 * 4,
-                   u < z_units ? ((uint32_t)(t0 * 2 + row) * (uint32_t)G + (uint32_t)(ga + gi)) * 4u : kOobB);
-        }
-        asm volatile("" ::: "memory");
-    }
-
-    // 2. the wave's K slice of X.  The MFMAs need lane (r, h) to hold
+    // 1. the wave's K slice of X.  The MFMAs need lane (r, h) to hold
     //    X[r][(g0 + i) * 128 + 32h + 8j .. + 8] for j = 0..3 (the 64 bytes at 64h of the
     //    group's row).
     //    Up to two groups per wave (XL): the wave pulls its slice into its own LDS region
@@ -232,11 +194,8 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     //    so that the four lanes of a row read 64 contiguous bytes per instruction, and a
     //    4 x 4 transpose across the lane rows (below) puts each chunk in place (rows past
     //    M read as 0).
-    //    Act-order: the M rows of X (LDS unit r U + (j ^ (r % 16)) holds unit j of row
-    //    r, U = K / 8 units per row) and perm come in by DMA instead
-    constexpr bool XL = !AO && GPW <= 2;
+    constexpr bool XL = GPW <= 2;
     u32x4_t xf[GPW][4];
-    const int U = pr.K / 8;
     unsigned char *xsl = lds + slice * block_xl_stride(GPW, TMAX); // XL: the slice's region
     if constexpr (XL) {
 #pragma unroll
@@ -249,20 +208,6 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
                                                 16u * (uint32_t)(c ^ r)
                                           : kOobB);
             }
-    } else if constexpr (AO) {
-        const __amdgpu_buffer_rsrc_t rp = rsrc_b(a.perm, (uint32_t)pr.K * 4u);
-        unsigned char *xa = lds + a.x_off;
-        unsigned char *pa = lds + a.p_off;
-        const int xunits = M * U, punits = pr.K / 4;
-        for (int u0 = w * 64; u0 < xunits; u0 += W * 64) {
-            const int u = u0 + lane;
-            const int r = u / U, j = (u - r * U) ^ (r & 15);
-            dma16_b(rx, xa + u0 * 16, u < xunits ? (uint32_t)r * (uint32_t)pr.K * 2u + 16u * (uint32_t)j : kOobB);
-        }
-        for (int u0 = w * 64; u0 < punits; u0 += W * 64) {
-            const int u = u0 + lane;
-            dma16_b(rp, pa + u0 * 16, u < punits ? 16u * (uint32_t)u : kOobB);
-        }
     } else {
 #pragma unroll
         for (int i = 0; i < GPW; ++i)
@@ -273,22 +218,19 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
                                                         : kOobB);
     }
 
-    // 3. the plain path: the scale and zero word of (tile, group) pair 4j + h (pairs
-    //    numbered tile-major) of the lane's column; then the codes of every (tile, group)
-    //    of the slice
+    // 2. the scale and zero word of (tile, group) pair 4j + h (pairs numbered tile-major)
+    //    of the lane's column; then the codes of every (tile, group) of the slice
     constexpr int PB = (TMAX * GPW + 3) / 4;
-    uint32_t sv[AO ? 1 : PB], zv[AO ? 1 : PB];
-    if constexpr (!AO) {
+    uint32_t sv[PB], zv[PB];
 #pragma unroll
-        for (int j = 0; j < PB; ++j) {
-            const int pp = 4 * j + h, tl = pp / GPW, i = pp - tl * GPW;
-            const int n = (t0 + tl) * 16 + c;
-            const bool live = tl < T && i < gn && n < N;
-            const uint32_t g = (uint32_t)(g0 + i);
-            sv[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, live ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobB, 0, 0);
-            zv[j] = __builtin_amdgcn_raw_buffer_load_b32(rz, live ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobB,
-                                                         0, 0);
-        }
+    for (int j = 0; j < PB; ++j) {
+        const int pp = 4 * j + h, tl = pp / GPW, i = pp - tl * GPW;
+        const int n = (t0 + tl) * 16 + c;
+        const bool live = tl < T && i < gn && n < N;
+        const uint32_t g = (uint32_t)(g0 + i);
+        sv[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, live ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobB, 0, 0);
+        zv[j] = __builtin_amdgcn_raw_buffer_load_b32(rz, live ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobB, 0,
+                                                     0);
     }
     u32x4_t wv[TMAX][GPW];
 #pragma unroll
@@ -318,42 +260,6 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
             for (int j = 0; j < 4; ++j)
                 xf[i][j] = *(const u32x4_t *)(xsl + i * 4096 + c * 256 + 16 * ((4 * h + j) ^ c));
     }
-    if constexpr (AO) {
-        // the DMA of this wave was issued before its TMAX GPW register loads: vmcnt(that
-        // many) means it has landed; the barrier makes every wave's part visible
-        constexpr int kAfter = TMAX * GPW;
-        static_assert(kAfter < 64, "vmcnt is a 6-bit counter");
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (kAfter & 15) | ((kAfter >> 4) << 14));
-        __syncthreads();
-    }
-
-    if constexpr (AO) {
-        // lane (c, h), fragment (i, j): X'[c][k .. k + 8), k = (g0 + i) 128 + 32h + 8j,
-        // gathered through perm (an entry past the row reads the row's last element);
-        // then a barrier, as the slice accumulators below reuse this LDS
-        const uint32_t *pa = (const uint32_t *)(lds + a.p_off);
-        const unsigned char *xa = lds + a.x_off + (size_t)c * U * 16;
-        const uint32_t last = (uint32_t)pr.K - 1u;
-#pragma unroll
-        for (int i = 0; i < GPW; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                xf[i][j] = u32x4_t{0u, 0u, 0u, 0u};
-                if (c < M && i < gn) {
-                    const int k = (g0 + i) * kGroup + 32 * h + 8 * j;
-                    const u32x4_t p0 = *(const u32x4_t *)(pa + k), p1 = *(const u32x4_t *)(pa + k + 4);
-                    uint32_t v[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t kk = min(e < 4 ? p0[e] : p1[e - 4], last);
-                        v[e] = *(const uint16_t *)(xa + (((kk >> 3) ^ (uint32_t)c) << 4) + ((kk & 7u) << 1));
-                    }
-                    xf[i][j] = u32x4_t{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
-                                       v[6] | (v[7] << 16)};
-                }
-            }
-        __syncthreads();
-    }
 
     // X in place (the fragment order of the codes), and S[r][g] = sum of row r of X over
     // group g from the matrix cores: four MFMAs of the group's X fragments against a B of
@@ -367,7 +273,7 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     f32x4_t Sv[GPW];
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
-        if constexpr (!AO && !XL)
+        if constexpr (!XL)
             transpose_rows4(xf[i]);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -379,7 +285,7 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
         Sv[i] = sv;
     }
 
-    // 4. per (tile, group): four MFMAs on the biased codes (P = sum x * (128 + q)), then
+    // 3. per (tile, group): four MFMAs on the biased codes (P = sum x * (128 + q)), then
     //    acc += s * (P - (128 + z) * S) in fp32
     uint32_t mask = 0x000F000Fu, bias = kBiasBits;
     asm volatile("" : "+v"(mask));
@@ -390,23 +296,18 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     for (int tl = 0; tl < TMAX; ++tl) {
         acc[tl] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (tl < T) {
-            const int srow = tl * 16 + c;
-            const uint16_t *scl = (const uint16_t *)sc_lds + srow * wpr * 2 +
-                                  (((t0 * 16 + srow) * G + ga) & 1) - ga;
-            const uint32_t *zl = (const uint32_t *)z_lds + (tl * 2 + (c >> 3)) * gnp - ga;
 #pragma unroll
             for (int i = 0; i < GPW; ++i) {
                 if (i < gn) {
-                    const int g = g0 + i;
                     f32x4_t d = {0.f, 0.f, 0.f, 0.f};
                     d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][0]), frag_b(wv[tl][i].x, mask, bias), d);
                     d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][1]), frag_b(wv[tl][i].y, mask, bias), d);
                     d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][2]), frag_b(wv[tl][i].z, mask, bias), d);
                     d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][3]), frag_b(wv[tl][i].w, mask, bias), d);
                     const int pp = tl * GPW + i;
-                    const uint32_t zw = AO ? zl[g] : row_bcast(zv[AO ? 0 : pp >> 2], pp & 3);
+                    const uint32_t zw = row_bcast(zv[pp >> 2], pp & 3);
                     const float zb = -(float)(kCodeBias + ((zw >> zsh) & 15u));
-                    const float s = f16_bits_to_f32(AO ? scl[g] : (uint16_t)row_bcast(sv[AO ? 0 : pp >> 2], pp & 3));
+                    const float s = f16_bits_to_f32((uint16_t)row_bcast(sv[pp >> 2], pp & 3));
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         acc[tl][e] = fmaf(s, fmaf(zb, Sv[i][e], d[e]), acc[tl][e]);
@@ -415,12 +316,12 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
         }
     }
 
-    // 5. the K slices of each tile added in slice order; lane (c, h) holds rows 4h .. 4h+3
+    // 4. the K slices of each tile added in slice order; lane (c, h) holds rows 4h .. 4h+3
     //    of column c.  Slice v's partial sums of tile tl: XL, in the slice's own region
-    //    (its X is no longer read); else [W][TMAX][64] from r_off
+    //    (its X is no longer read); else [W][TMAX][64] from the start of LDS
     auto slice_acc = [&](int v, int tl) -> f32x4_t * {
         return XL ? (f32x4_t *)(lds + v * block_xl_stride(GPW, TMAX) + tl * 1024)
-                  : (f32x4_t *)(lds + a.r_off) + (v * TMAX + tl) * 64;
+                  : (f32x4_t *)lds + (v * TMAX + tl) * 64;
     };
 #pragma unroll
     for (int tl = 0; tl < TMAX; ++tl)
@@ -567,35 +468,9 @@ BlockPlan plan_block(const int *N, const int *K, int count, int M, int tmax_hint
     if (p.gpw == 0 || p.tmax == 0)
         return p;
     p.waves = W;
-    // LDS: scales ([16 tmax][gpmax / 2 + 1] words) and zero words ([2 tmax][gpmax]), rounded up
-    // to whole DMA rounds; the slice accumulators [W][TMAX][64] of 16 B
-    const size_t sc = (size_t)((16 * p.tmax * (gpmax / 2 + 1) + 63) / 64 * 64) * 4;
-    const size_t zw = (size_t)((2 * p.tmax * gpmax + 63) / 64 * 64) * 4;
-    p.z_off = (int)((sc + 15) / 16 * 16);
-    p.r_off = (int)((p.z_off + zw + 15) / 16 * 16);
-    // up to two groups per wave, X goes through LDS (one region per K slice); else the
-    // slice accumulators sit from r_off (the act-order plan lays X and perm over them)
-    p.lds_bytes = p.gpw <= 2 ? (size_t)W * block_xl_stride(p.gpw, p.tmax)
-                             : (size_t)p.r_off + (size_t)W * p.tmax * 64 * 16;
-    p.ok = p.lds_bytes <= (size_t)kBlockLds;
-    return p;
-}
-
-// The plain plan of one projection, with the X rows (M K bf16) and perm (K int32) laid
-// over the slice accumulators (the kernel separates the two uses by a barrier).  K
-// stays whole, so the split-K cases (48 groups and more) take the separate gather.
-BlockPlan plan_block_ao(int N, int K, int M)
-{
-    BlockPlan p = plan_block(&N, &K, 1, M);
-    if (!p.ok || p.parts[0] != 1 || p.gpw > 2)
-        return BlockPlan{};
-    // both regions in whole DMA rounds (64 units of 16 bytes)
-    p.ao = 1;
-    p.x_off = p.r_off;
-    p.p_off = p.x_off + (M * (K / 8) + 63) / 64 * 64 * 16;
-    const size_t need = (size_t)p.p_off + (size_t)(K / 4 + 63) / 64 * 64 * 16;
-    const size_t acc = (size_t)p.r_off + (size_t)p.waves * p.tmax * 64 * 16;
-    p.lds_bytes = need > acc ? need : acc;
+    // LDS: up to two groups per wave, X goes through LDS (one region per K slice, later
+    // its slice accumulators); else the slice accumulators [W][TMAX][64] of 16 B
+    p.lds_bytes = p.gpw <= 2 ? (size_t)W * block_xl_stride(p.gpw, p.tmax) : (size_t)W * p.tmax * 64 * 16;
     p.ok = p.lds_bytes <= (size_t)kBlockLds;
     return p;
 }
@@ -605,17 +480,14 @@ BlockPlan plan_block_ao(int N, int K, int M)
 static hipError_t allow_block_lds(int)
 {
     const void *fns[] = {
-        (const void *)block_kernel<1, 1, false, false>, (const void *)block_kernel<1, 2, false, false>,
-        (const void *)block_kernel<1, 5, false, false>, (const void *)block_kernel<2, 1, false, false>,
-        (const void *)block_kernel<2, 2, false, false>, (const void *)block_kernel<2, 5, false, false>,
-        (const void *)block_kernel<3, 1, false, false>, (const void *)block_kernel<3, 2, false, false>,
-        (const void *)block_kernel<1, 1, false, true>,  (const void *)block_kernel<1, 2, false, true>,
-        (const void *)block_kernel<1, 5, false, true>,  (const void *)block_kernel<2, 1, false, true>,
-        (const void *)block_kernel<2, 2, false, true>,  (const void *)block_kernel<2, 5, false, true>,
-        (const void *)block_kernel<3, 1, false, true>,  (const void *)block_kernel<3, 2, false, true>,
-        (const void *)block_kernel<1, 1, true, false>,  (const void *)block_kernel<1, 2, true, false>,
-        (const void *)block_kernel<1, 5, true, false>,  (const void *)block_kernel<2, 1, true, false>,
-        (const void *)block_kernel<2, 2, true, false>,  (const void *)block_kernel<2, 5, true, false>};
+        (const void *)block_kernel<1, 1, false>, (const void *)block_kernel<1, 2, false>,
+        (const void *)block_kernel<1, 5, false>, (const void *)block_kernel<2, 1, false>,
+        (const void *)block_kernel<2, 2, false>, (const void *)block_kernel<2, 5, false>,
+        (const void *)block_kernel<3, 1, false>, (const void *)block_kernel<3, 2, false>,
+        (const void *)block_kernel<1, 1, true>,  (const void *)block_kernel<1, 2, true>,
+        (const void *)block_kernel<1, 5, true>,  (const void *)block_kernel<2, 1, true>,
+        (const void *)block_kernel<2, 2, true>,  (const void *)block_kernel<2, 5, true>,
+        (const void *)block_kernel<3, 1, true>,  (const void *)block_kernel<3, 2, true>};
     for (const void *f : fns) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kBlockLds);
         if (e != hipSuccess)
@@ -630,12 +502,6 @@ hipError_t launch_block(const BlockArgs &args, const BlockPlan &p, hipStream_t s
         return hipErrorInvalidValue;
     BlockArgs a = args;
     a.count = p.count;
-    a.z_off = p.z_off;
-    a.r_off = p.r_off;
-    a.x_off = p.x_off;
-    a.p_off = p.p_off;
-    if (p.ao && (p.count != 1 || !a.perm))
-        return hipErrorInvalidValue;
     for (int q = 0; q < p.count; ++q) {
         a.pr[q].wg0 = p.wg0[q];
         a.pr[q].nt = (a.pr[q].N + 15) / 16;
@@ -650,33 +516,27 @@ hipError_t launch_block(const BlockArgs &args, const BlockPlan &p, hipStream_t s
         return e;
     const dim3 grid(p.grid), block(64 * p.waves);
     const int multi = p.count > 1 ? 1 : 0;
-    switch (p.gpw * 1000 + p.tmax * 100 + (p.ao ? 10 : 0) + multi) {
-#define W4A16_BLOCK_CASE(GP, TM, AO, MU)                                                                       \
-    case GP * 1000 + TM * 100 + AO * 10 + MU:                                                                  \
-        hipLaunchKernelGGL((block_kernel<GP, TM, AO != 0, MU != 0>), grid, block, p.lds_bytes, stream, a);     \
+    switch (p.gpw * 1000 + p.tmax * 100 + multi) {
+#define W4A16_BLOCK_CASE(GP, TM, MU)                                                                           \
+    case GP * 1000 + TM * 100 + MU:                                                                            \
+        hipLaunchKernelGGL((block_kernel<GP, TM, MU != 0>), grid, block, p.lds_bytes, stream, a);              \
         break;
-        W4A16_BLOCK_CASE(1, 1, 0, 0)
-        W4A16_BLOCK_CASE(1, 2, 0, 0)
-        W4A16_BLOCK_CASE(1, 5, 0, 0)
-        W4A16_BLOCK_CASE(2, 1, 0, 0)
-        W4A16_BLOCK_CASE(2, 2, 0, 0)
-        W4A16_BLOCK_CASE(2, 5, 0, 0)
-        W4A16_BLOCK_CASE(3, 1, 0, 0)
-        W4A16_BLOCK_CASE(3, 2, 0, 0)
-        W4A16_BLOCK_CASE(1, 1, 0, 1)
-        W4A16_BLOCK_CASE(1, 2, 0, 1)
-        W4A16_BLOCK_CASE(1, 5, 0, 1)
-        W4A16_BLOCK_CASE(2, 1, 0, 1)
-        W4A16_BLOCK_CASE(2, 2, 0, 1)
-        W4A16_BLOCK_CASE(2, 5, 0, 1)
-        W4A16_BLOCK_CASE(3, 1, 0, 1)
-        W4A16_BLOCK_CASE(3, 2, 0, 1)
-        W4A16_BLOCK_CASE(1, 1, 1, 0)
-        W4A16_BLOCK_CASE(1, 2, 1, 0)
-        W4A16_BLOCK_CASE(1, 5, 1, 0)
-        W4A16_BLOCK_CASE(2, 1, 1, 0)
-        W4A16_BLOCK_CASE(2, 2, 1, 0)
-        W4A16_BLOCK_CASE(2, 5, 1, 0)
+        W4A16_BLOCK_CASE(1, 1, 0)
+        W4A16_BLOCK_CASE(1, 2, 0)
+        W4A16_BLOCK_CASE(1, 5, 0)
+        W4A16_BLOCK_CASE(2, 1, 0)
+        W4A16_BLOCK_CASE(2, 2, 0)
+        W4A16_BLOCK_CASE(2, 5, 0)
+        W4A16_BLOCK_CASE(3, 1, 0)
+        W4A16_BLOCK_CASE(3, 2, 0)
+        W4A16_BLOCK_CASE(1, 1, 1)
+        W4A16_BLOCK_CASE(1, 2, 1)
+        W4A16_BLOCK_CASE(1, 5, 1)
+        W4A16_BLOCK_CASE(2, 1, 1)
+        W4A16_BLOCK_CASE(2, 2, 1)
+        W4A16_BLOCK_CASE(2, 5, 1)
+        W4A16_BLOCK_CASE(3, 1, 1)
+        W4A16_BLOCK_CASE(3, 2, 1)
 #undef W4A16_BLOCK_CASE
     default:
         return hipErrorInvalidValue;

@@ -192,25 +192,17 @@ struct BlockArgs {
     BlockProb pr[kMaxProblemsBlock];
     int count, M, y_f32;
     unsigned char *ws;       // workspace base (partial sums, arrival counters)
-    const int32_t *perm;     // act-order plans (one projection, K whole): X'[k] = X[perm[k]]
-    int z_off, r_off;        // filled by launch_block
-    int x_off, p_off;        // act-order: LDS of the X rows and of perm
 };
 struct BlockPlan {
     int count, gpw, tmax, waves, grid;
-    int ao, x_off, p_off; // act-order plan: X rows and perm in LDS (over the slice accumulators)
     int wg0[kMaxProblemsBlock], ntg[kMaxProblemsBlock], parts[kMaxProblemsBlock], tmx[kMaxProblemsBlock];
     int tkt[kMaxProblemsBlock];
     size_t part_off[kMaxProblemsBlock];
-    int z_off, r_off;
     size_t lds_bytes, ws_bytes; // ws_bytes: 0 when no projection splits K
     bool ok;
 };
 BlockPlan plan_block(const int *N, const int *K, int count, int M, int tmax_hint = 0, int waves_hint = 0,
                      int parts_hint = 0);
-// one act-order projection with the gather of X folded into the kernel (K whole, the X
-// rows and perm in LDS); !ok when they do not fit
-BlockPlan plan_block_ao(int N, int K, int M);
 hipError_t launch_block(const BlockArgs &a, const BlockPlan &p, hipStream_t stream);
 // workspace of a single projection's block plan (the zero region included when K is split)
 size_t block_linear_ws(int M, int N, int K);

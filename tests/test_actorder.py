@@ -67,9 +67,8 @@ def test_pack_actorder_is_pack_of_permuted_codes():
 
 @pytest.mark.gpu
 # M = 1 (gathered inside the M = 1 kernel up to 40 groups, else by a separate launch),
-# 2 <= M <= 16 (inside the block kernel while the X rows fit in LDS and K stays whole:
-# odd group counts and row counts whose LDS regions end inside a DMA round included;
-# K = 9728 takes the separate gather), and M > 16
+# 2 <= M <= 16 and M > 16 (a gather launch, then the plain kernels: odd group counts,
+# row counts below 16, K split across workgroups at K = 9728)
 @pytest.mark.parametrize("M,N,K,sym", [(1, 520, 1280, False), (1, 136, 128, True), (1, 9728, 2560, False),
                                        (1, 2560, 9728, True), (1, 264, 6272, False), (2, 264, 384, True),
                                        (5, 264, 2560, True), (7, 520, 1408, False), (16, 1032, 2560, False),

@@ -32,9 +32,10 @@ def _asm(tmp_path_factory, name):
 
 # source, the fewest DMA waits it must contain: the chunked and the DMA private modes
 # in the single and the batched skinny kernels; the act-order instances of the M = 1
-# kernel (X of the row by DMA, perm and the codes after it); the act-order instances of
-# the block kernel (X rows, perm, scales and zero words by DMA)
-@pytest.mark.parametrize("name,least", [("skinny.hip", 24), ("gemv.hip", 2), ("block.hip", 6)])
+# kernel (X of the row by DMA, perm and the codes after it); the block kernel's
+# instances of up to two groups per wave (each wave's X slice by DMA, then its scale,
+# zero and code loads), single and batched
+@pytest.mark.parametrize("name,least", [("skinny.hip", 24), ("gemv.hip", 2), ("block.hip", 12)])
 def test_every_dma_wait_covers_the_dma(tmp_path_factory, name, least):
     skinny_asm = _asm(tmp_path_factory, name)
     kern, last_dma, after = None, None, 0
