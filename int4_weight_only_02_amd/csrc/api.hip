@@ -451,7 +451,25 @@ int w4a16_linear_gated(const void *X, const uint32_t *qweight_gate, const void *
         return W4A16_ERR_WORKSPACE;
 
     hipError_t e;
-    if (M <= kSkinnyMaxM) {
+    const BlockPlan bp = plan_block_gated(N, K, M);
+    if (bp.ok) {
+        // 2 <= M <= 16, K whole: the draft-block kernel with gate and up tiles of the same
+        // columns in each workgroup
+        BlockArgs a{};
+        for (int q = 0; q < 2; ++q) {
+            a.pr[q].X = (const uint16_t *)X;
+            a.pr[q].qw = q ? qweight_up : qweight_gate;
+            a.pr[q].scales = (const uint16_t *)(q ? scales_up : scales_gate);
+            a.pr[q].qz = q ? qzeros_up : qzeros_gate;
+            a.pr[q].Y = Y;
+            a.pr[q].N = N;
+            a.pr[q].K = K;
+        }
+        a.M = M;
+        a.y_f32 = y_dtype == W4A16_OUT_F32;
+        a.ws = (unsigned char *)workspace;
+        e = launch_block(a, bp, (hipStream_t)stream);
+    } else if (M <= kSkinnyMaxM) {
         // one launch: each workgroup holds gate and up tiles of the same columns
         const SkinnyPlan p = plan_skinny_pair(M, N, K);
         SkinnyArgs a{};

@@ -132,16 +132,22 @@ __device__ __forceinline__ void dma16_b(__amdgpu_buffer_rsrc_t r, unsigned char 
 }
 
 // GPW: the most groups a wave's K slice holds; TMAX: the most tiles a workgroup owns;
-// MULTI: several projections in the launch.
+// MODE 0: one projection; 1: several projections in the launch; 2: a gated pair (pr[0]
+// the gate, pr[1] the up projection, the same shape; K whole): tile slot 2u holds gate
+// tile t0 + u and slot 2u + 1 the up tile of the same columns, and the workgroup
+// stores silu(gate) * up (the MLP activation of the pages' target; Pith review,
+// Referee Report, Summary).
 //
 // The arguments live in memory that every CU reads through its scalar cache, and each
 // read that depends on an earlier one costs a round trip to memory (about half a
 // microsecond on a cold cache).  So every argument is read at a fixed offset: one
 // projection reads pr[0] directly; several find their projection with one compare per
 // entry (all entries read at once), then read its fields, two round trips in all.
-template <int GPW, int TMAX, bool MULTI>
+template <int GPW, int TMAX, int MODE>
 __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
 {
+    constexpr bool MULTI = MODE == 1, GATED = MODE == 2;
+    static_assert(!GATED || TMAX % 2 == 0, "gated slots come in pairs");
     extern __shared__ __align__(16) unsigned char lds[];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -161,7 +167,8 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     // tg * nt < 2^31: at most 2^16 tiles of 16 columns
     const int t0 = tg * pr.nt / pr.ntg;
     const int t1 = (tg + 1) * pr.nt / pr.ntg;
-    const int T = t1 - t0;
+    const int T = t1 - t0;            // column tiles
+    const int TS = GATED ? 2 * T : T; // live tile slots
     const int G = pr.K / kGroup, N = pr.N, M = a.M;
     const int Gp = (G + P - 1) / P;
     const int ga = part * Gp, gnp = min(Gp, G - ga); // the part's groups [ga, ga + gnp)
@@ -178,6 +185,11 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     const __amdgpu_buffer_rsrc_t rs = rsrc_b(pr.scales, (uint32_t)N * (uint32_t)G * 2u);
     const __amdgpu_buffer_rsrc_t rz = rsrc_b(pr.qz, (uint32_t)(N / 8) * (uint32_t)G * 4u);
     const __amdgpu_buffer_rsrc_t rx = rsrc_b(pr.X, (uint32_t)M * (uint32_t)pr.K * 2u);
+    // gated: the up projection's grid (the same shape)
+    const BlockProb &pu = a.pr[GATED ? 1 : 0];
+    const __amdgpu_buffer_rsrc_t rw2 = GATED ? rsrc_b(pu.qw, (uint32_t)N * rowb) : rw;
+    const __amdgpu_buffer_rsrc_t rs2 = GATED ? rsrc_b(pu.scales, (uint32_t)N * (uint32_t)G * 2u) : rs;
+    const __amdgpu_buffer_rsrc_t rz2 = GATED ? rsrc_b(pu.qz, (uint32_t)(N / 8) * (uint32_t)G * 4u) : rz;
 
     // 1. the wave's K slice of X.  The MFMAs need lane (r, h) to hold
     //    X[r][(g0 + i) * 128 + 32h + 8j .. + 8] for j = 0..3 (the 64 bytes at 64h of the
@@ -218,29 +230,36 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
                                                         : kOobB);
     }
 
-    // 2. the scale and zero word of (tile, group) pair 4j + h (pairs numbered tile-major)
-    //    of the lane's column; then the codes of every (tile, group) of the slice
-    constexpr int PB = (TMAX * GPW + 3) / 4;
-    uint32_t sv[PB], zv[PB];
+    // 2. the scale and zero word of (column tile, group) pair 4j + h (pairs numbered
+    //    tile-major) of the lane's column (gated: of each projection in turn, one buffer
+    //    per instruction); then the codes of every (tile slot, group) of the slice
+    constexpr int TC = GATED ? TMAX / 2 : TMAX; // column tiles
+    constexpr int PB = (TC * GPW + 3) / 4;      // parameter loads per projection
+    constexpr int NPB = GATED ? 2 * PB : PB;
+    uint32_t sv[NPB], zv[NPB];
 #pragma unroll
-    for (int j = 0; j < PB; ++j) {
-        const int pp = 4 * j + h, tl = pp / GPW, i = pp - tl * GPW;
-        const int n = (t0 + tl) * 16 + c;
-        const bool live = tl < T && i < gn && n < N;
-        const uint32_t g = (uint32_t)(g0 + i);
-        sv[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, live ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobB, 0, 0);
-        zv[j] = __builtin_amdgcn_raw_buffer_load_b32(rz, live ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobB, 0,
-                                                     0);
-    }
+    for (int sp = 0; sp < (GATED ? 2 : 1); ++sp)
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const int pp = 4 * j + h, u = pp / GPW, i = pp - u * GPW;
+            const int n = (t0 + u) * 16 + c;
+            const bool live = u < T && i < gn && n < N;
+            const uint32_t g = (uint32_t)(g0 + i);
+            sv[sp * PB + j] = __builtin_amdgcn_raw_buffer_load_b16(
+                sp ? rs2 : rs, live ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobB, 0, 0);
+            zv[sp * PB + j] = __builtin_amdgcn_raw_buffer_load_b32(
+                sp ? rz2 : rz, live ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobB, 0, 0);
+        }
     u32x4_t wv[TMAX][GPW];
 #pragma unroll
     for (int tl = 0; tl < TMAX; ++tl)
 #pragma unroll
         for (int i = 0; i < GPW; ++i) {
-            const int n = (t0 + tl) * 16 + c;
-            wv[tl][i] = ld16_b(rw, (tl < T && i < gn && n < N)
-                                       ? (uint32_t)n * rowb + (uint32_t)(g0 + i) * 64u + 16u * h
-                                       : kOobB);
+            const int u = GATED ? tl >> 1 : tl;
+            const int n = (t0 + u) * 16 + c;
+            wv[tl][i] = ld16_b((GATED && (tl & 1)) ? rw2 : rw,
+                               (u < T && i < gn && n < N) ? (uint32_t)n * rowb + (uint32_t)(g0 + i) * 64u + 16u * h
+                                                          : kOobB);
         }
     asm volatile("" ::: "memory");
     // every load of the wave is issued before any arithmetic on X: left to itself the
@@ -250,7 +269,7 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     if constexpr (XL) {
         // the DMA was issued before the parameter and code loads: vmcnt(that many) means
         // it has landed; then chunk 4h + j of row c sits in slot (4h + j) ^ c
-        constexpr int kAfter = 2 * PB + TMAX * GPW;
+        constexpr int kAfter = 2 * NPB + TMAX * GPW;
         static_assert(kAfter < 64, "vmcnt is a 6-bit counter");
         __builtin_amdgcn_s_waitcnt(0x0F70 | (kAfter & 15) | ((kAfter >> 4) << 14));
         asm volatile("" ::: "memory");
@@ -295,7 +314,7 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
 #pragma unroll
     for (int tl = 0; tl < TMAX; ++tl) {
         acc[tl] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (tl < T) {
+        if (tl < TS) {
 #pragma unroll
             for (int i = 0; i < GPW; ++i) {
                 if (i < gn) {
@@ -304,10 +323,11 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
                     d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][1]), frag_b(wv[tl][i].y, mask, bias), d);
                     d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][2]), frag_b(wv[tl][i].z, mask, bias), d);
                     d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf[i][3]), frag_b(wv[tl][i].w, mask, bias), d);
-                    const int pp = tl * GPW + i;
-                    const uint32_t zw = row_bcast(zv[pp >> 2], pp & 3);
+                    const int pp = (GATED ? tl >> 1 : tl) * GPW + i;
+                    const int pb = (GATED && (tl & 1)) ? PB : 0;
+                    const uint32_t zw = row_bcast(zv[pb + (pp >> 2)], pp & 3);
                     const float zb = -(float)(kCodeBias + ((zw >> zsh) & 15u));
-                    const float s = f16_bits_to_f32((uint16_t)row_bcast(sv[pp >> 2], pp & 3));
+                    const float s = f16_bits_to_f32((uint16_t)row_bcast(sv[pb + (pp >> 2)], pp & 3));
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         acc[tl][e] = fmaf(s, fmaf(zb, Sv[i][e], d[e]), acc[tl][e]);
@@ -325,7 +345,7 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     };
 #pragma unroll
     for (int tl = 0; tl < TMAX; ++tl)
-        if (tl < T)
+        if (tl < TS)
             slice_acc(slice, tl)[lane] = acc[tl];
     __syncthreads();
     __shared__ int s_last;
@@ -333,15 +353,32 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
     uint32_t *ctr = (uint32_t *)(a.ws + kOffCounters) + (size_t)(pr.tkt + tg) * kCounterStride;
     for (int e = threadIdx.x; e < T * 64; e += W * 64) {
         const int tl = e >> 6, l = e & 63;
-        f32x4_t y = slice_acc(0, tl)[l];
-        for (int v = 1; v < W; ++v) {
-            const f32x4_t o = slice_acc(v, tl)[l];
-            y[0] += o[0];
-            y[1] += o[1];
-            y[2] += o[2];
-            y[3] += o[3];
+        f32x4_t y;
+        if constexpr (GATED) {
+            // the gate and up sums of column tile tl (K whole), then silu(gate) * up
+            f32x4_t yg = slice_acc(0, 2 * tl)[l], yu = slice_acc(0, 2 * tl + 1)[l];
+            for (int v = 1; v < W; ++v) {
+                const f32x4_t og = slice_acc(v, 2 * tl)[l], ou = slice_acc(v, 2 * tl + 1)[l];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    yg[i] += og[i];
+                    yu[i] += ou[i];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                y[i] = silu_f32(yg[i]) * yu[i];
+        } else {
+            y = slice_acc(0, tl)[l];
+            for (int v = 1; v < W; ++v) {
+                const f32x4_t o = slice_acc(v, tl)[l];
+                y[0] += o[0];
+                y[1] += o[1];
+                y[2] += o[2];
+                y[3] += o[3];
+            }
         }
-        if (P == 1) {
+        if (GATED || P == 1) {
             store_rows(pr, a, y, t0 + tl, l, M, N);
         } else {
             // the part's partial sums, device-coherent, for the tile group's last arriver
@@ -351,7 +388,7 @@ __global__ __launch_bounds__(1024) void block_kernel(BlockArgs a)
                 __hip_atomic_store(dst + i, y[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    if (P > 1) {
+    if (!GATED && P > 1) {
         // parts of K meet in the workspace: each part stores its partial sums, then takes
         // an arrival ticket; the last to arrive adds the P parts in part order and stores
         // Y, so the result does not depend on the arrival order
@@ -475,19 +512,54 @@ BlockPlan plan_block(const int *N, const int *K, int count, int M, int tmax_hint
     return p;
 }
 
+// A gated pair (gate and up of the same shape, 2 <= M <= 16) in one launch: column
+// tiles spread over the CUs about once (up to 3 per workgroup, i.e. 6 tile slots), K
+// whole (up to 47 groups), up to two groups per wave.  !ok otherwise.
+BlockPlan plan_block_gated(int N, int K, int M)
+{
+    BlockPlan p{};
+    const int G = K / kGroup;
+    if (M < 2 || M > 16 || block_parts(K) != 1 || G < 1)
+        return p;
+    const int nt = (N + 15) / 16;
+    int T = (nt + kBlockCUs - 1) / kBlockCUs;
+    T = T < 1 ? 1 : T;
+    if (T > 3)
+        return p;
+    const int ntg = (nt + T - 1) / T;
+    const int tmx = (nt + ntg - 1) / ntg;
+    p.count = 1;
+    p.gated = 1;
+    p.parts[0] = 1;
+    p.ntg[0] = ntg;
+    p.tmx[0] = tmx;
+    p.grid = ntg;
+    p.tmax = 2 * tmx;
+    int W = (G + 1) / 2;
+    W = W < 1 ? 1 : W > 16 ? 16 : W;
+    const int gpw = (G + W - 1) / W;
+    if (gpw > 2)
+        return p;
+    p.gpw = gpw;
+    p.waves = W;
+    p.lds_bytes = (size_t)W * block_xl_stride(p.gpw, p.tmax);
+    p.ok = p.lds_bytes <= (size_t)kBlockLds;
+    return p;
+}
+
 // every block kernel may use up to kBlockLds bytes of dynamic LDS (beyond the 64 KB
 // default); raised once per device
 static hipError_t allow_block_lds(int)
 {
     const void *fns[] = {
-        (const void *)block_kernel<1, 1, false>, (const void *)block_kernel<1, 2, false>,
-        (const void *)block_kernel<1, 5, false>, (const void *)block_kernel<2, 1, false>,
-        (const void *)block_kernel<2, 2, false>, (const void *)block_kernel<2, 5, false>,
-        (const void *)block_kernel<3, 1, false>, (const void *)block_kernel<3, 2, false>,
-        (const void *)block_kernel<1, 1, true>,  (const void *)block_kernel<1, 2, true>,
-        (const void *)block_kernel<1, 5, true>,  (const void *)block_kernel<2, 1, true>,
-        (const void *)block_kernel<2, 2, true>,  (const void *)block_kernel<2, 5, true>,
-        (const void *)block_kernel<3, 1, true>,  (const void *)block_kernel<3, 2, true>};
+        (const void *)block_kernel<1, 1, 0>, (const void *)block_kernel<1, 2, 0>, (const void *)block_kernel<1, 5, 0>,
+        (const void *)block_kernel<2, 1, 0>, (const void *)block_kernel<2, 2, 0>, (const void *)block_kernel<2, 5, 0>,
+        (const void *)block_kernel<3, 1, 0>, (const void *)block_kernel<3, 2, 0>, (const void *)block_kernel<1, 1, 1>,
+        (const void *)block_kernel<1, 2, 1>, (const void *)block_kernel<1, 5, 1>, (const void *)block_kernel<2, 1, 1>,
+        (const void *)block_kernel<2, 2, 1>, (const void *)block_kernel<2, 5, 1>, (const void *)block_kernel<3, 1, 1>,
+        (const void *)block_kernel<3, 2, 1>, (const void *)block_kernel<1, 2, 2>, (const void *)block_kernel<1, 4, 2>,
+        (const void *)block_kernel<1, 6, 2>, (const void *)block_kernel<2, 2, 2>, (const void *)block_kernel<2, 4, 2>,
+        (const void *)block_kernel<2, 6, 2>};
     for (const void *f : fns) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kBlockLds);
         if (e != hipSuccess)
@@ -515,11 +587,11 @@ hipError_t launch_block(const BlockArgs &args, const BlockPlan &p, hipStream_t s
     if (e != hipSuccess)
         return e;
     const dim3 grid(p.grid), block(64 * p.waves);
-    const int multi = p.count > 1 ? 1 : 0;
-    switch (p.gpw * 1000 + p.tmax * 100 + multi) {
-#define W4A16_BLOCK_CASE(GP, TM, MU)                                                                           \
-    case GP * 1000 + TM * 100 + MU:                                                                            \
-        hipLaunchKernelGGL((block_kernel<GP, TM, MU != 0>), grid, block, p.lds_bytes, stream, a);              \
+    const int mode = p.gated ? 2 : p.count > 1 ? 1 : 0;
+    switch (p.gpw * 1000 + p.tmax * 100 + mode) {
+#define W4A16_BLOCK_CASE(GP, TM, MO)                                                                           \
+    case GP * 1000 + TM * 100 + MO:                                                                            \
+        hipLaunchKernelGGL((block_kernel<GP, TM, MO>), grid, block, p.lds_bytes, stream, a);                   \
         break;
         W4A16_BLOCK_CASE(1, 1, 0)
         W4A16_BLOCK_CASE(1, 2, 0)
@@ -537,6 +609,12 @@ hipError_t launch_block(const BlockArgs &args, const BlockPlan &p, hipStream_t s
         W4A16_BLOCK_CASE(2, 5, 1)
         W4A16_BLOCK_CASE(3, 1, 1)
         W4A16_BLOCK_CASE(3, 2, 1)
+        W4A16_BLOCK_CASE(1, 2, 2)
+        W4A16_BLOCK_CASE(1, 4, 2)
+        W4A16_BLOCK_CASE(1, 6, 2)
+        W4A16_BLOCK_CASE(2, 2, 2)
+        W4A16_BLOCK_CASE(2, 4, 2)
+        W4A16_BLOCK_CASE(2, 6, 2)
 #undef W4A16_BLOCK_CASE
     default:
         return hipErrorInvalidValue;

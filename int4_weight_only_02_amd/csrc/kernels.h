@@ -195,6 +195,7 @@ struct BlockArgs {
 };
 struct BlockPlan {
     int count, gpw, tmax, waves, grid;
+    int gated; // a gated pair: pr[0] the gate, pr[1] the up projection (count 1)
     int wg0[kMaxProblemsBlock], ntg[kMaxProblemsBlock], parts[kMaxProblemsBlock], tmx[kMaxProblemsBlock];
     int tkt[kMaxProblemsBlock];
     size_t part_off[kMaxProblemsBlock];
@@ -203,6 +204,8 @@ struct BlockPlan {
 };
 BlockPlan plan_block(const int *N, const int *K, int count, int M, int tmax_hint = 0, int waves_hint = 0,
                      int parts_hint = 0);
+// a gated pair in one launch (silu(gate) * up); !ok where K is split or too long
+BlockPlan plan_block_gated(int N, int K, int M);
 hipError_t launch_block(const BlockArgs &a, const BlockPlan &p, hipStream_t stream);
 // workspace of a single projection's block plan (the zero region included when K is split)
 size_t block_linear_ws(int M, int N, int K);
