@@ -9,12 +9,15 @@
 // as or more than the CU's share of the weights).  The kernel is shaped for that:
 //
 //   * One workgroup per CU (or a few), each owning a balanced run of 16-column
-//     tiles and ALL of K, so no partial sum ever crosses a workgroup (a
-//     cross-workgroup hand-off costs several round trips through the memory side).
-//   * K is split over the workgroup's waves; each wave loads its K slice of X once,
-//     straight into registers as MFMA A fragments (lane (r, h): row r, k-block h),
-//     and keeps it for every tile of the workgroup.  X is therefore read once per
-//     CU, with no LDS staging and no barrier in front of it.
+//     tiles and all of K (or, for long K, a part of it), so partial sums cross
+//     workgroups only between the parts of K (a cross-workgroup hand-off costs
+//     several round trips through the memory side).
+//   * K is split over the workgroup's waves; each wave pulls its K slice of X into
+//     its own LDS region by DMA in whole cache lines, reads it once into registers as
+//     MFMA A fragments (lane (r, h): row r, k-block h) and keeps it for every tile of
+//     the workgroup.  X is therefore read once per CU, with no barrier in front of it.
+//   * A gated pair (silu(gate) * up) takes gate and up tiles of the same columns in
+//     one workgroup and applies the activation in its epilogue.
 //   * The codes of every (tile, group) of the wave's slice are requested up front:
 //     lane (c, h) loads bytes 16h .. 16h+15 of column c's group, the B operand of
 //     four v_mfma_f32_16x16x32_bf16 on the exact biased codes 128 + q (every product
