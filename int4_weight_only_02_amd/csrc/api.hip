@@ -451,8 +451,26 @@ int w4a16_linear_gated(const void *X, const uint32_t *qweight_gate, const void *
         return W4A16_ERR_WORKSPACE;
 
     hipError_t e;
+    const GemvPlan gp = M == 1 ? plan_gemv_gated(N, K) : GemvPlan{};
     const BlockPlan bp = plan_block_gated(N, K, M);
-    if (bp.ok) {
+    if (gp.ok) {
+        // M = 1 up to 40 groups: the decode kernel with the gate and up codes of the same
+        // columns in each wave
+        GemvArgs a{};
+        a.X = (const uint16_t *)X;
+        a.qw = qweight_gate;
+        a.scales = (const uint16_t *)scales_gate;
+        a.qz = qzeros_gate;
+        a.qw2 = qweight_up;
+        a.scales2 = (const uint16_t *)scales_up;
+        a.qz2 = qzeros_up;
+        a.N = N;
+        a.K = K;
+        a.G = K / kGroup;
+        a.Y = Y;
+        a.y_f32 = y_dtype == W4A16_OUT_F32;
+        e = launch_gemv(a, gp, (hipStream_t)stream);
+    } else if (bp.ok) {
         // 2 <= M <= 16, K whole: the draft-block kernel with gate and up tiles of the same
         // columns in each workgroup
         BlockArgs a{};

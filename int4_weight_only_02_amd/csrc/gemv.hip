@@ -121,9 +121,14 @@ __host__ __device__ constexpr int gemv_s_off(int W, int NG) { return W * NG * 25
 __host__ __device__ constexpr int gemv_r_off(int W, int NG) { return W * NG * 256 + W * 64; }
 __host__ __device__ constexpr int gemv_x_off(int W, int NG) { return W * NG * 256 + W * 128; }
 
-template <int GPW, int PL, bool AO>
+// GATED: a gated pair (the MLP's silu(x Wg^T) * (x Wu^T); Pith review, Referee Report,
+// Summary): every wave loads the codes of the gate and of the up grid for the same
+// columns and groups, against the one slice of X, and the workgroup stores
+// silu(gate) * up.  Red then holds [W][2][16] partials.
+template <int GPW, int PL, bool AO, bool GATED = false>
 __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
 {
+    static_assert(!(AO && GATED), "the gated pair has no act-order form");
     constexpr int TC = PL == 3 ? 5 : 16 / PL; // columns per workgroup
     constexpr int NG = GPW * PL;            // groups per wave
     constexpr int XR = NG / 4;              // X slots per lane
@@ -141,12 +146,15 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
     const uint32_t rowb = (uint32_t)(K / 2);
     u32x4_t *xs = (u32x4_t *)lds + w * NG * 16;             // this wave's X slots, fragment order
     float *Ss = (float *)(lds + gemv_s_off(W, NG)) + w * 16; // S of the wave's groups
-    float *red = (float *)(lds + gemv_r_off(W, NG));         // [W][16] lane partials
+    float *red = (float *)(lds + gemv_r_off(W, NG));         // [W][16] lane partials ([W][2][16] gated)
 
     const __amdgpu_buffer_rsrc_t rw = rsrc_g(a.qw, (uint32_t)a.N * rowb);
     const __amdgpu_buffer_rsrc_t rs = rsrc_g(a.scales, (uint32_t)a.N * (uint32_t)G * 2u);
     const __amdgpu_buffer_rsrc_t rz = rsrc_g(a.qz, (uint32_t)(a.N / 8) * (uint32_t)G * 4u);
     const __amdgpu_buffer_rsrc_t rx = rsrc_g(a.X, (uint32_t)K * 2u);
+    const __amdgpu_buffer_rsrc_t rw2 = GATED ? rsrc_g(a.qw2, (uint32_t)a.N * rowb) : rw;
+    const __amdgpu_buffer_rsrc_t rs2 = GATED ? rsrc_g(a.scales2, (uint32_t)a.N * (uint32_t)G * 2u) : rs;
+    const __amdgpu_buffer_rsrc_t rz2 = GATED ? rsrc_g(a.qz2, (uint32_t)(a.N / 8) * (uint32_t)G * 4u) : rz;
 
     // 1. X: slot s = r * 64 + lane holds X'[(g0 + s / 16) * 128 + 8 (s % 16) .. + 8].
     //    Plain: one 16-byte load per slot.  Act-order: the row by DMA into LDS (every
@@ -185,19 +193,26 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
     //    bytes 16h .. of group g0 + i PL + p of column n.  The small parameter loads go
     //    first, so that they do not queue behind the code loads
     static_assert(GPW <= 4, "one lane row per instruction");
-    uint32_t sv, zv;
-    {
+    constexpr int NP = GATED ? 2 : 1; // grids: the gate, then the up projection
+    uint32_t sv[NP], zv[NP];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
         const int g = g0 + h * PL + p;
         const bool live = h < GPW && g < G && plive;
-        sv = __builtin_amdgcn_raw_buffer_load_b16(rs, live ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobG, 0, 0);
-        zv = __builtin_amdgcn_raw_buffer_load_b32(rz, live ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobG, 0, 0);
+        sv[q] = __builtin_amdgcn_raw_buffer_load_b16(q ? rs2 : rs, live ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobG,
+                                                     0, 0);
+        zv[q] = __builtin_amdgcn_raw_buffer_load_b32(
+            q ? rz2 : rz, live ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobG, 0, 0);
     }
-    u32x4_t wv[GPW];
+    u32x4_t wv[NP][GPW];
 #pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-        const int g = g0 + i * PL + p;
-        wv[i] = ld16_g(rw, (g < G && plive) ? (uint32_t)n * rowb + (uint32_t)g * 64u + 16u * h : kOobG);
-    }
+    for (int q = 0; q < NP; ++q)
+#pragma unroll
+        for (int i = 0; i < GPW; ++i) {
+            const int g = g0 + i * PL + p;
+            wv[q][i] = ld16_g(q ? rw2 : rw,
+                              (g < G && plive) ? (uint32_t)n * rowb + (uint32_t)g * 64u + 16u * h : kOobG);
+        }
     asm volatile("" ::: "memory");
 
     if constexpr (AO) {
@@ -245,21 +260,25 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
     asm volatile("" : "+v"(bias));
     const int zsh = (n & 7) * 4;
     const int m = nid % PL;
-    float acc = 0.f;
+    float acc[NP];
 #pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-        if (g0 + i * PL < G) {
-            f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < NP; ++q) {
+        acc[q] = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const u32x4_t xf = xs[(i * PL + m) * 16 + 4 * h + j];
-                const uint32_t wj = j == 0 ? wv[i].x : j == 1 ? wv[i].y : j == 2 ? wv[i].z : wv[i].w;
-                d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf), frag_r(wj, mask, bias), d);
+        for (int i = 0; i < GPW; ++i) {
+            if (g0 + i * PL < G) {
+                f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const u32x4_t xf = xs[(i * PL + m) * 16 + 4 * h + j];
+                    const uint32_t wj = j == 0 ? wv[q][i].x : j == 1 ? wv[q][i].y : j == 2 ? wv[q][i].z : wv[q][i].w;
+                    d = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xf), frag_r(wj, mask, bias), d);
+                }
+                const bool live = g0 + i * PL + p < G && plive;
+                const float s = live ? f16_bits_to_f32((uint16_t)to_row0(sv[q], i)) : 0.f;
+                const float zb = -(float)(kCodeBias + ((to_row0(zv[q], i) >> zsh) & 15u));
+                acc[q] = fmaf(s, fmaf(zb, Ss[i * PL + p], pick<PL>(d, p)), acc[q]);
             }
-            const bool live = g0 + i * PL + p < G && plive;
-            const float s = live ? f16_bits_to_f32((uint16_t)to_row0(sv, i)) : 0.f;
-            const float zb = -(float)(kCodeBias + ((to_row0(zv, i) >> zsh) & 15u));
-            acc = fmaf(s, fmaf(zb, Ss[i * PL + p], pick<PL>(d, p)), acc);
         }
     }
 
@@ -268,27 +287,36 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
     //    waves k, k + 4, ... (all its reads in flight together), the four lane rows are
     //    added by two exchanges, then the parts p by log2(PL) more (PL = 3: lane c adds
     //    those of lanes c + 5 and c + 10)
-    if (lane < 16)
-        red[w * 16 + lane] = acc;
+    if (lane < 16) {
+#pragma unroll
+        for (int q = 0; q < NP; ++q)
+            red[(w * NP + q) * 16 + lane] = acc[q];
+    }
     __syncthreads();
     if (w == 0) {
         const int slot = lane & 15, k = lane >> 4;
-        float y = 0.f;
+        float yq[NP];
 #pragma unroll
-        for (int v4 = 0; v4 < kGemvMaxWaves; v4 += 4)
-            if (v4 < W)
-                y += v4 + k < W ? red[(v4 + k) * 16 + slot] : 0.f;
-        y += __shfl_xor(y, 16);
-        y += __shfl_xor(y, 32);
-        if constexpr (PL == 3) {
-            const float y1 = __shfl(y, (lane + TC) & 63), y2 = __shfl(y, (lane + 2 * TC) & 63);
-            y = (y + y1) + y2;
-        } else {
-            if constexpr (PL >= 2)
-                y += __shfl_xor(y, TC);
-            if constexpr (PL >= 4)
-                y += __shfl_xor(y, 2 * TC);
+        for (int q = 0; q < NP; ++q) {
+            float y = 0.f;
+#pragma unroll
+            for (int v4 = 0; v4 < kGemvMaxWaves; v4 += 4)
+                if (v4 < W)
+                    y += v4 + k < W ? red[((v4 + k) * NP + q) * 16 + slot] : 0.f;
+            y += __shfl_xor(y, 16);
+            y += __shfl_xor(y, 32);
+            if constexpr (PL == 3) {
+                const float y1 = __shfl(y, (lane + TC) & 63), y2 = __shfl(y, (lane + 2 * TC) & 63);
+                y = (y + y1) + y2;
+            } else {
+                if constexpr (PL >= 2)
+                    y += __shfl_xor(y, TC);
+                if constexpr (PL >= 4)
+                    y += __shfl_xor(y, 2 * TC);
+            }
+            yq[q] = y;
         }
+        const float y = GATED ? silu_f32(yq[0]) * yq[NP - 1] : yq[0];
         if (lane < TC) {
             const int col = blockIdx.x * TC + lane;
             if (a.y_f32)
@@ -318,6 +346,19 @@ GemvPlan plan_gemv_with(int N, int K, int gpw, int pl, int ao)
     return p;
 }
 
+// the gated pair at M = 1 (up to 40 groups): the (2, 2) plan, the wave partials of both
+// projections in LDS
+GemvPlan plan_gemv_gated(int N, int K)
+{
+    if (K / kGroup > 40)
+        return GemvPlan{};
+    GemvPlan p = plan_gemv_with(N, K, 2, 2, 0);
+    p.gated = 1;
+    p.lds_bytes = (size_t)gemv_r_off(p.waves, 4) + (size_t)p.waves * 128;
+    p.ok = p.ok && p.lds_bytes <= (size_t)kGemvMaxLds;
+    return p;
+}
+
 GemvPlan plan_gemv(int N, int K, int ao)
 {
     // measured on MI355X at M = 1 (graph replays over rotating weights): two groups of
@@ -341,11 +382,14 @@ hipError_t launch_gemv(const GemvArgs &args, const GemvPlan &p, hipStream_t stre
     GemvArgs a = args;
     a.waves = p.waves;
     const dim3 grid(p.grid), block(64 * p.waves);
-    const int v = p.gpw * 100 + p.pl * 10 + (p.ao ? 1 : 0);
+    const int v = (p.gated ? 1000 : 0) + p.gpw * 100 + p.pl * 10 + (p.ao ? 1 : 0);
     switch (v) {
 #define W4A16_GEMV_CASE(GPW, PL, AO)                                                                           \
     case GPW * 100 + PL * 10 + AO:                                                                             \
         hipLaunchKernelGGL((gemv_kernel<GPW, PL, AO != 0>), grid, block, p.lds_bytes, stream, a);              \
+        break;
+    case 1000 + 2 * 100 + 2 * 10:
+        hipLaunchKernelGGL((gemv_kernel<2, 2, false, true>), grid, block, p.lds_bytes, stream, a);
         break;
         W4A16_GEMV_CASE(2, 2, 0)
         W4A16_GEMV_CASE(2, 2, 1)

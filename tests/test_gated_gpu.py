@@ -60,10 +60,12 @@ def test_gated_full_size(dev, workload, jg, ju, ydt):
     print("  max|dY|/tol %.2e" % r)
 
 
-# 2 <= M <= 16 with K whole runs the draft-block kernel (one to three column tiles per
-# workgroup, one or two groups per wave, ragged tile groups); K split into parts or
-# more than three tiles per CU fall back to the small-M pair plan
-SHAPES = [(1, 16, 128), (2, 48, 640), (3, 528, 1280), (4, 2064, 2560), (5, 1040, 384), (6, 1040, 128),
+# M = 1 up to 40 groups runs the decode kernel (one group, 40 groups with a ragged last
+# wave; 41 groups fall back to the small-M pair plan); 2 <= M <= 16 with K whole runs
+# the draft-block kernel (one to three column tiles per workgroup, one or two groups per
+# wave, ragged tile groups); K split into parts or more than three tiles per CU fall
+# back to the small-M pair plan
+SHAPES = [(1, 16, 128), (1, 1040, 5120), (1, 528, 5248), (2, 48, 640), (3, 528, 1280), (4, 2064, 2560), (5, 1040, 384), (6, 1040, 128),
           (8, 336, 9728), (12, 12304, 1280), (16, 4112, 2560), (16, 2560, 9728), (17, 528, 1280), (40, 1040, 640),
           (64, 272, 4096), (65, 528, 1280), (130, 1040, 640), (2000, 4112, 256)]
 
