@@ -451,7 +451,7 @@ int w4a16_linear_gated(const void *X, const uint32_t *qweight_gate, const void *
         return W4A16_ERR_WORKSPACE;
 
     hipError_t e;
-    const GemvPlan gp = M == 1 ? plan_gemv_gated(N, K) : GemvPlan{};
+    const GemvPlan gp = M == 1 ? plan_gemv_pair(N, K, 1) : GemvPlan{};
     const BlockPlan bp = plan_block_gated(N, K, M);
     if (gp.ok) {
         // M = 1 up to 40 groups: the decode kernel with the gate and up codes of the same
@@ -615,6 +615,39 @@ int w4a16_linear_batch(const w4a16_problem *problems, int count, int M, int grou
             a.M = M;
             a.y_f32 = y_dtype == W4A16_OUT_F32;
             return launch_block(a, bp, (hipStream_t)stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+        }
+    }
+    if (M == 1) {
+        // two projections of one shape that read the same X (gate and up): the decode
+        // kernel with both grids in each wave, up to 40 groups
+        int qs[2], nq = 0;
+        for (int q = 0; q < count; ++q)
+            if (problems[q].N != 0 && nq < 2)
+                qs[nq++] = q;
+        int live = 0;
+        for (int q = 0; q < count; ++q)
+            live += problems[q].N != 0 ? 1 : 0;
+        if (live == 2) {
+            const w4a16_problem &p0 = problems[qs[0]], &p1 = problems[qs[1]];
+            const GemvPlan gp = (p0.X == p1.X && p0.N == p1.N && p0.K == p1.K) ? plan_gemv_pair(p0.N, p0.K, 2)
+                                                                               : GemvPlan{};
+            if (gp.ok) {
+                GemvArgs a{};
+                a.X = (const uint16_t *)p0.X;
+                a.qw = p0.qweight;
+                a.scales = (const uint16_t *)p0.scales;
+                a.qz = p0.qzeros;
+                a.qw2 = p1.qweight;
+                a.scales2 = (const uint16_t *)p1.scales;
+                a.qz2 = p1.qzeros;
+                a.N = p0.N;
+                a.K = p0.K;
+                a.G = p0.K / kGroup;
+                a.Y = p0.Y;
+                a.Y2 = p1.Y;
+                a.y_f32 = y_dtype == W4A16_OUT_F32;
+                return launch_gemv(a, gp, (hipStream_t)stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+            }
         }
     }
     SkinnyMulti mp{};

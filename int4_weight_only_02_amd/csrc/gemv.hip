@@ -121,14 +121,17 @@ __host__ __device__ constexpr int gemv_s_off(int W, int NG) { return W * NG * 25
 __host__ __device__ constexpr int gemv_r_off(int W, int NG) { return W * NG * 256 + W * 64; }
 __host__ __device__ constexpr int gemv_x_off(int W, int NG) { return W * NG * 256 + W * 128; }
 
-// GATED: a gated pair (the MLP's silu(x Wg^T) * (x Wu^T); Pith review, Referee Report,
-// Summary): every wave loads the codes of the gate and of the up grid for the same
-// columns and groups, against the one slice of X, and the workgroup stores
-// silu(gate) * up.  Red then holds [W][2][16] partials.
-template <int GPW, int PL, bool AO, bool GATED = false>
+// PAIR 1: a gated pair (the MLP's silu(x Wg^T) * (x Wu^T); Pith review, Referee Report,
+// Summary): every wave loads the codes of the gate and of the up grid (qw2, scales2,
+// qz2) for the same columns and groups, against the one slice of X, and the workgroup
+// stores silu(gate) * up.  PAIR 2: the same two contractions, stored as they are (Y and
+// Y2: a batch of two projections of one shape that read the same X).  Red then holds
+// [W][2][16] partials.
+template <int GPW, int PL, bool AO, int PAIR = 0>
 __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
 {
-    static_assert(!(AO && GATED), "the gated pair has no act-order form");
+    constexpr bool GATED = PAIR == 1;
+    static_assert(!(AO && PAIR), "the pairs have no act-order form");
     constexpr int TC = PL == 3 ? 5 : 16 / PL; // columns per workgroup
     constexpr int NG = GPW * PL;            // groups per wave
     constexpr int XR = NG / 4;              // X slots per lane
@@ -146,15 +149,15 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
     const uint32_t rowb = (uint32_t)(K / 2);
     u32x4_t *xs = (u32x4_t *)lds + w * NG * 16;             // this wave's X slots, fragment order
     float *Ss = (float *)(lds + gemv_s_off(W, NG)) + w * 16; // S of the wave's groups
-    float *red = (float *)(lds + gemv_r_off(W, NG));         // [W][16] lane partials ([W][2][16] gated)
+    float *red = (float *)(lds + gemv_r_off(W, NG));         // [W][16] lane partials ([W][2][16] pairs)
 
     const __amdgpu_buffer_rsrc_t rw = rsrc_g(a.qw, (uint32_t)a.N * rowb);
     const __amdgpu_buffer_rsrc_t rs = rsrc_g(a.scales, (uint32_t)a.N * (uint32_t)G * 2u);
     const __amdgpu_buffer_rsrc_t rz = rsrc_g(a.qz, (uint32_t)(a.N / 8) * (uint32_t)G * 4u);
     const __amdgpu_buffer_rsrc_t rx = rsrc_g(a.X, (uint32_t)K * 2u);
-    const __amdgpu_buffer_rsrc_t rw2 = GATED ? rsrc_g(a.qw2, (uint32_t)a.N * rowb) : rw;
-    const __amdgpu_buffer_rsrc_t rs2 = GATED ? rsrc_g(a.scales2, (uint32_t)a.N * (uint32_t)G * 2u) : rs;
-    const __amdgpu_buffer_rsrc_t rz2 = GATED ? rsrc_g(a.qz2, (uint32_t)(a.N / 8) * (uint32_t)G * 4u) : rz;
+    const __amdgpu_buffer_rsrc_t rw2 = PAIR ? rsrc_g(a.qw2, (uint32_t)a.N * rowb) : rw;
+    const __amdgpu_buffer_rsrc_t rs2 = PAIR ? rsrc_g(a.scales2, (uint32_t)a.N * (uint32_t)G * 2u) : rs;
+    const __amdgpu_buffer_rsrc_t rz2 = PAIR ? rsrc_g(a.qz2, (uint32_t)(a.N / 8) * (uint32_t)G * 4u) : rz;
 
     // 1. X: slot s = r * 64 + lane holds X'[(g0 + s / 16) * 128 + 8 (s % 16) .. + 8].
     //    Plain: one 16-byte load per slot.  Act-order: the row by DMA into LDS (every
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
     //    bytes 16h .. of group g0 + i PL + p of column n.  The small parameter loads go
     //    first, so that they do not queue behind the code loads
     static_assert(GPW <= 4, "one lane row per instruction");
-    constexpr int NP = GATED ? 2 : 1; // grids: the gate, then the up projection
+    constexpr int NP = PAIR ? 2 : 1; // grids: the first (gate), then the second (up)
     uint32_t sv[NP], zv[NP];
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
@@ -323,6 +326,12 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
                 ((float *)a.Y)[col] = y;
             else
                 ((uint16_t *)a.Y)[col] = f32_to_bf16_rne(y);
+            if constexpr (PAIR == 2) {
+                if (a.y_f32)
+                    ((float *)a.Y2)[col] = yq[1];
+                else
+                    ((uint16_t *)a.Y2)[col] = f32_to_bf16_rne(yq[1]);
+            }
         }
     }
 }
@@ -346,14 +355,14 @@ GemvPlan plan_gemv_with(int N, int K, int gpw, int pl, int ao)
     return p;
 }
 
-// the gated pair at M = 1 (up to 40 groups): the (2, 2) plan, the wave partials of both
-// projections in LDS
-GemvPlan plan_gemv_gated(int N, int K)
+// the gated pair (pair 1) or two outputs (pair 2) at M = 1, up to 40 groups: the (2, 2)
+// plan, the wave partials of both projections in LDS
+GemvPlan plan_gemv_pair(int N, int K, int pair)
 {
-    if (K / kGroup > 40)
+    if (K / kGroup > 40 || (pair != 1 && pair != 2))
         return GemvPlan{};
     GemvPlan p = plan_gemv_with(N, K, 2, 2, 0);
-    p.gated = 1;
+    p.pair = pair;
     p.lds_bytes = (size_t)gemv_r_off(p.waves, 4) + (size_t)p.waves * 128;
     p.ok = p.ok && p.lds_bytes <= (size_t)kGemvMaxLds;
     return p;
@@ -382,14 +391,17 @@ hipError_t launch_gemv(const GemvArgs &args, const GemvPlan &p, hipStream_t stre
     GemvArgs a = args;
     a.waves = p.waves;
     const dim3 grid(p.grid), block(64 * p.waves);
-    const int v = (p.gated ? 1000 : 0) + p.gpw * 100 + p.pl * 10 + (p.ao ? 1 : 0);
+    const int v = p.pair * 1000 + p.gpw * 100 + p.pl * 10 + (p.ao ? 1 : 0);
     switch (v) {
 #define W4A16_GEMV_CASE(GPW, PL, AO)                                                                           \
     case GPW * 100 + PL * 10 + AO:                                                                             \
         hipLaunchKernelGGL((gemv_kernel<GPW, PL, AO != 0>), grid, block, p.lds_bytes, stream, a);              \
         break;
     case 1000 + 2 * 100 + 2 * 10:
-        hipLaunchKernelGGL((gemv_kernel<2, 2, false, true>), grid, block, p.lds_bytes, stream, a);
+        hipLaunchKernelGGL((gemv_kernel<2, 2, false, 1>), grid, block, p.lds_bytes, stream, a);
+        break;
+    case 2000 + 2 * 100 + 2 * 10:
+        hipLaunchKernelGGL((gemv_kernel<2, 2, false, 2>), grid, block, p.lds_bytes, stream, a);
         break;
         W4A16_GEMV_CASE(2, 2, 0)
         W4A16_GEMV_CASE(2, 2, 1)

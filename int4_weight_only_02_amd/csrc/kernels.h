@@ -153,7 +153,7 @@ hipError_t launch_skinny_multi(SkinnyMulti &mp, int M, size_t ws_bytes, hipStrea
 // wave w taking the gpw * pl groups from w gpw pl.
 struct GemvPlan {
     int gpw, pl, ao;  // code loads per lane, group parts per instruction, act-order
-    int gated;        // the gated pair (silu(gate) * up), qw2 / scales2 / qz2 the up grid
+    int pair;         // 1: the gated pair (silu(gate) * up); 2: two outputs; qw2 / scales2 / qz2 the second grid
     int waves, grid;  // waves per workgroup (each NG = gpw * pl groups), N / (16 / pl)
     size_t lds_bytes;
     bool ok;          // false: the shape needs another path
@@ -164,16 +164,17 @@ struct GemvArgs {
     const uint32_t *qw;
     const uint16_t *scales;
     const uint32_t *qz;
-    const uint32_t *qw2;     // gated pair only: the up projection's grid
+    const uint32_t *qw2;     // pairs only: the second (up) projection's grid
     const uint16_t *scales2;
     const uint32_t *qz2;
+    void *Y2;                // two outputs: the second projection's
     int N, K, G;
     void *Y;
     int y_f32;
     int waves; // copied from the plan by launch_gemv
 };
 GemvPlan plan_gemv(int N, int K, int ao);
-GemvPlan plan_gemv_gated(int N, int K);
+GemvPlan plan_gemv_pair(int N, int K, int pair); // pair 1: gated, 2: two outputs
 GemvPlan plan_gemv_with(int N, int K, int gpw, int pl, int ao);
 hipError_t launch_gemv(const GemvArgs &a, const GemvPlan &p, hipStream_t stream);
 

@@ -116,3 +116,28 @@ def test_batch_empty_entries_and_errors(dev):
     assert w4.w4a16_linear_batch([]) == []
     with pytest.raises(w4.W4A16Error):
         w4.w4a16_linear_batch([p] * 9)
+
+
+@pytest.mark.parametrize("K,N", [(2560, 9728), (5120, 1040), (128, 16), (5248, 528)])
+@pytest.mark.parametrize("ydt", ["f32", "bf16"])
+def test_batch_pair_one_row(dev, K, N, ydt):
+    # two projections of one shape reading the same X at M = 1 (gate and up): one launch
+    # of the decode kernel with both grids in each wave up to 40 groups (41 groups take
+    # the general small-M batch); each output against the oracle, and bit-identical to
+    # the single call where the pair runs (the same per-projection sums in the same order)
+    print("batch pair M=1", K, N, ydt, flush=True)
+    dt = torch.float32 if ydt == "f32" else torch.bfloat16
+    d0 = synth.linear_inputs(300 + K + N, 1, N, K)
+    d1 = synth.linear_inputs(301 + K + N, 1, N, K)
+    d1 = dict(d1, X=d0["X"])
+    p0, (oqw0, oqz0) = _prep(d0, dev)
+    p1, (oqw1, oqz1) = _prep(d1, dev)
+    p1 = (p0[0],) + tuple(p1[1:])  # the same X tensor
+    y0, y1 = w4.w4a16_linear_batch([p0, p1], out_dtype=dt)
+    s0 = w4.w4a16_linear(*p0, out_dtype=dt)
+    s1 = w4.w4a16_linear(*p1, out_dtype=dt)
+    torch.cuda.synchronize()
+    for d, (oqw, oqz), Y in ((d0, (oqw0, oqz0), y0), (d1, (oqw1, oqz1), y1)):
+        check(Y, oracle.linear(d["X"], oqw, d["scales"], oqz), "pair K=%d N=%d %s" % (K, N, ydt))
+    if K // 128 <= 40:
+        assert torch.equal(y0, s0) and torch.equal(y1, s1)
