@@ -435,14 +435,15 @@ static size_t block_ws_bytes(int N, int T, int P)
 // Measured on MI355X at M = 16 (graph replays, K = 2560 .. 9728, N = 1024 .. 19456): K
 // stays whole up to 47 groups (every CU reads all of X, and the hand-off of partial
 // sums between parts costs more than the X it saves); longer K is cut into parts of
-// at most 16 groups, so each CU reads a part of X (at K = 9728: 5 parts of 8 waves,
-// 0.2 us faster than 4 or 6 parts, 3 us faster than 7 or 8).  The tile groups then
-// spread the (tile group, part) workgroups of the whole launch about once over the
-// CUs, at most 5 tiles each.
+// at most 32 groups (so that a part's waves, two groups each, stay within 16), and
+// each CU reads a part of X.  At K = 9728, N = 2560: 3 parts of 13 waves with 2 tiles
+// per workgroup, 9.8-10.1 us, against 10.6-11.0 us for 4 to 6 parts.  The tile groups
+// then spread the (tile group, part) workgroups of the whole launch about once over
+// the CUs, at most 5 tiles each.
 static int block_parts(int K)
 {
     const int G = K / kGroup;
-    return G < 48 ? 1 : (G + 15) / 16;
+    return G < 48 ? 1 : (G + 31) / 32;
 }
 
 // Per projection the tile-group size T and the parts of K P (block_choose, or the
