@@ -26,6 +26,20 @@ int check_dims(int M, int N, int K)
     return W4A16_OK;
 }
 
+// 2 <= M <= 16: the draft-block kernel holds each workgroup's tiles at once, so a
+// launch with more (tile group, part) workgroups than CUs runs in several rounds, each
+// staging X again.  There the streaming small-M kernel is faster wherever it keeps X in
+// LDS (measured on MI355X, M = 2 .. 16: K = 2560, N = 24576 .. 151936, 11.5-56.5 against
+// 15.0-64.8 us; K = 9728, N = 9728, M <= 6, 16.3-19.0 against 22.4-22.8 us); with X read
+// from L2 it is slower (the same shape at M >= 8: 30-41 against 23 us).
+bool block_first(const BlockPlan &bp, int M, int N, int K)
+{
+    if (bp.grid <= 256)
+        return true;
+    const int xlds = plan_skinny(M, N, K, 0).xlds;
+    return xlds != 1 && xlds != 2;
+}
+
 // covers both the single-call plan and the plan the same projection gets inside a
 // batched launch, so that the sum over a batch's projections always suffices
 size_t linear_ws(int M, int N, int K)
@@ -355,7 +369,7 @@ int w4a16_linear(const void *X, const uint32_t *qweight, const void *scales, con
         a.y_f32 = y_dtype == W4A16_OUT_F32;
         e = launch_gemv(a, gp, (hipStream_t)stream);
     } else if (M >= 2 && M <= 16 && (bp = plan_block(&N, &K, 1, M)).ok && bp.ws_bytes <= workspace_bytes &&
-               (bp.ws_bytes == 0 || workspace)) {
+               (bp.ws_bytes == 0 || workspace) && block_first(bp, M, N, K)) {
         BlockArgs a{};
         a.ws = (unsigned char *)workspace;
         a.pr[0].X = (const uint16_t *)X;

@@ -463,6 +463,19 @@ BlockPlan plan_block(const int *N, const int *K, int count, int M, int tmax_hint
         units += (long long)((N[q] + 15) / 16) * block_parts(K[q]);
     int Tl = (int)((units + kBlockCUs - 1) / kBlockCUs);
     Tl = Tl < 1 ? 1 : Tl > 5 ? 5 : Tl;
+    // each projection rounds its tile groups up: take one more tile per workgroup where
+    // that keeps the launch within one round of the CUs (K = 9728, N = 4096: 86 x 3
+    // workgroups of 3 tiles would leave two for a second round; 64 x 3 of 4 tiles do not)
+    for (;;) {
+        long long wgs = 0;
+        for (int q = 0; q < count; ++q) {
+            const int G = K[q] / kGroup, P = block_parts(K[q]);
+            wgs += (long long)(((N[q] + 15) / 16 + Tl - 1) / Tl) * (P > G ? G : P);
+        }
+        if (wgs <= kBlockCUs || Tl >= 5)
+            break;
+        ++Tl;
+    }
     for (int q = 0; q < count; ++q) {
         int T = Tl, P = block_parts(K[q]);
         if (tmax_hint > 0)

@@ -62,6 +62,26 @@ def test_batch_mixed_shapes(dev, M):
         check(Y, oracle.linear(d["X"], oqw, d["scales"], oqz), "M=%d K=%d N=%d" % (M, K, N))
 
 
+# two projections per launch through the draft-block kernel's multi-projection
+# instances: one group per wave with 1, 2 and 3 tiles per workgroup (K = 128), three
+# groups per wave (41 groups) with 1 and 2 tiles; ragged tile groups throughout
+MULTI = [[(128, 264), (128, 136)], [(128, 2560), (128, 2568)], [(128, 9728), (128, 1032)],
+         [(5248, 264), (640, 136)], [(5248, 2568), (640, 2056)]]
+
+
+@pytest.mark.parametrize("M", [3, 16])
+@pytest.mark.parametrize("j", range(len(MULTI)))
+def test_batch_block_instances(dev, M, j):
+    shapes = MULTI[j]
+    print("batch block instances M", M, shapes, flush=True)
+    datas = [synth.linear_inputs(2000 + 17 * M + 5 * j + q, M, N, K) for q, (K, N) in enumerate(shapes)]
+    probs, oras = zip(*[_prep(d, dev) for d in datas])
+    ys = w4.w4a16_linear_batch(list(probs), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for (K, N), d, (oqw, oqz), Y in zip(shapes, datas, oras, ys):
+        check(Y, oracle.linear(d["X"], oqw, d["scales"], oqz), "M=%d K=%d N=%d" % (M, K, N))
+
+
 def _dyadic(seed, M, N, K):
     rng = np.random.default_rng(seed)
     G = K // 128

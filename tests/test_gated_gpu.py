@@ -66,6 +66,7 @@ def test_gated_full_size(dev, workload, jg, ju, ydt):
 # wave, ragged tile groups); K split into parts or more than three tiles per CU fall
 # back to the small-M pair plan
 SHAPES = [(1, 16, 128), (1, 1040, 5120), (1, 528, 5248), (2, 48, 640), (3, 528, 1280), (4, 2064, 2560), (5, 1040, 384), (6, 1040, 128),
+          (3, 4112, 128), (5, 8208, 128),
           (8, 336, 9728), (12, 12304, 1280), (16, 4112, 2560), (16, 2560, 9728), (17, 528, 1280), (40, 1040, 640),
           (64, 272, 4096), (65, 528, 1280), (130, 1040, 640), (2000, 4112, 256)]
 

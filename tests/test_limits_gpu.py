@@ -52,9 +52,9 @@ def test_large_m_at_the_mk_limit(dev):
 
 @pytest.mark.parametrize("M", [16, 1])
 def test_small_m_at_the_nk_limit(dev, M):
-    # 838856 columns: a 1 GiB packed grid; M = 16 runs the draft-block kernel (10486
-    # workgroups of 5 tiles), M = 1 the decode kernel (104857 workgroups of 8 columns);
-    # the lm_head call below runs the stream plan
+    # 838856 columns: a 1 GiB packed grid; M = 16 runs the small-M kernel's stream plan
+    # (persistent workgroups over 52429 tiles), M = 1 the decode kernel (104857
+    # workgroups of 8 columns); the lm_head call below runs the stream plan too
     K = 2560
     N = (LIMIT // K) // 8 * 8
     print("limit N*K", M, N, K, flush=True)

@@ -66,7 +66,17 @@ SMALL = [(1, 8, 128), (1, 512, 512), (2, 136, 384), (3, 1032, 1280), (5, 264, 25
          # columns x 3 group parts (N a multiple of 1280, more than 40 groups) with a
          # ragged last wave
          (1, 264, 1408), (1, 136, 1536), (1, 40, 5888), (1, 2568, 6144), (1, 1032, 16384),
-         (1, 9736, 2560), (1, 3000, 640), (1, 16, 36864), (1, 1280, 5376), (1, 3840, 7808)]
+         (1, 9736, 2560), (1, 3000, 640), (1, 16, 36864), (1, 1280, 5376), (1, 3840, 7808),
+         # 2 <= M <= 16, the draft-block kernel's instances: one group per wave with 1, 2 and
+         # 3 tiles per workgroup; three groups per wave with 2 tiles; two with 2 tiles and K
+         # whole; 4 tiles per workgroup with K in 3 parts (257 tiles: 65 workgroups per part
+         # instead of 86, which would leave two for a second round)
+         (16, 264, 128), (8, 4800, 128), (16, 9608, 128), (16, 4808, 5248), (16, 4800, 2560),
+         (16, 4104, 9728),
+         # more workgroups than CUs: the small-M kernel where it keeps X in LDS (whole, a
+         # persistent walk over 4097 tiles), the draft-block kernel in two rounds where the
+         # small-M kernel would read X from L2
+         (4, 9736, 9728), (16, 24584, 2560), (3, 65544, 256), (8, 9736, 9728)]
 
 
 @pytest.mark.parametrize("M,N,K", SMALL)
