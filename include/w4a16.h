@@ -273,6 +273,8 @@ int w4a16_linear_gated(const void *X, const uint32_t *qweight_gate, const void *
  * launch.  This call computes Y_q = X_q * W_q^T for every entry of
  * problems[0 .. count) as w4a16_linear would (same grid, same reading, same
  * accuracy bound), in one launch when M <= 64 (one after another when M > 64).
+ * At M = 1, entries that share X and K run as one launch of the decode kernel, each
+ * with its own run of workgroups, and give the same bits as single calls.
  *   problems  host array of count descriptors (read during the call only); each
  *             names its own device tensors X [M][K] bf16, qweight, scales, qzeros,
  *             Y [M][N], and its N and K (the layouts of w4a16_linear)

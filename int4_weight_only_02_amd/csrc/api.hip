@@ -663,6 +663,39 @@ int w4a16_linear_batch(const w4a16_problem *problems, int count, int M, int grou
                 return launch_gemv(a, gp, (hipStream_t)stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
             }
         }
+        // projections that read the same X (q, k and v): the decode kernel, each
+        // projection its own run of workgroups in one launch
+        GemvArgs a{};
+        int gn[W4A16_MAX_BATCH], wg0[W4A16_MAX_BATCH], nm = 0;
+        bool same = live >= 1 && live <= kMaxProblemsGemv;
+        const w4a16_problem *first = nullptr;
+        for (int q = 0; q < count && same; ++q) {
+            const w4a16_problem &pr = problems[q];
+            if (pr.N == 0)
+                continue;
+            if (!first)
+                first = &pr;
+            same = pr.X == first->X && pr.K == first->K;
+            a.pr[nm].qw = pr.qweight;
+            a.pr[nm].scales = (const uint16_t *)pr.scales;
+            a.pr[nm].qz = pr.qzeros;
+            a.pr[nm].Y = pr.Y;
+            a.pr[nm].N = pr.N;
+            gn[nm++] = pr.N;
+        }
+        if (same) {
+            const GemvPlan gp = plan_gemv_multi(gn, first->K, nm, wg0);
+            if (gp.ok) {
+                for (int q = 0; q < nm; ++q)
+                    a.pr[q].wg0 = wg0[q];
+                a.count = nm;
+                a.X = (const uint16_t *)first->X;
+                a.K = first->K;
+                a.G = first->K / kGroup;
+                a.y_f32 = y_dtype == W4A16_OUT_F32;
+                return launch_gemv(a, gp, (hipStream_t)stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+            }
+        }
     }
     SkinnyMulti mp{};
     int bn[W4A16_MAX_BATCH], bk[W4A16_MAX_BATCH], btw[W4A16_MAX_BATCH], nb = 0;

@@ -126,11 +126,13 @@ __host__ __device__ constexpr int gemv_x_off(int W, int NG) { return W * NG * 25
 // qz2) for the same columns and groups, against the one slice of X, and the workgroup
 // stores silu(gate) * up.  PAIR 2: the same two contractions, stored as they are (Y and
 // Y2: a batch of two projections of one shape that read the same X).  Red then holds
-// [W][2][16] partials.
+// [W][2][16] partials.  PAIR 3: several projections of the same X and K in one launch
+// (a.pr, a.count), each with its own run of workgroups; a workgroup finds its projection
+// with one compare per entry and then works as a single launch would.
 template <int GPW, int PL, bool AO, int PAIR = 0>
 __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
 {
-    constexpr bool GATED = PAIR == 1;
+    constexpr bool GATED = PAIR == 1, MULTI = PAIR == 3;
     static_assert(!(AO && PAIR), "the pairs have no act-order form");
     constexpr int TC = PL == 3 ? 5 : 16 / PL; // columns per workgroup
     constexpr int NG = GPW * PL;            // groups per wave
@@ -144,20 +146,38 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
     const int nid = lane & 15, h = lane >> 4;
     const int c = nid % TC, p = nid / TC;
     const bool plive = p < PL; // PL = 3: lane column 15 idle
-    const int n = blockIdx.x * TC + c;
+    const uint32_t *qwp = a.qw, *qzp = a.qz;
+    const uint16_t *sp = a.scales;
+    void *Yp = a.Y;
+    int N = a.N, bid = blockIdx.x;
+    if constexpr (MULTI) {
+        int q = 0;
+#pragma unroll
+        for (int j = 1; j < kMaxProblemsGemv; ++j)
+            q += (j < a.count && bid >= a.pr[j].wg0) ? 1 : 0;
+        const GemvArgs::Prob &pr = a.pr[q];
+        qwp = pr.qw;
+        sp = pr.scales;
+        qzp = pr.qz;
+        Yp = pr.Y;
+        N = pr.N;
+        bid -= pr.wg0;
+    }
+    const int n = bid * TC + c;
     const int g0 = w * NG;
     const uint32_t rowb = (uint32_t)(K / 2);
     u32x4_t *xs = (u32x4_t *)lds + w * NG * 16;             // this wave's X slots, fragment order
     float *Ss = (float *)(lds + gemv_s_off(W, NG)) + w * 16; // S of the wave's groups
     float *red = (float *)(lds + gemv_r_off(W, NG));         // [W][16] lane partials ([W][2][16] pairs)
 
-    const __amdgpu_buffer_rsrc_t rw = rsrc_g(a.qw, (uint32_t)a.N * rowb);
-    const __amdgpu_buffer_rsrc_t rs = rsrc_g(a.scales, (uint32_t)a.N * (uint32_t)G * 2u);
-    const __amdgpu_buffer_rsrc_t rz = rsrc_g(a.qz, (uint32_t)(a.N / 8) * (uint32_t)G * 4u);
+    constexpr int NP = (PAIR == 1 || PAIR == 2) ? 2 : 1; // grids per wave: the first (gate), then the second (up)
+    const __amdgpu_buffer_rsrc_t rw = rsrc_g(qwp, (uint32_t)N * rowb);
+    const __amdgpu_buffer_rsrc_t rs = rsrc_g(sp, (uint32_t)N * (uint32_t)G * 2u);
+    const __amdgpu_buffer_rsrc_t rz = rsrc_g(qzp, (uint32_t)(N / 8) * (uint32_t)G * 4u);
     const __amdgpu_buffer_rsrc_t rx = rsrc_g(a.X, (uint32_t)K * 2u);
-    const __amdgpu_buffer_rsrc_t rw2 = PAIR ? rsrc_g(a.qw2, (uint32_t)a.N * rowb) : rw;
-    const __amdgpu_buffer_rsrc_t rs2 = PAIR ? rsrc_g(a.scales2, (uint32_t)a.N * (uint32_t)G * 2u) : rs;
-    const __amdgpu_buffer_rsrc_t rz2 = PAIR ? rsrc_g(a.qz2, (uint32_t)(a.N / 8) * (uint32_t)G * 4u) : rz;
+    const __amdgpu_buffer_rsrc_t rw2 = NP == 2 ? rsrc_g(a.qw2, (uint32_t)N * rowb) : rw;
+    const __amdgpu_buffer_rsrc_t rs2 = NP == 2 ? rsrc_g(a.scales2, (uint32_t)N * (uint32_t)G * 2u) : rs;
+    const __amdgpu_buffer_rsrc_t rz2 = NP == 2 ? rsrc_g(a.qz2, (uint32_t)(N / 8) * (uint32_t)G * 4u) : rz;
 
     // 1. X: slot s = r * 64 + lane holds X'[(g0 + s / 16) * 128 + 8 (s % 16) .. + 8].
     //    Plain: one 16-byte load per slot.  Act-order: the row by DMA into LDS (every
@@ -196,16 +216,19 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
     //    bytes 16h .. of group g0 + i PL + p of column n.  The small parameter loads go
     //    first, so that they do not queue behind the code loads
     static_assert(GPW <= 4, "one lane row per instruction");
-    constexpr int NP = PAIR ? 2 : 1; // grids: the first (gate), then the second (up)
     uint32_t sv[NP], zv[NP];
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
         const int g = g0 + h * PL + p;
         const bool live = h < GPW && g < G && plive;
-        sv[q] = __builtin_amdgcn_raw_buffer_load_b16(q ? rs2 : rs, live ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobG,
-                                                     0, 0);
-        zv[q] = __builtin_amdgcn_raw_buffer_load_b32(
-            q ? rz2 : rz, live ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobG, 0, 0);
+        // the offsets go through a register, so that the compiler keeps one unconditional
+        // load each instead of a branch per case (whose register reuse could make the
+        // second load wait for the load of X)
+        uint32_t so = live ? ((uint32_t)n * (uint32_t)G + g) * 2u : kOobG;
+        uint32_t zo = live ? ((uint32_t)(n >> 3) * (uint32_t)G + g) * 4u : kOobG;
+        asm volatile("" : "+v"(so), "+v"(zo));
+        sv[q] = __builtin_amdgcn_raw_buffer_load_b16(q ? rs2 : rs, so, 0, 0);
+        zv[q] = __builtin_amdgcn_raw_buffer_load_b32(q ? rz2 : rz, zo, 0, 0);
     }
     u32x4_t wv[NP][GPW];
 #pragma unroll
@@ -216,7 +239,10 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
             wv[q][i] = ld16_g(q ? rw2 : rw,
                               (g < G && plive) ? (uint32_t)n * rowb + (uint32_t)g * 64u + 16u * h : kOobG);
         }
+    // every load of the wave is issued before any arithmetic on X (the scheduler would
+    // otherwise start the sums of X first and make the code loads wait for X to land)
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 
     if constexpr (AO) {
         // the DMA and the perm loads were issued before the 3 GPW loads above:
@@ -321,11 +347,11 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
         }
         const float y = GATED ? silu_f32(yq[0]) * yq[NP - 1] : yq[0];
         if (lane < TC) {
-            const int col = blockIdx.x * TC + lane;
+            const int col = bid * TC + lane;
             if (a.y_f32)
-                ((float *)a.Y)[col] = y;
+                ((float *)Yp)[col] = y;
             else
-                ((uint16_t *)a.Y)[col] = f32_to_bf16_rne(y);
+                ((uint16_t *)Yp)[col] = f32_to_bf16_rne(y);
             if constexpr (PAIR == 2) {
                 if (a.y_f32)
                     ((float *)a.Y2)[col] = yq[1];
@@ -384,6 +410,31 @@ GemvPlan plan_gemv(int N, int K, int ao)
     return plan_gemv_with(N, K, 3, 4, ao);
 }
 
+GemvPlan plan_gemv_multi(const int *N, int K, int count, int *wg0)
+{
+    if (count < 1 || count > kMaxProblemsGemv)
+        return GemvPlan{};
+    bool by5 = true;
+    for (int q = 0; q < count; ++q)
+        by5 = by5 && N[q] % (5 * 256) == 0;
+    // the single-projection choice, with five columns per workgroup only where every N
+    // is a whole number of rounds of the CUs
+    const int G = K / kGroup;
+    GemvPlan p = G <= 40 ? plan_gemv_with(N[0], K, 2, 2, 0)
+                 : by5   ? plan_gemv_with(N[0], K, 4, 3, 0)
+                         : plan_gemv_with(N[0], K, 3, 4, 0);
+    const int tc = p.pl == 3 ? 5 : 16 / p.pl;
+    int wg = 0;
+    for (int q = 0; q < count; ++q) {
+        p.ok = p.ok && N[q] >= 1 && N[q] % tc == 0;
+        wg0[q] = wg;
+        wg += N[q] / tc;
+    }
+    p.pair = 3;
+    p.grid = wg;
+    return p;
+}
+
 hipError_t launch_gemv(const GemvArgs &args, const GemvPlan &p, hipStream_t stream)
 {
     if (!p.ok)
@@ -402,6 +453,15 @@ hipError_t launch_gemv(const GemvArgs &args, const GemvPlan &p, hipStream_t stre
         break;
     case 2000 + 2 * 100 + 2 * 10:
         hipLaunchKernelGGL((gemv_kernel<2, 2, false, 2>), grid, block, p.lds_bytes, stream, a);
+        break;
+    case 3000 + 2 * 100 + 2 * 10:
+        hipLaunchKernelGGL((gemv_kernel<2, 2, false, 3>), grid, block, p.lds_bytes, stream, a);
+        break;
+    case 3000 + 3 * 100 + 4 * 10:
+        hipLaunchKernelGGL((gemv_kernel<3, 4, false, 3>), grid, block, p.lds_bytes, stream, a);
+        break;
+    case 3000 + 4 * 100 + 3 * 10:
+        hipLaunchKernelGGL((gemv_kernel<4, 3, false, 3>), grid, block, p.lds_bytes, stream, a);
         break;
         W4A16_GEMV_CASE(2, 2, 0)
         W4A16_GEMV_CASE(2, 2, 1)

@@ -151,9 +151,11 @@ hipError_t launch_skinny_multi(SkinnyMulti &mp, int M, size_t ws_bytes, hipStrea
 // ---------------------------------------------------------------- gemv (M = 1)
 // Workgroup b owns the TC = 16 / pl columns from b TC and all of K; its waves split K,
 // wave w taking the gpw * pl groups from w gpw pl.
+constexpr int kMaxProblemsGemv = 8; // projections per multi launch (pair 3)
 struct GemvPlan {
     int gpw, pl, ao;  // code loads per lane, group parts per instruction, act-order
-    int pair;         // 1: the gated pair (silu(gate) * up); 2: two outputs; qw2 / scales2 / qz2 the second grid
+    int pair;         // 1: the gated pair (silu(gate) * up); 2: two outputs; qw2 / scales2 / qz2 the second grid;
+                      // 3: several projections of one X (GemvArgs::pr), each its own workgroups
     int waves, grid;  // waves per workgroup (each NG = gpw * pl groups), N / (16 / pl)
     size_t lds_bytes;
     bool ok;          // false: the shape needs another path
@@ -172,8 +174,21 @@ struct GemvArgs {
     void *Y;
     int y_f32;
     int waves; // copied from the plan by launch_gemv
+    // pair 3: projection q owns workgroups wg0 .. of the launch (pr[0].wg0 = 0); every
+    // projection reads the same X and has the same K
+    struct Prob {
+        const uint32_t *qw;
+        const uint16_t *scales;
+        const uint32_t *qz;
+        void *Y;
+        int N, wg0;
+    } pr[kMaxProblemsGemv];
+    int count;
 };
 GemvPlan plan_gemv(int N, int K, int ao);
+// pair 3: count projections of the same K (and X); wg0[q] receives projection q's first
+// workgroup.  !ok unless every N fits the plan's columns per workgroup
+GemvPlan plan_gemv_multi(const int *N, int K, int count, int *wg0);
 GemvPlan plan_gemv_pair(int N, int K, int pair); // pair 1: gated, 2: two outputs
 GemvPlan plan_gemv_with(int N, int K, int gpw, int pl, int ao);
 hipError_t launch_gemv(const GemvArgs &a, const GemvPlan &p, hipStream_t stream);

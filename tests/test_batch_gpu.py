@@ -142,9 +142,10 @@ def test_batch_empty_entries_and_errors(dev):
 @pytest.mark.parametrize("ydt", ["f32", "bf16"])
 def test_batch_pair_one_row(dev, K, N, ydt):
     # two projections of one shape reading the same X at M = 1 (gate and up): one launch
-    # of the decode kernel with both grids in each wave up to 40 groups (41 groups take
-    # the general small-M batch); each output against the oracle, and bit-identical to
-    # the single call where the pair runs (the same per-projection sums in the same order)
+    # of the decode kernel with both grids in each wave up to 40 groups (41 groups: one
+    # launch of it with a run of workgroups per projection); each output against the
+    # oracle, and bit-identical to the single call (the same per-projection sums in the
+    # same order)
     print("batch pair M=1", K, N, ydt, flush=True)
     dt = torch.float32 if ydt == "f32" else torch.bfloat16
     d0 = synth.linear_inputs(300 + K + N, 1, N, K)
@@ -159,5 +160,49 @@ def test_batch_pair_one_row(dev, K, N, ydt):
     torch.cuda.synchronize()
     for d, (oqw, oqz), Y in ((d0, (oqw0, oqz0), y0), (d1, (oqw1, oqz1), y1)):
         check(Y, oracle.linear(d["X"], oqw, d["scales"], oqz), "pair K=%d N=%d %s" % (K, N, ydt))
-    if K // 128 <= 40:
-        assert torch.equal(y0, s0) and torch.equal(y1, s1)
+    assert torch.equal(y0, s0) and torch.equal(y1, s1)
+
+
+# projections that read the same X at M = 1 (q, k and v of a decode step): one launch of
+# the decode kernel, a run of workgroups per projection.  (K, [N, ...]): 20 groups (8
+# columns per workgroup); 76 groups with every N a multiple of 1280 (5 columns) and with
+# N a multiple of 4 only (4 columns); eight projections of one group, the last ragged;
+# a single projection between empty entries
+MULTI_ONE_X = [(2560, [4096, 1024, 1024]), (9728, [2560, 1280, 5120]), (9728, [2568, 1032]),
+               (128, [8, 16, 24, 32, 40, 48, 56, 1000]), (640, [0, 520, 0])]
+
+
+@pytest.mark.parametrize("j", range(len(MULTI_ONE_X)))
+@pytest.mark.parametrize("ydt", ["f32", "bf16"])
+def test_batch_multi_one_row(dev, j, ydt):
+    K, Ns = MULTI_ONE_X[j]
+    print("batch one X M=1", K, Ns, ydt, flush=True)
+    dt = torch.float32 if ydt == "f32" else torch.bfloat16
+    X = None
+    probs, cases = [], []
+    Xt = None
+    for q, N in enumerate(Ns):
+        d = synth.linear_inputs(700 + 13 * j + q, 1, max(N, 8), K)
+        if X is None:
+            X = d["X"]
+            Xt = dev_inputs(d, dev)["X"]
+        d = dict(d, X=X)
+        if N == 0:
+            pq = (Xt, torch.empty((0, K // 8), dtype=torch.int32, device=dev),
+                  torch.empty((0, K // 128), dtype=torch.float16, device=dev),
+                  torch.empty((0, K // 128), dtype=torch.int32, device=dev))
+            oq = (None, None)
+        else:
+            pq, oq = _prep(d, dev)
+            pq = (Xt,) + tuple(pq[1:])  # the same X tensor
+        probs.append(pq)
+        cases.append((N, d, oq))
+    ys = w4.w4a16_linear_batch(probs, out_dtype=dt)
+    singles = [w4.w4a16_linear(*pq, out_dtype=dt) if pq[1].shape[0] else None for pq in probs]
+    torch.cuda.synchronize()
+    for (N, d, (oqw, oqz)), Y, S in zip(cases, ys, singles):
+        if N == 0:
+            assert Y.shape == (1, 0)
+            continue
+        check(Y, oracle.linear(d["X"], oqw, d["scales"], oqz), "one X K=%d N=%d %s" % (K, N, ydt))
+        assert torch.equal(Y, S)
