@@ -138,6 +138,17 @@ def test_batch_graph_replays(dev):
     _check_replays(dev, ws, lambda: w4.w4a16_linear_batch(probs, outs=ys, workspace=ws), ys)
 
 
+def test_batch_one_x_graph_replays(dev):
+    # M = 1, three projections reading one X (q, k, v): one launch of the decode kernel
+    print("graph batch one X M=1", flush=True)
+    shapes = [(2560, 4096), (2560, 1024), (2560, 1024)]  # (K, N)
+    probs = [_packed(71 + q, 1, N, K, dev) for q, (K, N) in enumerate(shapes)]
+    probs = [(probs[0][0],) + p[1:] for p in probs]
+    ws = _workspace(dev, 1 << 24)
+    ys = [torch.empty((1, N), dtype=torch.bfloat16, device=dev) for K, N in shapes]
+    _check_replays(dev, ws, lambda: w4.w4a16_linear_batch(probs, outs=ys, workspace=ws), ys)
+
+
 def test_actorder_graph_replays(dev):
     M, N, K = 16, 2560, 9728
     print("graph act-order", M, N, K, flush=True)
