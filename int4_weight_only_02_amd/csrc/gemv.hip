@@ -327,16 +327,33 @@ __global__ __launch_bounds__(64 * kGemvMaxWaves) void gemv_kernel(GemvArgs a)
         float yq[NP];
 #pragma unroll
         for (int q = 0; q < NP; ++q) {
+            // every read in flight at once (a wave index past W reads wave 0's slot and
+            // adds zero), then the sum in wave order
+            float rv[kGemvMaxWaves / 4];
+#pragma unroll
+            for (int j = 0; j < kGemvMaxWaves / 4; ++j) {
+                const int v = 4 * j + k;
+                rv[j] = red[((v < W ? v : 0) * NP + q) * 16 + slot];
+            }
             float y = 0.f;
 #pragma unroll
-            for (int v4 = 0; v4 < kGemvMaxWaves; v4 += 4)
-                if (v4 < W)
-                    y += v4 + k < W ? red[((v4 + k) * NP + q) * 16 + slot] : 0.f;
-            y += __shfl_xor(y, 16);
-            y += __shfl_xor(y, 32);
+            for (int j = 0; j < kGemvMaxWaves / 4; ++j)
+                y += 4 * j + k < W ? rv[j] : 0.f;
+            // the four lane rows: two lane swaps (VALU, no LDS round trip); each lane
+            // adds its own value and its partner's, as an exchange with lane ^ 16, then
+            // lane ^ 32, would
+            {
+                const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+                y = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+                const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+                y = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+            }
             if constexpr (PL == 3) {
                 const float y1 = __shfl(y, (lane + TC) & 63), y2 = __shfl(y, (lane + 2 * TC) & 63);
                 y = (y + y1) + y2;
+            } else if constexpr (PL == 2) {
+                // lane ^ 8 within the row: a rotation of the row by 8 lanes
+                y += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(y), 0x128, 0xF, 0xF, false));
             } else {
                 if constexpr (PL >= 2)
                     y += __shfl_xor(y, TC);
